@@ -1,0 +1,381 @@
+"""Pins of the CPU oracle to facts the pages and the mathematics fix, independent of the oracle.
+
+Every check here compares the oracle with something other than itself: values the pages print,
+closed forms, library routines (numpy rounding, torch's float8 / bfloat16 / float16 casts, scipy's
+Student-t quantile), invariants, and brute force on tiny inputs.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from conftest import read_golden
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def _block_from_golden():
+    gd = read_golden("worked_block.txt")
+    raw = np.array([int(b, 16) for b in gd["bytes"]], dtype=np.uint8)
+    return gd, raw
+
+
+# ------------------------------------------------------------------------------------------------
+# the printed block ("What NVFP4 is and how it differs from NF4", stored-block figure)
+# ------------------------------------------------------------------------------------------------
+def test_worked_block_decodes_to_printed_values():
+    gd, raw = _block_from_golden()
+    want = np.array([float(v) for v in gd["values"]])
+    q = oracle.QTensor(raw.reshape(1, 8), np.array([[0x38]], dtype=np.uint8), np.float32(1.0))  # s = 1, g = 1
+    got = oracle.dequantize(q, "f64").ravel()
+    assert np.array_equal(got, want)
+    # the printed 4-bit codes, low nibble first
+    codes = [int(c, 2) for c in gd["codes"]]
+    assert [int(raw[j // 2] >> (4 * (j % 2))) & 15 for j in range(16)] == codes
+    assert [oracle.e2m1_value(c) for c in codes] == list(want)
+
+
+def test_worked_block_named_bytes():
+    # the three bytes the benchmark statement names explicitly
+    pairs = {0xDC: (-2.0, -3.0), 0x5F: (-6.0, 3.0), 0x01: (0.5, 0.0)}
+    for byte, (lo, hi) in pairs.items():
+        q = oracle.QTensor(np.array([[byte] * 8], dtype=np.uint8), np.array([[0x38]], dtype=np.uint8), 1.0)
+        got = oracle.dequantize(q, "f64").ravel()
+        assert (got[0], got[1]) == (lo, hi)
+
+
+def test_nibble_order_control():
+    # Swapping the nibbles of the printed block changes 14 of its 16 values (only 0x?? with equal
+    # nibbles would survive; none here).  On a whole matrix the swap raises the relative error to
+    # about sqrt(2), as the page's nibble-order control reports (9.47 % -> 141 %).
+    gd, raw = _block_from_golden()
+    swapped = ((raw << 4) | (raw >> 4)).astype(np.uint8)
+    s = np.array([[0x38]], dtype=np.uint8)
+    a = oracle.dequantize(oracle.QTensor(raw.reshape(1, 8), s, 1.0), "f64").ravel()
+    b = oracle.dequantize(oracle.QTensor(swapped.reshape(1, 8), s, 1.0), "f64").ravel()
+    assert np.sum(a != b) == 16
+    w = np.random.default_rng(7).standard_normal((256, 512)).astype(np.float32) * 0.02
+    q, _ = oracle.quantize(w)
+    ok = oracle.dequantize(q, "f64")
+    qs = oracle.QTensor(((q.codes << 4) | (q.codes >> 4)).astype(np.uint8), q.scales, q.g)
+    bad = oracle.dequantize(qs, "f64")
+    e_ok = np.linalg.norm(w - ok) / np.linalg.norm(w)
+    e_bad = np.linalg.norm(w - bad) / np.linalg.norm(w)
+    assert 0.05 < e_ok < 0.15
+    assert abs(e_bad - math.sqrt(2)) < 0.05
+
+
+def test_worked_weight_value():
+    # weight = E2M1 x block scale x global scale: -2.0 x 4.5 x 0.0017439 = -0.01570
+    gd, _ = _block_from_golden()
+    assert oracle.e4m3_value(0x49) == float(gd["block_scale"][0])
+    g = np.float32(float(gd["global_scale"][0]))
+    q = oracle.QTensor(np.array([[0x0C] + [0] * 7], dtype=np.uint8), np.array([[0x49]], dtype=np.uint8), g)
+    w = oracle.dequantize(q, "f32")[0, 0]
+    assert w == np.float32(np.float32(-2.0 * 4.5) * g)
+    assert abs(float(w) - float(gd["first_weight"][0])) <= 5e-6
+
+
+def test_worked_base_encodes_to_printed_code():
+    # The base weight -0.01941 under block scale 4.5 and global 0.0017439 lands on code 1100 (-2.0).
+    gd, _ = _block_from_golden()
+    code = oracle.element_code(float(gd["first_weight_base"][0]), 4.5, float(np.float32(0.0017439)))
+    assert code == int(gd["codes"][0], 2)
+
+
+# ------------------------------------------------------------------------------------------------
+# storage cost and range
+# ------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("shape", [(1, 16), (64, 256), (3, 4096), (17, 48)])
+def test_storage_is_4_5_bits(shape):
+    q, _ = oracle.quantize(np.random.default_rng(1).standard_normal(shape).astype(np.float32))
+    bits = (q.codes.nbytes + q.scales.nbytes) * 8
+    assert bits == 4.5 * shape[0] * shape[1]
+
+
+def test_range_and_amax_element():
+    rng = np.random.default_rng(3)
+    for trial in range(20):
+        w = (rng.standard_t(3, size=(32, 64)) * 10 ** rng.uniform(-6, 3)).astype(np.float32)
+        q, _ = oracle.quantize(w)
+        vals = np.array([oracle.e2m1_value(c) for c in range(16)])
+        lo, hi = q.codes & 15, q.codes >> 4
+        assert np.abs(vals[lo]).max() <= 6 and np.abs(vals[hi]).max() <= 6
+        r, c = np.unravel_index(np.argmax(np.abs(w)), w.shape)
+        assert q.scales[r, c // 16] == 0x7E
+        code = (q.codes[r, c // 2] >> (4 * (c % 2))) & 15
+        assert code & 7 == 7 and (code >> 3) == (w[r, c] < 0)
+        assert q.g == np.float32(np.abs(w).max() / np.float32(2688.0))
+
+
+# ------------------------------------------------------------------------------------------------
+# the two grids against library rounding
+# ------------------------------------------------------------------------------------------------
+def _e2m1_numpy(y):
+    """Round-half-to-even onto {0,.5,1,1.5,2,3,4,6} with numpy's rint, saturating at 6."""
+    y = np.asarray(y, dtype=np.float64)
+    out = np.where(y < 2, np.rint(y * 2) / 2, np.where(y < 4, np.rint(y), 2 * np.rint(y / 2)))
+    return np.minimum(out, 6.0)
+
+
+def test_e2m1_rounding_against_numpy_rint():
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    mids = (mags[1:] + mags[:-1]) / 2
+    probes = [0.0, 6.0, 7.0, 1e30, np.float32(np.inf)]
+    for m in np.concatenate([mags, mids]):
+        m32 = np.float32(m)
+        probes += [m32, np.nextafter(m32, np.float32(0)), np.nextafter(m32, np.float32(10))]
+    rnd = np.random.default_rng(11)
+    probes = np.concatenate([np.array(probes, dtype=np.float32),
+                             rnd.uniform(0, 8, 200000).astype(np.float32),
+                             (10.0 ** rnd.uniform(-45, 1, 50000)).astype(np.float32)])
+    idx = oracle.e2m1_index_array(probes)
+    want = _e2m1_numpy(np.where(np.isinf(probes), 1e300, probes))
+    assert np.array_equal(mags[idx], want)
+
+
+def test_e4m3_table_against_torch():
+    b = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = b.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.e4m3_value(i) for i in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    m = ~np.isnan(ref)
+    assert np.array_equal(got[m], ref[m])
+    assert oracle.e4m3_value(0x7E) == 448.0 and math.isnan(oracle.e4m3_value(0x7F))
+    assert oracle.e4m3_value(0x01) == 2.0 ** -9
+
+
+def test_e4m3_rounding_against_torch_cast():
+    vals = np.array([oracle.e4m3_value(i) for i in range(0x7F)], dtype=np.float64)
+    mids = (vals[1:] + vals[:-1]) / 2
+    probes = []
+    for m in np.concatenate([vals, mids]):
+        m32 = np.float32(m)
+        probes += [m32, np.nextafter(m32, np.float32(0)), np.nextafter(m32, np.float32(1e4))]
+    rnd = np.random.default_rng(12)
+    probes = np.concatenate([np.array(probes, dtype=np.float32),
+                             (2.0 ** rnd.uniform(-12, 8.8, 200000)).astype(np.float32)])
+    probes = probes[probes < 464]  # torch's cast has no saturation above the last midpoint
+    got = oracle.e4m3_encode_array(probes)
+    ref = torch.from_numpy(probes).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref)
+    # saturation: everything from the 448/480 midpoint up, including +inf, gives 0x7E
+    big = np.array([464, 465, 1000, 3e38, np.inf], dtype=np.float32)
+    assert np.all(oracle.e4m3_encode_array(big) == 0x7E)
+
+
+def test_f32_to_bf16_against_torch():
+    rnd = np.random.default_rng(13)
+    x = np.concatenate([rnd.standard_normal(100000).astype(np.float32),
+                        (rnd.integers(0, 2 ** 16, 50000) << 16 | 0x8000).astype(np.uint32).view(np.float32),
+                        np.array([0.0, -0.0, 1e-40, -1e-40, 3.4e38], dtype=np.float32)])
+    x = x[np.isfinite(x)]
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.f32_to_bf16_bits(x), want)
+
+
+def test_widen_f16_against_numpy():
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(4096, 16)
+    got = oracle.widen(h, oracle.F16)
+    want = h.view(np.float16).astype(np.float32)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    m = ~np.isnan(want)
+    assert np.array_equal(got[m].view(np.uint32), want[m].view(np.uint32))
+
+
+def test_widen_e4m3_with_scale_against_torch():
+    b = np.arange(256, dtype=np.uint32).astype(np.uint8).reshape(16, 16)
+    sc = np.float32(0.0123)
+    got = oracle.widen(b, oracle.E4M3, float(sc))
+    want = (torch.from_numpy(b).view(torch.float8_e4m3fn).to(torch.float32) * torch.tensor(sc)).numpy()
+    m = ~np.isnan(want)
+    assert np.array_equal(np.isnan(got), ~m)
+    assert np.array_equal(got[m], want[m])
+    # a missing weight_scale means 1.0
+    assert np.array_equal(oracle.widen(b, oracle.E4M3)[m],
+                          torch.from_numpy(b).view(torch.float8_e4m3fn).to(torch.float32).numpy()[m])
+
+
+# ------------------------------------------------------------------------------------------------
+# brute force on tiny inputs and invariants of the quantizer
+# ------------------------------------------------------------------------------------------------
+def test_block_scale_is_nearest_e4m3_of_ratio():
+    rnd = np.random.default_rng(21)
+    for _ in range(2000):
+        g = np.float32(10.0 ** rnd.uniform(-8, 2))
+        bamax = np.float32(float(g) * 6 * 10.0 ** rnd.uniform(-4, 2.8))
+        t = np.float32(bamax / np.float32(np.float32(6.0) * g))
+        want = 0x7E if t >= 464 else int(torch.tensor([t]).to(torch.float8_e4m3fn).view(torch.uint8)[0])
+        assert oracle.block_scale_byte(float(bamax), float(g)) == want
+
+
+def test_codes_are_nearest_grid_values_brute_force():
+    # For every element, the chosen E2M1 magnitude is the nearest grid point to |v| / (s g) computed
+    # exactly, unless |v| / (s g) sits within 1e-6 (relative) of a midpoint, where the fp32
+    # reciprocal-multiply may land on either side.
+    rnd = np.random.default_rng(22)
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    mids = (mags[1:] + mags[:-1]) / 2
+    for trial in range(300):
+        rows, nblk = 2, 3
+        w = (rnd.standard_normal((rows, 16 * nblk)) * 10.0 ** rnd.uniform(-5, 2)).astype(np.float32)
+        w[rnd.random(w.shape) < 0.1] = 0.0
+        q, _ = oracle.quantize(w)
+        for r in range(rows):
+            for c in range(16 * nblk):
+                s = oracle.e4m3_value(int(q.scales[r, c // 16]))
+                code = (int(q.codes[r, c // 2]) >> (4 * (c % 2))) & 15
+                assert (code >> 3) == int(np.signbit(w[r, c]))
+                if s == 0:
+                    assert code & 7 == 0
+                    continue
+                x = abs(float(w[r, c])) / (s * float(q.g))
+                if np.any(np.abs(x - mids) <= 1e-6 * max(x, 1e-30)):
+                    continue
+                nearest = np.argmin(np.abs(mags - min(x, 6.0)))
+                assert code & 7 == nearest, (x, code)
+
+
+def test_round_trip_is_identity():
+    # Codes and scales that dequantize to a tensor whose amax is 6 * 448 * g, with g a power of two:
+    # quantizing the expanded tensor (with amax fixed to 2688 g) returns the same bits.
+    rnd = np.random.default_rng(23)
+    for trial in range(20):
+        rows, cols = 8, 128
+        g = np.float32(2.0 ** rnd.integers(-30, 0))
+        codes = rnd.integers(0, 256, (rows, cols // 2), dtype=np.uint8)
+        scales = rnd.integers(1, 0x7F, (rows, cols // 16), dtype=np.uint8)
+        scales[0, 0] = 0x7E
+        # every block carries a +-6 in its first element
+        codes[:, ::8] = (codes[:, ::8] & 0xF0) | (0x7 | (rnd.integers(0, 2, (rows, cols // 16)) << 3)).astype(np.uint8)
+        q = oracle.QTensor(codes, scales, g)
+        w = oracle.dequantize(q, "f32")
+        q2, flags = oracle.quantize(w, amax=float(np.float32(2688.0) * g))
+        assert flags == 0 and q2.g == g
+        assert np.array_equal(q2.scales, scales)
+        assert np.array_equal(q2.codes, codes)
+
+
+def test_global_amax_is_numpy_max_and_zero_tensor():
+    rnd = np.random.default_rng(24)
+    w = rnd.standard_t(2, size=(50, 160)).astype(np.float32)
+    q, _ = oracle.quantize(w)
+    assert q.g == np.float32(np.float32(np.abs(w).max()) / np.float32(2688))
+    z, flags = oracle.quantize(np.zeros((4, 32), dtype=np.float32))
+    assert z.g == 0 and not z.scales.any() and not z.codes.any() and flags == 0
+    nz = -np.zeros((4, 32), dtype=np.float32)
+    z2, _ = oracle.quantize(nz)
+    assert np.all(z2.codes == 0x88)  # sign of -0 kept
+
+
+def test_nonfinite_input_flagged():
+    w = np.ones((2, 32), dtype=np.float32)
+    w[1, 5] = np.nan
+    assert oracle.quantize(w)[1] & 1
+    w[1, 5] = -np.inf
+    assert oracle.quantize(w)[1] & 1
+    b = np.zeros((1, 16), dtype=np.uint8)
+    b[0, 3] = 0x7F
+    assert oracle.quantize(b, oracle.E4M3, 1.0)[1] & 1
+
+
+def test_static_amax_clips():
+    # With a calibrated amax below the data's, large elements saturate at +-6 x 448 x g.
+    w = np.linspace(-10, 10, 64, dtype=np.float32).reshape(2, 32)
+    q, _ = oracle.quantize(w, amax=1.0)
+    d = oracle.dequantize(q, "f64")
+    assert np.max(np.abs(d)) == pytest.approx(6 * 448 * float(q.g))
+    assert q.g == np.float32(np.float32(1.0) / np.float32(2688))
+
+
+def test_expansion_is_single_rounding_of_exact_product():
+    rnd = np.random.default_rng(25)
+    codes = rnd.integers(0, 256, (16, 64), dtype=np.uint8)
+    scales = rnd.integers(0, 0x7F, (16, 8), dtype=np.uint8)
+    for g in [np.float32(0.0017439), np.float32(3.1e-39), np.float32(1.7e35)]:
+        q = oracle.QTensor(codes, scales, g)
+        f32 = oracle.dequantize(q, "f32")
+        c = np.where(np.arange(128) % 2 == 0, codes.repeat(2, 1) & 15, codes.repeat(2, 1) >> 4)
+        cs = np.array([oracle.e2m1_value(i) for i in range(16)], dtype=np.float32)[c] * \
+            np.array([oracle.e4m3_value(i) for i in range(128)], dtype=np.float32)[scales.repeat(16, 1)]
+        want = (cs * g).astype(np.float32)  # e2m1*s is exact in fp32; one fp32 multiply by g
+        assert np.array_equal(f32.view(np.uint32), want.view(np.uint32))
+        bf = oracle.dequantize(q, "bf16")
+        assert np.array_equal(bf, torch.from_numpy(want).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+
+
+# ------------------------------------------------------------------------------------------------
+# GEMM reference
+# ------------------------------------------------------------------------------------------------
+def test_gemm_one_hot_rows_reproduce_expansion():
+    rnd = np.random.default_rng(31)
+    w = rnd.standard_normal((48, 96)).astype(np.float32)
+    q, _ = oracle.quantize(w)
+    a = np.zeros((96, 96), dtype=np.float32)
+    a[np.arange(96), np.arange(96)] = 1.0
+    a_bits = oracle.f32_to_bf16_bits(a)
+    c = oracle.gemm_w4a16(a_bits, q)
+    assert np.array_equal(c.astype(np.float32), oracle.dequantize(q, "f32").T)
+
+
+def test_gemm_definition_brute_force_and_zero_weight():
+    rnd = np.random.default_rng(32)
+    a_bits = oracle.f32_to_bf16_bits(rnd.standard_normal((3, 32)).astype(np.float32))
+    q, _ = oracle.quantize(rnd.standard_normal((5, 32)).astype(np.float32))
+    c = oracle.gemm_w4a16(a_bits, q)
+    a = oracle.widen(a_bits, oracle.BF16).astype(np.float64)
+    w = oracle.dequantize(q, "f64")
+    for m in range(3):
+        for n in range(5):
+            assert c[m, n] == pytest.approx(sum(a[m, k] * w[n, k] for k in range(32)), rel=1e-14, abs=1e-300)
+    qz, _ = oracle.quantize(np.zeros((5, 32), dtype=np.float32))
+    assert not oracle.gemm_w4a16(a_bits, qz).any()
+
+
+def test_gemm_error_metric_floor():
+    cref = np.array([[1.0, -1.0, 1e-9]])
+    c = cref + np.array([[1e-4, 0, 5e-6]])
+    # the near-zero output is judged against 1e-2 of its row's largest magnitude
+    assert oracle.gemm_error(c, cref) == pytest.approx(5e-4)
+
+
+# ------------------------------------------------------------------------------------------------
+# percentile calibration
+# ------------------------------------------------------------------------------------------------
+def test_rank_nearest_rank_definition():
+    assert oracle.rank(99.9, 217088) == 216871
+    assert oracle.rank(100.0, 10) == 10
+    assert oracle.rank(50.0, 4) == 2
+    assert oracle.rank(1e-9, 1000) == 1
+    for n in [1, 7, 1000, 4096]:
+        perm = np.random.default_rng(n).permutation(np.arange(1, n + 1)).astype(np.float32).reshape(n, 1)
+        pct, mx = oracle.amax_percentile(perm, 99.9)
+        assert pct[0] == math.ceil(0.999 * n) and mx[0] == n
+
+
+def test_percentile_against_numpy_sort():
+    rnd = np.random.default_rng(41)
+    x = (rnd.standard_t(3, size=(1000, 12)) * rnd.choice([-1, 1], size=(1000, 12))).astype(np.float32)
+    x[5, 3] = -0.0
+    for p in [0.1, 50, 99, 99.9, 100]:
+        pct, mx = oracle.amax_percentile(x, p)
+        srt = np.sort(np.abs(x), axis=0)
+        k = math.ceil(p * 1000 / 100)
+        assert np.array_equal(pct, srt[k - 1]) and np.array_equal(mx, srt[-1])
+        pt, mt = oracle.amax_percentile(x, p, per_channel=False)
+        assert pt[0] == np.sort(np.abs(x).ravel())[math.ceil(p * x.size / 100) - 1] and mt[0] == np.abs(x).max()
+
+
+def test_percentile_student_t_closed_form():
+    # |t_3| has its 99.9 % point at the two-sided 0.1 % quantile of Student-t(3), 12.924.
+    # Over 217 088 rows the per-channel estimate has a standard error of about 0.30.
+    scipy_stats = pytest.importorskip("scipy.stats")
+    q = scipy_stats.t.ppf(1 - 0.0005, 3)
+    assert q == pytest.approx(12.924, abs=1e-3)
+    x = np.random.default_rng(5000).standard_t(3, size=(53 * 4096, 32)).astype(np.float32)
+    pct, mx = oracle.amax_percentile(x, 99.9)
+    assert np.all(np.abs(pct - q) < 1.3)
+    assert abs(pct.mean() - q) < 0.25
+    assert np.all(mx >= pct)
