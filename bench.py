@@ -1,0 +1,194 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 hot path on one MI355X.
+
+One step runs every operation of the path once, at the Qwen-Image attention-projection shapes
+(weight 3072 x 3072, 4096 tokens x 3072 channels):
+  quantize     W fp32 -> NVFP4 (run-time amax)                     [headline: GB/s]
+  requantize   W as FP8 E4M3 + per-tensor scale -> NVFP4
+  dequantize   NVFP4 W -> bf16
+  act_quantize A bf16 -> NVFP4 (dynamic, per-tensor run-time amax)
+  gemm_w4a16   C = A . W_hat^T, bf16 activations                    [headline: TFLOP/s]
+  gemm_w4a4    C = A_hat . W_hat^T, NVFP4 activations
+  gemv_w4a16   the first 2 rows of A against W (memory-bound form)
+  percentile   per-channel p99.9 and max of |A|
+Inputs are resident in HBM before timing; the step rotates over several input sets whose total
+size exceeds the 256 MB Infinity Cache, so repeated steps do not hit in cache.  Each operation is
+bracketed by events on the stream it runs on; the dominant kernel's roofline uses those times.
+
+Prints one JSON line.  Flags: --gpus (1 only), --steps, --warmup, --no-cpu-baseline.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 quantize GB/s; NVFP4-weight GEMM TFLOP/s at Qwen-Image shapes (1 GPU)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+M_TOK, N_OUT, K_IN = 4096, 3072, 3072
+GEMV_M = 2
+ROTATE_MIN_BYTES = 320 << 20
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the NVFP4 path here is a single-GPU kernel library "
+              "(row-sharding across GPUs needs only an all-reduce(max) of amax); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_gemm_nvfp4_amd as nv
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- inputs (synthetic, seeded), resident in HBM ----
+    w_np = synth.attn_proj_weight(N_OUT, K_IN)
+    a_bits = synth.attn_proj_activations(M_TOK, K_IN)
+    w8_np, w8_scale = synth.fp8_tensorwise(w_np)
+    w0 = torch.from_numpy(w_np).to(dev)
+    a0 = torch.from_numpy(a_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    w80 = torch.from_numpy(w8_np).to(dev)
+    set_bytes = w0.numel() * 4 + a0.numel() * 2 + w80.numel()
+    nsets = max(2, -(-ROTATE_MIN_BYTES // set_bytes))
+    sets = [(w0.clone(), a0.clone(), w80.clone()) for _ in range(nsets)]
+    del w0, a0, w80
+    src_scale = torch.tensor([w8_scale], dtype=torch.float32, device=dev)
+
+    # ---- outputs and workspaces, allocated once ----
+    qw = nv.NVFP4Tensor.empty(N_OUT, K_IN, dev)
+    qw8 = nv.NVFP4Tensor.empty(N_OUT, K_IN, dev)
+    qa = nv.NVFP4Tensor.empty(M_TOK, K_IN, dev)
+    wd = torch.empty((N_OUT, K_IN), dtype=torch.bfloat16, device=dev)
+    c16 = torch.empty((M_TOK, N_OUT), dtype=torch.float32, device=dev)
+    c4 = torch.empty((M_TOK, N_OUT), dtype=torch.float32, device=dev)
+    cv = torch.empty((GEMV_M, N_OUT), dtype=torch.float32, device=dev)
+    qws = torch.empty(nv.workspace_size(nv.OP_QUANTIZE, 0, 0), dtype=torch.uint8, device=dev)
+    qws2 = torch.empty_like(qws)
+    qws3 = torch.empty_like(qws)
+
+    ops = ["quantize", "requantize", "dequantize", "act_quantize", "gemm_w4a16", "gemm_w4a4", "gemv_w4a16",
+           "percentile"]
+
+    def step(i, events=None):
+        w, a, w8 = sets[i % nsets]
+        e = events
+        if e: e[0].record()
+        nv.quantize(w, out=qw, workspace=qws)
+        if e: e[1].record()
+        nv.quantize(w8, src_scale=src_scale, out=qw8, workspace=qws2)
+        if e: e[2].record()
+        nv.dequantize(qw, out=wd)
+        if e: e[3].record()
+        nv.quantize(a, out=qa, workspace=qws3)
+        if e: e[4].record()
+        nv.gemm(a, qw, out=c16)
+        if e: e[5].record()
+        nv.gemm(qa, qw, out=c4)
+        if e: e[6].record()
+        nv.gemm(a[:GEMV_M], qw, out=cv)
+        if e: e[7].record()
+        nv.amax_percentile(a, 99.9, per_channel=True)
+        if e: e[8].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    op_ms = {op: float(np.mean([evs[s][j].elapsed_time(evs[s][j + 1]) for s in range(args.steps)]))
+             for j, op in enumerate(ops)}
+
+    nW, nA = N_OUT * K_IN, M_TOK * K_IN
+    work = {  # algorithmic bytes (codec / memory-bound ops) or flops (GEMMs)
+        "quantize": ("GB/s", nW * 4.5625 + 4, HBM_PEAK_GBS),
+        "requantize": ("GB/s", nW * 1.5625 + 4, HBM_PEAK_GBS),
+        "dequantize": ("GB/s", nW * 2.5625, HBM_PEAK_GBS),
+        "act_quantize": ("GB/s", nA * 2.5625 + 4, HBM_PEAK_GBS),
+        "gemm_w4a16": ("TFLOP/s", 2.0 * M_TOK * N_OUT * K_IN, BF16_MFMA_PEAK_TFLOPS),
+        "gemm_w4a4": ("TFLOP/s", 2.0 * M_TOK * N_OUT * K_IN, BF16_MFMA_PEAK_TFLOPS),
+        "gemv_w4a16": ("GB/s", nW * 0.5625 + GEMV_M * K_IN * 2 + GEMV_M * N_OUT * 4, HBM_PEAK_GBS),
+        "percentile": ("GB/s", nA * 2.0, HBM_PEAK_GBS),
+    }
+    op_report = {}
+    for op in ops:
+        unit, amount, peak = work[op]
+        rate = amount / (op_ms[op] * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
+        op_report[op] = {"ms": round(op_ms[op], 5), "rate": round(rate, 2), "unit": unit,
+                         "frac_of_peak": round(rate / peak, 4)}
+
+    gemm_ms = op_ms["gemm_w4a16"]
+    dom = max(ops, key=lambda o: op_ms[o])
+    d_unit, d_amount, d_peak = work[dom]
+    d_rate = d_amount / (op_ms[dom] * 1e-3) / (1e9 if d_unit == "GB/s" else 1e12)
+    roofline = {"bound": "mfma" if d_unit == "TFLOP/s" else "hbm", "kernel": dom, "achieved": round(d_rate, 2),
+                "peak": d_peak, "unit": d_unit, "frac": round(d_rate / d_peak, 4), "traffic": None}
+
+    q_gbs = work["quantize"][1] / (op_ms["quantize"] * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(q_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "Qwen-Image attention projection: W 3072x3072 fp32 N(0,0.02^2); A 4096x3072 bf16 N(0,1) "
+                        "with 3 of 3072 channels x20; W also as FP8 E4M3 tensorwise; every NVFP4 hot-path op once "
+                        "per step",
+            "M": M_TOK, "N": N_OUT, "K": K_IN, "gemv_m": GEMV_M, "rotating_input_sets": nsets,
+            "rotating_bytes": nsets * set_bytes,
+        },
+        "gemm_tflops": round(2.0 * M_TOK * N_OUT * K_IN / (gemm_ms * 1e-3) / 1e12, 2),
+        "ops": op_report,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w_np)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w_np):
+    """The oracle's quantizer (plain scalar C, one thread) on the same 3072 x 3072 fp32 weight,
+    repeated until about 10 s of CPU time have passed."""
+    import oracle
+    n_bytes = w_np.size * 4.5625 + 4
+    reps, t = 0, 0.0
+    while t < 10.0 and reps < 20:
+        t0 = time.perf_counter()
+        oracle.quantize(w_np)
+        t += time.perf_counter() - t0
+        reps += 1
+    return {"value": round(n_bytes * reps / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} x quantize of the 3072x3072 fp32 weight (oracle C, single thread), {t:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,191 @@
+"""bit_gemm_nvfp4_amd -- NVFP4 quantization, expansion, NVFP4-weight GEMM and percentile
+calibration on AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libnvfp4.so`` (C ABI in ``include/nvfp4.h``).  This module only
+marshals arguments: every step of the computation runs in the library's HIP kernels.  PyTorch is
+used for device memory and the current stream.  There is no fallback path: if the library is
+missing, importing this package fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnvfp4.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m bit_gemm_nvfp4_amd.build` first")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+# ------------------------------------------------------------------------------------------------
+# C ABI declarations
+# ------------------------------------------------------------------------------------------------
+NVFP4_F32, NVFP4_BF16, NVFP4_F16, NVFP4_E4M3 = 0, 1, 2, 3
+OP_QUANTIZE, OP_DEQUANTIZE, OP_GEMM, OP_PERCENTILE = 0, 1, 2, 3
+STATUS_NAMES = ["NVFP4_OK", "NVFP4_ERR_NULL", "NVFP4_ERR_SHAPE", "NVFP4_ERR_ALIGN", "NVFP4_ERR_DTYPE",
+                "NVFP4_ERR_WORKSPACE", "NVFP4_ERR_ARG", "NVFP4_ERR_DEVICE", "NVFP4_ERR_LAUNCH"]
+EXPORTED = ["nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm", "amax_percentile", "nvfp4_workspace_size",
+            "nvfp4_status_string"]
+
+
+class CTensor(ctypes.Structure):
+    """Mirror of `nvfp4_tensor`."""
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("global_scale", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+_P, _I64, _I32, _SZ, _D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_double
+_PT = ctypes.POINTER(CTensor)
+lib.nvfp4_quantize.argtypes = [_P, _I32, _I64, _P, _P, _PT, _P, _P, _SZ, _P]
+lib.nvfp4_quantize.restype = _I32
+lib.nvfp4_dequantize.argtypes = [_PT, _P, _I32, _I64, _P]
+lib.nvfp4_dequantize.restype = _I32
+lib.nvfp4_gemm.argtypes = [_P, _PT, _I64, _I64, _PT, _P, _I64, _P, _SZ, _P]
+lib.nvfp4_gemm.restype = _I32
+lib.amax_percentile.argtypes = [_P, _I32, _I64, _I64, _I64, _D, _I32, _P, _P, _P, _P, _SZ, _P]
+lib.amax_percentile.restype = _I32
+lib.nvfp4_workspace_size.argtypes = [_I32, _I64, _I64, _I64]
+lib.nvfp4_workspace_size.restype = _SZ
+lib.nvfp4_status_string.argtypes = [_I32]
+lib.nvfp4_status_string.restype = ctypes.c_char_p
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        name = STATUS_NAMES[status] if 0 <= status < len(STATUS_NAMES) else str(status)
+        super().__init__(f"{where}: {name} ({lib.nvfp4_status_string(status).decode()})")
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise NVFP4Error(status, where)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+_DT = {torch.float32: NVFP4_F32, torch.bfloat16: NVFP4_BF16, torch.float16: NVFP4_F16,
+       torch.float8_e4m3fn: NVFP4_E4M3, torch.uint8: NVFP4_E4M3}
+
+
+# ------------------------------------------------------------------------------------------------
+# NVFP4 tensor
+# ------------------------------------------------------------------------------------------------
+@dataclass
+class NVFP4Tensor:
+    """Packed NVFP4 tensor of logical shape [rows, cols]: codes [rows, cols/2] uint8 (element 2j
+    in the low nibble of byte j), scales [rows, cols/16] uint8 (E4M3 bits), global_scale [1] fp32."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    global_scale: torch.Tensor
+
+    @property
+    def shape(self):
+        return (self.codes.shape[0], self.codes.shape[1] * 2)
+
+    @staticmethod
+    def empty(rows: int, cols: int, device) -> "NVFP4Tensor":
+        return NVFP4Tensor(torch.empty((rows, cols // 2), dtype=torch.uint8, device=device),
+                           torch.empty((rows, cols // 16), dtype=torch.uint8, device=device),
+                           torch.empty(1, dtype=torch.float32, device=device))
+
+    def c(self) -> CTensor:
+        r, c = self.shape
+        return CTensor(self.codes.data_ptr(), self.scales.data_ptr(), self.global_scale.data_ptr(), r, c)
+
+
+def workspace_size(op: int, rows: int, cols: int, k: int = 0) -> int:
+    return int(lib.nvfp4_workspace_size(op, rows, cols, k))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor | None:
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device) if nbytes > 0 else None
+
+
+# ------------------------------------------------------------------------------------------------
+# entry points
+# ------------------------------------------------------------------------------------------------
+def quantize(x: torch.Tensor, amax: torch.Tensor | None = None, src_scale: torch.Tensor | None = None,
+             flags: torch.Tensor | None = None, out: NVFP4Tensor | None = None,
+             workspace: torch.Tensor | None = None) -> NVFP4Tensor:
+    """Quantize a 2-D device tensor (fp32, bf16, fp16, or float8_e4m3fn / uint8 E4M3 bytes) to NVFP4.
+    amax: optional device fp32 [1] static amax; src_scale: optional device fp32 [1] per-tensor scale
+    of an E4M3 source; flags: optional device int32 [1] (bit 0 = non-finite input)."""
+    assert x.dim() == 2 and x.is_cuda
+    rows, cols = x.shape
+    if out is None:
+        out = NVFP4Tensor.empty(rows, cols, x.device)
+    ct = out.c()
+    ct.rows, ct.cols = rows, cols
+    if workspace is None and amax is None:
+        workspace = _workspace(workspace_size(OP_QUANTIZE, rows, cols), x.device)
+    st = lib.nvfp4_quantize(_ptr(x), _DT[x.dtype], x.stride(0) if rows > 0 else cols, _ptr(src_scale), _ptr(amax),
+                            ctypes.byref(ct), _ptr(flags), _ptr(workspace),
+                            0 if workspace is None else workspace.numel(), _stream(x.device))
+    _check(st, "nvfp4_quantize")
+    return out
+
+
+def dequantize(q: NVFP4Tensor, dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Expand NVFP4 to bf16 or fp32: w = e2m1 x block scale x global scale."""
+    rows, cols = q.shape
+    if out is None:
+        out = torch.empty((rows, cols), dtype=dtype, device=q.codes.device)
+    ct = q.c()
+    st = lib.nvfp4_dequantize(ctypes.byref(ct), _ptr(out), _DT[out.dtype], out.stride(0) if rows > 0 else cols,
+                              _stream(q.codes.device))
+    _check(st, "nvfp4_dequantize")
+    return out
+
+
+def gemm(a: torch.Tensor | NVFP4Tensor, w: NVFP4Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """C [M, N] fp32 = A . W_hat^T.  `a` is a bf16 [M, K] tensor (W4A16) or an NVFP4Tensor (W4A4)."""
+    n, k = w.shape
+    device = w.codes.device
+    if isinstance(a, NVFP4Tensor):
+        m = a.shape[0]
+        a_ct, a_ptr, lda = ctypes.byref(a.c()), None, k
+    else:
+        assert a.dtype == torch.bfloat16 and a.dim() == 2
+        m = a.shape[0]
+        lda = a.stride(0)
+        if a.numel() == 0:  # the W4A16 form is selected by a non-NULL pointer, even with no elements
+            a = torch.empty(8, dtype=torch.bfloat16, device=device)
+            lda = (k + 7) // 8 * 8 or 8
+        a_ct, a_ptr = None, _ptr(a)
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=device)
+    ws_bytes = workspace_size(OP_GEMM, m, n, k)
+    ws = _workspace(ws_bytes, device)
+    wct = w.c()
+    st = lib.nvfp4_gemm(a_ptr, a_ct, m, lda, ctypes.byref(wct), _ptr(out), out.stride(0) if m > 0 else n, _ptr(ws),
+                        ws_bytes, _stream(device))
+    _check(st, "nvfp4_gemm")
+    return out
+
+
+def amax_percentile(x: torch.Tensor, p: float = 99.9, per_channel: bool = True,
+                    flags: torch.Tensor | None = None, with_max: bool = True):
+    """Nearest-rank p-th percentile (and maximum) of |x| per column, or over the whole tensor."""
+    assert x.dim() == 2 and x.is_cuda
+    rows, cols = x.shape
+    n_out = cols if per_channel else 1
+    pct = torch.empty(n_out, dtype=torch.float32, device=x.device)
+    mx = torch.empty(n_out, dtype=torch.float32, device=x.device) if with_max else None
+    ws_bytes = workspace_size(OP_PERCENTILE, rows, cols, 1 if per_channel else 0)
+    ws = _workspace(ws_bytes, x.device)
+    st = lib.amax_percentile(_ptr(x), _DT[x.dtype], rows, cols, x.stride(0), float(p), 1 if per_channel else 0,
+                             _ptr(pct), _ptr(mx), _ptr(flags), _ptr(ws), ws_bytes, _stream(x.device))
+    _check(st, "amax_percentile")
+    return pct, mx

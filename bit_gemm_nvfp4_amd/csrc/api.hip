@@ -1,0 +1,204 @@
+// C ABI of libnvfp4.so: argument validation and dispatch to the gfx950 kernels.
+//
+// Every entry point validates all of its arguments before enqueuing anything, so an error status
+// means no work was queued.  No entry point synchronizes, allocates or keeps a pointer.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "internal.h"
+#include "nvfp4.h"
+
+namespace nvfp4 {
+
+__global__ void k_fill_zero_f32(float *c, int64_t rows, int64_t cols, int64_t ld) {
+    const int64_t n = rows * cols;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        c[(i / cols) * ld + i % cols] = 0.0f;
+}
+
+hipError_t launch_fill_zero_f32(float *c, int64_t rows, int64_t cols, int64_t ld, hipStream_t stream) {
+    if (rows > 0 && cols > 0) {
+        int64_t grid = (rows * cols + 255) / 256;
+        if (grid > 4096) grid = 4096;
+        hipLaunchKernelGGL(k_fill_zero_f32, dim3((unsigned)grid), dim3(256), 0, stream, c, rows, cols, ld);
+    }
+    return hipGetLastError();
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// Per-device cache: 0 = not checked, 1 = gfx950, 2 = other architecture.  Also the CU count.
+std::atomic<int> g_dev_state[kMaxDevices];
+std::atomic<int> g_dev_cus[kMaxDevices];
+
+// Check (once per device) that the current device is gfx950; returns its CU count or 0.
+int current_device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int st = g_dev_state[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+        const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        g_dev_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+        st = ok ? 1 : 2;
+        g_dev_state[dev].store(st, std::memory_order_release);
+    }
+    return st == 1 ? g_dev_cus[dev].load(std::memory_order_relaxed) : 0;
+}
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int elem_bytes(nvfp4_dtype dt) {
+    switch (dt) {
+    case NVFP4_F32: return 4;
+    case NVFP4_BF16:
+    case NVFP4_F16: return 2;
+    case NVFP4_E4M3: return 1;
+    default: return 0;
+    }
+}
+
+// Shape and alignment checks shared by every NVFP4 tensor argument.
+// codes and scales may be NULL only for a tensor with no elements; global_scale is always required.
+nvfp4_status check_qtensor(const nvfp4_tensor *t) {
+    if (!t || !t->global_scale) return NVFP4_ERR_NULL;
+    if (t->rows < 0 || t->cols < 0 || (t->cols % 16) != 0) return NVFP4_ERR_SHAPE;
+    const bool empty = t->rows == 0 || t->cols == 0;
+    if (!empty && (!t->codes || !t->scales)) return NVFP4_ERR_NULL;
+    if (!aligned16(t->codes) || !aligned16(t->scales) || !aligned4(t->global_scale)) return NVFP4_ERR_ALIGN;
+    return NVFP4_OK;
+}
+
+// A row-major matrix argument: ld >= cols and rows aligned to `align` bytes (16 for everything the
+// kernels read with 128-bit loads; 4 for the GEMM output, written one float at a time).  The
+// pointer may be NULL only when the matrix has no elements.
+nvfp4_status check_matrix(const void *p, int64_t rows, int64_t cols, int64_t ld, int eb, int align = 16) {
+    if (rows < 0 || cols < 0 || ld < cols) return NVFP4_ERR_SHAPE;
+    if (!p && rows != 0 && cols != 0) return NVFP4_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(p) % align) != 0 || (rows > 1 && ((ld * eb) % align) != 0))
+        return NVFP4_ERR_ALIGN;
+    return NVFP4_OK;
+}
+
+}  // namespace
+}  // namespace nvfp4
+
+using namespace nvfp4;
+
+extern "C" {
+
+const char *nvfp4_status_string(nvfp4_status s) {
+    switch (s) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_NULL: return "a required pointer is NULL";
+    case NVFP4_ERR_SHAPE: return "bad shape (negative size, cols % 16 != 0, ld < cols, or operands disagree)";
+    case NVFP4_ERR_ALIGN: return "a pointer or row start is not 16-byte aligned";
+    case NVFP4_ERR_DTYPE: return "dtype not accepted by this entry point";
+    case NVFP4_ERR_WORKSPACE: return "workspace missing or too small";
+    case NVFP4_ERR_ARG: return "bad argument";
+    case NVFP4_ERR_DEVICE: return "the current device is not gfx950";
+    case NVFP4_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+size_t nvfp4_workspace_size(int op, int64_t rows, int64_t cols, int64_t k) {
+    switch (op) {
+    case NVFP4_OP_QUANTIZE: return kQuantizeWsBytes;
+    case NVFP4_OP_PERCENTILE: return cols >= 0 ? percentile_ws_bytes(cols, k ? 1 : 0) : 0;
+    default: (void)rows; return 0;
+    }
+}
+
+nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype x_dtype, int64_t ld_x, const float *src_scale,
+                            const float *amax_in, const nvfp4_tensor *out, int32_t *flags, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    const int eb = elem_bytes(x_dtype);
+    if (eb == 0) return NVFP4_ERR_DTYPE;
+    nvfp4_status st = check_qtensor(out);
+    if (st != NVFP4_OK) return st;
+    st = check_matrix(x, out->rows, out->cols, ld_x, eb);
+    if (st != NVFP4_OK) return st;
+    if (src_scale && x_dtype != NVFP4_E4M3) return NVFP4_ERR_ARG;
+    if ((src_scale && !aligned4(src_scale)) || (amax_in && !aligned4(amax_in)) || (flags && !aligned4(flags)))
+        return NVFP4_ERR_ALIGN;
+    if (!amax_in && (!workspace || workspace_bytes < kQuantizeWsBytes)) return NVFP4_ERR_WORKSPACE;
+    if (workspace && !aligned16(workspace)) return NVFP4_ERR_ALIGN;
+    const int cus = current_device_cus();
+    if (cus == 0) return NVFP4_ERR_DEVICE;
+    hipError_t e = launch_quantize(x, x_dtype, ld_x, src_scale, amax_in, out, flags, workspace, cus, stream);
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+}
+
+nvfp4_status nvfp4_dequantize(const nvfp4_tensor *in, void *out, nvfp4_dtype out_dtype, int64_t ld_out,
+                              hipStream_t stream) {
+    nvfp4_status st = check_qtensor(in);
+    if (st != NVFP4_OK) return st;
+    if (out_dtype != NVFP4_F32 && out_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
+    st = check_matrix(out, in->rows, in->cols, ld_out, elem_bytes(out_dtype));
+    if (st != NVFP4_OK) return st;
+    const int cus = current_device_cus();
+    if (cus == 0) return NVFP4_ERR_DEVICE;
+    if (in->rows == 0 || in->cols == 0) return NVFP4_OK;
+    hipError_t e = launch_dequantize(in, out, out_dtype, ld_out, cus, stream);
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+}
+
+nvfp4_status nvfp4_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, int64_t lda, const nvfp4_tensor *w,
+                        float *c, int64_t ldc, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    if ((a_bf16 == nullptr) == (a_q == nullptr)) return NVFP4_ERR_ARG;
+    nvfp4_status st = check_qtensor(w);
+    if (st != NVFP4_OK) return st;
+    const int64_t N = w->rows, K = w->cols;
+    if (M < 0) return NVFP4_ERR_SHAPE;
+    if (a_q) {
+        st = check_qtensor(a_q);
+        if (st != NVFP4_OK) return st;
+        if (a_q->rows != M || a_q->cols != K) return NVFP4_ERR_SHAPE;
+    } else {
+        st = check_matrix(a_bf16, M, K, lda, 2);
+        if (st != NVFP4_OK) return st;
+    }
+    st = check_matrix(c, M, N, ldc, 4, 4);
+    if (st != NVFP4_OK) return st;
+    const int cus = current_device_cus();
+    if (cus == 0) return NVFP4_ERR_DEVICE;
+    hipError_t e = (K == 0) ? launch_fill_zero_f32(c, M, N, ldc, stream)
+                            : launch_gemm(a_bf16, a_q, M, lda, w, c, ldc, cus, stream);
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+}
+
+nvfp4_status amax_percentile(const void *x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols, int64_t ld_x, double p,
+                             int per_channel, float *out_pct, float *out_max, int32_t *flags, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+    if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16 && x_dtype != NVFP4_F16) return NVFP4_ERR_DTYPE;
+    if (!out_pct) return NVFP4_ERR_NULL;
+    nvfp4_status st = check_matrix(x, rows, cols, ld_x, elem_bytes(x_dtype));
+    if (st != NVFP4_OK) return st;
+    if (rows < 1 || cols < 1 || (cols % 16) != 0) return NVFP4_ERR_SHAPE;
+    if (!(p > 0.0 && p <= 100.0) || (per_channel != 0 && per_channel != 1)) return NVFP4_ERR_ARG;
+    const int64_t n = per_channel ? rows : rows * cols;
+    if (n > (int64_t)0xFFFFFFFFll) return NVFP4_ERR_SHAPE;
+    if (!aligned4(out_pct) || (out_max && !aligned4(out_max)) || (flags && !aligned4(flags))) return NVFP4_ERR_ALIGN;
+    if (!workspace || workspace_bytes < percentile_ws_bytes(cols, per_channel)) return NVFP4_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return NVFP4_ERR_ALIGN;
+    const int cus = current_device_cus();
+    if (cus == 0) return NVFP4_ERR_DEVICE;
+    // nearest rank, computed once here in double
+    double kk = std::ceil(p * (double)n / 100.0);
+    if (kk < 1.0) kk = 1.0;
+    if (kk > (double)n) kk = (double)n;
+    hipError_t e = launch_percentile(x, x_dtype, rows, cols, ld_x, (uint32_t)kk, per_channel, out_pct, out_max, flags,
+                                     workspace, cus, stream);
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+}
+
+}  // extern "C"

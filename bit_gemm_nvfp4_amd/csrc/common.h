@@ -1,0 +1,125 @@
+// Device-side building blocks shared by the NVFP4 kernels (gfx950 / CDNA4, wave64).
+//
+// Format facts used here ("Qwen-Image NVFP4 on a 16 GB Ada GPU", section "What NVFP4 is and how it
+// differs from NF4"): E2M1 codes with magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6} and a sign bit, one FP8
+// E4M3 scale per 16 elements of a row, one fp32 global scale, two codes per byte (low nibble first).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nvfp4.h"
+
+namespace nvfp4 {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// Bit casts take their operand by value: applying __builtin_bit_cast directly to an element of an
+// ext_vector_type reads the vector's first element with this compiler, so elements are copied first.
+__device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
+
+// ---------------------------------------------------------------------------------------------
+// E4M3 (OCP e4m3fn) block-scale bytes.
+// ---------------------------------------------------------------------------------------------
+// Round-to-nearest-even of a non-negative, non-NaN fp32 value onto the E4M3 grid, saturating at
+// 448 (0x7E).  Normal range: round the fp32 mantissa at bit 20 (3 kept bits) by integer add and
+// rebias the exponent; subnormal range (t < 2^-6, step 2^-9): rint(t * 2^9), where the scaling by
+// a power of two is exact and rint rounds half to even.
+__device__ __forceinline__ uint32_t e4m3_from_f32(float t) {
+    if (!(t < 448.0f)) return 0x7Eu;
+    if (t < 0.015625f) return (uint32_t)__builtin_rintf(t * 512.0f);
+    uint32_t u = f2u(t);
+    uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
+    uint32_t code = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);
+    return code < 0x7Eu ? code : 0x7Eu;
+}
+
+// Value of a non-negative E4M3 byte (0x00..0x7E) as fp32 (exact).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+    uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    if (e == 0) return (float)m * 0.001953125f;  // m * 2^-9
+    return u2f(((e + 120u) << 23) | (m << 20));
+}
+
+// ---------------------------------------------------------------------------------------------
+// E2M1 codes: hardware conversions with a unit scale.
+// ---------------------------------------------------------------------------------------------
+// Two fp32 -> two E2M1 codes written into byte SEL of `word` (first value in the low nibble).
+// With scale 1.0 the instruction is a plain round-to-nearest-even conversion that saturates at
+// +-6 and keeps the sign of zero; the exhaustive conversion test pins this against the oracle.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4_pk(uint32_t word, float a, float b) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, a, b, 1.0f, SEL);
+}
+
+// Eight fp32 -> one dword of eight E2M1 codes (element i in nibble i).
+__device__ __forceinline__ uint32_t fp4_pack8(const float *y) {
+    uint32_t w = 0;
+    w = fp4_pk<0>(w, y[0], y[1]);
+    w = fp4_pk<1>(w, y[2], y[3]);
+    w = fp4_pk<2>(w, y[4], y[5]);
+    w = fp4_pk<3>(w, y[6], y[7]);
+    return w;
+}
+
+// Four fp32 -> the low 16 bits of a dword (element i in nibble i).
+__device__ __forceinline__ uint32_t fp4_pack4(const float *y) {
+    uint32_t w = 0;
+    w = fp4_pk<0>(w, y[0], y[1]);
+    w = fp4_pk<1>(w, y[2], y[3]);
+    return w;
+}
+
+// One dword of eight E2M1 codes -> eight fp32 values (exact).
+__device__ __forceinline__ void fp4_unpack8_f32(uint32_t w, float *v) {
+    f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    v[0] = p0[0]; v[1] = p0[1]; v[2] = p1[0]; v[3] = p1[1];
+    v[4] = p2[0]; v[5] = p2[1]; v[6] = p3[0]; v[7] = p3[1];
+}
+
+// One dword of eight E2M1 codes -> four pairs of bf16 values (exact).
+__device__ __forceinline__ void fp4_unpack8_bf16x2(uint32_t w, bf16x2 *v) {
+    v[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
+    v[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
+    v[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
+    v[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Wave reductions (64 lanes).
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        uint32_t w = (uint32_t)__shfl_xor((int)v, o, kWave);
+        v = v > w ? v : w;
+    }
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// Pack two fp32 values that are exactly representable in bf16 (the decoded e2m1 x s products)
+// into one dword of two bf16 (first value in the low half): the high halves are the bf16 values.
+__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
+    return __builtin_amdgcn_perm(f2u(hi), f2u(lo), 0x07060302u);
+}
+
+}  // namespace nvfp4

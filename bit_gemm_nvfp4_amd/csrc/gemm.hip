@@ -1,0 +1,384 @@
+// NVFP4-weight GEMM for gfx950: C[M x N] fp32 = A . W_hat^T, W an NVFP4 tensor [N x K].
+//
+// What is computed: "Qwen-Image NVFP4 on a 16 GB Ada GPU", section "Running the NVFP4 weights on
+// Ada": without FP4 matrix hardware the packed weights are expanded to bf16 before the multiply and
+// the activations stay bf16 (W4A16); section "What NVFP4 is and how it differs from NF4": Blackwell
+// multiplies weights and activations both in 4 bits (W4A4, here with run-time quantized activations
+// as in "Qwen3-VL-8B-Instruct-heretic-NVFP4", "Runtime / hardware").
+//
+// Design for CDNA4 (prior art kept only where it holds): the E4M3 block scale is per 16 elements
+// with a 3-bit mantissa, while gfx950's scaled FP4 matrix instructions take power-of-two scales per
+// 32 elements, so they cannot reproduce NVFP4 values.  e2m1 x s has at most 6 significant bits and
+// lies in [2^-10, 2688], so it is exact in bf16: tiles are expanded exactly to bf16 in LDS and fed
+// to the bf16 matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation); the global scale(s)
+// multiply the fp32 sums in the epilogue.
+//
+// k_gemm_tile: BM x BN output tile per workgroup, K in steps of 64.  The next K step's global data
+// (bf16 A rows, W codes + scale bytes) is loaded into registers while the matrix cores work on the
+// current step from LDS; after a barrier the registers are expanded and written to LDS.
+// Workgroup ids are remapped so that the workgroups the hardware places on one XCD (ids congruent
+// mod 8) take neighbouring tiles that share W columns in that XCD's L2.
+//
+// k_gemv: for M <= 4 the product is bound by streaming W once from HBM.  A (expanded to bf16) sits
+// in LDS; each lane takes whole 16-element blocks of a W row, forms the 16-term dot products with
+// bf16 dot2 instructions and applies the block scale once per block; a wave reduction finishes
+// each row.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace nvfp4 {
+
+constexpr int kBK = 64;   // K per main-loop step (4 NVFP4 blocks)
+constexpr int kPad = 8;   // bf16 elements of row padding in LDS (16 bytes): spreads rows over banks
+constexpr int kLdsRow = kBK + kPad;
+
+// Expand 8 codes (one dword) with block scale s into 8 exact bf16 values (4 dwords).
+__device__ __forceinline__ u32x4 expand8(uint32_t w, float s) {
+    float v[8];
+    fp4_unpack8_f32(w, v);
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; q++) o[q] = pack_bf16_exact(v[2 * q] * s, v[2 * q + 1] * s);
+    return o;
+}
+
+// Raw global data of one 32-element NVFP4 chunk (two blocks): 16 code bytes and 2 scale bytes.
+struct QChunk {
+    u32x4 codes;
+    uint32_t sc;  // scale byte of block 0 in bits 0..7, block 1 in bits 8..15
+};
+
+// Load chunk (row, k0..k0+31) of an NVFP4 operand with `rows` rows and K columns.  Missing rows and
+// columns read as zero.  KALIGNED: K % 64 == 0, so whole 16-byte code loads and 2-byte scale loads
+// are aligned and in range.
+template <bool KALIGNED>
+__device__ __forceinline__ QChunk load_qchunk(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
+                                              int64_t row, int64_t rows, int64_t K, int64_t k0) {
+    QChunk c;
+    c.codes = u32x4{0u, 0u, 0u, 0u};
+    c.sc = 0u;
+    if (row >= rows) return c;
+    const uint8_t *crow = codes + row * (K / 2);
+    const uint8_t *srow = scales + row * (K / 16);
+    if (KALIGNED) {
+        c.codes = *reinterpret_cast<const u32x4 *>(crow + k0 / 2);
+        c.sc = *reinterpret_cast<const uint16_t *>(srow + k0 / 16);
+    } else {
+        if (k0 + 16 <= K) {
+            u32x2 lo = *reinterpret_cast<const u32x2 *>(crow + k0 / 2);
+            c.codes[0] = lo[0];
+            c.codes[1] = lo[1];
+            c.sc = srow[k0 / 16];
+        }
+        if (k0 + 32 <= K) {
+            u32x2 hi = *reinterpret_cast<const u32x2 *>(crow + k0 / 2 + 8);
+            c.codes[2] = hi[0];
+            c.codes[3] = hi[1];
+            c.sc |= (uint32_t)srow[k0 / 16 + 1] << 8;
+        }
+    }
+    return c;
+}
+
+// Expand a chunk into LDS row `dst` (32 bf16 = 64 bytes).
+__device__ __forceinline__ void store_qchunk(__bf16 *dst, const QChunk &c) {
+    const float s0 = e4m3_to_f32(c.sc & 0xFFu);
+    const float s1 = e4m3_to_f32((c.sc >> 8) & 0xFFu);
+    u32x4 *d = reinterpret_cast<u32x4 *>(dst);
+    d[0] = expand8(c.codes[0], s0);
+    d[1] = expand8(c.codes[1], s0);
+    d[2] = expand8(c.codes[2], s1);
+    d[3] = expand8(c.codes[3], s1);
+}
+
+template <int BM, int BN, int WM, int WN, bool A_Q, bool KALIGNED>
+__global__ __launch_bounds__(64 * WM *WN) void k_gemm_tile(const __bf16 *__restrict__ A, int64_t lda,
+                                                          const uint8_t *__restrict__ a_codes,
+                                                          const uint8_t *__restrict__ a_scales,
+                                                          const float *__restrict__ a_g,
+                                                          const uint8_t *__restrict__ w_codes,
+                                                          const uint8_t *__restrict__ w_scales,
+                                                          const float *__restrict__ w_g, float *__restrict__ C,
+                                                          int64_t ldc, int64_t M, int64_t N, int64_t K) {
+    constexpr int NT = 64 * WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
+    constexpr int TM = WTM / 32, TN = WTN / 32;   // 32x32 MFMA tiles per wave
+    constexpr int A_BF_PASSES = BM * (kBK / 8) / NT;   // 16-byte bf16 chunks of A per thread
+    constexpr int A_Q_PASSES = (BM * 2 + NT - 1) / NT;  // 32-element NVFP4 chunks of A per thread
+    constexpr int W_PASSES = (BN * 2 + NT - 1) / NT;
+    static_assert(BM * (kBK / 8) % NT == 0, "A tile must split evenly over the threads");
+
+    __shared__ __attribute__((aligned(16))) __bf16 As[BM * kLdsRow];
+    __shared__ __attribute__((aligned(16))) __bf16 Bs[BN * kLdsRow];
+
+    // ---- tile assignment: XCD-aware remap of the workgroup id ----
+    const int tiles_m = (int)((M + BM - 1) / BM);
+    const int tiles_n = (int)((N + BN - 1) / BN);
+    const int ntiles = tiles_m * tiles_n;
+    int id = blockIdx.x;
+    {
+        const int per_xcd = ntiles / 8;
+        if (per_xcd > 0 && id < per_xcd * 8) id = (id % 8) * per_xcd + id / 8;
+    }
+    const int tm_idx = id % tiles_m;
+    const int tn_idx = id / tiles_m;
+    const int64_t m0 = (int64_t)tm_idx * BM;
+    const int64_t n0 = (int64_t)tn_idx * BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wid = tid >> 6;
+    const int wm = wid / WN, wn = wid % WN;
+
+    // ---- register staging of one K step ----
+    u32x4 a_raw[A_Q ? 1 : A_BF_PASSES];
+    QChunk aq_raw[A_Q ? A_Q_PASSES : 1];
+    QChunk w_raw[W_PASSES];
+
+    auto load_step = [&](int64_t k0) {
+        if constexpr (!A_Q) {
+#pragma unroll
+            for (int p = 0; p < A_BF_PASSES; p++) {
+                const int idx = p * NT + tid;
+                const int r = idx / (kBK / 8), c8 = idx % (kBK / 8);
+                const int64_t gr = m0 + r, gk = k0 + c8 * 8;
+                if (gr < M && gk < K) {
+                    a_raw[p] = *reinterpret_cast<const u32x4 *>(A + gr * lda + gk);
+                } else {
+                    a_raw[p] = u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < A_Q_PASSES; p++) {
+                const int idx = p * NT + tid;
+                if (idx < BM * 2) {
+                    aq_raw[p] = load_qchunk<KALIGNED>(a_codes, a_scales, m0 + idx / 2, M, K, k0 + (idx % 2) * 32);
+                }
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < W_PASSES; p++) {
+            const int idx = p * NT + tid;
+            if (idx < BN * 2) {
+                w_raw[p] = load_qchunk<KALIGNED>(w_codes, w_scales, n0 + idx / 2, N, K, k0 + (idx % 2) * 32);
+            }
+        }
+    };
+    auto store_step = [&]() {
+        if constexpr (!A_Q) {
+#pragma unroll
+            for (int p = 0; p < A_BF_PASSES; p++) {
+                const int idx = p * NT + tid;
+                const int r = idx / (kBK / 8), c8 = idx % (kBK / 8);
+                *reinterpret_cast<u32x4 *>(&As[r * kLdsRow + c8 * 8]) = a_raw[p];
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < A_Q_PASSES; p++) {
+                const int idx = p * NT + tid;
+                if (idx < BM * 2) store_qchunk(&As[(idx / 2) * kLdsRow + (idx % 2) * 32], aq_raw[p]);
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < W_PASSES; p++) {
+            const int idx = p * NT + tid;
+            if (idx < BN * 2) store_qchunk(&Bs[(idx / 2) * kLdsRow + (idx % 2) * 32], w_raw[p]);
+        }
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
+
+    const int nsteps = (int)((K + kBK - 1) / kBK);
+    load_step(0);
+    store_step();
+    __syncthreads();
+    for (int ks = 0; ks < nsteps; ks++) {
+        if (ks + 1 < nsteps) load_step((int64_t)(ks + 1) * kBK);
+#pragma unroll
+        for (int kk = 0; kk < kBK / 16; kk++) {
+            const int kc = kk * 16 + 8 * (lane / 32);
+            bf16x8 af[TM], bfr[TN];
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+                af[i] = *reinterpret_cast<const bf16x8 *>(&As[(wm * WTM + i * 32 + (lane % 32)) * kLdsRow + kc]);
+#pragma unroll
+            for (int j = 0; j < TN; j++)
+                bfr[j] = *reinterpret_cast<const bf16x8 *>(&Bs[(wn * WTN + j * 32 + (lane % 32)) * kLdsRow + kc]);
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int j = 0; j < TN; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+        __syncthreads();
+        if (ks + 1 < nsteps) {
+            store_step();
+            __syncthreads();
+        }
+    }
+
+    // ---- epilogue: multiply by the global scale(s), store fp32 ----
+    const float gw = *w_g;
+    const float ga = A_Q ? *a_g : 1.0f;
+#pragma unroll
+    for (int i = 0; i < TM; i++) {
+#pragma unroll
+        for (int j = 0; j < TN; j++) {
+            const int64_t col = n0 + wn * WTN + j * 32 + (lane % 32);
+#pragma unroll
+            for (int e = 0; e < 16; e++) {
+                const int64_t row = m0 + wm * WTM + i * 32 + 8 * (e / 4) + 4 * (lane / 32) + (e % 4);
+                if (row < M && col < N) {
+                    float v = acc[i][j][e];
+                    if (A_Q) v = v * ga;
+                    C[row * ldc + col] = v * gw;
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// GEMV, M <= 4
+// ------------------------------------------------------------------------------------------------
+template <int MM, bool A_Q>
+__global__ __launch_bounds__(256) void k_gemv(const __bf16 *__restrict__ A, int64_t lda,
+                                              const uint8_t *__restrict__ a_codes,
+                                              const uint8_t *__restrict__ a_scales, const float *__restrict__ a_g,
+                                              const uint8_t *__restrict__ w_codes,
+                                              const uint8_t *__restrict__ w_scales, const float *__restrict__ w_g,
+                                              float *__restrict__ C, int64_t ldc, int64_t N, int64_t K) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t a_lds[];  // [MM][K/2] bf16 pairs
+    const int tid = threadIdx.x;
+    const int64_t kp = K / 2;
+    // stage A (expanded exactly to bf16 for the W4A4 form) in LDS
+    for (int64_t i = tid; i < MM * (K / 8); i += blockDim.x) {
+        const int64_t m = i / (K / 8), c8 = i % (K / 8);
+        u32x4 v;
+        if constexpr (!A_Q) {
+            v = *reinterpret_cast<const u32x4 *>(A + m * lda + c8 * 8);
+        } else {
+            const uint32_t w = *reinterpret_cast<const uint32_t *>(a_codes + m * (K / 2) + c8 * 4);
+            v = expand8(w, e4m3_to_f32(a_scales[m * (K / 16) + c8 / 2]));
+        }
+        *reinterpret_cast<u32x4 *>(&a_lds[m * kp + c8 * 4]) = v;
+    }
+    __syncthreads();
+
+    const float gw = *w_g;
+    const float ga = A_Q ? *a_g : 1.0f;
+    const int lane = tid & 63;
+    const int64_t nblk = K / 16;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + tid) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    for (int64_t n = wave; n < N; n += nwaves) {
+        float acc[MM];
+#pragma unroll
+        for (int m = 0; m < MM; m++) acc[m] = 0.0f;
+        const uint8_t *crow = w_codes + n * (K / 2);
+        const uint8_t *srow = w_scales + n * nblk;
+        for (int64_t b = lane; b < nblk; b += 64) {
+            const u32x2 cw = *reinterpret_cast<const u32x2 *>(crow + b * 8);
+            const float s = e4m3_to_f32(srow[b]);
+            bf16x2 wv[8];
+            fp4_unpack8_bf16x2(cw[0], wv);
+            fp4_unpack8_bf16x2(cw[1], wv + 4);
+#pragma unroll
+            for (int m = 0; m < MM; m++) {
+                const u32x4 *ap = reinterpret_cast<const u32x4 *>(&a_lds[m * kp + b * 8]);
+                const u32x4 a0 = ap[0], a1 = ap[1];
+                float part = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    part = __builtin_amdgcn_fdot2_f32_bf16(wv[q], as_bf16x2(a0[q]), part, false);
+                    part = __builtin_amdgcn_fdot2_f32_bf16(wv[4 + q], as_bf16x2(a1[q]), part, false);
+                }
+                acc[m] += part * s;
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MM; m++) {
+            const float t = wave_sum_f32(acc[m]);
+            if (lane == 0) {
+                float v = t;
+                if (A_Q) v = v * ga;
+                C[m * ldc + n] = v * gw;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// host launchers
+// ------------------------------------------------------------------------------------------------
+size_t gemv_lds_bytes(int64_t M, int64_t K) { return (size_t)M * (size_t)K * 2; }
+
+bool gemv_applies(int64_t M, int64_t K) { return M >= 1 && M <= 4 && gemv_lds_bytes(M, K) <= 64 * 1024; }
+
+template <int MM, bool A_Q>
+static void launch_gemv_t(const void *a_bf16, int64_t lda, const nvfp4_tensor *a_q, const nvfp4_tensor *w, float *c,
+                          int64_t ldc, int num_cus, hipStream_t stream) {
+    const int64_t N = w->rows, K = w->cols;
+    int64_t grid = (N + 3) / 4;
+    if (grid > (int64_t)num_cus * 8) grid = (int64_t)num_cus * 8;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL((k_gemv<MM, A_Q>), dim3((unsigned)grid), dim3(256), gemv_lds_bytes(MM, K), stream,
+                       (const __bf16 *)a_bf16, lda, A_Q ? a_q->codes : nullptr, A_Q ? a_q->scales : nullptr,
+                       A_Q ? a_q->global_scale : nullptr, w->codes, w->scales, w->global_scale, c, ldc, N, K);
+}
+
+template <bool A_Q>
+static void launch_gemv(int64_t M, const void *a_bf16, int64_t lda, const nvfp4_tensor *a_q, const nvfp4_tensor *w,
+                        float *c, int64_t ldc, int num_cus, hipStream_t stream) {
+    switch (M) {
+    case 1: launch_gemv_t<1, A_Q>(a_bf16, lda, a_q, w, c, ldc, num_cus, stream); break;
+    case 2: launch_gemv_t<2, A_Q>(a_bf16, lda, a_q, w, c, ldc, num_cus, stream); break;
+    case 3: launch_gemv_t<3, A_Q>(a_bf16, lda, a_q, w, c, ldc, num_cus, stream); break;
+    default: launch_gemv_t<4, A_Q>(a_bf16, lda, a_q, w, c, ldc, num_cus, stream); break;
+    }
+}
+
+template <int BM, int BN, int WM, int WN, bool A_Q>
+static void launch_tile(const void *a_bf16, int64_t lda, const nvfp4_tensor *a_q, int64_t M, const nvfp4_tensor *w,
+                        float *c, int64_t ldc, hipStream_t stream) {
+    const int64_t N = w->rows, K = w->cols;
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const bool kal = (K % kBK) == 0;
+    const uint8_t *ac = A_Q ? a_q->codes : nullptr;
+    const uint8_t *as = A_Q ? a_q->scales : nullptr;
+    const float *ag = A_Q ? a_q->global_scale : nullptr;
+    if (kal) {
+        hipLaunchKernelGGL((k_gemm_tile<BM, BN, WM, WN, A_Q, true>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0,
+                           stream, (const __bf16 *)a_bf16, lda, ac, as, ag, w->codes, w->scales, w->global_scale, c,
+                           ldc, M, N, K);
+    } else {
+        hipLaunchKernelGGL((k_gemm_tile<BM, BN, WM, WN, A_Q, false>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0,
+                           stream, (const __bf16 *)a_bf16, lda, ac, as, ag, w->codes, w->scales, w->global_scale, c,
+                           ldc, M, N, K);
+    }
+}
+
+hipError_t launch_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, int64_t lda, const nvfp4_tensor *w,
+                       float *c, int64_t ldc, int num_cus, hipStream_t stream) {
+    const int64_t K = w->cols;
+    if (M == 0 || w->rows == 0) return hipGetLastError();
+    if (gemv_applies(M, K)) {
+        if (a_q) launch_gemv<true>(M, a_bf16, lda, a_q, w, c, ldc, num_cus, stream);
+        else launch_gemv<false>(M, a_bf16, lda, a_q, w, c, ldc, num_cus, stream);
+        return hipGetLastError();
+    }
+    if (a_q) launch_tile<128, 128, 2, 2, true>(a_bf16, lda, a_q, M, w, c, ldc, stream);
+    else launch_tile<128, 128, 2, 2, false>(a_bf16, lda, a_q, M, w, c, ldc, stream);
+    return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,32 @@
+// Host-side launchers behind the C ABI (one per entry point).  Each enqueues its kernels on
+// `stream` and returns the HIP error of the launches; argument validation happens in api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "nvfp4.h"
+
+namespace nvfp4 {
+
+constexpr size_t kQuantizeWsBytes = 256;
+
+hipError_t launch_quantize(const void *x, nvfp4_dtype dt, int64_t ld_x, const float *src_scale, const float *amax_in,
+                           const nvfp4_tensor *out, int32_t *flags, void *workspace, int num_cus, hipStream_t stream);
+
+hipError_t launch_dequantize(const nvfp4_tensor *in, void *out, nvfp4_dtype out_dtype, int64_t ld_out, int num_cus,
+                             hipStream_t stream);
+
+hipError_t launch_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, int64_t lda, const nvfp4_tensor *w,
+                       float *c, int64_t ldc, int num_cus, hipStream_t stream);
+
+size_t percentile_ws_bytes(int64_t cols, int per_channel);
+
+hipError_t launch_percentile(const void *x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld_x, uint32_t k,
+                             int per_channel, float *out_pct, float *out_max, int32_t *flags, void *workspace,
+                             int num_cus, hipStream_t stream);
+
+hipError_t launch_fill_zero_f32(float *c, int64_t rows, int64_t cols, int64_t ld, hipStream_t stream);
+
+}  // namespace nvfp4

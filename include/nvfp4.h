@@ -1,0 +1,154 @@
+/*
+ * nvfp4.h -- C ABI of libnvfp4.so: NVFP4 quantization, expansion, the NVFP4-weight GEMM and
+ * percentile-amax calibration, as hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * The format ("Qwen-Image NVFP4 on a 16 GB Ada GPU: NVFP4 vs NF4, weight error, speed and the
+ * NF4 grain", section "What NVFP4 is and how it differs from NF4"):
+ *   - each element is an E2M1 code: sign bit, 2 exponent bits, 1 mantissa bit, magnitudes
+ *     {0, 0.5, 1, 1.5, 2, 3, 4, 6};
+ *   - each run of 16 consecutive elements along a row carries one FP8 E4M3 (OCP e4m3fn) scale;
+ *   - each tensor carries one fp32 global scale;
+ *   - value = E2M1 x block scale x global scale; two codes per byte, element 2j in the low
+ *     nibble of byte j (the stored-block figure "First NVFP4 block, as stored in the file");
+ *   - storage is 4.5 bits per element.
+ *
+ * Conventions for every entry point:
+ *   - all pointers are device memory owned by the caller; the library never allocates, frees
+ *     or retains them;
+ *   - work is enqueued on `stream` and the call returns without synchronizing;
+ *   - arguments are validated before anything is enqueued: on any error nothing runs and the
+ *     status says why; a failed kernel launch returns NVFP4_ERR_LAUNCH;
+ *   - data-dependent conditions (a NaN or infinity in the input) do not fail the call: they OR
+ *     bit 0 into the optional device int `flags`, which the caller clears;
+ *   - matrices are row-major with a row stride (`ld*`, in elements); every pointer and every
+ *     row start must be 16-byte aligned, except the fp32 GEMM output C, whose rows need 4 bytes
+ *     (NVFP4_ERR_ALIGN otherwise);
+ *   - the library checks once per device that it runs on gfx950 (NVFP4_ERR_DEVICE otherwise);
+ *   - the calls are thread-safe; calls that share a workspace buffer must be ordered by the
+ *     caller (same stream, or events).
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NVFP4_OK = 0,
+    NVFP4_ERR_NULL = 1,      /* a required pointer is NULL                                       */
+    NVFP4_ERR_SHAPE = 2,     /* negative size, cols % 16 != 0, ld < cols, or operands disagree   */
+    NVFP4_ERR_ALIGN = 3,     /* a pointer or a row start is not 16-byte aligned                  */
+    NVFP4_ERR_DTYPE = 4,     /* dtype not accepted by this entry point                          */
+    NVFP4_ERR_WORKSPACE = 5, /* workspace NULL or smaller than nvfp4_workspace_size()            */
+    NVFP4_ERR_ARG = 6,       /* p outside (0, 100], a bad mode flag, both/neither GEMM operand   */
+    NVFP4_ERR_DEVICE = 7,    /* the current device is not gfx950                                 */
+    NVFP4_ERR_LAUNCH = 8     /* the HIP runtime refused a launch                                 */
+} nvfp4_status;
+
+typedef enum {
+    NVFP4_F32 = 0,  /* IEEE binary32                                                           */
+    NVFP4_BF16 = 1, /* bfloat16                                                                */
+    NVFP4_F16 = 2,  /* IEEE binary16                                                           */
+    NVFP4_E4M3 = 3  /* OCP FP8 e4m3fn bytes (bias 7, no infinity, 0x7F / 0xFF are NaN)          */
+} nvfp4_dtype;
+
+/* An NVFP4 tensor of logical shape [rows x cols], cols % 16 == 0, dense:
+ *   codes        rows * cols/2 bytes, row-major; element 2j of a row in the low nibble of byte j
+ *   scales       rows * cols/16 bytes, row-major; E4M3 bit patterns, sign bit always 0
+ *   global_scale one float; element value = e2m1(code) * e4m3(scale) * (*global_scale)       */
+typedef struct {
+    uint8_t *codes;
+    uint8_t *scales;
+    float *global_scale;
+    int64_t rows, cols;
+} nvfp4_tensor;
+
+/* Operation selectors for nvfp4_workspace_size. */
+enum { NVFP4_OP_QUANTIZE = 0, NVFP4_OP_DEQUANTIZE = 1, NVFP4_OP_GEMM = 2, NVFP4_OP_PERCENTILE = 3 };
+
+/*
+ * nvfp4_quantize -- x [out->rows x out->cols] (row stride ld_x elements) -> NVFP4 `out`.
+ *
+ * Steps (the passage each follows):
+ *   1. widen to fp32; for an E4M3 source, v = fl(e4m3(b) * *src_scale), a NULL src_scale meaning
+ *      1.0 ("Qwen-Rapid-AIO-NVFP4", section "Why This Exists": FP8 weights are upcast to FP32
+ *      before re-quantizing, and some layers come without weight_scale);
+ *   2. amax = max |v| over the tensor, or *amax_in when given (a static, calibrated amax; values
+ *      beyond it clip to +-6 x 448 x g) -- activations use the run-time form
+ *      ("Qwen3-VL-8B-Instruct-heretic-NVFP4", "Quantization Details": per-tensor amax at run time);
+ *   3. g = fl(amax / 2688), 2688 = 6 x 448, written to *out->global_scale;
+ *   4. per 16-element block: scale byte = E4M3 round-to-nearest-even, saturating at 448, of
+ *      fl(bamax / fl(6 g)); 0 when g = 0;
+ *   5. per element: d = fl(s g), r = fl(1 / d), code = nearest E2M1 of fl(|v| r) (ties to the
+ *      even code, saturating at 6), sign bit = sign bit of v; s = 0 gives magnitude 0;
+ *   6. pack two codes per byte, low nibble first.
+ * Arguments: x_dtype any of nvfp4_dtype; src_scale only for NVFP4_E4M3 (must be > 0 if given);
+ * amax_in NULL for the run-time amax; flags nullable (bit 0 = non-finite input seen, outputs then
+ * unspecified); workspace of nvfp4_workspace_size(NVFP4_OP_QUANTIZE, rows, cols, 0) bytes.
+ * src_scale, amax_in, flags and workspace are device pointers.
+ */
+nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype x_dtype, int64_t ld_x, const float *src_scale,
+                            const float *amax_in, const nvfp4_tensor *out, int32_t *flags, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * nvfp4_dequantize -- the expander: NVFP4 `in` -> out [in->rows x in->cols] (row stride ld_out),
+ * w = fl(e2m1 x s x g) in fp32 ("Qwen-Image NVFP4 on a 16 GB Ada GPU", section "Running the NVFP4
+ * weights on Ada": each byte gives its two E2M1 values, each block's scale multiplies its 16
+ * values, then the global scale); bf16 output is the round-to-nearest-even of that fp32 value.
+ * out_dtype: NVFP4_F32 or NVFP4_BF16.  No workspace.
+ */
+nvfp4_status nvfp4_dequantize(const nvfp4_tensor *in, void *out, nvfp4_dtype out_dtype, int64_t ld_out,
+                              hipStream_t stream);
+
+/*
+ * nvfp4_gemm -- C [M x N] fp32 (row stride ldc) = A . W_hat^T, with W an NVFP4 tensor [N x K]
+ * (a PyTorch Linear weight, out-features x in-features):
+ *   - W4A16: a_bf16 [M x K] bf16 (row stride lda), a_q NULL: the weights are expanded exactly
+ *     to bf16 (e2m1 x s has at most 6 significant bits) inside the kernel, activations stay
+ *     bf16 ("Qwen-Image NVFP4 on a 16 GB Ada GPU", section "Running the NVFP4 weights on Ada");
+ *   - W4A4: a_q an NVFP4 tensor [M x K] (from nvfp4_quantize, run-time or static amax), a_bf16
+ *     NULL: both operands expanded exactly ("What NVFP4 is and how it differs from NF4": on
+ *     Blackwell weights and activations are both 4-bit; "Qwen3-VL-8B-Instruct-heretic-NVFP4",
+ *     "Runtime / hardware");
+ * products are summed in fp32 and the sum is multiplied by the global scale(s) at the end.
+ * Exactly one of a_bf16 / a_q must be non-NULL (NVFP4_ERR_ARG otherwise).  lda is ignored for
+ * W4A4.  workspace may be NULL when nvfp4_workspace_size(NVFP4_OP_GEMM, M, N, K) is 0.
+ */
+nvfp4_status nvfp4_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, int64_t lda,
+                        const nvfp4_tensor *w, float *c, int64_t ldc, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/*
+ * amax_percentile -- calibration statistic: for each column c of x [rows x cols] (per_channel
+ * = 1, out_pct/out_max hold cols floats) or for the whole tensor (per_channel = 0, one float),
+ * the nearest-rank p-th percentile of |x| (k = clamp(ceil(p n / 100), 1, n), the k-th smallest)
+ * and the maximum of |x| ("Qwen-Rapid-AIO-NVFP4", section "Recommended Model": p99.9 calibration
+ * instead of max aggregation; "Qwen-Image NVFP4 on a 16 GB Ada GPU", section "Quality: the error
+ * of each matrix": percentiles by nearest rank).  The selection is exact on the bit patterns.
+ * x_dtype: NVFP4_F32, NVFP4_BF16 or NVFP4_F16.  out_max and flags may be NULL.  workspace of
+ * nvfp4_workspace_size(NVFP4_OP_PERCENTILE, rows, cols, per_channel) bytes.  -0 counts as +0.
+ * rows must be >= 1.
+ */
+nvfp4_status amax_percentile(const void *x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                             double p, int per_channel, float *out_pct, float *out_max, int32_t *flags,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes an entry point needs (0 when none).  For NVFP4_OP_PERCENTILE the last argument
+ * is per_channel; for NVFP4_OP_GEMM the arguments are (M, N, K). */
+size_t nvfp4_workspace_size(int op, int64_t rows, int64_t cols, int64_t k);
+
+/* A static, human-readable name for a status code. */
+const char *nvfp4_status_string(nvfp4_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

@@ -1,0 +1,134 @@
+"""The C ABI library on the CPU: it loads, exports every function include/nvfp4.h declares, and
+rejects bad arguments before touching the GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import bit_gemm_nvfp4_amd as m
+    return m
+
+
+def test_header_declares_the_entry_points():
+    assert _declared_functions() == sorted(["nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm", "amax_percentile",
+                                            "nvfp4_workspace_size", "nvfp4_status_string"])
+
+
+def test_library_exports_every_declared_symbol(nv):
+    out = subprocess.run(["nm", "-D", "--defined-only", nv.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (\w+)$", out, flags=re.M))
+    for name in _declared_functions():
+        assert name in exported, name
+        assert getattr(nv.lib, name) is not None
+    assert sorted(nv.EXPORTED) == _declared_functions()
+
+
+def test_status_strings_and_workspace(nv):
+    for s in range(9):
+        assert nv.lib.nvfp4_status_string(s)
+    assert nv.lib.nvfp4_status_string(99) == b"unknown status"
+    assert nv.workspace_size(nv.OP_QUANTIZE, 10, 32) >= 4
+    assert nv.workspace_size(nv.OP_PERCENTILE, 100, 3072, 1) == 3072 * 259 * 4
+    assert nv.workspace_size(nv.OP_PERCENTILE, 100, 3072, 0) == 259 * 4
+    assert nv.workspace_size(nv.OP_GEMM, 4096, 3072, 3072) == 0
+
+
+FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced: validation fails first
+
+
+def _qt(nv, rows, cols, codes=FAKE, scales=FAKE, g=FAKE):
+    return nv.CTensor(codes, scales, g, rows, cols)
+
+
+def test_quantize_validation(nv):
+    q = nv.lib.nvfp4_quantize
+    t = _qt(nv, 4, 32)
+    P = ctypes.c_void_p
+    assert q(P(FAKE), 9, 32, None, None, ctypes.byref(t), None, P(FAKE), 256, None) == 4  # dtype
+    assert q(None, 0, 32, None, None, ctypes.byref(t), None, P(FAKE), 256, None) == 1  # NULL x
+    assert q(P(FAKE), 0, 32, None, None, None, None, P(FAKE), 256, None) == 1  # NULL out
+    bad = _qt(nv, 4, 24)
+    assert q(P(FAKE), 0, 24, None, None, ctypes.byref(bad), None, P(FAKE), 256, None) == 2  # cols % 16
+    assert q(P(FAKE), 0, 16, None, None, ctypes.byref(t), None, P(FAKE), 256, None) == 2  # ld < cols
+    neg = _qt(nv, -1, 32)
+    assert q(P(FAKE), 0, 32, None, None, ctypes.byref(neg), None, P(FAKE), 256, None) == 2
+    assert q(P(FAKE + 4), 0, 32, None, None, ctypes.byref(t), None, P(FAKE), 256, None) == 3  # align
+    assert q(P(FAKE), 1, 36, None, None, ctypes.byref(t), None, P(FAKE), 256, None) == 3  # row start 72 B
+    assert q(P(FAKE), 0, 32, P(FAKE), None, ctypes.byref(t), None, P(FAKE), 256, None) == 6  # scale w/o e4m3
+    assert q(P(FAKE), 0, 32, None, None, ctypes.byref(t), None, None, 0, None) == 5  # workspace
+    assert q(P(FAKE), 0, 32, None, None, ctypes.byref(t), None, P(FAKE), 8, None) == 5
+    unal = _qt(nv, 4, 32, codes=FAKE + 8)
+    assert q(P(FAKE), 0, 32, None, None, ctypes.byref(unal), None, P(FAKE), 256, None) == 3
+
+
+def test_dequantize_validation(nv):
+    d = nv.lib.nvfp4_dequantize
+    t = _qt(nv, 4, 32)
+    P = ctypes.c_void_p
+    assert d(None, P(FAKE), 0, 32, None) == 1
+    assert d(ctypes.byref(t), None, 0, 32, None) == 1
+    assert d(ctypes.byref(t), P(FAKE), 3, 32, None) == 4  # E4M3 output not offered
+    assert d(ctypes.byref(t), P(FAKE), 1, 20, None) == 2  # ld < cols
+    assert d(ctypes.byref(t), P(FAKE), 1, 36, None) == 3  # bf16 rows of 72 bytes
+    nog = _qt(nv, 4, 32, g=0)
+    assert d(ctypes.byref(nog), P(FAKE), 0, 32, None) == 1
+
+
+def test_gemm_validation(nv):
+    g = nv.lib.nvfp4_gemm
+    w = _qt(nv, 64, 128)
+    a = _qt(nv, 8, 128)
+    P = ctypes.c_void_p
+    assert g(None, None, 8, 128, ctypes.byref(w), P(FAKE), 64, None, 0, None) == 6  # neither form
+    assert g(P(FAKE), ctypes.byref(a), 8, 128, ctypes.byref(w), P(FAKE), 64, None, 0, None) == 6  # both
+    assert g(P(FAKE), None, 8, 128, None, P(FAKE), 64, None, 0, None) == 1
+    assert g(P(FAKE), None, 8, 64, ctypes.byref(w), P(FAKE), 64, None, 0, None) == 2  # lda < K
+    a_bad = _qt(nv, 8, 256)
+    assert g(None, ctypes.byref(a_bad), 8, 0, ctypes.byref(w), P(FAKE), 64, None, 0, None) == 2  # K mismatch
+    assert g(None, ctypes.byref(a), 9, 0, ctypes.byref(w), P(FAKE), 64, None, 0, None) == 2  # M mismatch
+    assert g(P(FAKE), None, 8, 128, ctypes.byref(w), P(FAKE), 32, None, 0, None) == 2  # ldc < N
+    assert g(P(FAKE), None, 8, 128, ctypes.byref(w), None, 64, None, 0, None) == 1  # NULL C
+    assert g(P(FAKE), None, -1, 128, ctypes.byref(w), P(FAKE), 64, None, 0, None) == 2
+    assert g(P(FAKE), None, 8, 132, ctypes.byref(w), P(FAKE), 64, None, 0, None) == 3  # A rows 264 B
+    assert g(P(FAKE), None, 8, 128, ctypes.byref(w), P(FAKE + 2), 64, None, 0, None) == 3  # C not 4-aligned
+
+
+def test_percentile_validation(nv):
+    f = nv.lib.amax_percentile
+    P = ctypes.c_void_p
+    ws = 3072 * 259 * 4
+    assert f(P(FAKE), 3, 10, 32, 32, 99.9, 1, P(FAKE), None, None, P(FAKE), ws, None) == 4  # e4m3 input
+    assert f(P(FAKE), 1, 10, 32, 32, 0.0, 1, P(FAKE), None, None, P(FAKE), ws, None) == 6  # p = 0
+    assert f(P(FAKE), 1, 10, 32, 32, 100.5, 1, P(FAKE), None, None, P(FAKE), ws, None) == 6
+    assert f(P(FAKE), 1, 10, 32, 32, float("nan"), 1, P(FAKE), None, None, P(FAKE), ws, None) == 6
+    assert f(P(FAKE), 1, 10, 32, 32, 99.9, 2, P(FAKE), None, None, P(FAKE), ws, None) == 6  # mode
+    assert f(P(FAKE), 1, 0, 32, 32, 99.9, 1, P(FAKE), None, None, P(FAKE), ws, None) == 2  # no rows
+    assert f(P(FAKE), 1, 10, 40, 40, 99.9, 1, P(FAKE), None, None, P(FAKE), ws, None) == 2  # cols % 16
+    assert f(P(FAKE), 1, 10, 32, 32, 99.9, 1, None, None, None, P(FAKE), ws, None) == 1
+    assert f(P(FAKE), 1, 10, 32, 32, 99.9, 1, P(FAKE), None, None, P(FAKE), 100, None) == 5
+    assert f(P(FAKE), 1, 10, 32, 32, 99.9, 1, P(FAKE), None, None, None, ws, None) == 5
+
+
+def test_valid_call_without_gpu_reports_device(nv):
+    # A fully valid call on a machine without a gfx950 device is refused with NVFP4_ERR_DEVICE
+    # before anything is enqueued.
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    t = _qt(nv, 4, 32)
+    P = ctypes.c_void_p
+    assert nv.lib.nvfp4_quantize(P(FAKE), 0, 32, None, None, ctypes.byref(t), None, P(FAKE), 256, None) == 7

@@ -1,0 +1,331 @@
+"""GPU parity: the HIP path (through the C ABI via the binding) against the CPU oracle.
+
+Codes, scale bytes, global scales, expanded values and percentiles are compared bit for bit;
+GEMM outputs within the floored max relative error 2e-3 of the FP64 definition.  Shapes span
+several tiles with ragged tails; the large workloads are covered at full size.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import DEV, bits16, padded, to_dev_bf16, to_dev_f16, to_dev_f32, to_dev_u8
+
+pytestmark = pytest.mark.gpu
+
+GEMM_TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import bit_gemm_nvfp4_amd as m
+    return m
+
+
+def _note(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _assert_q_equal(q, ref, what=""):
+    codes = q.codes.cpu().numpy()
+    scales = q.scales.cpu().numpy()
+    g = q.global_scale.cpu().numpy()[0]
+    assert g.view(np.uint32) == np.float32(ref.g).view(np.uint32), f"{what} global scale {g} vs {ref.g}"
+    bad_s = np.nonzero(scales != ref.scales)
+    assert bad_s[0].size == 0, f"{what} {bad_s[0].size} scale bytes differ, first at {bad_s[0][0]},{bad_s[1][0]}"
+    bad_c = np.nonzero(codes != ref.codes)
+    assert bad_c[0].size == 0, (f"{what} {bad_c[0].size} code bytes differ, first at {bad_c[0][0]},{bad_c[1][0]}: "
+                                f"{codes[bad_c[0][0], bad_c[1][0]]:#x} vs {ref.codes[bad_c[0][0], bad_c[1][0]]:#x}")
+
+
+# ------------------------------------------------------------------------------------------------
+# quantize
+# ------------------------------------------------------------------------------------------------
+def test_tiny_quantize_expand(nv):
+    d = synth.tiny()
+    _note("tiny 64x256 fp32")
+    q = nv.quantize(to_dev_f32(d["w"]))
+    ref, flags = oracle.quantize(d["w"])
+    _assert_q_equal(q, ref, "tiny")
+    f32 = nv.dequantize(q, torch.float32).cpu().numpy()
+    assert np.array_equal(f32.view(np.uint32), oracle.dequantize(ref, "f32").view(np.uint32))
+    bf = bits16(nv.dequantize(q, torch.bfloat16))
+    assert np.array_equal(bf, oracle.dequantize(ref, "bf16"))
+
+
+SHAPES = [(1, 16), (3, 48), (64, 256), (65, 1040), (7, 4096), (300, 272), (129, 2048)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_quantize_shapes_dtypes(nv, shape, dtype):
+    rows, cols = shape
+    _note(f"quantize {dtype} {shape}")
+    rng = np.random.default_rng(rows * 7919 + cols)
+    x = (rng.standard_t(4, size=shape) * 10.0 ** rng.uniform(-3, 1)).astype(np.float32)
+    x[rng.random(shape) < 0.05] = 0.0
+    x[rng.random(shape) < 0.02] *= -0.0
+    if dtype == "f32":
+        xd, ref = to_dev_f32(x), oracle.quantize(x)[0]
+    elif dtype == "bf16":
+        b = synth.bf16_bits(x)
+        xd, ref = to_dev_bf16(b), oracle.quantize(b, oracle.BF16)[0]
+    else:
+        h = x.astype(np.float16).view(np.uint16)
+        xd, ref = to_dev_f16(h), oracle.quantize(h, oracle.F16)[0]
+    _assert_q_equal(nv.quantize(xd), ref, f"{dtype} {shape}")
+    # the same matrix with a larger row stride
+    if rows > 1:
+        _assert_q_equal(nv.quantize(padded(xd, 16)), ref, f"{dtype} {shape} strided")
+
+
+def test_quantize_static_amax_clips(nv):
+    _note("static amax")
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((128, 512)).astype(np.float32)
+    for amax in [0.5, 1.0, 3.0, 1e6]:
+        ref, _ = oracle.quantize(x, amax=amax)
+        q = nv.quantize(to_dev_f32(x), amax=torch.tensor([amax], dtype=torch.float32, device=DEV))
+        _assert_q_equal(q, ref, f"amax {amax}")
+
+
+def test_quantize_zero_negzero_tiny(nv):
+    _note("zero / -0 / tiny magnitudes")
+    for x in [np.zeros((4, 64), np.float32), -np.zeros((4, 64), np.float32),
+              np.full((4, 64), 1e-40, np.float32), np.full((2, 32), 3e-45, np.float32)]:
+        ref, _ = oracle.quantize(x)
+        _assert_q_equal(nv.quantize(to_dev_f32(x)), ref, f"const {x.ravel()[0]}")
+    # blocks far below the tensor amax: scale byte 0, all magnitudes 0
+    x = np.ones((2, 64), np.float32) * 1e-9
+    x[0, 0] = 1e3
+    ref, _ = oracle.quantize(x)
+    _assert_q_equal(nv.quantize(to_dev_f32(x)), ref, "dynamic range")
+    # very small tensors: g denormal, s * g tiny, reciprocal overflow
+    rng = np.random.default_rng(6)
+    for scale in [1e-38, 1e-40, 1e-42, 1e-44]:
+        x = (rng.standard_normal((8, 64)) * scale).astype(np.float32)
+        ref, _ = oracle.quantize(x)
+        _assert_q_equal(nv.quantize(to_dev_f32(x)), ref, f"scale {scale}")
+
+
+def test_quantize_nonfinite_sets_flag(nv):
+    _note("non-finite flag")
+    for bad in [np.nan, np.inf, -np.inf]:
+        x = np.ones((4, 64), np.float32)
+        x[2, 17] = bad
+        flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+        nv.quantize(to_dev_f32(x), flags=flags)
+        assert flags.item() & 1
+        flags.zero_()
+        nv.quantize(to_dev_f32(x), amax=torch.tensor([1.0], device=DEV), flags=flags)
+        assert flags.item() & 1
+    flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+    nv.quantize(to_dev_f32(np.ones((4, 64), np.float32)), flags=flags)
+    assert flags.item() == 0
+
+
+def test_requantize_all_e4m3_bytes(nv):
+    _note("E4M3 source, all bytes")
+    b = np.arange(256, dtype=np.uint32).astype(np.uint8)
+    b = b[(b & 0x7F) != 0x7F]  # NaN bytes are checked by the flag test
+    x = np.tile(b, 16).reshape(-1, 16 * 2)[:, :32]
+    x = np.ascontiguousarray(np.concatenate([x, x[::-1]], axis=0))
+    for sc in [None, 0.0123, 1e-30, 3.7e3]:
+        ref, _ = oracle.quantize(x, oracle.E4M3, sc)
+        s = None if sc is None else torch.tensor([sc], dtype=torch.float32, device=DEV)
+        q = nv.quantize(to_dev_u8(x).view(torch.float8_e4m3fn), src_scale=s)
+        _assert_q_equal(q, ref, f"e4m3 scale {sc}")
+    x2 = x.copy()
+    x2[3, 5] = 0xFF
+    flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+    nv.quantize(to_dev_u8(x2), flags=flags)
+    assert flags.item() & 1
+
+
+def test_requantize_modulation_fp8(nv):
+    _note("requantize one 18432x3072 FP8 modulation weight")
+    b, sc = synth.modulation_fp8(0)
+    ref, _ = oracle.quantize(b, oracle.E4M3, float(sc))
+    q = nv.quantize(to_dev_u8(b), src_scale=torch.tensor([sc], dtype=torch.float32, device=DEV))
+    _assert_q_equal(q, ref, "modulation fp8")
+
+
+def test_quantize_attention_weight_full(nv):
+    _note("quantize 3072x3072 fp32 attention weight")
+    w = synth.attn_proj_weight()
+    ref, _ = oracle.quantize(w)
+    q = nv.quantize(to_dev_f32(w))
+    _assert_q_equal(q, ref, "attn weight")
+    f32 = nv.dequantize(q, torch.float32).cpu().numpy()
+    assert np.array_equal(f32.view(np.uint32), oracle.dequantize(ref, "f32").view(np.uint32))
+
+
+# ------------------------------------------------------------------------------------------------
+# dequantize
+# ------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("shape", [(1, 16), (5, 48), (33, 1024), (257, 272)])
+def test_dequantize_random_codes(nv, shape):
+    _note(f"dequantize {shape}")
+    rows, cols = shape
+    rng = np.random.default_rng(rows + cols)
+    codes = rng.integers(0, 256, (rows, cols // 2), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, (rows, cols // 16), dtype=np.uint8)
+    for g in [np.float32(0.0017439), np.float32(2.5e-39), np.float32(1e30)]:
+        ref = oracle.QTensor(codes, scales, g)
+        import bit_gemm_nvfp4_amd as nvm
+        q = nvm.NVFP4Tensor(to_dev_u8(codes), to_dev_u8(scales), torch.tensor([g], dtype=torch.float32, device=DEV))
+        f32 = nv.dequantize(q, torch.float32).cpu().numpy()
+        assert np.array_equal(f32.view(np.uint32), oracle.dequantize(ref, "f32").view(np.uint32))
+        bf = bits16(nv.dequantize(q, torch.bfloat16))
+        assert np.array_equal(bf, oracle.dequantize(ref, "bf16"))
+        if rows > 1:
+            out = padded(torch.empty((rows, cols), dtype=torch.bfloat16, device=DEV), 8)
+            nv.dequantize(q, out=out)
+            assert np.array_equal(bits16(out.contiguous()), oracle.dequantize(ref, "bf16"))
+
+
+# ------------------------------------------------------------------------------------------------
+# GEMM
+# ------------------------------------------------------------------------------------------------
+def _rand_q(nv, rows, cols, seed, sigma=0.02):
+    w = synth.normal_f32((rows, cols), sigma, seed)
+    ref, _ = oracle.quantize(w)
+    q = nv.quantize(to_dev_f32(w))
+    _assert_q_equal(q, ref, f"weight {rows}x{cols}")
+    return q, ref
+
+
+@pytest.mark.parametrize("mnk", [(16, 64, 256), (1, 64, 128), (2, 100, 48), (3, 33, 4096), (4, 17, 16),
+                                 (5, 70, 80), (37, 129, 272), (130, 257, 1024), (256, 128, 64), (300, 200, 3072)])
+def test_gemm_w4a16(nv, mnk):
+    m, n, k = mnk
+    _note(f"gemm w4a16 {mnk}")
+    q, ref = _rand_q(nv, n, k, seed=m * 31 + n)
+    a_bits = synth.bf16_bits(np.random.default_rng(m + k).standard_normal((m, k)).astype(np.float32))
+    c = nv.gemm(to_dev_bf16(a_bits), q).cpu().numpy()
+    err = oracle.gemm_error(c, oracle.gemm_w4a16(a_bits, ref))
+    assert err <= GEMM_TOL, err
+    if m > 1:  # strided A and C
+        a = padded(to_dev_bf16(a_bits), 8)
+        out = padded(torch.empty((m, n), dtype=torch.float32, device=DEV), 4)
+        nv.gemm(a, q, out=out)
+        assert np.array_equal(out.cpu().numpy(), c)
+
+
+@pytest.mark.parametrize("mnk", [(16, 64, 256), (2, 300, 1024), (4, 64, 16), (64, 96, 112), (200, 300, 512)])
+def test_gemm_w4a4(nv, mnk):
+    m, n, k = mnk
+    _note(f"gemm w4a4 {mnk}")
+    q, ref = _rand_q(nv, n, k, seed=m * 17 + n)
+    a_bits = synth.bf16_bits(np.random.default_rng(m * 3 + k).standard_normal((m, k)).astype(np.float32))
+    aq = nv.quantize(to_dev_bf16(a_bits))
+    aref, _ = oracle.quantize(a_bits, oracle.BF16)
+    _assert_q_equal(aq, aref, "activations")
+    c = nv.gemm(aq, q).cpu().numpy()
+    err = oracle.gemm_error(c, oracle.gemm_w4a4(aref, ref))
+    assert err <= GEMM_TOL, err
+
+
+def test_gemm_one_hot_reproduces_expansion(nv):
+    _note("gemm one-hot")
+    q, ref = _rand_q(nv, 192, 320, seed=99)
+    eye = np.zeros((320, 320), np.float32)
+    eye[np.arange(320), np.arange(320)] = 1.0
+    # exact equality of values (a -0 weight times 1 summed with +0 products gives +0)
+    c = nv.gemm(to_dev_bf16(synth.bf16_bits(eye)), q).cpu().numpy()
+    assert np.array_equal(c, oracle.dequantize(ref, "f32").T)
+    for m in [1, 2, 3, 4]:  # the GEMV path
+        cm = nv.gemm(to_dev_bf16(synth.bf16_bits(eye[:m])), q).cpu().numpy()
+        assert np.array_equal(cm, oracle.dequantize(ref, "f32").T[:m])
+
+
+def test_gemm_zero_weight_and_empty(nv):
+    _note("gemm zero weight / empty")
+    z = nv.quantize(to_dev_f32(np.zeros((64, 128), np.float32)))
+    a = to_dev_bf16(synth.bf16_bits(np.ones((8, 128), np.float32)))
+    assert not nv.gemm(a, z).cpu().numpy().any()
+    # K = 0: C = 0
+    import bit_gemm_nvfp4_amd as nvm
+    w0 = nvm.NVFP4Tensor(torch.zeros((5, 0), dtype=torch.uint8, device=DEV),
+                         torch.zeros((5, 0), dtype=torch.uint8, device=DEV), torch.ones(1, device=DEV))
+    a0 = torch.zeros((3, 0), dtype=torch.bfloat16, device=DEV)
+    out = torch.full((3, 5), 7.0, device=DEV)
+    nv.gemm(a0, w0, out=out)
+    assert not out.cpu().numpy().any()
+
+
+def test_gemm_attention_projection_full(nv):
+    _note("gemm w4a16 4096x3072x3072 (full) + w4a4")
+    w = synth.attn_proj_weight()
+    a_bits = synth.attn_proj_activations()
+    ref, _ = oracle.quantize(w)
+    q = nv.quantize(to_dev_f32(w))
+    _assert_q_equal(q, ref, "attn weight")
+    c = nv.gemm(to_dev_bf16(a_bits), q).cpu().numpy()
+    cref = oracle.gemm_w4a16(a_bits, ref)
+    err = oracle.gemm_error(c, cref)
+    _note(f"  W4A16 floored max rel err {err:.3e}, normwise {np.abs(c - cref).max() / np.abs(cref).max():.3e}")
+    assert err <= GEMM_TOL
+    aq = nv.quantize(to_dev_bf16(a_bits))
+    aref, _ = oracle.quantize(a_bits, oracle.BF16)
+    _assert_q_equal(aq, aref, "activations")
+    rows = np.random.default_rng(1).choice(4096, 256, replace=False)
+    c4 = nv.gemm(aq, q).cpu().numpy()[rows]
+    c4ref = oracle.gemm_f64(oracle.dequantize(aref, "f64")[rows], oracle.dequantize(ref, "f64"))
+    assert oracle.gemm_error(c4, c4ref) <= GEMM_TOL
+
+
+def test_gemv_modulation_full(nv):
+    _note("gemv M=2 over 18432x3072")
+    w = synth.modulation_weight()
+    ref, _ = oracle.quantize(w)
+    q = nv.quantize(to_dev_f32(w))
+    _assert_q_equal(q, ref, "modulation weight")
+    a_bits = synth.modulation_activations()
+    c = nv.gemm(to_dev_bf16(a_bits), q).cpu().numpy()
+    assert oracle.gemm_error(c, oracle.gemm_w4a16(a_bits, ref)) <= GEMM_TOL
+
+
+# ------------------------------------------------------------------------------------------------
+# percentile
+# ------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
+@pytest.mark.parametrize("shape", [(1, 16), (7, 48), (1000, 272), (4097, 64)])
+def test_percentile(nv, dtype, shape):
+    _note(f"percentile {dtype} {shape}")
+    rng = np.random.default_rng(shape[0] + shape[1])
+    x = rng.standard_t(3, size=shape).astype(np.float32)
+    x[rng.random(shape) < 0.01] = -0.0
+    if dtype == "bf16":
+        src, xd, odt = synth.bf16_bits(x), None, oracle.BF16
+        xd = to_dev_bf16(src)
+    elif dtype == "f16":
+        src, odt = x.astype(np.float16).view(np.uint16), oracle.F16
+        xd = to_dev_f16(src)
+    else:
+        src, odt = x, oracle.F32
+        xd = to_dev_f32(src)
+    for p in [99.9, 50.0, 100.0, 1e-6]:
+        for per_channel in [True, False]:
+            pct, mx = nv.amax_percentile(xd, p, per_channel)
+            rp, rm = oracle.amax_percentile(src, p, per_channel, dtype=odt)
+            assert np.array_equal(pct.cpu().numpy(), rp), (p, per_channel)
+            assert np.array_equal(mx.cpu().numpy(), rm), (p, per_channel)
+    if shape[0] > 1:
+        pct, mx = nv.amax_percentile(padded(xd, 16), 99.9)
+        rp, rm = oracle.amax_percentile(src, 99.9, dtype=odt)
+        assert np.array_equal(pct.cpu().numpy(), rp)
+
+
+def test_percentile_calibration_full_rows(nv):
+    # 53 x 4096 rows of Student-t(3) at the calibration size, on 128 of the 3072 channels
+    _note("percentile 217088 x 128 bf16")
+    x = synth.calib_activations(cols=128)
+    pct, mx = nv.amax_percentile(to_dev_bf16(x), 99.9)
+    rp, rm = oracle.amax_percentile(x, 99.9, dtype=oracle.BF16)
+    assert np.array_equal(pct.cpu().numpy(), rp) and np.array_equal(mx.cpu().numpy(), rm)
