@@ -93,6 +93,39 @@ __device__ __forceinline__ void store_qchunk(__bf16 *dst, const QChunk &c) {
     d[3] = expand8(c.codes[3], s1);
 }
 
+// A buffer resource over [base, base + bytes): loads at offsets at or past `bytes` return zero
+// instead of touching memory, which keeps the main-loop loads free of branches at tile edges.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Chunk (tile row r, k0 .. k0 + 31) of an NVFP4 operand through buffer resources whose bases are the
+// tile's first row (K % 64 == 0: code rows are K/2 bytes, scale rows K/16 bytes).
+__device__ __forceinline__ QChunk load_qchunk_buf(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs, uint32_t r,
+                                                  uint32_t K, uint32_t k0) {
+    QChunk c;
+    c.codes = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, r * (K / 2) + k0 / 2, 0, 0));
+    c.sc = __builtin_amdgcn_raw_buffer_load_b16(rs, r * (K / 16) + k0 / 16, 0, 0);
+    return c;
+}
+
+// Tile id -> (m-tile, n-tile).  The hardware hands workgroup i to XCD i % 8; ids are first remapped
+// so that each XCD receives a contiguous run of tile ids, and that run is walked in groups of GM
+// m-tiles, so the tiles one XCD works on at a time share a few A row blocks and W column blocks in
+// its L2.
+__device__ __forceinline__ void tile_coords(int id, int tiles_m, int tiles_n, int &tm, int &tn) {
+    const int ntiles = tiles_m * tiles_n;
+    const int per_xcd = ntiles / 8;
+    if (per_xcd > 0 && id < per_xcd * 8) id = (id % 8) * per_xcd + id / 8;
+    const int GM = tiles_m < 4 ? tiles_m : 4;
+    const int group = id / (GM * tiles_n);
+    const int first_m = group * GM;
+    const int gm = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
+    const int r = id - group * GM * tiles_n;
+    tm = first_m + r % gm;
+    tn = r / gm;
+}
+
 template <int BM, int BN, int WM, int WN, bool A_Q, bool KALIGNED>
 __global__ __launch_bounds__(64 * WM *WN) void k_gemm_tile(const __bf16 *__restrict__ A, int64_t lda,
                                                           const uint8_t *__restrict__ a_codes,
@@ -108,22 +141,17 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_tile(const __bf16 *__restr
     constexpr int A_BF_PASSES = BM * (kBK / 8) / NT;   // 16-byte bf16 chunks of A per thread
     constexpr int A_Q_PASSES = (BM * 2 + NT - 1) / NT;  // 32-element NVFP4 chunks of A per thread
     constexpr int W_PASSES = (BN * 2 + NT - 1) / NT;
+    constexpr int STAGE = (BM + BN) * kLdsRow;          // bf16 elements per LDS stage
     static_assert(BM * (kBK / 8) % NT == 0, "A tile must split evenly over the threads");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
 
-    __shared__ __attribute__((aligned(16))) __bf16 As[BM * kLdsRow];
-    __shared__ __attribute__((aligned(16))) __bf16 Bs[BN * kLdsRow];
+    // two stages of [A tile | W tile], rows padded to 72 bf16 (144 bytes)
+    __shared__ __attribute__((aligned(16))) __bf16 smem[2 * STAGE];
 
-    // ---- tile assignment: XCD-aware remap of the workgroup id ----
     const int tiles_m = (int)((M + BM - 1) / BM);
     const int tiles_n = (int)((N + BN - 1) / BN);
-    const int ntiles = tiles_m * tiles_n;
-    int id = blockIdx.x;
-    {
-        const int per_xcd = ntiles / 8;
-        if (per_xcd > 0 && id < per_xcd * 8) id = (id % 8) * per_xcd + id / 8;
-    }
-    const int tm_idx = id % tiles_m;
-    const int tn_idx = id / tiles_m;
+    int tm_idx, tn_idx;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, tm_idx, tn_idx);
     const int64_t m0 = (int64_t)tm_idx * BM;
     const int64_t n0 = (int64_t)tn_idx * BN;
 
@@ -132,12 +160,54 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_tile(const __bf16 *__restr
     const int wid = tid >> 6;
     const int wm = wid / WN, wn = wid % WN;
 
-    // ---- register staging of one K step ----
-    u32x4 a_raw[A_Q ? 1 : A_BF_PASSES];
-    QChunk aq_raw[A_Q ? A_Q_PASSES : 1];
-    QChunk w_raw[W_PASSES];
+    // ---- register staging of one K step (two sets: loads run two steps ahead) ----
+    struct Staging {
+        u32x4 a[A_Q ? 1 : A_BF_PASSES];
+        QChunk aq[A_Q ? A_Q_PASSES : 1];
+        QChunk w[W_PASSES];
+    };
+    Staging st0, st1;
 
-    auto load_step = [&](int64_t k0) {
+    // K % 64 == 0: buffer loads relative to the tile's first row; rows past M or N read as zero.
+    __amdgpu_buffer_rsrc_t ra = make_rsrc(A, 0), rac = make_rsrc(a_codes, 0), ras = make_rsrc(a_scales, 0),
+                           rwc = make_rsrc(w_codes, 0), rws = make_rsrc(w_scales, 0);
+    if constexpr (KALIGNED) {
+        const int64_t mrows = (M - m0) < BM ? (M - m0) : BM;
+        const int64_t nrows = (N - n0) < BN ? (N - n0) : BN;
+        if constexpr (!A_Q) {
+            ra = make_rsrc(A + m0 * lda, ((mrows - 1) * lda + K) * 2);
+        } else {
+            rac = make_rsrc(a_codes + m0 * (K / 2), mrows * (K / 2));
+            ras = make_rsrc(a_scales + m0 * (K / 16), mrows * (K / 16));
+        }
+        rwc = make_rsrc(w_codes + n0 * (K / 2), nrows * (K / 2));
+        rws = make_rsrc(w_scales + n0 * (K / 16), nrows * (K / 16));
+    }
+
+    auto load_step = [&](int64_t k0, Staging &st) {
+        if constexpr (KALIGNED) {
+            if constexpr (!A_Q) {
+#pragma unroll
+                for (int p = 0; p < A_BF_PASSES; p++) {
+                    const int idx = p * NT + tid;
+                    const uint32_t r = idx / (kBK / 8), c8 = idx % (kBK / 8);
+                    st.a[p] = __builtin_bit_cast(
+                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (uint32_t)((r * lda + k0 + c8 * 8) * 2), 0, 0));
+                }
+            } else {
+#pragma unroll
+                for (int p = 0; p < A_Q_PASSES; p++) {
+                    const int idx = (p * NT + tid) % (BM * 2);  // spare lanes repeat a valid chunk
+                    st.aq[p] = load_qchunk_buf(rac, ras, idx / 2, (uint32_t)K, (uint32_t)k0 + (idx % 2) * 32);
+                }
+            }
+#pragma unroll
+            for (int p = 0; p < W_PASSES; p++) {
+                const int idx = (p * NT + tid) % (BN * 2);
+                st.w[p] = load_qchunk_buf(rwc, rws, idx / 2, (uint32_t)K, (uint32_t)k0 + (idx % 2) * 32);
+            }
+            return;
+        }
         if constexpr (!A_Q) {
 #pragma unroll
             for (int p = 0; p < A_BF_PASSES; p++) {
@@ -145,9 +215,9 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_tile(const __bf16 *__restr
                 const int r = idx / (kBK / 8), c8 = idx % (kBK / 8);
                 const int64_t gr = m0 + r, gk = k0 + c8 * 8;
                 if (gr < M && gk < K) {
-                    a_raw[p] = *reinterpret_cast<const u32x4 *>(A + gr * lda + gk);
+                    st.a[p] = *reinterpret_cast<const u32x4 *>(A + gr * lda + gk);
                 } else {
-                    a_raw[p] = u32x4{0u, 0u, 0u, 0u};
+                    st.a[p] = u32x4{0u, 0u, 0u, 0u};
                 }
             }
         } else {
@@ -155,7 +225,7 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_tile(const __bf16 *__restr
             for (int p = 0; p < A_Q_PASSES; p++) {
                 const int idx = p * NT + tid;
                 if (idx < BM * 2) {
-                    aq_raw[p] = load_qchunk<KALIGNED>(a_codes, a_scales, m0 + idx / 2, M, K, k0 + (idx % 2) * 32);
+                    st.aq[p] = load_qchunk<false>(a_codes, a_scales, m0 + idx / 2, M, K, k0 + (idx % 2) * 32);
                 }
             }
         }
@@ -163,30 +233,60 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_tile(const __bf16 *__restr
         for (int p = 0; p < W_PASSES; p++) {
             const int idx = p * NT + tid;
             if (idx < BN * 2) {
-                w_raw[p] = load_qchunk<KALIGNED>(w_codes, w_scales, n0 + idx / 2, N, K, k0 + (idx % 2) * 32);
+                st.w[p] = load_qchunk<false>(w_codes, w_scales, n0 + idx / 2, N, K, k0 + (idx % 2) * 32);
             }
         }
     };
-    auto store_step = [&]() {
-        if constexpr (!A_Q) {
-#pragma unroll
-            for (int p = 0; p < A_BF_PASSES; p++) {
-                const int idx = p * NT + tid;
-                const int r = idx / (kBK / 8), c8 = idx % (kBK / 8);
-                *reinterpret_cast<u32x4 *>(&As[r * kLdsRow + c8 * 8]) = a_raw[p];
-            }
-        } else {
+
+    // Writing one K step into LDS is split into units, each one 16-byte LDS store: a copy of 8 bf16
+    // A values, or the exact bf16 expansion of 8 NVFP4 codes (one code dword).  The units are spread
+    // over the four 16-deep MFMA slices of the previous step, so that the expansion arithmetic of
+    // step ks + 1 issues between the matrix instructions of step ks.
+    constexpr int A_UNITS = A_Q ? A_Q_PASSES * 4 : A_BF_PASSES;
+    constexpr int W_UNITS = W_PASSES * 4;
+    constexpr int UNITS = A_UNITS + W_UNITS;
+    float a_s[A_Q ? A_Q_PASSES * 2 : 1], w_s[W_PASSES * 2];
+    auto decode_scales = [&](const Staging &st) {
+        if constexpr (A_Q) {
 #pragma unroll
             for (int p = 0; p < A_Q_PASSES; p++) {
-                const int idx = p * NT + tid;
-                if (idx < BM * 2) store_qchunk(&As[(idx / 2) * kLdsRow + (idx % 2) * 32], aq_raw[p]);
+                a_s[2 * p] = e4m3_to_f32(st.aq[p].sc & 0xFFu);
+                a_s[2 * p + 1] = e4m3_to_f32((st.aq[p].sc >> 8) & 0xFFu);
             }
         }
 #pragma unroll
         for (int p = 0; p < W_PASSES; p++) {
-            const int idx = p * NT + tid;
-            if (idx < BN * 2) store_qchunk(&Bs[(idx / 2) * kLdsRow + (idx % 2) * 32], w_raw[p]);
+            w_s[2 * p] = e4m3_to_f32(st.w[p].sc & 0xFFu);
+            w_s[2 * p + 1] = e4m3_to_f32((st.w[p].sc >> 8) & 0xFFu);
         }
+    };
+    auto store_unit = [&](int u, __bf16 *As, __bf16 *Bs, const Staging &st) {
+        if (u < A_UNITS) {
+            if constexpr (!A_Q) {
+                const int idx = u * NT + tid;
+                const int r = idx / (kBK / 8), c8 = idx % (kBK / 8);
+                *reinterpret_cast<u32x4 *>(&As[r * kLdsRow + c8 * 8]) = st.a[u];
+            } else {
+                const int p = u / 4, q = u % 4;
+                const int idx = p * NT + tid;
+                if (BM * 2 % NT == 0 || idx < BM * 2)
+                    *reinterpret_cast<u32x4 *>(&As[(idx / 2) * kLdsRow + (idx % 2) * 32 + q * 8]) =
+                        expand8(st.aq[p].codes[q], a_s[2 * p + q / 2]);
+            }
+        } else {
+            const int p = (u - A_UNITS) / 4, q = (u - A_UNITS) % 4;
+            const int idx = p * NT + tid;
+            if (BN * 2 % NT == 0 || idx < BN * 2)
+                *reinterpret_cast<u32x4 *>(&Bs[(idx / 2) * kLdsRow + (idx % 2) * 32 + q * 8]) =
+                    expand8(st.w[p].codes[q], w_s[2 * p + q / 2]);
+        }
+    };
+    auto store_step = [&](int stage, const Staging &st) {
+        __bf16 *As = smem + stage * STAGE;
+        __bf16 *Bs = As + BM * kLdsRow;
+        decode_scales(st);
+#pragma unroll
+        for (int u = 0; u < UNITS; u++) store_unit(u, As, Bs, st);
     };
 
     f32x16 acc[TM][TN];
@@ -197,12 +297,13 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_tile(const __bf16 *__restr
 #pragma unroll
             for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
 
-    const int nsteps = (int)((K + kBK - 1) / kBK);
-    load_step(0);
-    store_step();
-    __syncthreads();
-    for (int ks = 0; ks < nsteps; ks++) {
-        if (ks + 1 < nsteps) load_step((int64_t)(ks + 1) * kBK);
+    // Matrix work of one step from LDS stage `stage`, with the LDS writes of the next step (into
+    // stage `nstage`, from registers `nxt`) interleaved.
+    auto compute = [&](int stage, int nstage, const Staging &nxt) {
+        const __bf16 *As = smem + stage * STAGE;
+        const __bf16 *Bs = As + BM * kLdsRow;
+        __bf16 *nAs = smem + nstage * STAGE;
+        __bf16 *nBs = nAs + BM * kLdsRow;
 #pragma unroll
         for (int kk = 0; kk < kBK / 16; kk++) {
             const int kc = kk * 16 + 8 * (lane / 32);
@@ -218,13 +319,35 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_tile(const __bf16 *__restr
 #pragma unroll
                 for (int j = 0; j < TN; j++)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            if (kk == 0) decode_scales(nxt);
+#pragma unroll
+            for (int u = 0; u < UNITS; u++)
+                if (u * (kBK / 16) / UNITS == kk) store_unit(u, nAs, nBs, nxt);
         }
+    };
+
+    // Step ks computes from LDS stage ks & 1.  While it runs, the registers hold the global data of
+    // step ks + 1 (issued one step earlier) and the loads of step ks + 2 are issued; the expansion
+    // of step ks + 1 into the other stage (last read before the previous barrier) is interleaved
+    // with the matrix work, and one barrier ends the step.  Loads past the last step repeat the
+    // last step (harmless) so that the loop body has no data-dependent branches.
+    const int nsteps = (int)((K + kBK - 1) / kBK);
+    const int last = nsteps - 1;
+    auto kstep = [&](int s) -> int64_t { return (int64_t)(s < last ? s : last) * kBK; };
+    load_step(0, st0);
+    load_step(kstep(1), st1);
+    store_step(0, st0);
+    __syncthreads();
+    int ks = 0;
+    for (; ks + 2 <= nsteps; ks += 2) {
+        load_step(kstep(ks + 2), st0);
+        compute(0, 1, st1);
         __syncthreads();
-        if (ks + 1 < nsteps) {
-            store_step();
-            __syncthreads();
-        }
+        load_step(kstep(ks + 3), st1);
+        compute(1, 0, st0);
+        __syncthreads();
     }
+    if (ks < nsteps) compute(0, 1, st1);
 
     // ---- epilogue: multiply by the global scale(s), store fp32 ----
     const float gw = *w_g;
@@ -367,6 +490,49 @@ static void launch_tile(const void *a_bf16, int64_t lda, const nvfp4_tensor *a_q
     }
 }
 
+// Tile shapes, chosen per problem by a cost model: rounds of tiles over the CUs times the work one
+// CU does per round (tile area x co-resident tiles), divided by the shape's measured throughput per
+// CU relative to the largest tile on MI355X (larger tiles amortize the W expansion and the LDS
+// traffic over more output).
+struct TileCfg {
+    int bm, bn, per_cu;
+    double eff;
+};
+static const TileCfg kTiles[] = {
+    {256, 256, 1, 1.00},  // 8 waves, 64 x 128 per wave
+    {256, 192, 1, 0.97},  // 8 waves, 64 x 96 per wave
+    {128, 256, 1, 0.79},  // 8 waves, 64 x 64 per wave
+    {128, 128, 2, 0.72},  // 4 waves, 64 x 64 per wave, two workgroups per CU
+};
+
+static int choose_tile(int64_t M, int64_t N, int num_cus) {
+    int best = 0;
+    double best_cost = 1e300;
+    for (int i = 0; i < (int)(sizeof(kTiles) / sizeof(kTiles[0])); i++) {
+        const TileCfg &t = kTiles[i];
+        const double tiles = (double)((M + t.bm - 1) / t.bm) * (double)((N + t.bn - 1) / t.bn);
+        const double slots = (double)num_cus * t.per_cu;
+        const double rounds = (double)(int64_t)((tiles + slots - 1) / slots);
+        const double cost = rounds * t.per_cu * t.bm * t.bn / t.eff;
+        if (cost < best_cost) {
+            best_cost = cost;
+            best = i;
+        }
+    }
+    return best;
+}
+
+template <bool A_Q>
+static void launch_tiled(const void *a_bf16, int64_t lda, const nvfp4_tensor *a_q, int64_t M, const nvfp4_tensor *w,
+                         float *c, int64_t ldc, int num_cus, hipStream_t stream) {
+    switch (choose_tile(M, w->rows, num_cus)) {
+    case 0: launch_tile<256, 256, 4, 2, A_Q>(a_bf16, lda, a_q, M, w, c, ldc, stream); break;
+    case 1: launch_tile<256, 192, 4, 2, A_Q>(a_bf16, lda, a_q, M, w, c, ldc, stream); break;
+    case 2: launch_tile<128, 256, 2, 4, A_Q>(a_bf16, lda, a_q, M, w, c, ldc, stream); break;
+    default: launch_tile<128, 128, 2, 2, A_Q>(a_bf16, lda, a_q, M, w, c, ldc, stream); break;
+    }
+}
+
 hipError_t launch_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, int64_t lda, const nvfp4_tensor *w,
                        float *c, int64_t ldc, int num_cus, hipStream_t stream) {
     const int64_t K = w->cols;
@@ -376,8 +542,8 @@ hipError_t launch_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, i
         else launch_gemv<false>(M, a_bf16, lda, a_q, w, c, ldc, num_cus, stream);
         return hipGetLastError();
     }
-    if (a_q) launch_tile<128, 128, 2, 2, true>(a_bf16, lda, a_q, M, w, c, ldc, stream);
-    else launch_tile<128, 128, 2, 2, false>(a_bf16, lda, a_q, M, w, c, ldc, stream);
+    if (a_q) launch_tiled<true>(a_bf16, lda, a_q, M, w, c, ldc, num_cus, stream);
+    else launch_tiled<false>(a_bf16, lda, a_q, M, w, c, ldc, num_cus, stream);
     return hipGetLastError();
 }
 

@@ -10,7 +10,9 @@
 
 namespace nvfp4 {
 
-constexpr size_t kQuantizeWsBytes = 256;
+// Quantize workspace: a few words plus one 64-bit slot per workgroup of the single-pass kernel
+// (two workgroups per CU, so 2040 slots cover parts with up to 1020 CUs).
+constexpr size_t kQuantizeWsBytes = 16384;
 
 hipError_t launch_quantize(const void *x, nvfp4_dtype dt, int64_t ld_x, const float *src_scale, const float *amax_in,
                            const nvfp4_tensor *out, int32_t *flags, void *workspace, int num_cus, hipStream_t stream);

@@ -8,13 +8,12 @@
 // bf16 / fp16 (two passes: 8 + 7 bits) and 31 bits for fp32 (four passes: 8 + 8 + 8 + 7 bits).
 // Each pass:
 //   k_pct_hist    histogram of the next digit over the elements whose higher digits match the
-//                 channel's prefix; one workgroup per (64 x lanes' channels, row chunk), counters in
-//                 LDS laid out [digit][channel] so that the 64 lanes of a wave, which hold 64
-//                 different channels, never hit one address; merged into global counters with
-//                 atomics (integer, so the result does not depend on the order); the first pass
-//                 also takes the per-channel maximum key;
-//   k_pct_select  one thread per channel scans its 2^d counters, picks the digit holding the
-//                 remaining rank, narrows the prefix, and clears the counters for the next pass;
+//                 channel's prefix: one workgroup per (64 channels, row chunk), 16-byte loads, LDS
+//                 counters [digit][channel] merged into global counters with integer atomics (so
+//                 the result does not depend on the order); the first pass also takes the
+//                 per-channel maximum key;
+//   k_pct_select  one wave per channel: a prefix sum over its counters picks the digit holding the
+//                 remaining rank, narrows the prefix and clears the counters for the next pass;
 //                 the last pass writes the results.
 #include <hip/hip_runtime.h>
 
@@ -36,14 +35,18 @@ __global__ void k_pct_init(uint32_t *ws, int64_t nch, uint32_t k) {
         ws[i] = (i >= nch && i < 2 * nch) ? k : 0u;
 }
 
-// DT: NVFP4_F32 (31-bit keys, one channel per lane) or NVFP4_BF16 / NVFP4_F16 (15-bit keys, two
-// channels per lane, one 32-bit load per lane and row).
+// One workgroup per (64 channels, row chunk).  Every lane loads 16 bytes of a row per step (8 bf16 /
+// fp16 or 4 fp32 channels), so one wave load covers whole 128- or 256-byte row segments of several
+// rows; counters live in LDS as [digit][channel] (64 KB, two workgroups per CU).  DT: NVFP4_F32
+// (31-bit keys), NVFP4_BF16 or NVFP4_F16 (15-bit keys).
 template <int DT>
 __global__ __launch_bounds__(256) void k_pct_hist(const uint8_t *__restrict__ x, int64_t rows, int64_t cols,
                                                   int64_t ld_bytes, int per_channel, int rows_per_wg, int shift,
                                                   int dbits, int first_pass, uint32_t *__restrict__ ws) {
-    constexpr int CPL = (DT == NVFP4_F32) ? 1 : 2;
-    constexpr int WCH = 64 * CPL;
+    constexpr int EPL = (DT == NVFP4_F32) ? 4 : 8;  // channels per lane (one 16-byte load)
+    constexpr int LPR = 64 / EPL;                    // lanes per 64-channel row segment
+    constexpr int RPW = 64 / LPR;                    // rows per wave load
+    constexpr int WCH = 64;
     __shared__ uint32_t hist[256 * WCH];
     const int64_t nch = per_channel ? cols : 1;
     uint32_t *prefix = ws, *maxkey = ws + 2 * nch, *ghist = ws + 3 * nch;
@@ -53,13 +56,13 @@ __global__ __launch_bounds__(256) void k_pct_hist(const uint8_t *__restrict__ x,
 
     const int64_t c0 = (int64_t)blockIdx.x * WCH;
     const int64_t r0 = (int64_t)blockIdx.y * rows_per_wg;
-    int64_t r1 = r0 + rows_per_wg;
-    if (r1 > rows) r1 = rows;
-    const int64_t cl = c0 + lane * CPL;  // first channel of this lane
-    const bool active = cl < cols;
-    uint32_t pre[CPL], mk[CPL];
+    const int64_t r1 = (r0 + rows_per_wg) < rows ? (r0 + rows_per_wg) : rows;
+    const int lc = (lane % LPR) * EPL;  // first local channel of this lane
+    const int64_t cl = c0 + lc;
+    const bool active = cl < cols;      // cols % 16 == 0: a lane's channels are all in or all out
+    uint32_t pre[EPL], mk[EPL];
 #pragma unroll
-    for (int j = 0; j < CPL; j++) {
+    for (int j = 0; j < EPL; j++) {
         pre[j] = (active && !first_pass) ? prefix[per_channel ? cl + j : 0] : 0u;
         mk[j] = 0u;
     }
@@ -67,84 +70,122 @@ __global__ __launch_bounds__(256) void k_pct_hist(const uint8_t *__restrict__ x,
     const int hs = shift + dbits;  // bits above the current digit
     __syncthreads();
 
+    auto account = [&](const u32x4 &v) {
+        uint32_t key[EPL];
+        if constexpr (DT == NVFP4_F32) {
+#pragma unroll
+            for (int j = 0; j < 4; j++) key[j] = v[j] & 0x7FFFFFFFu;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                key[2 * j] = v[j] & 0x7FFFu;
+                key[2 * j + 1] = (v[j] >> 16) & 0x7FFFu;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < EPL; j++) {
+            if (first_pass) mk[j] = max(mk[j], key[j]);
+            if ((key[j] >> hs) == pre[j]) atomicAdd(&hist[((key[j] >> shift) & dmask) * WCH + lc + j], 1u);
+        }
+    };
     if (active) {
         const uint8_t *base = x + cl * (DT == NVFP4_F32 ? 4 : 2);
-        constexpr int U = 8;
-        int64_t r = r0 + wid;
-        auto account = [&](uint32_t key, int j) {
-            if (first_pass) mk[j] = max(mk[j], key);
-            if (hs >= 32 || (key >> hs) == pre[j]) atomicAdd(&hist[((key >> shift) & dmask) * WCH + lane * CPL + j], 1u);
-        };
-        for (; r + 4 * (U - 1) < r1; r += 4 * U) {
-            uint32_t w[U];
+        constexpr int U = 4;
+        const int64_t step = 4 * RPW;  // rows per workgroup step
+        int64_t r = r0 + wid * RPW + lane / LPR;
+        for (; r + (U - 1) * step < r1; r += U * step) {
+            u32x4 v[U];
 #pragma unroll
-            for (int u = 0; u < U; u++) w[u] = *reinterpret_cast<const uint32_t *>(base + (r + 4 * u) * ld_bytes);
+            for (int u = 0; u < U; u++) v[u] = *reinterpret_cast<const u32x4 *>(base + (r + u * step) * ld_bytes);
 #pragma unroll
-            for (int u = 0; u < U; u++) {
-                if constexpr (CPL == 1) {
-                    account(w[u] & 0x7FFFFFFFu, 0);
-                } else {
-                    account(w[u] & 0x7FFFu, 0);
-                    account((w[u] >> 16) & 0x7FFFu, 1);
-                }
-            }
+            for (int u = 0; u < U; u++) account(v[u]);
         }
-        for (; r < r1; r += 4) {
-            const uint32_t w = *reinterpret_cast<const uint32_t *>(base + r * ld_bytes);
-            if constexpr (CPL == 1) {
-                account(w & 0x7FFFFFFFu, 0);
-            } else {
-                account(w & 0x7FFFu, 0);
-                account((w >> 16) & 0x7FFFu, 1);
-            }
-        }
+        for (; r < r1; r += step) account(*reinterpret_cast<const u32x4 *>(base + r * ld_bytes));
         if (first_pass) {
 #pragma unroll
-            for (int j = 0; j < CPL; j++) atomicMax(&maxkey[per_channel ? cl + j : 0], mk[j]);
+            for (int j = 0; j < EPL; j++) atomicMax(&maxkey[per_channel ? cl + j : 0], mk[j]);
         }
     }
     __syncthreads();
     const int nbins = 1 << dbits;
-    for (int i = tid; i < nbins * WCH; i += 256) {
-        const uint32_t cnt = hist[i];
-        const int64_t ch = c0 + (i % WCH);
-        if (cnt && ch < cols) atomicAdd(&ghist[(per_channel ? ch : 0) * 256 + i / WCH], cnt);
+    if (per_channel) {
+        for (int i = tid; i < nbins * WCH; i += 256) {
+            const uint32_t cnt = hist[i];
+            const int64_t ch = c0 + (i % WCH);
+            if (cnt && ch < cols) atomicAdd(&ghist[ch * 256 + i / WCH], cnt);
+        }
+    } else {
+        // the whole tensor is one channel: add up the local channels of each bin first
+        for (int b = tid; b < nbins; b += 256) {
+            uint32_t cnt = 0;
+            for (int c = 0; c < WCH; c++) cnt += hist[b * WCH + c];
+            if (cnt) atomicAdd(&ghist[b], cnt);
+        }
     }
 }
 
-// One thread per channel.  last: write key -> value of the selected element and of the maximum.
+// One wave per channel: a prefix sum over the 2^d counters (4 per lane) finds the digit that holds
+// the remaining rank; the counters are cleared for the next pass.  last: write key -> value of the
+// selected element and of the maximum.
 template <int DT>
-__global__ void k_pct_select(uint32_t *__restrict__ ws, int64_t nch, int shift, int dbits, int last,
-                             float *__restrict__ out_pct, float *__restrict__ out_max, int32_t *__restrict__ flags) {
-    const int64_t ch = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+__global__ __launch_bounds__(256) void k_pct_select(uint32_t *__restrict__ ws, int64_t nch, int dbits, int last,
+                                                    float *__restrict__ out_pct, float *__restrict__ out_max,
+                                                    int32_t *__restrict__ flags) {
+    const int64_t ch = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int lane = threadIdx.x & 63;
     if (ch >= nch) return;
     uint32_t *prefix = ws, *krem = ws + nch, *maxkey = ws + 2 * nch, *h = ws + 3 * nch + ch * 256;
     const int nbins = 1 << dbits;
-    uint32_t need = krem[ch], cum = 0;
-    int d = nbins - 1;
-    for (int i = 0; i < nbins; i++) {
-        const uint32_t c = h[i];
-        if (cum + c >= need) {
-            d = i;
-            break;
-        }
-        cum += c;
+    uint32_t c[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) c[j] = (4 * lane + j < nbins) ? h[4 * lane + j] : 0u;
+    const uint32_t mine = c[0] + c[1] + c[2] + c[3];
+    uint32_t incl = mine;  // inclusive scan over lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = (uint32_t)__shfl_up((int)incl, o, 64);
+        if (lane >= o) incl += t;
     }
-    for (int i = 0; i < nbins; i++) h[i] = 0u;
-    const uint32_t p = (prefix[ch] << dbits) | (uint32_t)d;
-    prefix[ch] = p;
-    krem[ch] = need - cum;
-    if (last) {
-        auto to_f32 = [](uint32_t key) -> float {
-            if (DT == NVFP4_F32) return u2f(key);
-            if (DT == NVFP4_BF16) return u2f(key << 16);
-            return (float)__builtin_bit_cast(_Float16, (uint16_t)key);
-        };
-        const uint32_t mk = maxkey[ch];
-        const uint32_t inf_key = (DT == NVFP4_F32) ? 0x7F800000u : (DT == NVFP4_BF16 ? 0x7F80u : 0x7C00u);
-        if (mk >= inf_key && flags) atomicOr(flags, 1);
-        out_pct[ch] = to_f32(p);
-        if (out_max) out_max[ch] = to_f32(mk);
+    const uint32_t need = krem[ch];
+    const uint32_t excl = incl - mine;
+    const bool here = (excl < need) && (incl >= need);
+    const uint64_t hit = __ballot(here);
+    const int src = hit ? __builtin_ctzll(hit) : 63;
+    int d = 4 * lane + 3;
+    uint32_t before = excl;
+    if (here) {
+        uint32_t cum = excl;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            if (cum + c[j] >= need) {
+                d = 4 * lane + j;
+                break;
+            }
+            cum += c[j];
+        }
+        before = cum;
+    }
+    d = __shfl(d, src, 64);
+    before = (uint32_t)__shfl((int)before, src, 64);
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+        if (4 * lane + j < nbins) h[4 * lane + j] = 0u;
+    if (lane == 0) {
+        const uint32_t p = (prefix[ch] << dbits) | (uint32_t)d;
+        prefix[ch] = p;
+        krem[ch] = need - before;
+        if (last) {
+            auto to_f32 = [](uint32_t key) -> float {
+                if (DT == NVFP4_F32) return u2f(key);
+                if (DT == NVFP4_BF16) return u2f(key << 16);
+                return (float)__builtin_bit_cast(_Float16, (uint16_t)key);
+            };
+            const uint32_t mk = maxkey[ch];
+            const uint32_t inf_key = (DT == NVFP4_F32) ? 0x7F800000u : (DT == NVFP4_BF16 ? 0x7F80u : 0x7C00u);
+            if (mk >= inf_key && flags) atomicOr(flags, 1);
+            out_pct[ch] = to_f32(p);
+            if (out_max) out_max[ch] = to_f32(mk);
+        }
     }
 }
 
@@ -153,15 +194,18 @@ static hipError_t launch_pct_t(const void *x, int64_t rows, int64_t cols, int64_
                                float *out_pct, float *out_max, int32_t *flags, uint32_t *ws, int num_cus,
                                hipStream_t stream) {
     constexpr int EB = (DT == NVFP4_F32) ? 4 : 2;
-    constexpr int WCH = (DT == NVFP4_F32) ? 64 : 128;
+    constexpr int WCH = 64;
     constexpr int KEYBITS = (DT == NVFP4_F32) ? 31 : 15;
     const int64_t nch = per_channel ? cols : 1;
     hipLaunchKernelGGL(k_pct_init, dim3((unsigned)((nch * 259 + 255) / 256 < 4096 ? (nch * 259 + 255) / 256 : 4096)),
                        dim3(256), 0, stream, ws, nch, k);
+    // Enough workgroups to cover the CUs twice, but at least 1024 rows each: every workgroup pays for
+    // clearing and merging 64 channels x 256 counters, which few rows would not amortize.
     const int64_t cgroups = (cols + WCH - 1) / WCH;
-    int64_t target = (int64_t)num_cus * 4;
+    const int64_t target = (int64_t)num_cus * 2;
     int64_t rchunks = (target + cgroups - 1) / cgroups;
-    if (rchunks > rows) rchunks = rows;
+    const int64_t max_chunks = (rows + 1023) / 1024;
+    if (rchunks > max_chunks) rchunks = max_chunks;
     if (rchunks < 1) rchunks = 1;
     if (rchunks > 65535) rchunks = 65535;
     const int rows_per_wg = (int)((rows + rchunks - 1) / rchunks);
@@ -176,8 +220,8 @@ static hipError_t launch_pct_t(const void *x, int64_t rows, int64_t cols, int64_
                            first ? 1 : 0, ws);
         consumed += dbits;
         const int last = consumed == KEYBITS;
-        hipLaunchKernelGGL(k_pct_select<DT>, dim3((unsigned)((nch + 255) / 256)), dim3(256), 0, stream, ws, nch, shift,
-                           dbits, last, out_pct, out_max, flags);
+        hipLaunchKernelGGL(k_pct_select<DT>, dim3((unsigned)((nch + 3) / 4)), dim3(256), 0, stream, ws, nch, dbits,
+                           last, out_pct, out_max, flags);
         first = false;
     }
     return hipGetLastError();

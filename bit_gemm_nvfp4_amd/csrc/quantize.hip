@@ -7,21 +7,19 @@
 //   s_byte = E4M3_RNE_SAT(fl(bamax / fl(6 g)))      per 16 consecutive elements of a row
 //   code   = sign(v) | E2M1_RNE_SAT(fl(|v| * fl(1 / fl(s g))))   per element, packed low nibble first
 //
-// Launch structure (all on the caller's stream):
-//   k_ws_clear          zero the amax word of the workspace (a kernel, not a memset, so that the
-//                       sequence can be captured into a graph)
-//   k_amax<SRC>         max |v| over the tensor as an integer max of the magnitude bit patterns
-//                       (non-negative floats order like their bit patterns; NaN patterns sort
-//                       above infinity, so a non-finite input shows up in the result)
-//   k_encode<SRC>       one wave encodes 64 blocks (1024 elements) per tile:
-//                         - every lane loads 16 bytes per 16-byte vector, so each load instruction
-//                           covers 1 KiB of contiguous input;
-//                         - block maxima are reduced over the lanes that share a block, then
-//                           re-distributed so that lane L owns block L of the tile and does the
-//                           per-block divisions once;
-//                         - the per-block reciprocal goes back to the lanes holding the elements,
-//                           which convert two values per instruction to E2M1.
+// Work decomposition: one wave encodes a tile of 64 blocks (1024 elements).  Every lane loads 16
+// bytes per 16-byte vector, so each load instruction covers 1 KiB of contiguous input; block maxima
+// are reduced over the lanes that share a block and re-distributed so that lane L owns block L of
+// the tile and does the per-block divisions once; the per-block reciprocal goes back to the lanes
+// holding the elements, which convert two values per instruction to E2M1.  The maximum is an
+// integer max of magnitude bit patterns (non-negative floats order like their bit patterns; NaN
+// patterns sort above infinity, so a non-finite input shows up in it).
+//
+// Launches (on the caller's stream): run-time amax -> k_quant_fused, one launch that reads the input
+// once (below); static amax -> k_encode, one pass.
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 
 #include "common.h"
 #include "internal.h"
@@ -120,8 +118,6 @@ __device__ __forceinline__ uint32_t vec_absmax_bits(const u32x4 &raw) {
     return m;
 }
 
-__global__ void k_ws_clear(uint32_t *ws) { ws[threadIdx.x] = 0u; }
-
 // Address of 16-byte vector `vi` of the tensor (vectors numbered row-major over the logical
 // [rows x cols] shape).  Contiguous tensors are linear; otherwise split into row and column.
 __device__ __forceinline__ const u32x4 *vec_addr(const uint8_t *x, uint64_t vi, uint32_t vpr, int64_t ld_bytes,
@@ -132,163 +128,271 @@ __device__ __forceinline__ const u32x4 *vec_addr(const uint8_t *x, uint64_t vi, 
     return reinterpret_cast<const u32x4 *>(x + r * (uint64_t)ld_bytes) + c;
 }
 
+// ---------------------------------------------------------------------------------------------
+// One wave, one tile = 64 consecutive blocks (1024 elements).  Lane l holds vectors j * 64 + l of
+// the tile (j < VPB), so each load instruction of the wave covers 1 KiB of contiguous input.
+// ---------------------------------------------------------------------------------------------
+struct TileGeom {
+    const uint8_t *x;
+    uint64_t nblocks;
+    uint32_t vpr;  // vectors per row
+    int64_t ld_bytes;
+    int contiguous;
+};
+
 template <int SRC>
-__global__ __launch_bounds__(256) void k_amax(const uint8_t *__restrict__ x, uint64_t nvec, uint32_t vpr,
-                                              int64_t ld_bytes, int contiguous, uint32_t *__restrict__ ws) {
-    __shared__ uint32_t red[4];
-    uint32_t m = 0;
-    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-    uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    // four independent loads in flight per lane
-    for (; i + 3 * stride < nvec; i += 4 * stride) {
-        u32x4 a = *vec_addr(x, i, vpr, ld_bytes, contiguous);
-        u32x4 b = *vec_addr(x, i + stride, vpr, ld_bytes, contiguous);
-        u32x4 c = *vec_addr(x, i + 2 * stride, vpr, ld_bytes, contiguous);
-        u32x4 d = *vec_addr(x, i + 3 * stride, vpr, ld_bytes, contiguous);
-        m = max(m, max(max(vec_absmax_bits<SRC>(a), vec_absmax_bits<SRC>(b)),
-                       max(vec_absmax_bits<SRC>(c), vec_absmax_bits<SRC>(d))));
-    }
-    for (; i < nvec; i += stride) m = max(m, vec_absmax_bits<SRC>(*vec_addr(x, i, vpr, ld_bytes, contiguous)));
-    m = wave_max_u32(m);
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    if (lane == 0) red[wid] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t t = max(max(red[0], red[1]), max(red[2], red[3]));
-        atomicMax(ws, t);
+struct TileRegs {
+    u32x4 raw[kVpb<SRC>];
+};
+
+template <int SRC>
+__device__ __forceinline__ void tile_load(TileRegs<SRC> &t, const TileGeom &gm, uint64_t tile, int lane) {
+    constexpr int VPB = kVpb<SRC>;
+#pragma unroll
+    for (int j = 0; j < VPB; j++) {
+        const uint32_t vt = j * 64 + lane;
+        const uint64_t blk = tile * 64 + vt / VPB;
+        if (blk < gm.nblocks)
+            t.raw[j] = *vec_addr(gm.x, blk * VPB + vt % VPB, gm.vpr, gm.ld_bytes, gm.contiguous);
+        else
+            t.raw[j] = u32x4{0u, 0u, 0u, 0u};
     }
 }
 
-// Global scale from the amax word (or the static amax) -- every thread computes the same value.
+// Block maxima: reduce over the VPB lanes holding one block, then hand block L of the tile to lane
+// L.  Returns the largest magnitude bit pattern of lane L's block (0 past the end of the tensor).
 template <int SRC>
-__device__ __forceinline__ float global_scale(const uint32_t *ws, const float *amax_in, float sc, bool *nonfinite) {
-    float amax;
-    if (amax_in) {
-        amax = *amax_in;
-    } else if constexpr (SRC == NVFP4_E4M3) {
-        uint32_t b = *ws;
-        *nonfinite = (b == 0x7Fu);
-        amax = e4m3_to_f32(b) * sc;
-        if (!(amax <= 3.402823466e38f)) *nonfinite = true;
-    } else {
-        uint32_t bits = *ws;
-        *nonfinite = bits >= 0x7F800000u;
-        amax = u2f(bits);
-    }
-    return amax / 2688.0f;
-}
-
-template <int SRC>
-__global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ x, uint64_t nblocks, uint32_t bpr,
-                                                int64_t ld_bytes, int contiguous, const float *__restrict__ src_scale,
-                                                const float *__restrict__ amax_in, const uint32_t *__restrict__ ws,
-                                                uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
-                                                float *__restrict__ g_out, int32_t *__restrict__ flags) {
-    constexpr int EPV = kEpv<SRC>;
+__device__ __forceinline__ uint32_t tile_block_max(const TileRegs<SRC> &t, int lane) {
     constexpr int VPB = kVpb<SRC>;
     constexpr int BPL = 64 / VPB;  // blocks covered by one 64-lane load
-    const int lane = threadIdx.x & 63;
+    uint32_t pm[VPB];
+#pragma unroll
+    for (int j = 0; j < VPB; j++) {
+        pm[j] = vec_absmax_bits<SRC>(t.raw[j]);
+#pragma unroll
+        for (int o = 1; o < VPB; o <<= 1) pm[j] = max(pm[j], (uint32_t)__shfl_xor((int)pm[j], o, 64));
+    }
+    if constexpr (VPB == 1) {
+        return pm[0];
+    } else {
+        const int src = (lane % BPL) * VPB;
+        const int jj = lane / BPL;
+        uint32_t bm = 0;
+#pragma unroll
+        for (int j = 0; j < VPB; j++) {
+            const uint32_t v = (uint32_t)__shfl((int)pm[j], src, 64);
+            if (j == jj) bm = v;
+        }
+        return bm;
+    }
+}
+
+// Encode one tile whose lane-L block maximum is `bm`, given the global scale g (and 6 g).
+template <int SRC>
+__device__ __forceinline__ void tile_encode(const TileRegs<SRC> &t, uint32_t bm, float g, float six_g, float sc,
+                                            uint64_t tile, uint64_t nblocks, uint8_t *__restrict__ codes,
+                                            uint8_t *__restrict__ scales, int32_t *__restrict__ flags, int lane) {
+    constexpr int EPV = kEpv<SRC>;
+    constexpr int VPB = kVpb<SRC>;
+    constexpr int BPL = 64 / VPB;
+    const uint64_t blk0 = tile * 64;
+    float bamax;
+    bool bad;
+    if constexpr (SRC == NVFP4_E4M3) {
+        bad = (bm == 0x7Fu);
+        bamax = e4m3_to_f32(bm) * sc;
+        bad = bad || !(bamax <= 3.402823466e38f);
+    } else {
+        bad = bm >= 0x7F800000u;
+        bamax = u2f(bm);
+    }
+    const uint64_t myblk = blk0 + lane;
+    bad = bad && (myblk < nblocks);
+    if (__any(bad) && lane == 0 && flags) atomicOr(flags, 1);
+    // per-block scale byte and reciprocal (lane L owns block L)
+    uint32_t sbyte = 0;
+    if (g != 0.0f) sbyte = e4m3_from_f32(bamax / six_g);
+    const float s = e4m3_to_f32(sbyte);
+    const float r = (s == 0.0f) ? 0.0f : 1.0f / (s * g);
+    if (myblk < nblocks) scales[myblk] = (uint8_t)sbyte;
+    // each lane converts its own vectors with its block's reciprocal
+#pragma unroll
+    for (int j = 0; j < VPB; j++) {
+        const uint32_t vt = j * 64 + lane;
+        const uint64_t blk = blk0 + vt / VPB;
+        float rj;
+        if constexpr (VPB == 1) {
+            rj = r;
+        } else {
+            rj = __shfl(r, j * BPL + lane / VPB, 64);
+        }
+        float v[EPV];
+        widen<SRC>(t.raw[j], sc, v);
+        float y[EPV];
+        if (__builtin_expect(__builtin_isinf(rj), 0)) {
+            // tiny s * g: fl(1 / d) overflowed; |v| * inf saturates, 0 stays 0 (no 0 * inf)
+#pragma unroll
+            for (int e = 0; e < EPV; e++) y[e] = (v[e] == 0.0f) ? v[e] : v[e] * rj;
+        } else {
+#pragma unroll
+            for (int e = 0; e < EPV; e++) y[e] = v[e] * rj;
+        }
+        if (blk < nblocks) {
+            uint8_t *dst = codes + (blk * VPB + vt % VPB) * (EPV / 2);
+            if constexpr (EPV == 4) {
+                *reinterpret_cast<uint16_t *>(dst) = (uint16_t)fp4_pack4(y);
+            } else if constexpr (EPV == 8) {
+                *reinterpret_cast<uint32_t *>(dst) = fp4_pack8(y);
+            } else {
+                *reinterpret_cast<u32x2 *>(dst) = u32x2{fp4_pack8(y), fp4_pack8(y + 8)};
+            }
+        }
+    }
+}
+
+// amax word (integer max of magnitude patterns; for E4M3 the largest magnitude byte) -> fp32 amax.
+template <int SRC>
+__device__ __forceinline__ float amax_from_bits(uint32_t bits, float sc, bool *nonfinite) {
+    if constexpr (SRC == NVFP4_E4M3) {
+        *nonfinite = (bits == 0x7Fu);
+        const float a = e4m3_to_f32(bits) * sc;
+        if (!(a <= 3.402823466e38f)) *nonfinite = true;
+        return a;
+    } else {
+        *nonfinite = bits >= 0x7F800000u;
+        return u2f(bits);
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Static (calibrated) amax: the global scale is known up front, so one pass encodes.
+// ---------------------------------------------------------------------------------------------
+template <int SRC>
+__global__ __launch_bounds__(256) void k_encode(TileGeom gm, const float *__restrict__ src_scale,
+                                                const float *__restrict__ amax_in, uint8_t *__restrict__ codes,
+                                                uint8_t *__restrict__ scales, float *__restrict__ g_out,
+                                                int32_t *__restrict__ flags) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const float sc = (SRC == NVFP4_E4M3 && src_scale) ? *src_scale : 1.0f;
+    const float g = *amax_in / 2688.0f;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *g_out = g;
+    const float six_g = 6.0f * g;
+    const uint64_t ntiles = (gm.nblocks + 63) / 64;
+    const uint64_t nwaves = (uint64_t)gridDim.x * 4;
+    uint64_t tile = (uint64_t)blockIdx.x * 4 + wid;
+    if (tile >= ntiles) return;
+    TileRegs<SRC> cur;
+    tile_load<SRC>(cur, gm, tile, lane);
+    for (;;) {
+        const uint64_t next = tile + nwaves;
+        TileRegs<SRC> nxt;
+        if (next < ntiles) tile_load<SRC>(nxt, gm, next, lane);  // prefetch while encoding
+        const uint32_t bm = tile_block_max<SRC>(cur, lane);
+        tile_encode<SRC>(cur, bm, g, six_g, sc, tile, gm.nblocks, codes, scales, flags, lane);
+        if (next >= ntiles) break;
+        tile = next;
+        cur = nxt;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Single-pass path: one launch of at most two workgroups per CU, small enough that every workgroup
+// is resident at once on an otherwise idle GPU.  Each wave loads its TPW tiles and keeps them in
+// registers while the grid agrees on amax, then encodes them from registers, so the input crosses
+// HBM once.  Tiles beyond the register capacity are streamed for the maximum and read again for
+// the encode.
+//
+// Agreement on amax: every workgroup publishes one 64-bit word (call epoch << 32 | its partial
+// maximum) in its workspace slot, and wave 0 of every workgroup polls all slots until each carries
+// this call's epoch.  The payload travels inside the atomic word, so relaxed device-scope atomics
+// suffice (no cache maintenance in the loop).  The epoch differs between calls, so the workspace
+// needs no clearing and earlier contents are ignored.  The poll is bounded: if other work kept some
+// workgroups from being scheduled for that long, bit 1 of `flags` is set and the outputs are
+// invalid, instead of a hang.
+// ---------------------------------------------------------------------------------------------
+constexpr int kSlotBase = 16;       // workspace words before the 64-bit slots (8-byte aligned)
+constexpr int kFusedPerCu = 2;      // workgroups per CU of the single-pass kernel
+constexpr uint32_t kPollLimit = 1u << 22;
+
+template <int SRC, int TPW>
+__global__ __launch_bounds__(256) void k_quant_fused(TileGeom gm, const float *__restrict__ src_scale,
+                                                     uint32_t *__restrict__ ws, uint32_t epoch,
+                                                     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
+                                                     float *__restrict__ g_out, int32_t *__restrict__ flags) {
+    __shared__ uint32_t red[4];
+    __shared__ uint32_t amax_bits;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const uint64_t ntiles = (gm.nblocks + 63) / 64;
+    const uint64_t wave = (uint64_t)blockIdx.x * 4 + wid, nwaves = (uint64_t)gridDim.x * 4;
+    const float sc = (SRC == NVFP4_E4M3 && src_scale) ? *src_scale : 1.0f;
+    uint64_t *slots = reinterpret_cast<uint64_t *>(ws + kSlotBase);
+
+    // ---- phase 1: load the resident tiles, block maxima, tensor maximum ----
+    TileRegs<SRC> t[TPW];
+    uint32_t bm[TPW];
+#pragma unroll
+    for (int s = 0; s < TPW; s++) tile_load<SRC>(t[s], gm, wave + s * nwaves, lane);
+    uint32_t m = 0;
+#pragma unroll
+    for (int s = 0; s < TPW; s++) {
+        bm[s] = tile_block_max<SRC>(t[s], lane);
+        m = max(m, bm[s]);
+    }
+    for (uint64_t tile = wave + TPW * nwaves; tile < ntiles; tile += nwaves) {
+        TileRegs<SRC> o;
+        tile_load<SRC>(o, gm, tile, lane);
+#pragma unroll
+        for (int j = 0; j < kVpb<SRC>; j++) m = max(m, vec_absmax_bits<SRC>(o.raw[j]));
+    }
+    m = wave_max_u32(m);
+    if (lane == 0) red[wid] = m;
+    __syncthreads();
+    if (wid == 0) {
+        if (lane == 0) {
+            const uint32_t wgmax = max(max(red[0], red[1]), max(red[2], red[3]));
+            __hip_atomic_store(&slots[blockIdx.x], ((uint64_t)epoch << 32) | wgmax, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // ---- wait for every workgroup's slot of this call, reduce the maxima ----
+        uint32_t a = 0;
+        for (uint32_t it = 0;; it++) {
+            bool ready = true;
+            a = 0;
+            for (uint32_t i = lane; i < gridDim.x; i += 64) {
+                const uint64_t v = __hip_atomic_load(&slots[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if ((uint32_t)(v >> 32) != epoch) ready = false;
+                a = max(a, (uint32_t)v);
+            }
+            if (__all(ready)) break;
+            if (it >= kPollLimit) {
+                if (lane == 0 && flags) atomicOr(flags, 2);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        a = wave_max_u32(a);
+        if (lane == 0) amax_bits = a;
+    }
+    __syncthreads();
+    m = amax_bits;
     bool nonfinite = false;
-    const float g = global_scale<SRC>(ws, amax_in, sc, &nonfinite);
+    const float g = amax_from_bits<SRC>(m, sc, &nonfinite) / 2688.0f;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         *g_out = g;
         if (nonfinite && flags) atomicOr(flags, 1);
     }
     const float six_g = 6.0f * g;
-    const uint32_t vpr = bpr * VPB;  // vectors per row
-    const uint64_t ntiles = (nblocks + 63) / 64;
-    const uint64_t wave0 = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-    const uint64_t nwaves = ((uint64_t)gridDim.x * blockDim.x) >> 6;
 
-    for (uint64_t tile = wave0; tile < ntiles; tile += nwaves) {
-        const uint64_t blk0 = tile * 64;
-        // ---- load VPB vectors per lane: vector j*64+lane of the tile ----
-        u32x4 raw[VPB];
+    // ---- phase 2: encode the resident tiles, then the streamed ones ----
 #pragma unroll
-        for (int j = 0; j < VPB; j++) {
-            const uint32_t vt = j * 64 + lane;
-            const uint64_t blk = blk0 + vt / VPB;
-            if (blk < nblocks) {
-                raw[j] = *vec_addr(x, blk * VPB + vt % VPB, vpr, ld_bytes, contiguous);
-            } else {
-                raw[j] = u32x4{0u, 0u, 0u, 0u};
-            }
-        }
-        // ---- block maxima: reduce over the VPB lanes holding one block ----
-        uint32_t pm[VPB];
-#pragma unroll
-        for (int j = 0; j < VPB; j++) {
-            pm[j] = vec_absmax_bits<SRC>(raw[j]);
-#pragma unroll
-            for (int o = 1; o < VPB; o <<= 1) pm[j] = max(pm[j], (uint32_t)__shfl_xor((int)pm[j], o, 64));
-        }
-        // ---- lane L takes block L of the tile ----
-        uint32_t bm;
-        if constexpr (VPB == 1) {
-            bm = pm[0];
-        } else {
-            const int src = (lane % BPL) * VPB;
-            const int jj = lane / BPL;
-            bm = 0;
-#pragma unroll
-            for (int j = 0; j < VPB; j++) {
-                uint32_t t = (uint32_t)__shfl((int)pm[j], src, 64);
-                if (j == jj) bm = t;
-            }
-        }
-        float bamax;
-        bool bad;
-        if constexpr (SRC == NVFP4_E4M3) {
-            bad = (bm == 0x7Fu);
-            bamax = e4m3_to_f32(bm) * sc;
-            bad = bad || !(bamax <= 3.402823466e38f);
-        } else {
-            bad = bm >= 0x7F800000u;
-            bamax = u2f(bm);
-        }
-        const uint64_t myblk = blk0 + lane;
-        bad = bad && (myblk < nblocks);
-        if (__any(bad) && lane == 0 && flags) atomicOr(flags, 1);
-        // ---- per-block scale byte and reciprocal ----
-        uint32_t sbyte = 0;
-        if (g != 0.0f) sbyte = e4m3_from_f32(bamax / six_g);
-        const float s = e4m3_to_f32(sbyte);
-        const float r = (s == 0.0f) ? 0.0f : 1.0f / (s * g);
-        if (myblk < nblocks) scales[myblk] = (uint8_t)sbyte;
-        // ---- encode: each lane converts its own vectors with its block's reciprocal ----
-#pragma unroll
-        for (int j = 0; j < VPB; j++) {
-            const uint32_t vt = j * 64 + lane;
-            const uint64_t blk = blk0 + vt / VPB;
-            float rj;
-            if constexpr (VPB == 1) {
-                rj = r;
-            } else {
-                rj = __shfl(r, j * BPL + lane / VPB, 64);
-            }
-            float v[EPV];
-            widen<SRC>(raw[j], sc, v);
-            float y[EPV];
-            if (__builtin_expect(__builtin_isinf(rj), 0)) {
-                // tiny s * g: fl(1 / d) overflowed; |v| * inf saturates, 0 stays 0 (no 0 * inf)
-#pragma unroll
-                for (int e = 0; e < EPV; e++) y[e] = (v[e] == 0.0f) ? v[e] : v[e] * rj;
-            } else {
-#pragma unroll
-                for (int e = 0; e < EPV; e++) y[e] = v[e] * rj;
-            }
-            if (blk < nblocks) {
-                uint8_t *dst = codes + (blk * VPB + vt % VPB) * (EPV / 2);
-                if constexpr (EPV == 4) {
-                    *reinterpret_cast<uint16_t *>(dst) = (uint16_t)fp4_pack4(y);
-                } else if constexpr (EPV == 8) {
-                    *reinterpret_cast<uint32_t *>(dst) = fp4_pack8(y);
-                } else {
-                    *reinterpret_cast<u32x2 *>(dst) = u32x2{fp4_pack8(y), fp4_pack8(y + 8)};
-                }
-            }
-        }
+    for (int s = 0; s < TPW; s++) {
+        const uint64_t tile = wave + s * nwaves;
+        if (tile < ntiles) tile_encode<SRC>(t[s], bm[s], g, six_g, sc, tile, gm.nblocks, codes, scales, flags, lane);
+    }
+    for (uint64_t tile = wave + TPW * nwaves; tile < ntiles; tile += nwaves) {
+        TileRegs<SRC> o;
+        tile_load<SRC>(o, gm, tile, lane);
+        tile_encode<SRC>(o, tile_block_max<SRC>(o, lane), g, six_g, sc, tile, gm.nblocks, codes, scales, flags, lane);
     }
 }
 
@@ -299,27 +403,55 @@ static int grid_for(uint64_t work_items, int per_block, int max_blocks) {
     return (int)b;
 }
 
+// A different value for every call (the barrier's epoch); starts from an arbitrary point.
+static uint32_t next_epoch() {
+    static std::atomic<uint32_t> counter{0x9E3779B9u};
+    return counter.fetch_add(0x61C88647u, std::memory_order_relaxed) | 1u;
+}
+
+template <int SRC, int TPW>
+static void launch_fused(const TileGeom &gm, int grid, const float *src_scale, uint32_t *ws, const nvfp4_tensor *out,
+                         int32_t *flags, hipStream_t stream) {
+    hipLaunchKernelGGL((k_quant_fused<SRC, TPW>), dim3(grid), dim3(256), 0, stream, gm, src_scale, ws, next_epoch(),
+                       out->codes, out->scales, out->global_scale, flags);
+}
+
+// Tiles spread over all CUs (two workgroups each, so that two waves share every SIMD and hide each
+// other's latencies; fewer for small tensors); tiles per wave rounded up to a supported residency,
+// 16 at most (the rest streams twice).
+template <int SRC>
+static void launch_fused_any(const TileGeom &gm, const float *src_scale, uint32_t *ws, const nvfp4_tensor *out,
+                             int32_t *flags, int num_cus, hipStream_t stream) {
+    const uint64_t ntiles = (gm.nblocks + 63) / 64;
+    const int grid = grid_for(ntiles, 4, kFusedPerCu * num_cus);
+    const uint64_t tpw = (ntiles + 4 * (uint64_t)grid - 1) / (4 * (uint64_t)grid);
+    if (tpw <= 1) launch_fused<SRC, 1>(gm, grid, src_scale, ws, out, flags, stream);
+    else if (tpw <= 2) launch_fused<SRC, 2>(gm, grid, src_scale, ws, out, flags, stream);
+    else if (tpw <= 4) launch_fused<SRC, 4>(gm, grid, src_scale, ws, out, flags, stream);
+    else if (tpw <= 6) launch_fused<SRC, 6>(gm, grid, src_scale, ws, out, flags, stream);
+    else if (tpw <= 8) launch_fused<SRC, 8>(gm, grid, src_scale, ws, out, flags, stream);
+    else if (tpw <= 12) launch_fused<SRC, 12>(gm, grid, src_scale, ws, out, flags, stream);
+    else launch_fused<SRC, 16>(gm, grid, src_scale, ws, out, flags, stream);
+}
+
 template <int SRC>
 static hipError_t launch_quantize_t(const void *x, int64_t ld_x, int64_t rows, int64_t cols, const float *src_scale,
                                     const float *amax_in, const nvfp4_tensor *out, int32_t *flags, uint32_t *ws,
                                     int num_cus, hipStream_t stream) {
     constexpr int EB = SrcTraits<SRC>::kElemBytes;
-    const int64_t ld_bytes = ld_x * EB;
-    const int contiguous = (ld_x == cols) ? 1 : 0;
-    const uint64_t nblocks = (uint64_t)rows * (uint64_t)(cols / 16);
-    const uint32_t bpr = (uint32_t)(cols / 16);
+    TileGeom gm;
+    gm.x = (const uint8_t *)x;
+    gm.nblocks = (uint64_t)rows * (uint64_t)(cols / 16);
+    gm.vpr = (uint32_t)(cols / 16) * (uint32_t)kVpb<SRC>;
+    gm.ld_bytes = ld_x * EB;
+    gm.contiguous = (ld_x == cols) ? 1 : 0;
+    const uint64_t ntiles = (gm.nblocks + 63) / 64;
     if (!amax_in) {
-        hipLaunchKernelGGL(k_ws_clear, dim3(1), dim3(1), 0, stream, ws);
-        const uint64_t nvec = nblocks * kVpb<SRC>;
-        const int grid = grid_for(nvec, 256 * 4, num_cus * 8);
-        hipLaunchKernelGGL(k_amax<SRC>, dim3(grid), dim3(256), 0, stream, (const uint8_t *)x, nvec,
-                           bpr * (uint32_t)kVpb<SRC>, ld_bytes, contiguous, ws);
+        launch_fused_any<SRC>(gm, src_scale, ws, out, flags, num_cus, stream);
+        return hipGetLastError();
     }
-    // one wave per 64-block tile, 4 waves per workgroup; cap at 16 workgroups per CU
-    const uint64_t ntiles = (nblocks + 63) / 64;
-    const int grid = grid_for(ntiles, 4, num_cus * 16);
-    hipLaunchKernelGGL(k_encode<SRC>, dim3(grid), dim3(256), 0, stream, (const uint8_t *)x, nblocks, bpr, ld_bytes,
-                       contiguous, src_scale, amax_in, ws, out->codes, out->scales, out->global_scale, flags);
+    hipLaunchKernelGGL(k_encode<SRC>, dim3(grid_for(ntiles, 4, num_cus * 8)), dim3(256), 0, stream, gm, src_scale,
+                       amax_in, out->codes, out->scales, out->global_scale, flags);
     return hipGetLastError();
 }
 

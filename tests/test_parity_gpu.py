@@ -329,3 +329,32 @@ def test_percentile_calibration_full_rows(nv):
     pct, mx = nv.amax_percentile(to_dev_bf16(x), 99.9)
     rp, rm = oracle.amax_percentile(x, 99.9, dtype=oracle.BF16)
     assert np.array_equal(pct.cpu().numpy(), rp) and np.array_equal(mx.cpu().numpy(), rm)
+
+
+# shapes that select each of the GEMM kernel's tile configurations (256x256, 256x192, 128x256,
+# 128x128), with aligned and ragged K and ragged M / N edges
+@pytest.mark.parametrize("mnk", [(576, 16384, 64), (448, 16512, 64), (130, 1000, 128), (704, 10880, 128),
+                                 (3000, 5000, 80), (250, 12400, 48)])
+def test_gemm_tile_configs(nv, mnk):
+    m, n, k = mnk
+    _note(f"gemm tile configs {mnk}")
+    q, ref = _rand_q(nv, n, k, seed=m + n + k)
+    a_bits = synth.bf16_bits(np.random.default_rng(m * 7 + k).standard_normal((m, k)).astype(np.float32))
+    c = nv.gemm(to_dev_bf16(a_bits), q).cpu().numpy()
+    assert oracle.gemm_error(c, oracle.gemm_w4a16(a_bits, ref)) <= GEMM_TOL
+    aq = nv.quantize(to_dev_bf16(a_bits))
+    aref, _ = oracle.quantize(a_bits, oracle.BF16)
+    _assert_q_equal(aq, aref, "activations")
+    c4 = nv.gemm(aq, q).cpu().numpy()
+    assert oracle.gemm_error(c4, oracle.gemm_w4a4(aref, ref)) <= GEMM_TOL
+
+
+def test_quantize_large_tensor_overflow_path(nv):
+    # more tiles than the single-pass kernel holds in registers: part of the input is read twice
+    _note("quantize 16384 x 8192 fp32 (128 M elements)")
+    rng = np.random.default_rng(77)
+    x = (rng.standard_normal((16384, 8192)) * 0.01).astype(np.float32)
+    x[123, 4567] = 0.75
+    q = nv.quantize(to_dev_f32(x))
+    ref, _ = oracle.quantize(x)
+    _assert_q_equal(q, ref, "large")
