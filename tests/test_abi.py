@@ -71,6 +71,8 @@ def test_quantize_validation(nv):
     assert q(P(FAKE), 0, 32, P(FAKE), None, ctypes.byref(t), None, P(FAKE), 256, None) == 6  # scale w/o e4m3
     assert q(P(FAKE), 0, 32, None, None, ctypes.byref(t), None, None, 0, None) == 5  # workspace
     assert q(P(FAKE), 0, 32, None, None, ctypes.byref(t), None, P(FAKE), 8, None) == 5
+    ws = nv.workspace_size(nv.OP_QUANTIZE, 4, 32)
+    assert q(P(FAKE), 0, 32, None, None, ctypes.byref(t), None, P(FAKE), ws - 1, None) == 5
     unal = _qt(nv, 4, 32, codes=FAKE + 8)
     assert q(P(FAKE), 0, 32, None, None, ctypes.byref(unal), None, P(FAKE), 256, None) == 3
 
@@ -131,4 +133,5 @@ def test_valid_call_without_gpu_reports_device(nv):
         pytest.skip("a GPU is present")
     t = _qt(nv, 4, 32)
     P = ctypes.c_void_p
-    assert nv.lib.nvfp4_quantize(P(FAKE), 0, 32, None, None, ctypes.byref(t), None, P(FAKE), 256, None) == 7
+    ws = nv.workspace_size(nv.OP_QUANTIZE, 4, 32)
+    assert nv.lib.nvfp4_quantize(P(FAKE), 0, 32, None, None, ctypes.byref(t), None, P(FAKE), ws, None) == 7
