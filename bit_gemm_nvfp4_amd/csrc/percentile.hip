@@ -8,10 +8,10 @@
 // bf16 / fp16 (two passes: 8 + 7 bits) and 31 bits for fp32 (four passes: 8 + 8 + 8 + 7 bits).
 // Each pass:
 //   k_pct_hist    histogram of the next digit over the elements whose higher digits match the
-//                 channel's prefix: one workgroup per (64 channels, row chunk), 16-byte loads, LDS
-//                 counters [digit][channel] merged into global counters with integer atomics (so
-//                 the result does not depend on the order); the first pass also takes the
-//                 per-channel maximum key;
+//                 channel's prefix: one workgroup per (64 channels, row chunk), LDS counters
+//                 [digit][channel] merged into global counters with integer atomics (so the result
+//                 does not depend on the order); the first pass also takes the per-channel
+//                 maximum key;
 //   k_pct_select  one wave per channel: a prefix sum over its counters picks the digit holding the
 //                 remaining rank, narrows the prefix and clears the counters for the next pass;
 //                 the last pass writes the results.
@@ -35,24 +35,30 @@ __global__ void k_pct_init(uint32_t *ws, int64_t nch, uint32_t k) {
         ws[i] = (i >= nch && i < 2 * nch) ? k : 0u;
 }
 
-// One workgroup per (64 channels, row chunk).  Every lane loads 16 bytes of a row per step (8 bf16 /
-// fp16 or 4 fp32 channels), so one wave load covers whole 128- or 256-byte row segments of several
-// rows; counters live in LDS as [digit][channel] (64 KB, two workgroups per CU).  DT: NVFP4_F32
-// (31-bit keys), NVFP4_BF16 or NVFP4_F16 (15-bit keys).
-template <int DT>
-__global__ __launch_bounds__(256) void k_pct_hist(const uint8_t *__restrict__ x, int64_t rows, int64_t cols,
-                                                  int64_t ld_bytes, int per_channel, int rows_per_wg, int shift,
-                                                  int dbits, int first_pass, uint32_t *__restrict__ ws) {
+// One workgroup per (64 channels, row chunk).  Every lane loads 16 bytes of a row (8 bf16 / fp16
+// or 4 fp32 channels), so one wave load covers whole 128- or 256-byte row segments of several rows;
+// U rows are in flight per lane (rows past the chunk are masked).  Counters live in LDS as
+// [digit][channel] (64 KB, two workgroups per CU).  DT: NVFP4_F32 (31-bit keys), NVFP4_BF16 or
+// NVFP4_F16 (15-bit keys).
+constexpr int kPctThreads = 256;
+
+template <int DT, int U>
+__global__ __launch_bounds__(kPctThreads) void k_pct_hist(const uint8_t *__restrict__ x, int64_t rows, int64_t cols,
+                                                          int64_t ld_bytes, int per_channel, int rows_per_wg,
+                                                          int shift, int dbits, int first_pass,
+                                                          uint32_t *__restrict__ ws) {
     constexpr int EPL = (DT == NVFP4_F32) ? 4 : 8;  // channels per lane (one 16-byte load)
     constexpr int LPR = 64 / EPL;                    // lanes per 64-channel row segment
     constexpr int RPW = 64 / LPR;                    // rows per wave load
+    constexpr int NW = kPctThreads / 64;
+    constexpr int STEP = NW * RPW;                   // rows per workgroup load step
     constexpr int WCH = 64;
     __shared__ uint32_t hist[256 * WCH];
     const int64_t nch = per_channel ? cols : 1;
     uint32_t *prefix = ws, *maxkey = ws + 2 * nch, *ghist = ws + 3 * nch;
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    for (int i = tid; i < 256 * WCH; i += 256) hist[i] = 0u;
+    for (int i = tid; i < 256 * WCH / 4; i += kPctThreads) reinterpret_cast<u32x4 *>(hist)[i] = u32x4{0u, 0u, 0u, 0u};
 
     const int64_t c0 = (int64_t)blockIdx.x * WCH;
     const int64_t r0 = (int64_t)blockIdx.y * rows_per_wg;
@@ -90,17 +96,25 @@ __global__ __launch_bounds__(256) void k_pct_hist(const uint8_t *__restrict__ x,
     };
     if (active) {
         const uint8_t *base = x + cl * (DT == NVFP4_F32 ? 4 : 2);
-        constexpr int U = 4;
-        const int64_t step = 4 * RPW;  // rows per workgroup step
         int64_t r = r0 + wid * RPW + lane / LPR;
-        for (; r + (U - 1) * step < r1; r += U * step) {
+        for (; r + (int64_t)(U - 1) * STEP < r1; r += (int64_t)U * STEP) {  // full batches
             u32x4 v[U];
 #pragma unroll
-            for (int u = 0; u < U; u++) v[u] = *reinterpret_cast<const u32x4 *>(base + (r + u * step) * ld_bytes);
+            for (int u = 0; u < U; u++) v[u] = *reinterpret_cast<const u32x4 *>(base + (r + (int64_t)u * STEP) * ld_bytes);
 #pragma unroll
             for (int u = 0; u < U; u++) account(v[u]);
         }
-        for (; r < r1; r += step) account(*reinterpret_cast<const u32x4 *>(base + r * ld_bytes));
+        if (r < r1) {  // last, partial batch: rows past the chunk are masked
+            u32x4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int64_t rr = r + (int64_t)u * STEP;
+                v[u] = rr < r1 ? *reinterpret_cast<const u32x4 *>(base + rr * ld_bytes) : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < U; u++)
+                if (r + (int64_t)u * STEP < r1) account(v[u]);
+        }
         if (first_pass) {
 #pragma unroll
             for (int j = 0; j < EPL; j++) atomicMax(&maxkey[per_channel ? cl + j : 0], mk[j]);
@@ -109,14 +123,14 @@ __global__ __launch_bounds__(256) void k_pct_hist(const uint8_t *__restrict__ x,
     __syncthreads();
     const int nbins = 1 << dbits;
     if (per_channel) {
-        for (int i = tid; i < nbins * WCH; i += 256) {
+        for (int i = tid; i < nbins * WCH; i += kPctThreads) {
             const uint32_t cnt = hist[i];
             const int64_t ch = c0 + (i % WCH);
             if (cnt && ch < cols) atomicAdd(&ghist[ch * 256 + i / WCH], cnt);
         }
     } else {
         // the whole tensor is one channel: add up the local channels of each bin first
-        for (int b = tid; b < nbins; b += 256) {
+        for (int b = tid; b < nbins; b += kPctThreads) {
             uint32_t cnt = 0;
             for (int c = 0; c < WCH; c++) cnt += hist[b * WCH + c];
             if (cnt) atomicAdd(&ghist[b], cnt);
@@ -200,7 +214,8 @@ static hipError_t launch_pct_t(const void *x, int64_t rows, int64_t cols, int64_
     hipLaunchKernelGGL(k_pct_init, dim3((unsigned)((nch * 259 + 255) / 256 < 4096 ? (nch * 259 + 255) / 256 : 4096)),
                        dim3(256), 0, stream, ws, nch, k);
     // Enough workgroups to cover the CUs twice, but at least 1024 rows each: every workgroup pays for
-    // clearing and merging 64 channels x 256 counters, which few rows would not amortize.
+    // clearing and merging 64 channels x 256 counters, which few rows would not amortize.  Long
+    // chunks keep 16 rows in flight per lane, short ones 4.
     const int64_t cgroups = (cols + WCH - 1) / WCH;
     const int64_t target = (int64_t)num_cus * 2;
     int64_t rchunks = (target + cgroups - 1) / cgroups;
@@ -210,14 +225,20 @@ static hipError_t launch_pct_t(const void *x, int64_t rows, int64_t cols, int64_
     if (rchunks > 65535) rchunks = 65535;
     const int rows_per_wg = (int)((rows + rchunks - 1) / rchunks);
     rchunks = (rows + rows_per_wg - 1) / rows_per_wg;
+    const bool deep = rows_per_wg >= 8192;
     int consumed = 0;
     bool first = true;
     while (consumed < KEYBITS) {
         const int dbits = (KEYBITS - consumed) >= 8 ? 8 : (KEYBITS - consumed);
         const int shift = KEYBITS - consumed - dbits;
-        hipLaunchKernelGGL(k_pct_hist<DT>, dim3((unsigned)cgroups, (unsigned)rchunks), dim3(256), 0, stream,
-                           (const uint8_t *)x, rows, cols, ld_x * EB, per_channel, rows_per_wg, shift, dbits,
-                           first ? 1 : 0, ws);
+        if (deep)
+            hipLaunchKernelGGL((k_pct_hist<DT, 16>), dim3((unsigned)cgroups, (unsigned)rchunks), dim3(kPctThreads), 0,
+                               stream, (const uint8_t *)x, rows, cols, ld_x * EB, per_channel, rows_per_wg, shift,
+                               dbits, first ? 1 : 0, ws);
+        else
+            hipLaunchKernelGGL((k_pct_hist<DT, 4>), dim3((unsigned)cgroups, (unsigned)rchunks), dim3(kPctThreads), 0,
+                               stream, (const uint8_t *)x, rows, cols, ld_x * EB, per_channel, rows_per_wg, shift,
+                               dbits, first ? 1 : 0, ws);
         consumed += dbits;
         const int last = consumed == KEYBITS;
         hipLaunchKernelGGL(k_pct_select<DT>, dim3((unsigned)((nch + 3) / 4)), dim3(256), 0, stream, ws, nch, dbits,
