@@ -40,6 +40,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after the timed steps, copy a buffer of this many MiB three times (a plain copy of "
+                         "known size, for scaling HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -84,6 +87,9 @@ def main():
 
     ops = ["quantize", "requantize", "dequantize", "act_quantize", "gemm_w4a16", "gemm_w4a4", "gemv_w4a16",
            "percentile"]
+    # kernels each op launches (the roofline is reported for the longest single-kernel op)
+    n_kernels = {"quantize": 1, "requantize": 1, "dequantize": 1, "act_quantize": 1, "gemm_w4a16": 1,
+                 "gemm_w4a4": 1, "gemv_w4a16": 1, "percentile": 5}
 
     def step(i, events=None):
         w, a, w8 = sets[i % nsets]
@@ -136,14 +142,15 @@ def main():
         unit, amount, peak = work[op]
         rate = amount / (op_ms[op] * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
         op_report[op] = {"ms": round(op_ms[op], 5), "rate": round(rate, 2), "unit": unit,
-                         "frac_of_peak": round(rate / peak, 4)}
+                         "frac_of_peak": round(rate / peak, 4), "kernels": n_kernels[op]}
 
     gemm_ms = op_ms["gemm_w4a16"]
-    dom = max(ops, key=lambda o: op_ms[o])
+    dom = max((o for o in ops if n_kernels[o] == 1), key=lambda o: op_ms[o])
     d_unit, d_amount, d_peak = work[dom]
     d_rate = d_amount / (op_ms[dom] * 1e-3) / (1e9 if d_unit == "GB/s" else 1e12)
     roofline = {"bound": "mfma" if d_unit == "TFLOP/s" else "hbm", "kernel": dom, "achieved": round(d_rate, 2),
-                "peak": d_peak, "unit": d_unit, "frac": round(d_rate / d_peak, 4), "traffic": None}
+                "peak": d_peak, "unit": d_unit, "frac": round(d_rate / d_peak, 4),
+                "traffic": measured_traffic(dom)}
 
     q_gbs = work["quantize"][1] / (op_ms["quantize"] * 1e-3) / 1e9
     out = {
@@ -172,7 +179,37 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w_np)
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     print(json.dumps(out), flush=True)
+
+
+def measured_traffic(op):
+    """HBM bytes per launch of the op's kernel from the committed counter summary, if that summary was
+    taken on the current kernel source (it records the source's SHA-256); otherwise None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_attention_projection.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    src = fields.get(f"{op}.source")
+    if not src or f"{op}.bytes" not in fields:
+        return None
+    h = hashlib.sha256()
+    for p in src.split(","):
+        h.update(open(os.path.join(ROOT, p.strip()), "rb").read())
+    if h.hexdigest() != fields.get(f"{op}.source_sha256"):
+        return None
+    return float(fields[f"{op}.bytes"])
 
 
 def cpu_baseline(w_np):
