@@ -13,9 +13,20 @@
 // to the bf16 matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation); the global scale(s)
 // multiply the fp32 sums in the epilogue.
 //
-// k_gemm_tile: BM x BN output tile per workgroup, K in steps of 64.  The next K step's global data
-// (bf16 A rows, W codes + scale bytes) is loaded into registers while the matrix cores work on the
-// current step from LDS; after a barrier the registers are expanded and written to LDS.
+// k_gemm_mfma (K % 64 == 0): BM x BN output tile per workgroup, K in steps of 64.
+//   - bf16 A rows go straight from global memory into LDS (buffer loads with the LDS bit), three
+//     stages deep, so a tile arrives two steps before it is used without passing through registers;
+//     each 128-byte LDS row stores its 16-byte chunks XOR-swizzled by the row index, which keeps the
+//     matrix-fragment reads free of bank conflicts without padding.
+//   - NVFP4 operands (W, and A in the W4A4 form) are loaded two steps ahead into registers, one
+//     code dword (8 elements) and its scale byte per unit, spread evenly over all threads; the
+//     units of step s + 1 are expanded exactly and written to the other LDS stage between the
+//     matrix instructions of step s.  One barrier ends each step.
+//   - The block scale byte is decoded by the hardware FP8 conversion (OCP e4m3).
+//   - W4A4 expands both operands to f16 instead of bf16: e2m1 x s lies in [2^-10, 2688] with at
+//     most 6 significant bits, so it is exact in f16 as well, and the f16 form needs half the
+//     instructions (packed conversion, then one packed multiply per pair).
+// k_gemm_tile: the same tiling for K % 64 != 0, with plain loads and bounds checks on K.
 // Workgroup ids are remapped so that the workgroups the hardware places on one XCD (ids congruent
 // mod 8) take neighbouring tiles that share W columns in that XCD's L2.
 //
@@ -24,6 +35,8 @@
 // bf16 dot2 instructions and applies the block scale once per block; a wave reduction finishes
 // each row.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "common.h"
 #include "internal.h"
@@ -44,16 +57,27 @@ __device__ __forceinline__ u32x4 expand8(uint32_t w, float s) {
     return o;
 }
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// Expand 8 codes (one dword) with block scale s (as an f16 pair (s, s)) into 8 exact f16 values.
+__device__ __forceinline__ u32x4 expand8_f16(uint32_t w, f16x2 s2) {
+    u32x4 o;
+    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2);
+    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2);
+    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2);
+    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2);
+    return o;
+}
+
 // Raw global data of one 32-element NVFP4 chunk (two blocks): 16 code bytes and 2 scale bytes.
 struct QChunk {
     u32x4 codes;
     uint32_t sc;  // scale byte of block 0 in bits 0..7, block 1 in bits 8..15
 };
 
-// Load chunk (row, k0..k0+31) of an NVFP4 operand with `rows` rows and K columns.  Missing rows and
-// columns read as zero.  KALIGNED: K % 64 == 0, so whole 16-byte code loads and 2-byte scale loads
-// are aligned and in range.
-template <bool KALIGNED>
+// Load chunk (row, k0..k0+31) of an NVFP4 operand with `rows` rows and K columns (K % 16 == 0).
+// Missing rows and columns read as zero.
 __device__ __forceinline__ QChunk load_qchunk(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
                                               int64_t row, int64_t rows, int64_t K, int64_t k0) {
     QChunk c;
@@ -62,51 +86,25 @@ __device__ __forceinline__ QChunk load_qchunk(const uint8_t *__restrict__ codes,
     if (row >= rows) return c;
     const uint8_t *crow = codes + row * (K / 2);
     const uint8_t *srow = scales + row * (K / 16);
-    if (KALIGNED) {
-        c.codes = *reinterpret_cast<const u32x4 *>(crow + k0 / 2);
-        c.sc = *reinterpret_cast<const uint16_t *>(srow + k0 / 16);
-    } else {
-        if (k0 + 16 <= K) {
-            u32x2 lo = *reinterpret_cast<const u32x2 *>(crow + k0 / 2);
-            c.codes[0] = lo[0];
-            c.codes[1] = lo[1];
-            c.sc = srow[k0 / 16];
-        }
-        if (k0 + 32 <= K) {
-            u32x2 hi = *reinterpret_cast<const u32x2 *>(crow + k0 / 2 + 8);
-            c.codes[2] = hi[0];
-            c.codes[3] = hi[1];
-            c.sc |= (uint32_t)srow[k0 / 16 + 1] << 8;
-        }
+    if (k0 + 16 <= K) {
+        u32x2 lo = *reinterpret_cast<const u32x2 *>(crow + k0 / 2);
+        c.codes[0] = lo[0];
+        c.codes[1] = lo[1];
+        c.sc = srow[k0 / 16];
+    }
+    if (k0 + 32 <= K) {
+        u32x2 hi = *reinterpret_cast<const u32x2 *>(crow + k0 / 2 + 8);
+        c.codes[2] = hi[0];
+        c.codes[3] = hi[1];
+        c.sc |= (uint32_t)srow[k0 / 16 + 1] << 8;
     }
     return c;
-}
-
-// Expand a chunk into LDS row `dst` (32 bf16 = 64 bytes).
-__device__ __forceinline__ void store_qchunk(__bf16 *dst, const QChunk &c) {
-    const float s0 = e4m3_to_f32(c.sc & 0xFFu);
-    const float s1 = e4m3_to_f32((c.sc >> 8) & 0xFFu);
-    u32x4 *d = reinterpret_cast<u32x4 *>(dst);
-    d[0] = expand8(c.codes[0], s0);
-    d[1] = expand8(c.codes[1], s0);
-    d[2] = expand8(c.codes[2], s1);
-    d[3] = expand8(c.codes[3], s1);
 }
 
 // A buffer resource over [base, base + bytes): loads at offsets at or past `bytes` return zero
 // instead of touching memory, which keeps the main-loop loads free of branches at tile edges.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// Chunk (tile row r, k0 .. k0 + 31) of an NVFP4 operand through buffer resources whose bases are the
-// tile's first row (K % 64 == 0: code rows are K/2 bytes, scale rows K/16 bytes).
-__device__ __forceinline__ QChunk load_qchunk_buf(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs, uint32_t r,
-                                                  uint32_t K, uint32_t k0) {
-    QChunk c;
-    c.codes = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, r * (K / 2) + k0 / 2, 0, 0));
-    c.sc = __builtin_amdgcn_raw_buffer_load_b16(rs, r * (K / 16) + k0 / 16, 0, 0);
-    return c;
 }
 
 // Tile id -> (m-tile, n-tile).  The hardware hands workgroup i to XCD i % 8; ids are first remapped
@@ -126,7 +124,7 @@ __device__ __forceinline__ void tile_coords(int id, int tiles_m, int tiles_n, in
     tn = r / gm;
 }
 
-template <int BM, int BN, int WM, int WN, bool A_Q, bool KALIGNED>
+template <int BM, int BN, int WM, int WN, bool A_Q>
 __global__ __launch_bounds__(64 * WM *WN) void k_gemm_tile(const __bf16 *__restrict__ A, int64_t lda,
                                                           const uint8_t *__restrict__ a_codes,
                                                           const uint8_t *__restrict__ a_scales,
@@ -168,46 +166,7 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_tile(const __bf16 *__restr
     };
     Staging st0, st1;
 
-    // K % 64 == 0: buffer loads relative to the tile's first row; rows past M or N read as zero.
-    __amdgpu_buffer_rsrc_t ra = make_rsrc(A, 0), rac = make_rsrc(a_codes, 0), ras = make_rsrc(a_scales, 0),
-                           rwc = make_rsrc(w_codes, 0), rws = make_rsrc(w_scales, 0);
-    if constexpr (KALIGNED) {
-        const int64_t mrows = (M - m0) < BM ? (M - m0) : BM;
-        const int64_t nrows = (N - n0) < BN ? (N - n0) : BN;
-        if constexpr (!A_Q) {
-            ra = make_rsrc(A + m0 * lda, ((mrows - 1) * lda + K) * 2);
-        } else {
-            rac = make_rsrc(a_codes + m0 * (K / 2), mrows * (K / 2));
-            ras = make_rsrc(a_scales + m0 * (K / 16), mrows * (K / 16));
-        }
-        rwc = make_rsrc(w_codes + n0 * (K / 2), nrows * (K / 2));
-        rws = make_rsrc(w_scales + n0 * (K / 16), nrows * (K / 16));
-    }
-
     auto load_step = [&](int64_t k0, Staging &st) {
-        if constexpr (KALIGNED) {
-            if constexpr (!A_Q) {
-#pragma unroll
-                for (int p = 0; p < A_BF_PASSES; p++) {
-                    const int idx = p * NT + tid;
-                    const uint32_t r = idx / (kBK / 8), c8 = idx % (kBK / 8);
-                    st.a[p] = __builtin_bit_cast(
-                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (uint32_t)((r * lda + k0 + c8 * 8) * 2), 0, 0));
-                }
-            } else {
-#pragma unroll
-                for (int p = 0; p < A_Q_PASSES; p++) {
-                    const int idx = (p * NT + tid) % (BM * 2);  // spare lanes repeat a valid chunk
-                    st.aq[p] = load_qchunk_buf(rac, ras, idx / 2, (uint32_t)K, (uint32_t)k0 + (idx % 2) * 32);
-                }
-            }
-#pragma unroll
-            for (int p = 0; p < W_PASSES; p++) {
-                const int idx = (p * NT + tid) % (BN * 2);
-                st.w[p] = load_qchunk_buf(rwc, rws, idx / 2, (uint32_t)K, (uint32_t)k0 + (idx % 2) * 32);
-            }
-            return;
-        }
         if constexpr (!A_Q) {
 #pragma unroll
             for (int p = 0; p < A_BF_PASSES; p++) {
@@ -225,7 +184,7 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_tile(const __bf16 *__restr
             for (int p = 0; p < A_Q_PASSES; p++) {
                 const int idx = p * NT + tid;
                 if (idx < BM * 2) {
-                    st.aq[p] = load_qchunk<false>(a_codes, a_scales, m0 + idx / 2, M, K, k0 + (idx % 2) * 32);
+                    st.aq[p] = load_qchunk(a_codes, a_scales, m0 + idx / 2, M, K, k0 + (idx % 2) * 32);
                 }
             }
         }
@@ -233,7 +192,7 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_tile(const __bf16 *__restr
         for (int p = 0; p < W_PASSES; p++) {
             const int idx = p * NT + tid;
             if (idx < BN * 2) {
-                st.w[p] = load_qchunk<false>(w_codes, w_scales, n0 + idx / 2, N, K, k0 + (idx % 2) * 32);
+                st.w[p] = load_qchunk(w_codes, w_scales, n0 + idx / 2, N, K, k0 + (idx % 2) * 32);
             }
         }
     };
@@ -371,6 +330,252 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_tile(const __bf16 *__restr
 }
 
 // ------------------------------------------------------------------------------------------------
+// k_gemm_mfma: K % 64 == 0
+// ------------------------------------------------------------------------------------------------
+template <int V>
+struct StepIdx {
+    static constexpr int value = V;
+};
+
+// s_waitcnt immediate: wait until at most `vm` vector-memory and `lgkm` LDS operations are pending.
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | ((vm >> 4) << 14); }
+
+// 16 bytes per lane from buffer `r` at (voff + soff) straight into LDS: lane l writes lds + 16 l.
+__device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
+}
+
+template <int BM, int BN, int WM, int WN, bool A_Q>
+__global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restrict__ A, int64_t lda,
+                                                          const uint8_t *__restrict__ a_codes,
+                                                          const uint8_t *__restrict__ a_scales,
+                                                          const float *__restrict__ a_g,
+                                                          const uint8_t *__restrict__ w_codes,
+                                                          const uint8_t *__restrict__ w_scales,
+                                                          const float *__restrict__ w_g, float *__restrict__ C,
+                                                          int64_t ldc, int64_t M, int64_t N, int64_t K) {
+    constexpr int NT = 64 * WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;    // wave tile
+    constexpr int TM = WTM / 32, TN = WTN / 32;    // 32x32 MFMA tiles per wave
+    constexpr int ROWB = kBK * 2;                  // LDS row: 64 16-bit values, no padding
+    constexpr int A_STAGE = BM * ROWB, W_STAGE = BN * ROWB;
+    constexpr int NA = A_Q ? 2 : 3;                // A stages (three for the two-step-ahead DMA)
+    constexpr int W_OFF = NA * A_STAGE;
+    constexpr int LDS_BYTES = W_OFF + 2 * W_STAGE;
+    constexpr int WD = BN * 8 / NT;                // W code dwords per thread per step
+    constexpr int AD = A_Q ? BM * 8 / NT : 0;      // A code dwords per thread per step (W4A4)
+    constexpr int QD = AD + WD;                    // expansion units per thread per step
+    constexpr int A_DMA = A_Q ? 0 : BM / 8 / (WM * WN);  // 1 KiB direct-to-LDS loads per wave per step
+    constexpr int VM_STEP = A_DMA + 2 * QD;        // vector-memory instructions issued per step
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(BN * 8 % NT == 0 && BM * 8 % NT == 0 && (A_Q || BM / 8 % (WM * WN) == 0), "even split");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
+    static_assert(VM_STEP < 64, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
+
+    const int tiles_m = (int)((M + BM - 1) / BM);
+    const int tiles_n = (int)((N + BN - 1) / BN);
+    int tm_idx, tn_idx;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, tm_idx, tn_idx);
+    const int64_t m0 = (int64_t)tm_idx * BM;
+    const int64_t n0 = (int64_t)tn_idx * BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wid / WN, wn = wid % WN;
+
+    // Buffer resources start at the tile's first row; rows past M or N fall outside them and read
+    // as zero, so no load needs a bounds check (those rows only feed outputs that are not stored).
+    const int64_t mrows = (M - m0) < BM ? (M - m0) : BM;
+    const int64_t nrows = (N - n0) < BN ? (N - n0) : BN;
+    __amdgpu_buffer_rsrc_t ra = make_rsrc(A, 0);
+    __amdgpu_buffer_rsrc_t rc[2], rs[2];  // NVFP4 codes / scales: [0] A (W4A4), [1] W
+    rc[0] = rs[0] = make_rsrc(a_codes, 0);
+    if constexpr (!A_Q) {
+        ra = make_rsrc(A + m0 * lda, ((mrows - 1) * lda + K) * 2);
+    } else {
+        rc[0] = make_rsrc(a_codes + m0 * (K / 2), mrows * (K / 2));
+        rs[0] = make_rsrc(a_scales + m0 * (K / 16), mrows * (K / 16));
+    }
+    rc[1] = make_rsrc(w_codes + n0 * (K / 2), nrows * (K / 2));
+    rs[1] = make_rsrc(w_scales + n0 * (K / 16), nrows * (K / 16));
+
+    // Expansion unit u of this thread: code dword d = tid + NT * j of the step's tile (row d / 8,
+    // dword d % 8), j = u for A (u < AD), u - AD for W.  LDS rows hold 16-byte chunks at chunk
+    // index (chunk ^ row % 8).
+    uint32_t q_coff[QD], q_soff[QD], q_lds[QD];
+#pragma unroll
+    for (int u = 0; u < QD; u++) {
+        const int j = u < AD ? u : u - AD;
+        const uint32_t d = (uint32_t)(tid + NT * j), row = d >> 3, c = d & 7;
+        q_coff[u] = row * (uint32_t)(K / 2) + c * 4;
+        q_soff[u] = row * (uint32_t)(K / 16) + (c >> 1);
+        q_lds[u] = (u < AD ? 0u : (uint32_t)W_OFF) + row * ROWB + ((c ^ (row & 7)) << 4);
+    }
+    // Direct-to-LDS load b of this wave fills the 1 KiB LDS block of tile rows (wid * A_DMA + b) * 8
+    // .. + 7: lane l writes 16 bytes at l * 16, i.e. row l / 8, swizzled chunk l % 8, so it loads
+    // logical chunk (l % 8) ^ (row % 8).
+    uint32_t a_dma_off;
+    {
+        const uint32_t row = (uint32_t)(wid * A_DMA) * 8 + (uint32_t)(lane >> 3);
+        const uint32_t c = (uint32_t)((lane & 7) ^ ((lane >> 3) & 7));
+        a_dma_off = row * (uint32_t)lda * 2 + c * 16;
+    }
+    // Fragment reads: 32x32x16 operands take row (lane % 32), k = 16 kk + 8 (lane / 32) .. + 7.
+    uint32_t offA[4], offB[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++) {
+        const uint32_t ch = ((uint32_t)(2 * kk + (lane >> 5)) ^ (uint32_t)(lane & 7)) << 4;
+        offA[kk] = (uint32_t)(wm * WTM + (lane & 31)) * ROWB + ch;
+        offB[kk] = (uint32_t)W_OFF + (uint32_t)(wn * WTN + (lane & 31)) * ROWB + ch;
+    }
+
+    uint32_t qc[2][QD], qs[2][QD];  // two register sets of code dwords and scale bytes
+
+    const int nsteps = (int)(K / kBK);
+    const int last = nsteps - 1;
+    // Loads past the last step repeat it: harmless, and the loop body stays free of branches.
+    auto issue = [&](int s, int a_stage, int r) {
+        const uint32_t k0 = (uint32_t)((s < last ? s : last) * kBK);
+        if constexpr (!A_Q) {
+#pragma unroll
+            for (int b = 0; b < A_DMA; b++)
+                load_to_lds16(ra, smem + a_stage * A_STAGE + (wid * A_DMA + b) * 1024,
+                              a_dma_off + (uint32_t)(b * 8) * (uint32_t)lda * 2, k0 * 2);
+        }
+#pragma unroll
+        for (int u = 0; u < QD; u++) {
+            const int o = u < AD ? 0 : 1;
+            qc[r][u] = __builtin_amdgcn_raw_buffer_load_b32(rc[o], q_coff[u], k0 / 2, 0);
+            qs[r][u] = __builtin_amdgcn_raw_buffer_load_b8(rs[o], q_soff[u], k0 / 16, 0);
+        }
+    };
+    auto expand_unit = [&](int u, int r, int a_stage, int w_stage) {
+        const uint32_t base = u < AD ? (uint32_t)(a_stage * A_STAGE) : (uint32_t)(w_stage * W_STAGE);
+        const float sc = __builtin_amdgcn_cvt_f32_fp8((int)qs[r][u], 0);
+        u32x4 v;
+        if constexpr (A_Q) {
+            const _Float16 sh = (_Float16)sc;
+            v = expand8_f16(qc[r][u], f16x2{sh, sh});
+        } else {
+            v = expand8(qc[r][u], sc);
+        }
+        *reinterpret_cast<u32x4 *>(smem + base + q_lds[u]) = v;
+    };
+    // End of a step: this step's loads may still be in flight, everything older (the A tile of the
+    // next step) has landed; LDS writes are done; then the workgroup barrier.
+    auto end_step = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(VM_STEP, 0));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
+
+    // prologue: steps 0 and 1 in flight, step 0 expanded
+    issue(0, 0, 0);
+    issue(1, 1, 1);
+#pragma unroll
+    for (int u = 0; u < QD; u++) expand_unit(u, 0, 0, 0);
+    end_step();
+
+    // Step s (S = s mod 6, so stage indices are constants): issue the loads of step s + 2, then the
+    // four 16-deep slices of matrix work from stages s, with the expansion of step s + 1 spread
+    // between them.
+    auto step = [&](auto Sc, int s) {
+        constexpr int S = decltype(Sc)::value;
+        constexpr int SA = A_Q ? S % 2 : S % 3;
+        constexpr int SW = S % 2;
+        constexpr int SN = (S + 1) % 2;
+        issue(s + 2, (S + 2) % 3, S % 2);
+        typedef typename std::conditional<A_Q, f16x8, bf16x8>::type frag_t;
+        frag_t af[2][TM], bfr[2][TN];
+        auto load_frags = [&](int kk, int b) {
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+                af[b][i] = *reinterpret_cast<const frag_t *>(smem + SA * A_STAGE + offA[kk] + i * 32 * ROWB);
+#pragma unroll
+            for (int j = 0; j < TN; j++)
+                bfr[b][j] = *reinterpret_cast<const frag_t *>(smem + SW * W_STAGE + offB[kk] + j * 32 * ROWB);
+        };
+        load_frags(0, 0);
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) {
+            if (kk < 3) load_frags(kk + 1, (kk + 1) & 1);
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int j = 0; j < TN; j++) {
+                    if constexpr (A_Q)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[kk & 1][i], bfr[kk & 1][j], acc[i][j], 0, 0, 0);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][i], bfr[kk & 1][j], acc[i][j], 0, 0, 0);
+                }
+#pragma unroll
+            for (int u = 0; u < QD; u++)
+                if (u * 4 / QD == kk) expand_unit(u, SN, SN, SN);
+            // order within the slice: next fragments' reads, then matrix instructions with the
+            // expansion arithmetic placed between them, then the LDS writes
+            if (kk < 3) __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - 3, 0);
+        }
+        end_step();
+    };
+
+    int s = 0;
+    for (; s + 6 <= nsteps; s += 6) {
+        step(StepIdx<0>{}, s);
+        step(StepIdx<1>{}, s + 1);
+        step(StepIdx<2>{}, s + 2);
+        step(StepIdx<3>{}, s + 3);
+        step(StepIdx<4>{}, s + 4);
+        step(StepIdx<5>{}, s + 5);
+    }
+    if (s < nsteps) step(StepIdx<0>{}, s);
+    if (s + 1 < nsteps) step(StepIdx<1>{}, s + 1);
+    if (s + 2 < nsteps) step(StepIdx<2>{}, s + 2);
+    if (s + 3 < nsteps) step(StepIdx<3>{}, s + 3);
+    if (s + 4 < nsteps) step(StepIdx<4>{}, s + 4);
+    // no direct-to-LDS load may still be writing when the workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+
+    // ---- epilogue: multiply by the global scale(s), store fp32 ----
+    const float gw = *w_g;
+    const float ga = A_Q ? *a_g : 1.0f;
+#pragma unroll
+    for (int i = 0; i < TM; i++) {
+#pragma unroll
+        for (int j = 0; j < TN; j++) {
+            const int64_t col = n0 + wn * WTN + j * 32 + (lane % 32);
+#pragma unroll
+            for (int e = 0; e < 16; e++) {
+                const int64_t row = m0 + wm * WTM + i * 32 + 8 * (e / 4) + 4 * (lane / 32) + (e % 4);
+                if (row < M && col < N) {
+                    float v = acc[i][j][e];
+                    if (A_Q) v = v * ga;
+                    C[row * ldc + col] = v * gw;
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
 // GEMV, M <= 4
 // ------------------------------------------------------------------------------------------------
 template <int MM, bool A_Q>
@@ -475,18 +680,20 @@ static void launch_tile(const void *a_bf16, int64_t lda, const nvfp4_tensor *a_q
                         float *c, int64_t ldc, hipStream_t stream) {
     const int64_t N = w->rows, K = w->cols;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    const bool kal = (K % kBK) == 0;
     const uint8_t *ac = A_Q ? a_q->codes : nullptr;
     const uint8_t *as = A_Q ? a_q->scales : nullptr;
     const float *ag = A_Q ? a_q->global_scale : nullptr;
-    if (kal) {
-        hipLaunchKernelGGL((k_gemm_tile<BM, BN, WM, WN, A_Q, true>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0,
-                           stream, (const __bf16 *)a_bf16, lda, ac, as, ag, w->codes, w->scales, w->global_scale, c,
-                           ldc, M, N, K);
+    // k_gemm_mfma addresses one tile's rows with 32-bit buffer offsets
+    const int64_t lim = (int64_t)1 << 31;
+    const bool fits = (int64_t)(BM + 1) * (A_Q ? K / 2 : lda * 2) + K * 2 < lim && (int64_t)BN * (K / 2) < lim;
+    if (K % kBK == 0 && fits) {
+        hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, A_Q>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0, stream,
+                           (const __bf16 *)a_bf16, lda, ac, as, ag, w->codes, w->scales, w->global_scale, c, ldc, M,
+                           N, K);
     } else {
-        hipLaunchKernelGGL((k_gemm_tile<BM, BN, WM, WN, A_Q, false>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0,
-                           stream, (const __bf16 *)a_bf16, lda, ac, as, ag, w->codes, w->scales, w->global_scale, c,
-                           ldc, M, N, K);
+        hipLaunchKernelGGL((k_gemm_tile<BM, BN, WM, WN, A_Q>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0, stream,
+                           (const __bf16 *)a_bf16, lda, ac, as, ag, w->codes, w->scales, w->global_scale, c, ldc, M,
+                           N, K);
     }
 }
 

@@ -409,29 +409,54 @@ static uint32_t next_epoch() {
     return counter.fetch_add(0x61C88647u, std::memory_order_relaxed) | 1u;
 }
 
+// Largest residency (tiles per wave) whose registers still leave room for two workgroups per CU.
+template <int SRC>
+constexpr int kMaxTpw = SRC == NVFP4_F32 ? 6 : SRC == NVFP4_BF16 ? 8 : SRC == NVFP4_F16 ? 12 : 16;
+
+// Workgroups of k_quant_fused<SRC, TPW> that can be resident on one CU (at most kFusedPerCu),
+// from the runtime's occupancy calculation; computed once per instantiation.
+template <int SRC, int TPW>
+static int fused_per_cu() {
+    static std::atomic<int> cached{0};
+    int n = cached.load(std::memory_order_relaxed);
+    if (n == 0) {
+        int b = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_quant_fused<SRC, TPW>, 256, 0) != hipSuccess || b < 1)
+            b = 1;
+        n = b < kFusedPerCu ? b : kFusedPerCu;
+        cached.store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// The grid barrier needs every workgroup resident at once, so the grid never exceeds what the
+// CUs hold; waves then take more tiles than TPW and stream the rest.
 template <int SRC, int TPW>
 static void launch_fused(const TileGeom &gm, int grid, const float *src_scale, uint32_t *ws, const nvfp4_tensor *out,
-                         int32_t *flags, hipStream_t stream) {
+                         int32_t *flags, int num_cus, hipStream_t stream) {
+    const int cap = fused_per_cu<SRC, TPW>() * num_cus;
+    if (grid > cap) grid = cap;
     hipLaunchKernelGGL((k_quant_fused<SRC, TPW>), dim3(grid), dim3(256), 0, stream, gm, src_scale, ws, next_epoch(),
                        out->codes, out->scales, out->global_scale, flags);
 }
 
 // Tiles spread over all CUs (two workgroups each, so that two waves share every SIMD and hide each
 // other's latencies; fewer for small tensors); tiles per wave rounded up to a supported residency,
-// 16 at most (the rest streams twice).
+// kMaxTpw<SRC> at most (the rest streams twice).
 template <int SRC>
 static void launch_fused_any(const TileGeom &gm, const float *src_scale, uint32_t *ws, const nvfp4_tensor *out,
                              int32_t *flags, int num_cus, hipStream_t stream) {
     const uint64_t ntiles = (gm.nblocks + 63) / 64;
     const int grid = grid_for(ntiles, 4, kFusedPerCu * num_cus);
     const uint64_t tpw = (ntiles + 4 * (uint64_t)grid - 1) / (4 * (uint64_t)grid);
-    if (tpw <= 1) launch_fused<SRC, 1>(gm, grid, src_scale, ws, out, flags, stream);
-    else if (tpw <= 2) launch_fused<SRC, 2>(gm, grid, src_scale, ws, out, flags, stream);
-    else if (tpw <= 4) launch_fused<SRC, 4>(gm, grid, src_scale, ws, out, flags, stream);
-    else if (tpw <= 6) launch_fused<SRC, 6>(gm, grid, src_scale, ws, out, flags, stream);
-    else if (tpw <= 8) launch_fused<SRC, 8>(gm, grid, src_scale, ws, out, flags, stream);
-    else if (tpw <= 12) launch_fused<SRC, 12>(gm, grid, src_scale, ws, out, flags, stream);
-    else launch_fused<SRC, 16>(gm, grid, src_scale, ws, out, flags, stream);
+    constexpr int T = kMaxTpw<SRC>;
+    if (tpw <= 1) launch_fused<SRC, 1>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
+    else if (tpw <= 2) launch_fused<SRC, 2>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
+    else if (tpw <= 4) launch_fused<SRC, 4>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
+    else if (tpw <= 6 || T == 6) launch_fused<SRC, 6>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
+    else if (tpw <= 8 || T == 8) launch_fused<SRC, (T < 8 ? T : 8)>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
+    else if (tpw <= 12 || T == 12) launch_fused<SRC, (T < 12 ? T : 12)>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
+    else launch_fused<SRC, T>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
 }
 
 template <int SRC>

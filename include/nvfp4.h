@@ -89,8 +89,10 @@ enum { NVFP4_OP_QUANTIZE = 0, NVFP4_OP_DEQUANTIZE = 1, NVFP4_OP_GEMM = 2, NVFP4_
  *      even code, saturating at 6), sign bit = sign bit of v; s = 0 gives magnitude 0;
  *   6. pack two codes per byte, low nibble first.
  * Arguments: x_dtype any of nvfp4_dtype; src_scale only for NVFP4_E4M3 (must be > 0 if given);
- * amax_in NULL for the run-time amax; flags nullable (bit 0 = non-finite input seen, outputs then
- * unspecified); workspace of nvfp4_workspace_size(NVFP4_OP_QUANTIZE, rows, cols, 0) bytes.
+ * amax_in NULL for the run-time amax; flags nullable (bit 0 = non-finite input seen; bit 1 = the
+ * run-time amax could not be agreed because other work kept part of the grid off the GPU for a
+ * bounded wait; outputs are unspecified when either is set); workspace of
+ * nvfp4_workspace_size(NVFP4_OP_QUANTIZE, rows, cols, 0) bytes.
  * src_scale, amax_in, flags and workspace are device pointers.
  */
 nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype x_dtype, int64_t ld_x, const float *src_scale,

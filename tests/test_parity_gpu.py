@@ -31,6 +31,16 @@ def _note(*a):
     sys.stdout.flush()
 
 
+def _quant(nv, x, **kw):
+    """nvfp4_quantize with a flags word that must stay clear: no non-finite input and no
+    incomplete grid agreement on amax."""
+    flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+    q = nv.quantize(x, flags=flags, **kw)
+    f = int(flags.item())
+    assert f == 0, f"quantize flags {f:#x}"
+    return q
+
+
 def _assert_q_equal(q, ref, what=""):
     codes = q.codes.cpu().numpy()
     scales = q.scales.cpu().numpy()
@@ -49,7 +59,7 @@ def _assert_q_equal(q, ref, what=""):
 def test_tiny_quantize_expand(nv):
     d = synth.tiny()
     _note("tiny 64x256 fp32")
-    q = nv.quantize(to_dev_f32(d["w"]))
+    q = _quant(nv, to_dev_f32(d["w"]))
     ref, flags = oracle.quantize(d["w"])
     _assert_q_equal(q, ref, "tiny")
     f32 = nv.dequantize(q, torch.float32).cpu().numpy()
@@ -78,10 +88,10 @@ def test_quantize_shapes_dtypes(nv, shape, dtype):
     else:
         h = x.astype(np.float16).view(np.uint16)
         xd, ref = to_dev_f16(h), oracle.quantize(h, oracle.F16)[0]
-    _assert_q_equal(nv.quantize(xd), ref, f"{dtype} {shape}")
+    _assert_q_equal(_quant(nv, xd), ref, f"{dtype} {shape}")
     # the same matrix with a larger row stride
     if rows > 1:
-        _assert_q_equal(nv.quantize(padded(xd, 16)), ref, f"{dtype} {shape} strided")
+        _assert_q_equal(_quant(nv, padded(xd, 16)), ref, f"{dtype} {shape} strided")
 
 
 def test_quantize_static_amax_clips(nv):
@@ -90,7 +100,7 @@ def test_quantize_static_amax_clips(nv):
     x = rng.standard_normal((128, 512)).astype(np.float32)
     for amax in [0.5, 1.0, 3.0, 1e6]:
         ref, _ = oracle.quantize(x, amax=amax)
-        q = nv.quantize(to_dev_f32(x), amax=torch.tensor([amax], dtype=torch.float32, device=DEV))
+        q = _quant(nv, to_dev_f32(x), amax=torch.tensor([amax], dtype=torch.float32, device=DEV))
         _assert_q_equal(q, ref, f"amax {amax}")
 
 
@@ -99,18 +109,18 @@ def test_quantize_zero_negzero_tiny(nv):
     for x in [np.zeros((4, 64), np.float32), -np.zeros((4, 64), np.float32),
               np.full((4, 64), 1e-40, np.float32), np.full((2, 32), 3e-45, np.float32)]:
         ref, _ = oracle.quantize(x)
-        _assert_q_equal(nv.quantize(to_dev_f32(x)), ref, f"const {x.ravel()[0]}")
+        _assert_q_equal(_quant(nv, to_dev_f32(x)), ref, f"const {x.ravel()[0]}")
     # blocks far below the tensor amax: scale byte 0, all magnitudes 0
     x = np.ones((2, 64), np.float32) * 1e-9
     x[0, 0] = 1e3
     ref, _ = oracle.quantize(x)
-    _assert_q_equal(nv.quantize(to_dev_f32(x)), ref, "dynamic range")
+    _assert_q_equal(_quant(nv, to_dev_f32(x)), ref, "dynamic range")
     # very small tensors: g denormal, s * g tiny, reciprocal overflow
     rng = np.random.default_rng(6)
     for scale in [1e-38, 1e-40, 1e-42, 1e-44]:
         x = (rng.standard_normal((8, 64)) * scale).astype(np.float32)
         ref, _ = oracle.quantize(x)
-        _assert_q_equal(nv.quantize(to_dev_f32(x)), ref, f"scale {scale}")
+        _assert_q_equal(_quant(nv, to_dev_f32(x)), ref, f"scale {scale}")
 
 
 def test_quantize_nonfinite_sets_flag(nv):
@@ -138,7 +148,7 @@ def test_requantize_all_e4m3_bytes(nv):
     for sc in [None, 0.0123, 1e-30, 3.7e3]:
         ref, _ = oracle.quantize(x, oracle.E4M3, sc)
         s = None if sc is None else torch.tensor([sc], dtype=torch.float32, device=DEV)
-        q = nv.quantize(to_dev_u8(x).view(torch.float8_e4m3fn), src_scale=s)
+        q = _quant(nv, to_dev_u8(x).view(torch.float8_e4m3fn), src_scale=s)
         _assert_q_equal(q, ref, f"e4m3 scale {sc}")
     x2 = x.copy()
     x2[3, 5] = 0xFF
@@ -151,7 +161,7 @@ def test_requantize_modulation_fp8(nv):
     _note("requantize one 18432x3072 FP8 modulation weight")
     b, sc = synth.modulation_fp8(0)
     ref, _ = oracle.quantize(b, oracle.E4M3, float(sc))
-    q = nv.quantize(to_dev_u8(b), src_scale=torch.tensor([sc], dtype=torch.float32, device=DEV))
+    q = _quant(nv, to_dev_u8(b), src_scale=torch.tensor([sc], dtype=torch.float32, device=DEV))
     _assert_q_equal(q, ref, "modulation fp8")
 
 
@@ -159,7 +169,7 @@ def test_quantize_attention_weight_full(nv):
     _note("quantize 3072x3072 fp32 attention weight")
     w = synth.attn_proj_weight()
     ref, _ = oracle.quantize(w)
-    q = nv.quantize(to_dev_f32(w))
+    q = _quant(nv, to_dev_f32(w))
     _assert_q_equal(q, ref, "attn weight")
     f32 = nv.dequantize(q, torch.float32).cpu().numpy()
     assert np.array_equal(f32.view(np.uint32), oracle.dequantize(ref, "f32").view(np.uint32))
@@ -195,7 +205,7 @@ def test_dequantize_random_codes(nv, shape):
 def _rand_q(nv, rows, cols, seed, sigma=0.02):
     w = synth.normal_f32((rows, cols), sigma, seed)
     ref, _ = oracle.quantize(w)
-    q = nv.quantize(to_dev_f32(w))
+    q = _quant(nv, to_dev_f32(w))
     _assert_q_equal(q, ref, f"weight {rows}x{cols}")
     return q, ref
 
@@ -223,7 +233,7 @@ def test_gemm_w4a4(nv, mnk):
     _note(f"gemm w4a4 {mnk}")
     q, ref = _rand_q(nv, n, k, seed=m * 17 + n)
     a_bits = synth.bf16_bits(np.random.default_rng(m * 3 + k).standard_normal((m, k)).astype(np.float32))
-    aq = nv.quantize(to_dev_bf16(a_bits))
+    aq = _quant(nv, to_dev_bf16(a_bits))
     aref, _ = oracle.quantize(a_bits, oracle.BF16)
     _assert_q_equal(aq, aref, "activations")
     c = nv.gemm(aq, q).cpu().numpy()
@@ -246,7 +256,7 @@ def test_gemm_one_hot_reproduces_expansion(nv):
 
 def test_gemm_zero_weight_and_empty(nv):
     _note("gemm zero weight / empty")
-    z = nv.quantize(to_dev_f32(np.zeros((64, 128), np.float32)))
+    z = _quant(nv, to_dev_f32(np.zeros((64, 128), np.float32)))
     a = to_dev_bf16(synth.bf16_bits(np.ones((8, 128), np.float32)))
     assert not nv.gemm(a, z).cpu().numpy().any()
     # K = 0: C = 0
@@ -264,14 +274,14 @@ def test_gemm_attention_projection_full(nv):
     w = synth.attn_proj_weight()
     a_bits = synth.attn_proj_activations()
     ref, _ = oracle.quantize(w)
-    q = nv.quantize(to_dev_f32(w))
+    q = _quant(nv, to_dev_f32(w))
     _assert_q_equal(q, ref, "attn weight")
     c = nv.gemm(to_dev_bf16(a_bits), q).cpu().numpy()
     cref = oracle.gemm_w4a16(a_bits, ref)
     err = oracle.gemm_error(c, cref)
     _note(f"  W4A16 floored max rel err {err:.3e}, normwise {np.abs(c - cref).max() / np.abs(cref).max():.3e}")
     assert err <= GEMM_TOL
-    aq = nv.quantize(to_dev_bf16(a_bits))
+    aq = _quant(nv, to_dev_bf16(a_bits))
     aref, _ = oracle.quantize(a_bits, oracle.BF16)
     _assert_q_equal(aq, aref, "activations")
     rows = np.random.default_rng(1).choice(4096, 256, replace=False)
@@ -284,7 +294,7 @@ def test_gemv_modulation_full(nv):
     _note("gemv M=2 over 18432x3072")
     w = synth.modulation_weight()
     ref, _ = oracle.quantize(w)
-    q = nv.quantize(to_dev_f32(w))
+    q = _quant(nv, to_dev_f32(w))
     _assert_q_equal(q, ref, "modulation weight")
     a_bits = synth.modulation_activations()
     c = nv.gemm(to_dev_bf16(a_bits), q).cpu().numpy()
@@ -342,7 +352,7 @@ def test_gemm_tile_configs(nv, mnk):
     a_bits = synth.bf16_bits(np.random.default_rng(m * 7 + k).standard_normal((m, k)).astype(np.float32))
     c = nv.gemm(to_dev_bf16(a_bits), q).cpu().numpy()
     assert oracle.gemm_error(c, oracle.gemm_w4a16(a_bits, ref)) <= GEMM_TOL
-    aq = nv.quantize(to_dev_bf16(a_bits))
+    aq = _quant(nv, to_dev_bf16(a_bits))
     aref, _ = oracle.quantize(a_bits, oracle.BF16)
     _assert_q_equal(aq, aref, "activations")
     c4 = nv.gemm(aq, q).cpu().numpy()
@@ -355,6 +365,6 @@ def test_quantize_large_tensor_overflow_path(nv):
     rng = np.random.default_rng(77)
     x = (rng.standard_normal((16384, 8192)) * 0.01).astype(np.float32)
     x[123, 4567] = 0.75
-    q = nv.quantize(to_dev_f32(x))
+    q = _quant(nv, to_dev_f32(x))
     ref, _ = oracle.quantize(x)
     _assert_q_equal(q, ref, "large")
