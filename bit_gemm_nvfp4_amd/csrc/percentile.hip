@@ -15,6 +15,13 @@
 //   k_pct_select  one wave per channel: a prefix sum over its counters picks the digit holding the
 //                 remaining rank, narrows the prefix and clears the counters for the next pass;
 //                 the last pass writes the results.
+// When the rank sits within 16 of either end of a channel (p99.9 over a few thousand rows: the
+// 5th largest of 4096), one pass suffices instead:
+//   k_pct_topm        every lane keeps, per channel it owns, the M largest keys it has seen (a
+//                     compare-exchange chain, branch-free), waves merge theirs through LDS, and each
+//                     workgroup stores its list and maximum per channel; for a rank near the bottom
+//                     the keys are complemented, so the same code keeps the smallest;
+//   k_pct_topm_final  one thread per channel merges the workgroups' lists and picks the rank.
 #include <hip/hip_runtime.h>
 
 #include "common.h"
@@ -203,6 +210,208 @@ __global__ __launch_bounds__(256) void k_pct_select(uint32_t *__restrict__ ws, i
     }
 }
 
+
+// ---------------------------------------------------------------------------------------------
+// One-pass selection near either end of each channel.
+// ---------------------------------------------------------------------------------------------
+// Workspace per channel (uint32 words, at most 259 of them): rchunks lists of M keys, then
+// rchunks maxima.
+constexpr int kTopmMax = 16;
+
+// Packed pair of 16-bit keys (bf16 / fp16 magnitudes, one channel per half) or one 31-bit key.
+template <bool H>
+__device__ __forceinline__ uint32_t key_max(uint32_t a, uint32_t b) {
+    if constexpr (H) {
+        typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
+    } else {
+        return a > b ? a : b;
+    }
+}
+template <bool H>
+__device__ __forceinline__ uint32_t key_min(uint32_t a, uint32_t b) {
+    if constexpr (H) {
+        typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
+    } else {
+        return a < b ? a : b;
+    }
+}
+// Insert key k into the descending list L[0..M): each step keeps the larger and passes the smaller on.
+template <bool H, int M>
+__device__ __forceinline__ void topm_insert(uint32_t (&L)[M], uint32_t k) {
+#pragma unroll
+    for (int i = 0; i < M; i++) {
+        const uint32_t hi = key_max<H>(L[i], k);
+        k = key_min<H>(L[i], k);
+        L[i] = hi;
+    }
+}
+
+// One workgroup per (64 * CPL channels, row chunk); lane l owns CPL consecutive channels (one 8-byte
+// load per row: four bf16 / fp16 or two fp32, kept as two words of packed or single keys), the
+// eight waves take every eighth row, two batches of U rows in flight per lane.  Keys are the
+// magnitude bits, XOR-complemented when `invert` (then the lists hold the smallest originals).
+// The waves' lists are then merged pairwise through LDS in three rounds.
+constexpr int kTopmWaves = 8;
+constexpr int kTopmU = 8;
+
+template <int DT, int M>
+__global__ __launch_bounds__(64 * kTopmWaves) void k_pct_topm(const uint8_t *__restrict__ x, int64_t rows,
+                                                             int64_t cols, int64_t ld_bytes, int rows_per_wg,
+                                                             int invert, int rchunks, uint32_t *__restrict__ ws) {
+    constexpr bool H = DT != NVFP4_F32;
+    constexpr int CPL = H ? 4 : 2;  // channels per lane
+    constexpr int CPW = H ? 2 : 1;  // channels per word
+    constexpr int U = kTopmU;
+    constexpr int NW = kTopmWaves;
+    __shared__ uint32_t lst[NW / 2][M + 1][2][64];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int64_t c0 = ((int64_t)blockIdx.x * 64 + lane) * CPL;
+    const bool active = c0 < cols;  // cols % 16 == 0: all channels of a lane are in or out
+    const int64_t r0 = (int64_t)blockIdx.y * rows_per_wg;
+    const int64_t r1 = (r0 + rows_per_wg) < rows ? (r0 + rows_per_wg) : rows;
+    const uint32_t mask = H ? 0x7FFF7FFFu : 0x7FFFFFFFu;
+    const uint32_t flip = invert ? mask : 0u;
+    // the chunk's rows only: loads past its last row read zero
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(x + r0 * ld_bytes), (short)0, (int)((r1 - r0) * ld_bytes), 0x00020000);
+    const uint32_t col_off = (uint32_t)(c0 * (H ? 2 : 4));
+    uint32_t L[2][M], mx[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < M; i++) L[0][i] = L[1][i] = 0u;
+    auto load = [&](int64_t r, u32x2 (&v)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; u++)
+            v[u] = __builtin_amdgcn_raw_buffer_load_b64(rsrc, (uint32_t)((r - r0 + NW * u) * ld_bytes) + col_off, 0, 0);
+    };
+    // rows past the chunk enter the lists as key 0, which sorts last and never displaces a real
+    // key, and the maxima as 0
+    auto account = [&](int64_t r, const u32x2 (&v)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const uint32_t okm = (r + NW * u < r1) ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const uint32_t k = v[u][h] & mask;
+                mx[h] = key_max<H>(mx[h], k);
+                topm_insert<H, M>(L[h], (k ^ flip) & okm);
+            }
+        }
+    };
+    if (active) {
+        u32x2 va[U], vb[U];
+        int64_t r = r0 + wid;
+        load(r, va);
+        for (; r < r1; r += 2 * NW * U) {
+            load(r + NW * U, vb);
+            account(r, va);
+            if (r + NW * U >= r1) break;
+            load(r + 2 * NW * U, va);
+            account(r + NW * U, vb);
+        }
+    }
+    for (int half = NW / 2; half >= 1; half /= 2) {
+        if (wid >= half && wid < 2 * half) {
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+#pragma unroll
+                for (int i = 0; i < M; i++) lst[wid - half][i][h][lane] = L[h][i];
+                lst[wid - half][M][h][lane] = mx[h];
+            }
+        }
+        __syncthreads();
+        if (wid < half) {
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+#pragma unroll
+                for (int i = 0; i < M; i++) topm_insert<H, M>(L[h], lst[wid][i][h][lane]);
+                mx[h] = key_max<H>(mx[h], lst[wid][M][h][lane]);
+            }
+        }
+        __syncthreads();
+    }
+    if (wid != 0 || !active) return;
+    const int64_t per_ch = (int64_t)rchunks * (M + 1);
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+#pragma unroll
+        for (int q = 0; q < CPW; q++) {
+            uint32_t *p = ws + (c0 + h * CPW + q) * per_ch;
+#pragma unroll
+            for (int i = 0; i < M; i++) p[(int64_t)blockIdx.y * M + i] = H ? (L[h][i] >> (16 * q)) & 0xFFFFu : L[h][i];
+            p[(int64_t)rchunks * M + blockIdx.y] = H ? (mx[h] >> (16 * q)) & 0xFFFFu : mx[h];
+        }
+    }
+}
+
+// One wave per channel: lane c holds workgroup c's descending list; m rounds each take the largest
+// head across the lanes (the lowest such lane pops it); the m-th value taken is the rank sought.
+template <int DT, int M>
+__global__ __launch_bounds__(256) void k_pct_topm_final(const uint32_t *__restrict__ ws, int64_t cols, int rchunks,
+                                                        int m, int invert, float *__restrict__ out_pct,
+                                                        float *__restrict__ out_max, int32_t *__restrict__ flags) {
+    const int64_t ch = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int lane = threadIdx.x & 63;
+    if (ch >= cols) return;
+    const int64_t per_ch = (int64_t)rchunks * (M + 1);
+    const uint32_t *p = ws + ch * per_ch;
+    uint32_t L[M], mx = 0u;
+#pragma unroll
+    for (int i = 0; i < M; i++) L[i] = lane < rchunks ? p[lane * M + i] : 0u;
+    if (lane < rchunks) mx = p[(int64_t)rchunks * M + lane];
+    uint32_t key = 0u;
+    for (int t = 0; t < m; t++) {
+        key = wave_max_u32(L[0]);
+        const uint64_t holders = __ballot(L[0] == key);
+        if (lane == __builtin_ctzll(holders)) {
+#pragma unroll
+            for (int i = 0; i + 1 < M; i++) L[i] = L[i + 1];
+            L[M - 1] = 0u;
+        }
+    }
+    mx = wave_max_u32(mx);
+    if (lane != 0) return;
+    const uint32_t kmask = (DT == NVFP4_F32) ? 0x7FFFFFFFu : 0x7FFFu;
+    if (invert) key ^= kmask;
+    auto to_f32 = [](uint32_t k) -> float {
+        if (DT == NVFP4_F32) return u2f(k);
+        if (DT == NVFP4_BF16) return u2f(k << 16);
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)k);
+    };
+    const uint32_t inf_key = (DT == NVFP4_F32) ? 0x7F800000u : (DT == NVFP4_BF16 ? 0x7F80u : 0x7C00u);
+    if (mx >= inf_key && flags) atomicOr(flags, 1);
+    out_pct[ch] = to_f32(key);
+    if (out_max) out_max[ch] = to_f32(mx);
+}
+
+// Returns false (nothing launched) when a row chunk would exceed 32-bit buffer offsets.
+template <int DT, int M>
+static bool launch_topm(const void *x, int64_t rows, int64_t cols, int64_t ld_x, uint32_t m, int invert,
+                        float *out_pct, float *out_max, int32_t *flags, uint32_t *ws, int num_cus,
+                        hipStream_t stream) {
+    constexpr int CPL = DT != NVFP4_F32 ? 4 : 2;
+    constexpr int EB = DT == NVFP4_F32 ? 4 : 2;
+    const int64_t cgroups = (cols + 64 * CPL - 1) / (64 * CPL);
+    // two workgroups per CU, at least 64 rows each; the lists must fit the workspace and the
+    // final wave (one lane per list)
+    int64_t rchunks = ((int64_t)num_cus * 2 + cgroups - 1) / cgroups;
+    const int64_t by_rows = (rows + 63) / 64;
+    int64_t by_ws = 259 / (M + 1);
+    if (by_ws > 64) by_ws = 64;
+    if (rchunks > by_rows) rchunks = by_rows;
+    if (rchunks > by_ws) rchunks = by_ws;
+    if (rchunks < 1) rchunks = 1;
+    const int rows_per_wg = (int)((rows + rchunks - 1) / rchunks);
+    rchunks = (rows + rows_per_wg - 1) / rows_per_wg;
+    if ((int64_t)(rows_per_wg + 2 * kTopmWaves * kTopmU) * ld_x * EB >= ((int64_t)1 << 31)) return false;
+    hipLaunchKernelGGL((k_pct_topm<DT, M>), dim3((unsigned)cgroups, (unsigned)rchunks), dim3(64 * kTopmWaves), 0,
+                       stream, (const uint8_t *)x, rows, cols, ld_x * EB, rows_per_wg, invert, (int)rchunks, ws);
+    hipLaunchKernelGGL((k_pct_topm_final<DT, M>), dim3((unsigned)((cols + 3) / 4)), dim3(256), 0, stream, ws, cols,
+                       (int)rchunks, (int)m, invert, out_pct, out_max, flags);
+    return true;
+}
+
 template <int DT>
 static hipError_t launch_pct_t(const void *x, int64_t rows, int64_t cols, int64_t ld_x, uint32_t k, int per_channel,
                                float *out_pct, float *out_max, int32_t *flags, uint32_t *ws, int num_cus,
@@ -211,6 +420,20 @@ static hipError_t launch_pct_t(const void *x, int64_t rows, int64_t cols, int64_
     constexpr int WCH = 64;
     constexpr int KEYBITS = (DT == NVFP4_F32) ? 31 : 15;
     const int64_t nch = per_channel ? cols : 1;
+    if (per_channel) {
+        // rank near the top (m-th largest) or the bottom (k-th smallest): one pass
+        const uint32_t n = (uint32_t)rows, mtop = n - k + 1;
+        const bool top = mtop <= k;
+        const uint32_t m = top ? mtop : k;
+        if (m <= (uint32_t)kTopmMax) {
+            const int inv = top ? 0 : 1;
+            bool done;
+            if (m <= 4) done = launch_topm<DT, 4>(x, rows, cols, ld_x, m, inv, out_pct, out_max, flags, ws, num_cus, stream);
+            else if (m <= 8) done = launch_topm<DT, 8>(x, rows, cols, ld_x, m, inv, out_pct, out_max, flags, ws, num_cus, stream);
+            else done = launch_topm<DT, 16>(x, rows, cols, ld_x, m, inv, out_pct, out_max, flags, ws, num_cus, stream);
+            if (done) return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL(k_pct_init, dim3((unsigned)((nch * 259 + 255) / 256 < 4096 ? (nch * 259 + 255) / 256 : 4096)),
                        dim3(256), 0, stream, ws, nch, k);
     // Enough workgroups to cover the CUs twice, but at least 1024 rows each: every workgroup pays for

@@ -320,7 +320,9 @@ def test_percentile(nv, dtype, shape):
     else:
         src, odt = x, oracle.F32
         xd = to_dev_f32(src)
-    for p in [99.9, 50.0, 100.0, 1e-6]:
+    # 99.9 / 100 / 1e-6 and 99.63 / 0.3 take the one-pass path near either end of a channel (up
+    # to 16 from the end), 50 the radix path
+    for p in [99.9, 50.0, 100.0, 1e-6, 99.63, 0.3]:
         for per_channel in [True, False]:
             pct, mx = nv.amax_percentile(xd, p, per_channel)
             rp, rm = oracle.amax_percentile(src, p, per_channel, dtype=odt)
@@ -330,6 +332,15 @@ def test_percentile(nv, dtype, shape):
         pct, mx = nv.amax_percentile(padded(xd, 16), 99.9)
         rp, rm = oracle.amax_percentile(src, 99.9, dtype=odt)
         assert np.array_equal(pct.cpu().numpy(), rp)
+
+
+def test_percentile_attention_activations_full(nv):
+    # the activations of the attention projection, per-channel p99.9 (the 5th largest of 4096)
+    _note("percentile 4096 x 3072 bf16")
+    a_bits = synth.attn_proj_activations(4096, 3072)
+    pct, mx = nv.amax_percentile(to_dev_bf16(a_bits), 99.9)
+    rp, rm = oracle.amax_percentile(a_bits, 99.9, dtype=oracle.BF16)
+    assert np.array_equal(pct.cpu().numpy(), rp) and np.array_equal(mx.cpu().numpy(), rm)
 
 
 def test_percentile_calibration_full_rows(nv):
