@@ -112,7 +112,12 @@ size_t nvfp4_workspace_size(int op, int64_t rows, int64_t cols, int64_t k) {
     switch (op) {
     case NVFP4_OP_QUANTIZE: return kQuantizeWsBytes;
     case NVFP4_OP_PERCENTILE: return cols >= 0 ? percentile_ws_bytes(cols, k ? 1 : 0) : 0;
-    default: (void)rows; return 0;
+    case NVFP4_OP_GEMM: {
+        // planned for the current device's CU count (256, an MI355X, when none can be queried)
+        const int cus = current_device_cus();
+        return gemm_ws_bytes(rows, cols, k, cus > 0 ? cus : 256);
+    }
+    default: return 0;
     }
 }
 
@@ -152,8 +157,6 @@ nvfp4_status nvfp4_dequantize(const nvfp4_tensor *in, void *out, nvfp4_dtype out
 
 nvfp4_status nvfp4_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, int64_t lda, const nvfp4_tensor *w,
                         float *c, int64_t ldc, void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     if ((a_bf16 == nullptr) == (a_q == nullptr)) return NVFP4_ERR_ARG;
     nvfp4_status st = check_qtensor(w);
     if (st != NVFP4_OK) return st;
@@ -169,10 +172,11 @@ nvfp4_status nvfp4_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, 
     }
     st = check_matrix(c, M, N, ldc, 4, 4);
     if (st != NVFP4_OK) return st;
+    if (workspace && !aligned16(workspace)) return NVFP4_ERR_ALIGN;
     const int cus = current_device_cus();
     if (cus == 0) return NVFP4_ERR_DEVICE;
     hipError_t e = (K == 0) ? launch_fill_zero_f32(c, M, N, ldc, stream)
-                            : launch_gemm(a_bf16, a_q, M, lda, w, c, ldc, cus, stream);
+                            : launch_gemm(a_bf16, a_q, M, lda, w, c, ldc, workspace, workspace_bytes, cus, stream);
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
 }
 

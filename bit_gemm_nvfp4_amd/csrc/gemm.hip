@@ -353,7 +353,8 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
                                                           const uint8_t *__restrict__ w_codes,
                                                           const uint8_t *__restrict__ w_scales,
                                                           const float *__restrict__ w_g, float *__restrict__ C,
-                                                          int64_t ldc, int64_t M, int64_t N, int64_t K) {
+                                                          int64_t ldc, int64_t M, int64_t N, int64_t K,
+                                                          int slice_steps) {
     constexpr int NT = 64 * WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;    // wave tile
     constexpr int TM = WTM / 32, TN = WTN / 32;    // 32x32 MFMA tiles per wave
@@ -433,11 +434,14 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
 
     uint32_t qc[2][QD], qs[2][QD];  // two register sets of code dwords and scale bytes
 
-    const int nsteps = (int)(K / kBK);
+    // K slice of this workgroup (split-K: blockIdx.y; otherwise the whole of K)
+    const int total_steps = (int)(K / kBK);
+    const int kbase = (int)blockIdx.y * slice_steps;
+    const int nsteps = (total_steps - kbase) < slice_steps ? (total_steps - kbase) : slice_steps;
     const int last = nsteps - 1;
     // Loads past the last step repeat it: harmless, and the loop body stays free of branches.
     auto issue = [&](int s, int a_stage, int r) {
-        const uint32_t k0 = (uint32_t)((s < last ? s : last) * kBK);
+        const uint32_t k0 = (uint32_t)((kbase + (s < last ? s : last)) * kBK);
         if constexpr (!A_Q) {
 #pragma unroll
             for (int b = 0; b < A_DMA; b++)
@@ -554,9 +558,12 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
     // no direct-to-LDS load may still be writing when the workgroup's LDS is released
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
 
-    // ---- epilogue: multiply by the global scale(s), store fp32 ----
-    const float gw = *w_g;
-    const float ga = A_Q ? *a_g : 1.0f;
+    // ---- epilogue: multiply by the global scale(s), store fp32; a K slice of a split product
+    // (w_g == nullptr) stores its raw partial sums into its own [M x ldc] plane of C instead ----
+    const bool partial = w_g == nullptr;
+    const float gw = partial ? 1.0f : *w_g;
+    const float ga = (A_Q && !partial) ? *a_g : 1.0f;
+    float *Cs = C + (int64_t)blockIdx.y * M * ldc;
 #pragma unroll
     for (int i = 0; i < TM; i++) {
 #pragma unroll
@@ -567,11 +574,35 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
                 const int64_t row = m0 + wm * WTM + i * 32 + 8 * (e / 4) + 4 * (lane / 32) + (e % 4);
                 if (row < M && col < N) {
                     float v = acc[i][j][e];
-                    if (A_Q) v = v * ga;
-                    C[row * ldc + col] = v * gw;
+                    if (!partial) {
+                        if (A_Q) v = v * ga;
+                        v = v * gw;
+                    }
+                    Cs[row * ldc + col] = v;
                 }
             }
         }
+    }
+}
+
+// Sum of the split-K partial planes P[s] ([M x ldp] each) in slice order, times the global
+// scale(s): C = ((sum_s P[s]) * g_a) * g_w.  One thread per output element.
+template <bool A_Q>
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__ P, int splits, int64_t M, int64_t N,
+                                                       int64_t ldp, const float *__restrict__ a_g,
+                                                       const float *__restrict__ w_g, float *__restrict__ C,
+                                                       int64_t ldc) {
+    const float gw = *w_g;
+    const float ga = A_Q ? *a_g : 1.0f;
+    const int64_t total = M * N;
+    const int64_t plane = M * ldp;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = i / N, c = i - r * N;
+        const float *p = P + r * ldp + c;
+        float v = p[0];
+        for (int s = 1; s < splits; s++) v += p[(int64_t)s * plane];
+        if (A_Q) v = v * ga;
+        C[r * ldc + c] = v * gw;
     }
 }
 
@@ -675,32 +706,11 @@ static void launch_gemv(int64_t M, const void *a_bf16, int64_t lda, const nvfp4_
     }
 }
 
-template <int BM, int BN, int WM, int WN, bool A_Q>
-static void launch_tile(const void *a_bf16, int64_t lda, const nvfp4_tensor *a_q, int64_t M, const nvfp4_tensor *w,
-                        float *c, int64_t ldc, hipStream_t stream) {
-    const int64_t N = w->rows, K = w->cols;
-    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    const uint8_t *ac = A_Q ? a_q->codes : nullptr;
-    const uint8_t *as = A_Q ? a_q->scales : nullptr;
-    const float *ag = A_Q ? a_q->global_scale : nullptr;
-    // k_gemm_mfma addresses one tile's rows with 32-bit buffer offsets
-    const int64_t lim = (int64_t)1 << 31;
-    const bool fits = (int64_t)(BM + 1) * (A_Q ? K / 2 : lda * 2) + K * 2 < lim && (int64_t)BN * (K / 2) < lim;
-    if (K % kBK == 0 && fits) {
-        hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, A_Q>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0, stream,
-                           (const __bf16 *)a_bf16, lda, ac, as, ag, w->codes, w->scales, w->global_scale, c, ldc, M,
-                           N, K);
-    } else {
-        hipLaunchKernelGGL((k_gemm_tile<BM, BN, WM, WN, A_Q>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0, stream,
-                           (const __bf16 *)a_bf16, lda, ac, as, ag, w->codes, w->scales, w->global_scale, c, ldc, M,
-                           N, K);
-    }
-}
-
-// Tile shapes, chosen per problem by a cost model: rounds of tiles over the CUs times the work one
-// CU does per round (tile area x co-resident tiles), divided by the shape's measured throughput per
-// CU relative to the largest tile on MI355X (larger tiles amortize the W expansion and the LDS
-// traffic over more output).
+// Tile shapes, chosen per problem by a cost model: rounds of workgroups over the CUs times the work
+// one CU does per round (tile area x K steps per workgroup x co-resident tiles), divided by the
+// shape's measured throughput per CU relative to the largest tile on MI355X (larger tiles amortize
+// the W expansion and the LDS traffic over more output), plus, for split-K, the pass that reads
+// the partial planes back.
 struct TileCfg {
     int bm, bn, per_cu;
     double eff;
@@ -711,37 +721,98 @@ static const TileCfg kTiles[] = {
     {128, 256, 1, 0.79},  // 8 waves, 64 x 64 per wave
     {128, 128, 2, 0.72},  // 4 waves, 64 x 64 per wave, two workgroups per CU
 };
+constexpr double kUsPerTileStep = 2.0;      // one 256 x 256 x 64 step on one CU, microseconds
+constexpr double kReduceBytesPerUs = 4.0e6;  // HBM rate of the partial-sum pass
+constexpr int kMaxSplits = 8;
 
-static int choose_tile(int64_t M, int64_t N, int num_cus) {
-    int best = 0;
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int num_cus) {
+    GemmPlan best{0, 1, (int)((K + kBK - 1) / kBK)};
     double best_cost = 1e300;
+    const int64_t steps = (K + kBK - 1) / kBK;
+    const bool splittable = K % kBK == 0;
     for (int i = 0; i < (int)(sizeof(kTiles) / sizeof(kTiles[0])); i++) {
         const TileCfg &t = kTiles[i];
         const double tiles = (double)((M + t.bm - 1) / t.bm) * (double)((N + t.bn - 1) / t.bn);
         const double slots = (double)num_cus * t.per_cu;
-        const double rounds = (double)(int64_t)((tiles + slots - 1) / slots);
-        const double cost = rounds * t.per_cu * t.bm * t.bn / t.eff;
-        if (cost < best_cost) {
-            best_cost = cost;
-            best = i;
+        for (int sp = 1; sp <= (splittable ? kMaxSplits : 1); sp *= 2) {
+            const int64_t per = (steps + sp - 1) / sp;
+            if (sp > 1 && per < 8) break;
+            const int used = (int)((steps + per - 1) / per);
+            const double rounds = (double)(int64_t)((tiles * used + slots - 1) / slots);
+            double cost = rounds * t.per_cu * (t.bm * t.bn / 65536.0) * (double)per * kUsPerTileStep / t.eff;
+            if (used > 1) cost += (double)(used + 1) * (double)M * (double)N * 4.0 / kReduceBytesPerUs;
+            if (cost < best_cost) {
+                best_cost = cost;
+                best = GemmPlan{i, used, (int)per};
+            }
         }
     }
     return best;
 }
 
+size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus) {
+    if (M <= 0 || N <= 0 || K <= 0 || gemv_applies(M, K)) return 0;
+    const GemmPlan p = plan_gemm(M, N, K, num_cus);
+    return p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)N * 4 : 0;
+}
+
+template <int BM, int BN, int WM, int WN, bool A_Q>
+static void launch_tile(const void *a_bf16, int64_t lda, const nvfp4_tensor *a_q, int64_t M, const nvfp4_tensor *w,
+                        float *c, int64_t ldc, const GemmPlan &plan, float *partials, hipStream_t stream) {
+    const int64_t N = w->rows, K = w->cols;
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const uint8_t *ac = A_Q ? a_q->codes : nullptr;
+    const uint8_t *as = A_Q ? a_q->scales : nullptr;
+    const float *ag = A_Q ? a_q->global_scale : nullptr;
+    // k_gemm_mfma addresses one tile's rows with 32-bit buffer offsets
+    const int64_t lim = (int64_t)1 << 31;
+    const bool fits = (int64_t)(BM + 1) * (A_Q ? K / 2 : lda * 2) + K * 2 < lim && (int64_t)BN * (K / 2) < lim;
+    if (K % kBK == 0 && fits) {
+        if (partials) {
+            // K slices into their own planes of the workspace, then the ordered sum and scaling
+            hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, A_Q>), dim3((unsigned)tiles, (unsigned)plan.splits),
+                               dim3(64 * WM * WN), 0, stream, (const __bf16 *)a_bf16, lda, ac, as, ag, w->codes,
+                               w->scales, nullptr, partials, N, M, N, K, plan.slice_steps);
+            const int64_t total = M * N;
+            const int64_t blocks = (total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536;
+            hipLaunchKernelGGL((k_splitk_reduce<A_Q>), dim3((unsigned)blocks), dim3(256), 0, stream, partials,
+                               plan.splits, M, N, N, ag, w->global_scale, c, ldc);
+            return;
+        }
+        hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, A_Q>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0, stream,
+                           (const __bf16 *)a_bf16, lda, ac, as, ag, w->codes, w->scales, w->global_scale, c, ldc, M,
+                           N, K, (int)(K / kBK));
+    } else {
+        hipLaunchKernelGGL((k_gemm_tile<BM, BN, WM, WN, A_Q>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0, stream,
+                           (const __bf16 *)a_bf16, lda, ac, as, ag, w->codes, w->scales, w->global_scale, c, ldc, M,
+                           N, K);
+    }
+}
+
 template <bool A_Q>
 static void launch_tiled(const void *a_bf16, int64_t lda, const nvfp4_tensor *a_q, int64_t M, const nvfp4_tensor *w,
-                         float *c, int64_t ldc, int num_cus, hipStream_t stream) {
-    switch (choose_tile(M, w->rows, num_cus)) {
-    case 0: launch_tile<256, 256, 4, 2, A_Q>(a_bf16, lda, a_q, M, w, c, ldc, stream); break;
-    case 1: launch_tile<256, 192, 4, 2, A_Q>(a_bf16, lda, a_q, M, w, c, ldc, stream); break;
-    case 2: launch_tile<128, 256, 2, 4, A_Q>(a_bf16, lda, a_q, M, w, c, ldc, stream); break;
-    default: launch_tile<128, 128, 2, 2, A_Q>(a_bf16, lda, a_q, M, w, c, ldc, stream); break;
+                         float *c, int64_t ldc, void *workspace, size_t workspace_bytes, int num_cus,
+                         hipStream_t stream) {
+    GemmPlan plan = plan_gemm(M, w->rows, w->cols, num_cus);
+    float *partials = nullptr;
+    if (plan.splits > 1) {
+        // split-K needs its partial planes; without room for them the product runs unsplit
+        if (workspace && workspace_bytes >= (size_t)plan.splits * (size_t)M * (size_t)w->rows * 4)
+            partials = reinterpret_cast<float *>(workspace);
+        else
+            plan = GemmPlan{plan.cfg, 1, (int)(w->cols / kBK)};
+    }
+    switch (plan.cfg) {
+    case 0: launch_tile<256, 256, 4, 2, A_Q>(a_bf16, lda, a_q, M, w, c, ldc, plan, partials, stream); break;
+    case 1: launch_tile<256, 192, 4, 2, A_Q>(a_bf16, lda, a_q, M, w, c, ldc, plan, partials, stream); break;
+    case 2: launch_tile<128, 256, 2, 4, A_Q>(a_bf16, lda, a_q, M, w, c, ldc, plan, partials, stream); break;
+    default: launch_tile<128, 128, 2, 2, A_Q>(a_bf16, lda, a_q, M, w, c, ldc, plan, partials, stream); break;
     }
 }
 
 hipError_t launch_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, int64_t lda, const nvfp4_tensor *w,
-                       float *c, int64_t ldc, int num_cus, hipStream_t stream) {
+                       float *c, int64_t ldc, void *workspace, size_t workspace_bytes, int num_cus,
+                       hipStream_t stream) {
     const int64_t K = w->cols;
     if (M == 0 || w->rows == 0) return hipGetLastError();
     if (gemv_applies(M, K)) {
@@ -749,8 +820,8 @@ hipError_t launch_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, i
         else launch_gemv<false>(M, a_bf16, lda, a_q, w, c, ldc, num_cus, stream);
         return hipGetLastError();
     }
-    if (a_q) launch_tiled<true>(a_bf16, lda, a_q, M, w, c, ldc, num_cus, stream);
-    else launch_tiled<false>(a_bf16, lda, a_q, M, w, c, ldc, num_cus, stream);
+    if (a_q) launch_tiled<true>(a_bf16, lda, a_q, M, w, c, ldc, workspace, workspace_bytes, num_cus, stream);
+    else launch_tiled<false>(a_bf16, lda, a_q, M, w, c, ldc, workspace, workspace_bytes, num_cus, stream);
     return hipGetLastError();
 }
 

@@ -20,8 +20,20 @@ hipError_t launch_quantize(const void *x, nvfp4_dtype dt, int64_t ld_x, const fl
 hipError_t launch_dequantize(const nvfp4_tensor *in, void *out, nvfp4_dtype out_dtype, int64_t ld_out, int num_cus,
                              hipStream_t stream);
 
+// GEMM execution plan: tile shape (index into the shape table), number of K slices (split-K when
+// > 1: each slice writes an fp32 partial plane, then an ordered sum) and K steps of 64 per slice.
+struct GemmPlan {
+    int cfg;
+    int splits;
+    int slice_steps;
+};
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int num_cus);
+// Workspace bytes the plan for this problem uses (its split-K partial planes), 0 if none.
+size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus);
+
 hipError_t launch_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, int64_t lda, const nvfp4_tensor *w,
-                       float *c, int64_t ldc, int num_cus, hipStream_t stream);
+                       float *c, int64_t ldc, void *workspace, size_t workspace_bytes, int num_cus,
+                       hipStream_t stream);
 
 size_t percentile_ws_bytes(int64_t cols, int per_channel);
 

@@ -311,10 +311,11 @@ __global__ __launch_bounds__(256) void k_encode(TileGeom gm, const float *__rest
 // invalid, instead of a hang.
 // ---------------------------------------------------------------------------------------------
 constexpr int kSlotBase = 16;       // workspace words before the 64-bit slots (8-byte aligned)
+
 constexpr int kFusedPerCu = 2;      // workgroups per CU of the single-pass kernel
 constexpr uint32_t kPollLimit = 1u << 22;
 
-template <int SRC, int TPW>
+template <int SRC, int TPW, int PB>
 __global__ __launch_bounds__(256) void k_quant_fused(TileGeom gm, const float *__restrict__ src_scale,
                                                      uint32_t *__restrict__ ws, uint32_t epoch,
                                                      uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
@@ -338,11 +339,15 @@ __global__ __launch_bounds__(256) void k_quant_fused(TileGeom gm, const float *_
         bm[s] = tile_block_max<SRC>(t[s], lane);
         m = max(m, bm[s]);
     }
-    for (uint64_t tile = wave + TPW * nwaves; tile < ntiles; tile += nwaves) {
-        TileRegs<SRC> o;
-        tile_load<SRC>(o, gm, tile, lane);
+    // tiles beyond the resident ones are streamed, PB loads in flight per wave
+    for (uint64_t tile = wave + TPW * nwaves; tile < ntiles; tile += PB * nwaves) {
+        TileRegs<SRC> o[PB];
 #pragma unroll
-        for (int j = 0; j < kVpb<SRC>; j++) m = max(m, vec_absmax_bits<SRC>(o.raw[j]));
+        for (int b = 0; b < PB; b++) tile_load<SRC>(o[b], gm, tile + b * nwaves, lane);
+#pragma unroll
+        for (int b = 0; b < PB; b++)
+#pragma unroll
+            for (int j = 0; j < kVpb<SRC>; j++) m = max(m, vec_absmax_bits<SRC>(o[b].raw[j]));
     }
     m = wave_max_u32(m);
     if (lane == 0) red[wid] = m;
@@ -389,10 +394,17 @@ __global__ __launch_bounds__(256) void k_quant_fused(TileGeom gm, const float *_
         const uint64_t tile = wave + s * nwaves;
         if (tile < ntiles) tile_encode<SRC>(t[s], bm[s], g, six_g, sc, tile, gm.nblocks, codes, scales, flags, lane);
     }
-    for (uint64_t tile = wave + TPW * nwaves; tile < ntiles; tile += nwaves) {
-        TileRegs<SRC> o;
-        tile_load<SRC>(o, gm, tile, lane);
-        tile_encode<SRC>(o, tile_block_max<SRC>(o, lane), g, six_g, sc, tile, gm.nblocks, codes, scales, flags, lane);
+    for (uint64_t tile = wave + TPW * nwaves; tile < ntiles; tile += PB * nwaves) {
+        TileRegs<SRC> o[PB];
+#pragma unroll
+        for (int b = 0; b < PB; b++) tile_load<SRC>(o[b], gm, tile + b * nwaves, lane);
+#pragma unroll
+        for (int b = 0; b < PB; b++) {
+            const uint64_t tb = tile + b * nwaves;
+            if (tb < ntiles)
+                tile_encode<SRC>(o[b], tile_block_max<SRC>(o[b], lane), g, six_g, sc, tb, gm.nblocks, codes, scales,
+                                 flags, lane);
+        }
     }
 }
 
@@ -412,16 +424,22 @@ static uint32_t next_epoch() {
 // Largest residency (tiles per wave) whose registers still leave room for two workgroups per CU.
 template <int SRC>
 constexpr int kMaxTpw = SRC == NVFP4_F32 ? 6 : SRC == NVFP4_BF16 ? 8 : SRC == NVFP4_F16 ? 12 : 16;
+// For tensors beyond the residency: fewer resident tiles, so that the streamed rest can keep
+// kStreamBatch loads in flight per wave within the same register budget.
+template <int SRC>
+constexpr int kStreamTpw = SRC == NVFP4_F32 ? 4 : SRC == NVFP4_BF16 ? 6 : SRC == NVFP4_F16 ? 8 : 16;
+template <int SRC>
+constexpr int kStreamBatch = SRC == NVFP4_F32 ? 2 : 4;
 
 // Workgroups of k_quant_fused<SRC, TPW> that can be resident on one CU (at most kFusedPerCu),
 // from the runtime's occupancy calculation; computed once per instantiation.
-template <int SRC, int TPW>
+template <int SRC, int TPW, int PB>
 static int fused_per_cu() {
     static std::atomic<int> cached{0};
     int n = cached.load(std::memory_order_relaxed);
     if (n == 0) {
         int b = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_quant_fused<SRC, TPW>, 256, 0) != hipSuccess || b < 1)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_quant_fused<SRC, TPW, PB>, 256, 0) != hipSuccess || b < 1)
             b = 1;
         n = b < kFusedPerCu ? b : kFusedPerCu;
         cached.store(n, std::memory_order_relaxed);
@@ -431,18 +449,18 @@ static int fused_per_cu() {
 
 // The grid barrier needs every workgroup resident at once, so the grid never exceeds what the
 // CUs hold; waves then take more tiles than TPW and stream the rest.
-template <int SRC, int TPW>
+template <int SRC, int TPW, int PB = 1>
 static void launch_fused(const TileGeom &gm, int grid, const float *src_scale, uint32_t *ws, const nvfp4_tensor *out,
                          int32_t *flags, int num_cus, hipStream_t stream) {
-    const int cap = fused_per_cu<SRC, TPW>() * num_cus;
+    const int cap = fused_per_cu<SRC, TPW, PB>() * num_cus;
     if (grid > cap) grid = cap;
-    hipLaunchKernelGGL((k_quant_fused<SRC, TPW>), dim3(grid), dim3(256), 0, stream, gm, src_scale, ws, next_epoch(),
+    hipLaunchKernelGGL((k_quant_fused<SRC, TPW, PB>), dim3(grid), dim3(256), 0, stream, gm, src_scale, ws, next_epoch(),
                        out->codes, out->scales, out->global_scale, flags);
 }
 
 // Tiles spread over all CUs (two workgroups each, so that two waves share every SIMD and hide each
-// other's latencies; fewer for small tensors); tiles per wave rounded up to a supported residency,
-// kMaxTpw<SRC> at most (the rest streams twice).
+// other's latencies; fewer for small tensors); tiles per wave rounded up to a supported residency.
+// Beyond kMaxTpw<SRC> tiles per wave the streaming variant runs (the rest is read twice).
 template <int SRC>
 static void launch_fused_any(const TileGeom &gm, const float *src_scale, uint32_t *ws, const nvfp4_tensor *out,
                              int32_t *flags, int num_cus, hipStream_t stream) {
@@ -450,12 +468,16 @@ static void launch_fused_any(const TileGeom &gm, const float *src_scale, uint32_
     const int grid = grid_for(ntiles, 4, kFusedPerCu * num_cus);
     const uint64_t tpw = (ntiles + 4 * (uint64_t)grid - 1) / (4 * (uint64_t)grid);
     constexpr int T = kMaxTpw<SRC>;
+    if (tpw > (uint64_t)T) {
+        launch_fused<SRC, kStreamTpw<SRC>, kStreamBatch<SRC>>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
+        return;
+    }
     if (tpw <= 1) launch_fused<SRC, 1>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
     else if (tpw <= 2) launch_fused<SRC, 2>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
     else if (tpw <= 4) launch_fused<SRC, 4>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
-    else if (tpw <= 6 || T == 6) launch_fused<SRC, 6>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
-    else if (tpw <= 8 || T == 8) launch_fused<SRC, (T < 8 ? T : 8)>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
-    else if (tpw <= 12 || T == 12) launch_fused<SRC, (T < 12 ? T : 12)>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
+    else if (tpw <= 6) launch_fused<SRC, 6>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
+    else if (tpw <= 8) launch_fused<SRC, (T < 8 ? T : 8)>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
+    else if (tpw <= 12) launch_fused<SRC, (T < 12 ? T : 12)>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
     else launch_fused<SRC, T>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
 }
 

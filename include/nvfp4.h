@@ -121,7 +121,9 @@ nvfp4_status nvfp4_dequantize(const nvfp4_tensor *in, void *out, nvfp4_dtype out
  *     "Runtime / hardware");
  * products are summed in fp32 and the sum is multiplied by the global scale(s) at the end.
  * Exactly one of a_bf16 / a_q must be non-NULL (NVFP4_ERR_ARG otherwise).  lda is ignored for
- * W4A4.  workspace may be NULL when nvfp4_workspace_size(NVFP4_OP_GEMM, M, N, K) is 0.
+ * W4A4.  workspace (16-byte aligned, or NULL): with nvfp4_workspace_size(NVFP4_OP_GEMM, M, N, K)
+ * bytes, problems with few output tiles and a long K are split along K (fp32 partial sums per
+ * slice in the workspace, then summed in slice order); with less, or NULL, the unsplit kernel runs.
  */
 nvfp4_status nvfp4_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, int64_t lda,
                         const nvfp4_tensor *w, float *c, int64_t ldc, void *workspace, size_t workspace_bytes,
@@ -143,7 +145,8 @@ nvfp4_status amax_percentile(const void *x, nvfp4_dtype x_dtype, int64_t rows, i
                              void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace bytes an entry point needs (0 when none).  For NVFP4_OP_PERCENTILE the last argument
- * is per_channel; for NVFP4_OP_GEMM the arguments are (M, N, K). */
+ * is per_channel; for NVFP4_OP_GEMM the arguments are (M, N, K), and the size is planned for the
+ * current device (an MI355X's 256 CUs when none can be queried). */
 size_t nvfp4_workspace_size(int op, int64_t rows, int64_t cols, int64_t k);
 
 /* A static, human-readable name for a status code. */

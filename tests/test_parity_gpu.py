@@ -370,6 +370,24 @@ def test_gemm_tile_configs(nv, mnk):
     assert oracle.gemm_error(c4, oracle.gemm_w4a4(aref, ref)) <= GEMM_TOL
 
 
+# few output tiles and a long K: the product is split along K (partial planes in the workspace,
+# summed in slice order); ragged M and N edges, and the Qwen3-VL MLP down projection
+@pytest.mark.parametrize("mnk", [(100, 1000, 4096), (512, 4096, 12288)])
+def test_gemm_split_k(nv, mnk):
+    m, n, k = mnk
+    _note(f"gemm split-K {mnk}")
+    assert nv.workspace_size(nv.OP_GEMM, m, n, k) > 0
+    q, ref = _rand_q(nv, n, k, seed=m + n + k, sigma=0.015)
+    a_bits = synth.bf16_bits(np.random.default_rng(m + 5).standard_normal((m, k)).astype(np.float32))
+    c = nv.gemm(to_dev_bf16(a_bits), q).cpu().numpy()
+    assert oracle.gemm_error(c, oracle.gemm_w4a16(a_bits, ref)) <= GEMM_TOL
+    aq = _quant(nv, to_dev_bf16(a_bits))
+    aref, _ = oracle.quantize(a_bits, oracle.BF16)
+    _assert_q_equal(aq, aref, "activations")
+    c4 = nv.gemm(aq, q).cpu().numpy()
+    assert oracle.gemm_error(c4, oracle.gemm_w4a4(aref, ref)) <= GEMM_TOL
+
+
 def test_quantize_large_tensor_overflow_path(nv):
     # more tiles than the single-pass kernel holds in registers: part of the input is read twice
     _note("quantize 16384 x 8192 fp32 (128 M elements)")
