@@ -33,7 +33,7 @@
 // k_gemv: for M <= 4 the product is bound by streaming W once from HBM.  A (expanded to bf16) sits
 // in LDS; each lane takes whole 16-element blocks of a W row, forms the 16-term dot products with
 // bf16 dot2 instructions and applies the block scale once per block; a wave reduction finishes
-// each row.
+// each row.  A wave works on two rows at once with all their loads issued ahead of the arithmetic.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -618,7 +618,36 @@ __global__ __launch_bounds__(256) void k_gemv(const __bf16 *__restrict__ A, int6
                                               float *__restrict__ C, int64_t ldc, int64_t N, int64_t K) {
     extern __shared__ __attribute__((aligned(16))) uint32_t a_lds[];  // [MM][K/2] bf16 pairs
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
     const int64_t kp = K / 2;
+    const int64_t nblk = K / 16;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + tid) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+
+    // A wave takes two rows at a time (n and n + nwaves) and, per batch, UB blocks per lane of each;
+    // all loads of a batch are issued before any is used.  Lanes past the row's last block load
+    // that block again and add nothing.
+    constexpr int UB = 4;
+    u32x2 cw[2][UB];
+    uint32_t sb[2][UB];
+    auto load_batch = [&](const int64_t (&rows)[2], int64_t b0) {
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+#pragma unroll
+            for (int u = 0; u < UB; u++) {
+                int64_t b = b0 + lane + 64 * u;
+                b = b < nblk ? b : nblk - 1;
+                cw[h][u] = *reinterpret_cast<const u32x2 *>(w_codes + rows[h] * (K / 2) + b * 8);
+                sb[h][u] = w_scales[rows[h] * nblk + b];
+            }
+    };
+    // the first batch is in flight while A is staged
+    int64_t n = wave;
+    if (n < N) {
+        const int64_t rows[2] = {n, (n + nwaves) < N ? (n + nwaves) : n};
+        load_batch(rows, 0);
+    }
+
     // stage A (expanded exactly to bf16 for the W4A4 form) in LDS
     for (int64_t i = tid; i < MM * (K / 8); i += blockDim.x) {
         const int64_t m = i / (K / 8), c8 = i % (K / 8);
@@ -635,42 +664,148 @@ __global__ __launch_bounds__(256) void k_gemv(const __bf16 *__restrict__ A, int6
 
     const float gw = *w_g;
     const float ga = A_Q ? *a_g : 1.0f;
-    const int lane = tid & 63;
-    const int64_t nblk = K / 16;
-    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + tid) >> 6;
-    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
-    for (int64_t n = wave; n < N; n += nwaves) {
-        float acc[MM];
+    for (; n < N; n += 2 * nwaves) {
+        const int64_t rows[2] = {n, (n + nwaves) < N ? (n + nwaves) : n};
+        float acc[2][MM];
 #pragma unroll
-        for (int m = 0; m < MM; m++) acc[m] = 0.0f;
-        const uint8_t *crow = w_codes + n * (K / 2);
-        const uint8_t *srow = w_scales + n * nblk;
-        for (int64_t b = lane; b < nblk; b += 64) {
-            const u32x2 cw = *reinterpret_cast<const u32x2 *>(crow + b * 8);
-            const float s = e4m3_to_f32(srow[b]);
-            bf16x2 wv[8];
-            fp4_unpack8_bf16x2(cw[0], wv);
-            fp4_unpack8_bf16x2(cw[1], wv + 4);
+        for (int h = 0; h < 2; h++)
 #pragma unroll
-            for (int m = 0; m < MM; m++) {
-                const u32x4 *ap = reinterpret_cast<const u32x4 *>(&a_lds[m * kp + b * 8]);
-                const u32x4 a0 = ap[0], a1 = ap[1];
-                float part = 0.0f;
+            for (int m = 0; m < MM; m++) acc[h][m] = 0.0f;
+        for (int64_t b0 = 0; b0 < nblk; b0 += 64 * UB) {
+            if (b0 > 0 || n != wave) load_batch(rows, b0);
 #pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    part = __builtin_amdgcn_fdot2_f32_bf16(wv[q], as_bf16x2(a0[q]), part, false);
-                    part = __builtin_amdgcn_fdot2_f32_bf16(wv[4 + q], as_bf16x2(a1[q]), part, false);
+            for (int u = 0; u < UB; u++) {
+                const int64_t b = b0 + lane + 64 * u;
+                const int64_t bc = b < nblk ? b : nblk - 1;
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    const float sc = __builtin_amdgcn_cvt_f32_fp8((int)sb[h][u], 0);
+                    bf16x2 wv[8];
+                    fp4_unpack8_bf16x2(cw[h][u][0], wv);
+                    fp4_unpack8_bf16x2(cw[h][u][1], wv + 4);
+#pragma unroll
+                    for (int m = 0; m < MM; m++) {
+                        const u32x4 *ap = reinterpret_cast<const u32x4 *>(&a_lds[m * kp + bc * 8]);
+                        const u32x4 a0 = ap[0], a1 = ap[1];
+                        float part = 0.0f;
+#pragma unroll
+                        for (int q = 0; q < 4; q++) {
+                            part = __builtin_amdgcn_fdot2_f32_bf16(wv[q], as_bf16x2(a0[q]), part, false);
+                            part = __builtin_amdgcn_fdot2_f32_bf16(wv[4 + q], as_bf16x2(a1[q]), part, false);
+                        }
+                        acc[h][m] += b < nblk ? part * sc : 0.0f;
+                    }
                 }
-                acc[m] += part * s;
             }
         }
 #pragma unroll
-        for (int m = 0; m < MM; m++) {
-            const float t = wave_sum_f32(acc[m]);
-            if (lane == 0) {
-                float v = t;
-                if (A_Q) v = v * ga;
-                C[m * ldc + n] = v * gw;
+        for (int h = 0; h < 2; h++) {
+            if (h == 1 && rows[1] == rows[0]) break;
+#pragma unroll
+            for (int m = 0; m < MM; m++) {
+                const float t = wave_sum_f32(acc[h][m]);
+                if (lane == 0) {
+                    float v = t;
+                    if (A_Q) v = v * ga;
+                    C[m * ldc + rows[h]] = v * gw;
+                }
+            }
+        }
+    }
+}
+
+// k_gemv_reg: the same product for K <= 4096 without LDS.  Lane l works on blocks l + 64 u (u < UB) of
+// every row it visits, so it loads those blocks of A (expanded to bf16 for W4A4) into registers
+// once; a wave then streams pairs of W rows with all their loads issued ahead of the arithmetic.
+template <int MM, bool A_Q, int UB>
+__global__ __launch_bounds__(256) void k_gemv_reg(const __bf16 *__restrict__ A, int64_t lda,
+                                                  const uint8_t *__restrict__ a_codes,
+                                                  const uint8_t *__restrict__ a_scales, const float *__restrict__ a_g,
+                                                  const uint8_t *__restrict__ w_codes,
+                                                  const uint8_t *__restrict__ w_scales, const float *__restrict__ w_g,
+                                                  float *__restrict__ C, int64_t ldc, int64_t N, int64_t K) {
+    const int lane = threadIdx.x & 63;
+    const int64_t nblk = K / 16;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    // lanes past the last block use the last block and add nothing
+    int64_t blk[UB];
+#pragma unroll
+    for (int u = 0; u < UB; u++) {
+        const int64_t b = lane + 64 * u;
+        blk[u] = b < nblk ? b : nblk - 1;
+    }
+    u32x2 cw[2][UB];
+    uint32_t sb[2][UB];
+    auto load_rows = [&](const int64_t (&rows)[2]) {
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+#pragma unroll
+            for (int u = 0; u < UB; u++) {
+                cw[h][u] = *reinterpret_cast<const u32x2 *>(w_codes + rows[h] * (K / 2) + blk[u] * 8);
+                sb[h][u] = w_scales[rows[h] * nblk + blk[u]];
+            }
+    };
+    // A's blocks of this lane, 16 bf16 each
+    u32x4 av[MM][UB][2];
+#pragma unroll
+    for (int m = 0; m < MM; m++)
+#pragma unroll
+        for (int u = 0; u < UB; u++) {
+            if constexpr (!A_Q) {
+                const u32x4 *ap = reinterpret_cast<const u32x4 *>(A + m * lda + blk[u] * 16);
+                av[m][u][0] = ap[0];
+                av[m][u][1] = ap[1];
+            } else {
+                const u32x2 c = *reinterpret_cast<const u32x2 *>(a_codes + m * (K / 2) + blk[u] * 8);
+                const float s = __builtin_amdgcn_cvt_f32_fp8((int)a_scales[m * nblk + blk[u]], 0);
+                av[m][u][0] = expand8(c[0], s);
+                av[m][u][1] = expand8(c[1], s);
+            }
+        }
+    const float gw = *w_g;
+    const float ga = A_Q ? *a_g : 1.0f;
+    for (int64_t n = wave; n < N; n += 2 * nwaves) {
+        const int64_t rows[2] = {n, (n + nwaves) < N ? (n + nwaves) : n};
+        load_rows(rows);
+        float acc[2][MM];
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+#pragma unroll
+            for (int m = 0; m < MM; m++) acc[h][m] = 0.0f;
+#pragma unroll
+        for (int u = 0; u < UB; u++) {
+            const bool live = lane + 64 * u < nblk;
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const float sc = __builtin_amdgcn_cvt_f32_fp8((int)sb[h][u], 0);
+                bf16x2 wv[8];
+                fp4_unpack8_bf16x2(cw[h][u][0], wv);
+                fp4_unpack8_bf16x2(cw[h][u][1], wv + 4);
+#pragma unroll
+                for (int m = 0; m < MM; m++) {
+                    const u32x4 a0 = av[m][u][0], a1 = av[m][u][1];
+                    float part = 0.0f;
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        part = __builtin_amdgcn_fdot2_f32_bf16(wv[q], as_bf16x2(a0[q]), part, false);
+                        part = __builtin_amdgcn_fdot2_f32_bf16(wv[4 + q], as_bf16x2(a1[q]), part, false);
+                    }
+                    acc[h][m] += live ? part * sc : 0.0f;
+                }
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            if (h == 1 && rows[1] == rows[0]) break;
+#pragma unroll
+            for (int m = 0; m < MM; m++) {
+                const float t = wave_sum_f32(acc[h][m]);
+                if (lane == 0) {
+                    float v = t;
+                    if (A_Q) v = v * ga;
+                    C[m * ldc + rows[h]] = v * gw;
+                }
             }
         }
     }
@@ -683,12 +818,30 @@ size_t gemv_lds_bytes(int64_t M, int64_t K) { return (size_t)M * (size_t)K * 2; 
 
 bool gemv_applies(int64_t M, int64_t K) { return M >= 1 && M <= 4 && gemv_lds_bytes(M, K) <= 64 * 1024; }
 
+template <int MM, bool A_Q, int UB>
+static void launch_gemv_reg(const void *a_bf16, int64_t lda, const nvfp4_tensor *a_q, const nvfp4_tensor *w,
+                            float *c, int64_t ldc, int num_cus, hipStream_t stream) {
+    const int64_t N = w->rows, K = w->cols;
+    int64_t grid = (N + 7) / 8;  // one pass of two rows per wave, at most 16 workgroups per CU
+    if (grid > (int64_t)num_cus * 16) grid = (int64_t)num_cus * 16;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL((k_gemv_reg<MM, A_Q, UB>), dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16 *)a_bf16,
+                       lda, A_Q ? a_q->codes : nullptr, A_Q ? a_q->scales : nullptr, A_Q ? a_q->global_scale : nullptr,
+                       w->codes, w->scales, w->global_scale, c, ldc, N, K);
+}
+
 template <int MM, bool A_Q>
 static void launch_gemv_t(const void *a_bf16, int64_t lda, const nvfp4_tensor *a_q, const nvfp4_tensor *w, float *c,
                           int64_t ldc, int num_cus, hipStream_t stream) {
     const int64_t N = w->rows, K = w->cols;
-    int64_t grid = (N + 3) / 4;
-    if (grid > (int64_t)num_cus * 8) grid = (int64_t)num_cus * 8;
+    const int64_t ub = (K / 16 + 63) / 64;  // blocks per lane
+    if (ub <= 1) return launch_gemv_reg<MM, A_Q, 1>(a_bf16, lda, a_q, w, c, ldc, num_cus, stream);
+    if (ub <= 2) return launch_gemv_reg<MM, A_Q, 2>(a_bf16, lda, a_q, w, c, ldc, num_cus, stream);
+    if (ub <= 3) return launch_gemv_reg<MM, A_Q, 3>(a_bf16, lda, a_q, w, c, ldc, num_cus, stream);
+    if (ub <= 4) return launch_gemv_reg<MM, A_Q, 4>(a_bf16, lda, a_q, w, c, ldc, num_cus, stream);
+    // a wave takes two rows per pass, one pass per wave up to 16 workgroups per CU
+    int64_t grid = (N + 7) / 8;
+    if (grid > (int64_t)num_cus * 16) grid = (int64_t)num_cus * 16;
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL((k_gemv<MM, A_Q>), dim3((unsigned)grid), dim3(256), gemv_lds_bytes(MM, K), stream,
                        (const __bf16 *)a_bf16, lda, A_Q ? a_q->codes : nullptr, A_Q ? a_q->scales : nullptr,
