@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import oracle
+import synth
 from conftest import read_golden
 
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
@@ -379,3 +380,19 @@ def test_percentile_student_t_closed_form():
     assert np.all(np.abs(pct - q) < 1.3)
     assert abs(pct.mean() - q) < 0.25
     assert np.all(mx >= pct)
+
+
+def test_gemm_against_unquantized_tracks_weight_error():
+    # With independent Gaussian weight errors, the W4A16 product's Frobenius error against the
+    # unquantized product equals the weight's relative quantization error (about 9.5 % for
+    # N(0, 0.02) weights, the Gaussian counterpart of the pages' per-matrix 6.3-9.6 %).  A wrong
+    # scale, sign or nibble order anywhere in quantize, expand or GEMM breaks the equality.
+    w = synth.normal_f32((256, 1024), 0.02, 11)
+    a = synth.bf16_bits(np.random.default_rng(12).standard_normal((128, 1024)).astype(np.float32))
+    q, _ = oracle.quantize(w)
+    werr = np.linalg.norm(oracle.dequantize(q, "f64") - w) / np.linalg.norm(w)
+    cq = oracle.gemm_w4a16(a, q)
+    cu = oracle.gemm_f64(oracle.bf16_bits_to_f64(a), w.astype(np.float64))
+    cerr = np.linalg.norm(cq - cu) / np.linalg.norm(cu)
+    assert 0.07 < werr < 0.12
+    assert 0.85 * werr < cerr < 1.15 * werr

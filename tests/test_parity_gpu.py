@@ -279,7 +279,11 @@ def test_gemm_attention_projection_full(nv):
     c = nv.gemm(to_dev_bf16(a_bits), q).cpu().numpy()
     cref = oracle.gemm_w4a16(a_bits, ref)
     err = oracle.gemm_error(c, cref)
-    _note(f"  W4A16 floored max rel err {err:.3e}, normwise {np.abs(c - cref).max() / np.abs(cref).max():.3e}")
+    # informational: the NVFP4 product against the unquantized one (fp32 W, bf16 A) in fp64
+    cu = oracle.gemm_f64(oracle.bf16_bits_to_f64(a_bits[:256]), w.astype(np.float64))
+    qerr = np.linalg.norm(c[:256] - cu) / np.linalg.norm(cu)
+    _note(f"  W4A16 floored max rel err {err:.3e}, normwise {np.abs(c - cref).max() / np.abs(cref).max():.3e}, "
+          f"vs unquantized (256 rows, Frobenius) {qerr:.3e}")
     assert err <= GEMM_TOL
     aq = _quant(nv, to_dev_bf16(a_bits))
     aref, _ = oracle.quantize(a_bits, oracle.BF16)
