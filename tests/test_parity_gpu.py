@@ -210,8 +210,11 @@ def _rand_q(nv, rows, cols, seed, sigma=0.02):
     return q, ref
 
 
+# M <= 4 takes the GEMV kernels: A in registers up to K = 4096 (here 16 .. 4096), A in LDS beyond
+# (6144, 8192)
 @pytest.mark.parametrize("mnk", [(16, 64, 256), (1, 64, 128), (2, 100, 48), (3, 33, 4096), (4, 17, 16),
-                                 (5, 70, 80), (37, 129, 272), (130, 257, 1024), (256, 128, 64), (300, 200, 3072)])
+                                 (5, 70, 80), (37, 129, 272), (130, 257, 1024), (256, 128, 64), (300, 200, 3072),
+                                 (2, 300, 8192), (4, 129, 6144)])
 def test_gemm_w4a16(nv, mnk):
     m, n, k = mnk
     _note(f"gemm w4a16 {mnk}")
@@ -227,7 +230,8 @@ def test_gemm_w4a16(nv, mnk):
         assert np.array_equal(out.cpu().numpy(), c)
 
 
-@pytest.mark.parametrize("mnk", [(16, 64, 256), (2, 300, 1024), (4, 64, 16), (64, 96, 112), (200, 300, 512)])
+@pytest.mark.parametrize("mnk", [(16, 64, 256), (2, 300, 1024), (4, 64, 16), (64, 96, 112), (200, 300, 512),
+                                 (2, 100, 8192)])
 def test_gemm_w4a4(nv, mnk):
     m, n, k = mnk
     _note(f"gemm w4a4 {mnk}")
