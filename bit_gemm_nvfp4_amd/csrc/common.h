@@ -31,25 +31,24 @@ __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_c
 // ---------------------------------------------------------------------------------------------
 // E4M3 (OCP e4m3fn) block-scale bytes.
 // ---------------------------------------------------------------------------------------------
-// Round-to-nearest-even of a non-negative, non-NaN fp32 value onto the E4M3 grid, saturating at
-// 448 (0x7E).  Normal range: round the fp32 mantissa at bit 20 (3 kept bits) by integer add and
-// rebias the exponent; subnormal range (t < 2^-6, step 2^-9): rint(t * 2^9), where the scaling by
-// a power of two is exact and rint rounds half to even.
+// Round-to-nearest-even of a non-negative fp32 value onto the E4M3 grid, saturating at 448 (0x7E;
+// NaN also gives 0x7E).  Normal range: round the fp32 mantissa at bit 20 (3 kept bits) by integer
+// add and rebias the exponent; subnormal range (t < 2^-6, step 2^-9): rint(t * 2^9), where the
+// scaling by a power of two is exact and rint rounds half to even.  Both are computed and the
+// right one selected, so the conversion has no branches.
 __device__ __forceinline__ uint32_t e4m3_from_f32(float t) {
-    if (!(t < 448.0f)) return 0x7Eu;
-    if (t < 0.015625f) return (uint32_t)__builtin_rintf(t * 512.0f);
-    uint32_t u = f2u(t);
-    uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
+    const uint32_t sub = (uint32_t)__builtin_rintf(__builtin_fminf(t, 0.015625f) * 512.0f);
+    const uint32_t u = f2u(t);
+    const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
     uint32_t code = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);
-    return code < 0x7Eu ? code : 0x7Eu;
+    code = code < 0x7Eu ? code : 0x7Eu;
+    const uint32_t v = t < 0.015625f ? sub : code;
+    return t < 448.0f ? v : 0x7Eu;
 }
 
-// Value of a non-negative E4M3 byte (0x00..0x7E) as fp32 (exact).
-__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-    uint32_t e = (b >> 3) & 15u, m = b & 7u;
-    if (e == 0) return (float)m * 0.001953125f;  // m * 2^-9
-    return u2f(((e + 120u) << 23) | (m << 20));
-}
+// Value of a non-negative E4M3 byte (0x00..0x7E) as fp32 (exact): the hardware OCP e4m3
+// conversion.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) { return __builtin_amdgcn_cvt_f32_fp8((int)b, 0); }
 
 // ---------------------------------------------------------------------------------------------
 // E2M1 codes: hardware conversions with a unit scale.
@@ -62,9 +61,10 @@ __device__ __forceinline__ uint32_t fp4_pk(uint32_t word, float a, float b) {
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, a, b, 1.0f, SEL);
 }
 
-// Eight fp32 -> one dword of eight E2M1 codes (element i in nibble i).
+// Eight fp32 -> one dword of eight E2M1 codes (element i in nibble i).  Every byte of the result is
+// written, so the starting value of the dword does not matter (an input register avoids a move).
 __device__ __forceinline__ uint32_t fp4_pack8(const float *y) {
-    uint32_t w = 0;
+    uint32_t w = f2u(y[0]);
     w = fp4_pk<0>(w, y[0], y[1]);
     w = fp4_pk<1>(w, y[2], y[3]);
     w = fp4_pk<2>(w, y[4], y[5]);
@@ -72,9 +72,9 @@ __device__ __forceinline__ uint32_t fp4_pack8(const float *y) {
     return w;
 }
 
-// Four fp32 -> the low 16 bits of a dword (element i in nibble i).
+// Four fp32 -> the low 16 bits of a dword (element i in nibble i); the high 16 bits are unspecified.
 __device__ __forceinline__ uint32_t fp4_pack4(const float *y) {
-    uint32_t w = 0;
+    uint32_t w = f2u(y[0]);
     w = fp4_pk<0>(w, y[0], y[1]);
     w = fp4_pk<1>(w, y[2], y[3]);
     return w;

@@ -187,8 +187,13 @@ __device__ __forceinline__ uint32_t tile_block_max(const TileRegs<SRC> &t, int l
     }
 }
 
-// Encode one tile whose lane-L block maximum is `bm`, given the global scale g (and 6 g).
-template <int SRC>
+// Encode one tile whose lane-L block maximum is `bm`, given the global scale g (and 6 g).  The
+// per-block work (lane L owns block L) has no branches; the conversions of a tile take one of two
+// wave-uniform paths: the plain one, or, when some block's reciprocal overflowed, one that keeps
+// zeros at zero.  Tiles wholly inside the tensor store without per-lane bounds checks.
+// CHECK_FINITE: set bit 0 of `flags` for a non-finite block here (callers that derive the global
+// scale from the run-time tensor maximum flag that maximum instead, which covers every block).
+template <int SRC, bool CHECK_FINITE = true>
 __device__ __forceinline__ void tile_encode(const TileRegs<SRC> &t, uint32_t bm, float g, float six_g, float sc,
                                             uint64_t tile, uint64_t nblocks, uint8_t *__restrict__ codes,
                                             uint8_t *__restrict__ scales, int32_t *__restrict__ flags, int lane) {
@@ -196,6 +201,7 @@ __device__ __forceinline__ void tile_encode(const TileRegs<SRC> &t, uint32_t bm,
     constexpr int VPB = kVpb<SRC>;
     constexpr int BPL = 64 / VPB;
     const uint64_t blk0 = tile * 64;
+    const bool full = blk0 + 64 <= nblocks;  // wave-uniform
     float bamax;
     bool bad;
     if constexpr (SRC == NVFP4_E4M3) {
@@ -207,46 +213,64 @@ __device__ __forceinline__ void tile_encode(const TileRegs<SRC> &t, uint32_t bm,
         bamax = u2f(bm);
     }
     const uint64_t myblk = blk0 + lane;
-    bad = bad && (myblk < nblocks);
-    if (__any(bad) && lane == 0 && flags) atomicOr(flags, 1);
-    // per-block scale byte and reciprocal (lane L owns block L)
-    uint32_t sbyte = 0;
-    if (g != 0.0f) sbyte = e4m3_from_f32(bamax / six_g);
+    if constexpr (CHECK_FINITE) {
+        bad = bad && (myblk < nblocks);
+        if (__any(bad) && lane == 0 && flags) atomicOr(flags, 1);
+    }
+    // per-block scale byte and reciprocal (lane L owns block L); a zero scale (g = 0, or a block
+    // of zeros) gives reciprocal 0
+    const float q = bamax / six_g;
+    const uint32_t sbyte = g != 0.0f ? e4m3_from_f32(q) : 0u;
     const float s = e4m3_to_f32(sbyte);
-    const float r = (s == 0.0f) ? 0.0f : 1.0f / (s * g);
-    if (myblk < nblocks) scales[myblk] = (uint8_t)sbyte;
-    // each lane converts its own vectors with its block's reciprocal
+    const float rd = 1.0f / (s * g);
+    const float r = s == 0.0f ? 0.0f : rd;
+    if (full || myblk < nblocks) scales[myblk] = (uint8_t)sbyte;
+    // each lane's vectors take their block's reciprocal
+    float rj[VPB];
 #pragma unroll
-    for (int j = 0; j < VPB; j++) {
-        const uint32_t vt = j * 64 + lane;
-        const uint64_t blk = blk0 + vt / VPB;
-        float rj;
-        if constexpr (VPB == 1) {
-            rj = r;
-        } else {
-            rj = __shfl(r, j * BPL + lane / VPB, 64);
-        }
+    for (int j = 0; j < VPB; j++) rj[j] = VPB == 1 ? r : __shfl(r, j * BPL + lane / VPB, 64);
+    uint32_t out[VPB][EPV / 8 > 0 ? EPV / 8 : 1];
+    auto convert = [&](int j, bool keep_zero) {
         float v[EPV];
         widen<SRC>(t.raw[j], sc, v);
         float y[EPV];
-        if (__builtin_expect(__builtin_isinf(rj), 0)) {
-            // tiny s * g: fl(1 / d) overflowed; |v| * inf saturates, 0 stays 0 (no 0 * inf)
 #pragma unroll
-            for (int e = 0; e < EPV; e++) y[e] = (v[e] == 0.0f) ? v[e] : v[e] * rj;
+        for (int e = 0; e < EPV; e++) y[e] = (keep_zero && v[e] == 0.0f) ? v[e] : v[e] * rj[j];
+        if constexpr (EPV == 4) {
+            out[j][0] = fp4_pack4(y);
+        } else if constexpr (EPV == 8) {
+            out[j][0] = fp4_pack8(y);
         } else {
+            out[j][0] = fp4_pack8(y);
+            out[j][1] = fp4_pack8(y + 8);
+        }
+    };
+    if (__builtin_expect(__any(__builtin_isinf(r)), 0)) {
+        // tiny s * g: fl(1 / d) overflowed; |v| * inf saturates, 0 stays 0 (no 0 * inf)
 #pragma unroll
-            for (int e = 0; e < EPV; e++) y[e] = v[e] * rj;
+        for (int j = 0; j < VPB; j++) convert(j, true);
+    } else {
+#pragma unroll
+        for (int j = 0; j < VPB; j++) convert(j, false);
+    }
+    auto store = [&](int j) {
+        const uint32_t vt = j * 64 + lane;
+        uint8_t *dst = codes + ((blk0 + vt / VPB) * VPB + vt % VPB) * (EPV / 2);
+        if constexpr (EPV == 4) {
+            *reinterpret_cast<uint16_t *>(dst) = (uint16_t)out[j][0];
+        } else if constexpr (EPV == 8) {
+            *reinterpret_cast<uint32_t *>(dst) = out[j][0];
+        } else {
+            *reinterpret_cast<u32x2 *>(dst) = u32x2{out[j][0], out[j][1]};
         }
-        if (blk < nblocks) {
-            uint8_t *dst = codes + (blk * VPB + vt % VPB) * (EPV / 2);
-            if constexpr (EPV == 4) {
-                *reinterpret_cast<uint16_t *>(dst) = (uint16_t)fp4_pack4(y);
-            } else if constexpr (EPV == 8) {
-                *reinterpret_cast<uint32_t *>(dst) = fp4_pack8(y);
-            } else {
-                *reinterpret_cast<u32x2 *>(dst) = u32x2{fp4_pack8(y), fp4_pack8(y + 8)};
-            }
-        }
+    };
+    if (full) {
+#pragma unroll
+        for (int j = 0; j < VPB; j++) store(j);
+    } else {
+#pragma unroll
+        for (int j = 0; j < VPB; j++)
+            if (blk0 + (j * 64 + lane) / VPB < nblocks) store(j);
     }
 }
 
@@ -272,7 +296,7 @@ __global__ __launch_bounds__(256) void k_encode(TileGeom gm, const float *__rest
                                                 const float *__restrict__ amax_in, uint8_t *__restrict__ codes,
                                                 uint8_t *__restrict__ scales, float *__restrict__ g_out,
                                                 int32_t *__restrict__ flags) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const float sc = (SRC == NVFP4_E4M3 && src_scale) ? *src_scale : 1.0f;
     const float g = *amax_in / 2688.0f;
     if (blockIdx.x == 0 && threadIdx.x == 0) *g_out = g;
@@ -303,10 +327,11 @@ __global__ __launch_bounds__(256) void k_encode(TileGeom gm, const float *__rest
 // the encode.
 //
 // Agreement on amax: every workgroup publishes one 64-bit word (call epoch << 32 | its partial
-// maximum) in its workspace slot, and wave 0 of every workgroup polls all slots until each carries
-// this call's epoch.  The payload travels inside the atomic word, so relaxed device-scope atomics
-// suffice (no cache maintenance in the loop).  The epoch differs between calls, so the workspace
-// needs no clearing and earlier contents are ignored.  The poll is bounded: if other work kept some
+// maximum) in its workspace slot; workgroup 0 polls all slots until each carries this call's
+// epoch, then publishes (epoch << 32 | tensor maximum) in a result word that the other workgroups
+// poll.  The payload travels inside the atomic word, so relaxed device-scope atomics suffice (no
+// cache maintenance in the loop).  The epoch differs between calls, so the workspace needs no
+// clearing and earlier contents are ignored.  The polls are bounded: if other work kept some
 // workgroups from being scheduled for that long, bit 1 of `flags` is set and the outputs are
 // invalid, instead of a hang.
 // ---------------------------------------------------------------------------------------------
@@ -322,11 +347,12 @@ __global__ __launch_bounds__(256) void k_quant_fused(TileGeom gm, const float *_
                                                      float *__restrict__ g_out, int32_t *__restrict__ flags) {
     __shared__ uint32_t red[4];
     __shared__ uint32_t amax_bits;
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint64_t ntiles = (gm.nblocks + 63) / 64;
     const uint64_t wave = (uint64_t)blockIdx.x * 4 + wid, nwaves = (uint64_t)gridDim.x * 4;
     const float sc = (SRC == NVFP4_E4M3 && src_scale) ? *src_scale : 1.0f;
     uint64_t *slots = reinterpret_cast<uint64_t *>(ws + kSlotBase);
+    uint64_t *result = reinterpret_cast<uint64_t *>(ws);
 
     // ---- phase 1: load the resident tiles, block maxima, tensor maximum ----
     TileRegs<SRC> t[TPW];
@@ -358,22 +384,51 @@ __global__ __launch_bounds__(256) void k_quant_fused(TileGeom gm, const float *_
             __hip_atomic_store(&slots[blockIdx.x], ((uint64_t)epoch << 32) | wgmax, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
-        // ---- wait for every workgroup's slot of this call, reduce the maxima ----
+        // ---- workgroup 0 waits for every slot of this call and publishes the maximum in the
+        // result word; the others wait for the result word only (one load per poll, so the
+        // polling adds almost no memory traffic while other workgroups still stream input) ----
         uint32_t a = 0;
-        for (uint32_t it = 0;; it++) {
-            bool ready = true;
-            a = 0;
-            for (uint32_t i = lane; i < gridDim.x; i += 64) {
-                const uint64_t v = __hip_atomic_load(&slots[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if ((uint32_t)(v >> 32) != epoch) ready = false;
-                a = max(a, (uint32_t)v);
+        if (blockIdx.x == 0) {
+            // all loads of a chunk of 8 slots per lane in flight at once
+            const uint32_t G = gridDim.x;
+            for (uint32_t it = 0;; it++) {
+                bool ready = true;
+                a = 0;
+                for (uint32_t base = 0; base < G; base += 512) {
+                    uint64_t v[8];
+#pragma unroll
+                    for (int k = 0; k < 8; k++) {
+                        const uint32_t i = base + (uint32_t)lane + 64u * k;
+                        v[k] = i < G ? __hip_atomic_load(&slots[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                     : (uint64_t)epoch << 32;
+                    }
+#pragma unroll
+                    for (int k = 0; k < 8; k++) {
+                        if ((uint32_t)(v[k] >> 32) != epoch) ready = false;
+                        a = max(a, (uint32_t)v[k]);
+                    }
+                }
+                if (__all(ready)) break;
+                if (it >= kPollLimit) {
+                    if (lane == 0 && flags) atomicOr(flags, 2);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
             }
-            if (__all(ready)) break;
-            if (it >= kPollLimit) {
-                if (lane == 0 && flags) atomicOr(flags, 2);
-                break;
+            a = wave_max_u32(a);
+            if (lane == 0)
+                __hip_atomic_store(result, ((uint64_t)epoch << 32) | a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            for (uint32_t it = 0;; it++) {
+                const uint64_t v = __hip_atomic_load(result, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                a = (uint32_t)v;
+                if ((uint32_t)(v >> 32) == epoch) break;
+                if (it >= kPollLimit) {
+                    if (lane == 0 && flags) atomicOr(flags, 2);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
             }
-            __builtin_amdgcn_s_sleep(1);
         }
         a = wave_max_u32(a);
         if (lane == 0) amax_bits = a;
@@ -392,7 +447,8 @@ __global__ __launch_bounds__(256) void k_quant_fused(TileGeom gm, const float *_
 #pragma unroll
     for (int s = 0; s < TPW; s++) {
         const uint64_t tile = wave + s * nwaves;
-        if (tile < ntiles) tile_encode<SRC>(t[s], bm[s], g, six_g, sc, tile, gm.nblocks, codes, scales, flags, lane);
+        if (tile < ntiles)
+            tile_encode<SRC, false>(t[s], bm[s], g, six_g, sc, tile, gm.nblocks, codes, scales, flags, lane);
     }
     for (uint64_t tile = wave + TPW * nwaves; tile < ntiles; tile += PB * nwaves) {
         TileRegs<SRC> o[PB];
@@ -402,8 +458,8 @@ __global__ __launch_bounds__(256) void k_quant_fused(TileGeom gm, const float *_
         for (int b = 0; b < PB; b++) {
             const uint64_t tb = tile + b * nwaves;
             if (tb < ntiles)
-                tile_encode<SRC>(o[b], tile_block_max<SRC>(o[b], lane), g, six_g, sc, tb, gm.nblocks, codes, scales,
-                                 flags, lane);
+                tile_encode<SRC, false>(o[b], tile_block_max<SRC>(o[b], lane), g, six_g, sc, tb, gm.nblocks, codes,
+                                        scales, flags, lane);
         }
     }
 }
