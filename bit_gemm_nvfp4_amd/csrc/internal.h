@@ -11,7 +11,7 @@
 namespace nvfp4 {
 
 // Quantize workspace: a few words plus one 64-bit slot per workgroup of the single-pass kernel
-// (two workgroups per CU, so 2040 slots cover parts with up to 1020 CUs).
+// (2040 slots: four workgroups per CU on parts with up to 510 CUs, two on larger ones).
 constexpr size_t kQuantizeWsBytes = 16384;
 
 hipError_t launch_quantize(const void *x, nvfp4_dtype dt, int64_t ld_x, const float *src_scale, const float *amax_in,

@@ -187,48 +187,54 @@ __device__ __forceinline__ uint32_t tile_block_max(const TileRegs<SRC> &t, int l
     }
 }
 
-// Encode one tile whose lane-L block maximum is `bm`, given the global scale g (and 6 g).  The
-// per-block work (lane L owns block L) has no branches; the conversions of a tile take one of two
-// wave-uniform paths: the plain one, or, when some block's reciprocal overflowed, one that keeps
-// zeros at zero.  Tiles wholly inside the tensor store without per-lane bounds checks.
-// CHECK_FINITE: set bit 0 of `flags` for a non-finite block here (callers that derive the global
-// scale from the run-time tensor maximum flag that maximum instead, which covers every block).
-template <int SRC, bool CHECK_FINITE = true>
-__device__ __forceinline__ void tile_encode(const TileRegs<SRC> &t, uint32_t bm, float g, float six_g, float sc,
-                                            uint64_t tile, uint64_t nblocks, uint8_t *__restrict__ codes,
-                                            uint8_t *__restrict__ scales, int32_t *__restrict__ flags, int lane) {
+// Per-block scale byte and reciprocal for the block whose largest magnitude pattern is `bm` (lane
+// L of a tile owns block L), given the global scale g (and 6 g).  No branches; a zero scale (g = 0,
+// or a block of zeros) gives reciprocal 0.
+struct BlockScale {
+    uint32_t sbyte;
+    float r;
+};
+
+template <int SRC>
+__device__ __forceinline__ float block_amax(uint32_t bm, float sc) {
+    if constexpr (SRC == NVFP4_E4M3) return e4m3_to_f32(bm) * sc;
+    else return u2f(bm);
+}
+
+template <int SRC>
+__device__ __forceinline__ bool block_nonfinite(uint32_t bm, float sc) {
+    if constexpr (SRC == NVFP4_E4M3) return bm == 0x7Fu || !(block_amax<SRC>(bm, sc) <= 3.402823466e38f);
+    else return bm >= 0x7F800000u;
+}
+
+template <int SRC>
+__device__ __forceinline__ BlockScale block_scale(uint32_t bm, float g, float six_g, float sc) {
+    const float q = block_amax<SRC>(bm, sc) / six_g;
+    BlockScale b;
+    b.sbyte = g != 0.0f ? e4m3_from_f32(q) : 0u;
+    const float s = e4m3_to_f32(b.sbyte);
+    const float rd = 1.0f / (s * g);
+    b.r = s == 0.0f ? 0.0f : rd;
+    return b;
+}
+
+// Write one tile: the scale bytes (lane L: block L) and the codes, each lane converting its own
+// vectors with its block's reciprocal.  The conversions take one of two wave-uniform paths: the
+// plain one, or, when some block's reciprocal overflowed, one that keeps zeros at zero.  Tiles
+// wholly inside the tensor store without per-lane bounds checks.
+template <int SRC>
+__device__ __forceinline__ void tile_store(const TileRegs<SRC> &t, BlockScale b, float sc, uint64_t tile,
+                                           uint64_t nblocks, uint8_t *__restrict__ codes,
+                                           uint8_t *__restrict__ scales, int lane) {
     constexpr int EPV = kEpv<SRC>;
     constexpr int VPB = kVpb<SRC>;
     constexpr int BPL = 64 / VPB;
     const uint64_t blk0 = tile * 64;
     const bool full = blk0 + 64 <= nblocks;  // wave-uniform
-    float bamax;
-    bool bad;
-    if constexpr (SRC == NVFP4_E4M3) {
-        bad = (bm == 0x7Fu);
-        bamax = e4m3_to_f32(bm) * sc;
-        bad = bad || !(bamax <= 3.402823466e38f);
-    } else {
-        bad = bm >= 0x7F800000u;
-        bamax = u2f(bm);
-    }
-    const uint64_t myblk = blk0 + lane;
-    if constexpr (CHECK_FINITE) {
-        bad = bad && (myblk < nblocks);
-        if (__any(bad) && lane == 0 && flags) atomicOr(flags, 1);
-    }
-    // per-block scale byte and reciprocal (lane L owns block L); a zero scale (g = 0, or a block
-    // of zeros) gives reciprocal 0
-    const float q = bamax / six_g;
-    const uint32_t sbyte = g != 0.0f ? e4m3_from_f32(q) : 0u;
-    const float s = e4m3_to_f32(sbyte);
-    const float rd = 1.0f / (s * g);
-    const float r = s == 0.0f ? 0.0f : rd;
-    if (full || myblk < nblocks) scales[myblk] = (uint8_t)sbyte;
-    // each lane's vectors take their block's reciprocal
+    if (full || blk0 + lane < nblocks) scales[blk0 + lane] = (uint8_t)b.sbyte;
     float rj[VPB];
 #pragma unroll
-    for (int j = 0; j < VPB; j++) rj[j] = VPB == 1 ? r : __shfl(r, j * BPL + lane / VPB, 64);
+    for (int j = 0; j < VPB; j++) rj[j] = VPB == 1 ? b.r : __shfl(b.r, j * BPL + lane / VPB, 64);
     uint32_t out[VPB][EPV / 8 > 0 ? EPV / 8 : 1];
     auto convert = [&](int j, bool keep_zero) {
         float v[EPV];
@@ -245,7 +251,7 @@ __device__ __forceinline__ void tile_encode(const TileRegs<SRC> &t, uint32_t bm,
             out[j][1] = fp4_pack8(y + 8);
         }
     };
-    if (__builtin_expect(__any(__builtin_isinf(r)), 0)) {
+    if (__builtin_expect(__any(__builtin_isinf(b.r)), 0)) {
         // tiny s * g: fl(1 / d) overflowed; |v| * inf saturates, 0 stays 0 (no 0 * inf)
 #pragma unroll
         for (int j = 0; j < VPB; j++) convert(j, true);
@@ -253,15 +259,15 @@ __device__ __forceinline__ void tile_encode(const TileRegs<SRC> &t, uint32_t bm,
 #pragma unroll
         for (int j = 0; j < VPB; j++) convert(j, false);
     }
+    // vector vt = j * 64 + lane of the tile holds elements (blk0 * VPB + vt) * EPV ..
+    uint8_t *dst = codes + (blk0 * VPB + lane) * (EPV / 2);
     auto store = [&](int j) {
-        const uint32_t vt = j * 64 + lane;
-        uint8_t *dst = codes + ((blk0 + vt / VPB) * VPB + vt % VPB) * (EPV / 2);
         if constexpr (EPV == 4) {
-            *reinterpret_cast<uint16_t *>(dst) = (uint16_t)out[j][0];
+            *reinterpret_cast<uint16_t *>(dst + j * 64 * (EPV / 2)) = (uint16_t)out[j][0];
         } else if constexpr (EPV == 8) {
-            *reinterpret_cast<uint32_t *>(dst) = out[j][0];
+            *reinterpret_cast<uint32_t *>(dst + j * 64 * (EPV / 2)) = out[j][0];
         } else {
-            *reinterpret_cast<u32x2 *>(dst) = u32x2{out[j][0], out[j][1]};
+            *reinterpret_cast<u32x2 *>(dst + j * 64 * (EPV / 2)) = u32x2{out[j][0], out[j][1]};
         }
     };
     if (full) {
@@ -272,6 +278,20 @@ __device__ __forceinline__ void tile_encode(const TileRegs<SRC> &t, uint32_t bm,
         for (int j = 0; j < VPB; j++)
             if (blk0 + (j * 64 + lane) / VPB < nblocks) store(j);
     }
+}
+
+// Encode one tile whose lane-L block maximum is `bm`.  CHECK_FINITE: set bit 0 of `flags` for a
+// non-finite block here (callers that derive the global scale from the run-time tensor maximum
+// flag that maximum instead, which covers every block).
+template <int SRC, bool CHECK_FINITE = true>
+__device__ __forceinline__ void tile_encode(const TileRegs<SRC> &t, uint32_t bm, float g, float six_g, float sc,
+                                            uint64_t tile, uint64_t nblocks, uint8_t *__restrict__ codes,
+                                            uint8_t *__restrict__ scales, int32_t *__restrict__ flags, int lane) {
+    if constexpr (CHECK_FINITE) {
+        const bool bad = block_nonfinite<SRC>(bm, sc) && (tile * 64 + lane < nblocks);
+        if (__any(bad) && lane == 0 && flags) atomicOr(flags, 1);
+    }
+    tile_store<SRC>(t, block_scale<SRC>(bm, g, six_g, sc), sc, tile, nblocks, codes, scales, lane);
 }
 
 // amax word (integer max of magnitude patterns; for E4M3 the largest magnitude byte) -> fp32 amax.
@@ -320,7 +340,7 @@ __global__ __launch_bounds__(256) void k_encode(TileGeom gm, const float *__rest
 }
 
 // ---------------------------------------------------------------------------------------------
-// Single-pass path: one launch of at most two workgroups per CU, small enough that every workgroup
+// Single-pass path: one launch of at most four workgroups per CU, small enough that every workgroup
 // is resident at once on an otherwise idle GPU.  Each wave loads its TPW tiles and keeps them in
 // registers while the grid agrees on amax, then encodes them from registers, so the input crosses
 // HBM once.  Tiles beyond the register capacity are streamed for the maximum and read again for
@@ -337,7 +357,7 @@ __global__ __launch_bounds__(256) void k_encode(TileGeom gm, const float *__rest
 // ---------------------------------------------------------------------------------------------
 constexpr int kSlotBase = 16;       // workspace words before the 64-bit slots (8-byte aligned)
 
-constexpr int kFusedPerCu = 2;      // workgroups per CU of the single-pass kernel
+constexpr int kFusedPerCu = 4;      // most workgroups per CU of the single-pass kernel
 constexpr uint32_t kPollLimit = 1u << 22;
 
 template <int SRC, int TPW, int PB>
@@ -444,11 +464,15 @@ __global__ __launch_bounds__(256) void k_quant_fused(TileGeom gm, const float *_
     const float six_g = 6.0f * g;
 
     // ---- phase 2: encode the resident tiles, then the streamed ones ----
+    // the per-block divisions of all resident tiles first (independent, so they overlap), then
+    // the conversions and stores tile by tile
+    BlockScale bs[TPW];
+#pragma unroll
+    for (int s = 0; s < TPW; s++) bs[s] = block_scale<SRC>(bm[s], g, six_g, sc);
 #pragma unroll
     for (int s = 0; s < TPW; s++) {
         const uint64_t tile = wave + s * nwaves;
-        if (tile < ntiles)
-            tile_encode<SRC, false>(t[s], bm[s], g, six_g, sc, tile, gm.nblocks, codes, scales, flags, lane);
+        if (tile < ntiles) tile_store<SRC>(t[s], bs[s], sc, tile, gm.nblocks, codes, scales, lane);
     }
     for (uint64_t tile = wave + TPW * nwaves; tile < ntiles; tile += PB * nwaves) {
         TileRegs<SRC> o[PB];
@@ -477,9 +501,14 @@ static uint32_t next_epoch() {
     return counter.fetch_add(0x61C88647u, std::memory_order_relaxed) | 1u;
 }
 
-// Largest residency (tiles per wave) whose registers still leave room for two workgroups per CU.
+// Largest residency (tiles per wave) whose registers still leave room for four workgroups per CU
+// (at most 128 VGPRs), and for two.
+template <int SRC>
+constexpr int kMaxTpw4 = SRC == NVFP4_F32 ? 4 : SRC == NVFP4_BF16 ? 5 : SRC == NVFP4_F16 ? 8 : 12;
 template <int SRC>
 constexpr int kMaxTpw = SRC == NVFP4_F32 ? 6 : SRC == NVFP4_BF16 ? 8 : SRC == NVFP4_F16 ? 12 : 16;
+// Workgroup slots the quantize workspace holds.
+constexpr int kMaxSlots = (int)((kQuantizeWsBytes - kSlotBase * 4) / 8);
 // For tensors beyond the residency: fewer resident tiles, so that the streamed rest can keep
 // kStreamBatch loads in flight per wave within the same register budget.
 template <int SRC>
@@ -514,27 +543,44 @@ static void launch_fused(const TileGeom &gm, int grid, const float *src_scale, u
                        out->codes, out->scales, out->global_scale, flags);
 }
 
-// Tiles spread over all CUs (two workgroups each, so that two waves share every SIMD and hide each
-// other's latencies; fewer for small tensors); tiles per wave rounded up to a supported residency.
-// Beyond kMaxTpw<SRC> tiles per wave the streaming variant runs (the rest is read twice).
+// Resident launch: tiles per wave rounded up to a supported residency, at most T.
+template <int SRC, int T>
+static void launch_resident(const TileGeom &gm, int grid, uint64_t tpw, const float *src_scale, uint32_t *ws,
+                            const nvfp4_tensor *out, int32_t *flags, int num_cus, hipStream_t stream) {
+    if (tpw <= 1) launch_fused<SRC, 1>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
+    else if (tpw <= 2) launch_fused<SRC, 2>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
+    else if (tpw <= 3) launch_fused<SRC, 3>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
+    else if (tpw <= 4 || T < 5) launch_fused<SRC, (T < 4 ? T : 4)>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
+    else if (tpw <= 5 || T < 6) launch_fused<SRC, (T < 5 ? T : 5)>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
+    else if (tpw <= 6 || T < 8) launch_fused<SRC, (T < 6 ? T : 6)>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
+    else if (tpw <= 8 || T < 12) launch_fused<SRC, (T < 8 ? T : 8)>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
+    else if (tpw <= 12 || T < 16) launch_fused<SRC, (T < 12 ? T : 12)>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
+    else launch_fused<SRC, T>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
+}
+
+// Tiles spread over all CUs: four workgroups each (four waves per SIMD hide each other's
+// latencies) when every wave's tiles then fit the smaller register budget, else two workgroups
+// each with up to kMaxTpw resident tiles; fewer workgroups for small tensors.  Beyond that the
+// streaming variant runs (the rest is read twice).
 template <int SRC>
 static void launch_fused_any(const TileGeom &gm, const float *src_scale, uint32_t *ws, const nvfp4_tensor *out,
                              int32_t *flags, int num_cus, hipStream_t stream) {
     const uint64_t ntiles = (gm.nblocks + 63) / 64;
-    const int grid = grid_for(ntiles, 4, kFusedPerCu * num_cus);
+    if (4 * num_cus <= kMaxSlots) {
+        const int grid4 = grid_for(ntiles, 4, 4 * num_cus);
+        const uint64_t tpw4 = (ntiles + 4 * (uint64_t)grid4 - 1) / (4 * (uint64_t)grid4);
+        if (tpw4 <= (uint64_t)kMaxTpw4<SRC>) {
+            launch_resident<SRC, kMaxTpw4<SRC>>(gm, grid4, tpw4, src_scale, ws, out, flags, num_cus, stream);
+            return;
+        }
+    }
+    const int grid = grid_for(ntiles, 4, 2 * num_cus);
     const uint64_t tpw = (ntiles + 4 * (uint64_t)grid - 1) / (4 * (uint64_t)grid);
-    constexpr int T = kMaxTpw<SRC>;
-    if (tpw > (uint64_t)T) {
+    if (tpw > (uint64_t)kMaxTpw<SRC>) {
         launch_fused<SRC, kStreamTpw<SRC>, kStreamBatch<SRC>>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
         return;
     }
-    if (tpw <= 1) launch_fused<SRC, 1>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
-    else if (tpw <= 2) launch_fused<SRC, 2>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
-    else if (tpw <= 4) launch_fused<SRC, 4>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
-    else if (tpw <= 6) launch_fused<SRC, 6>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
-    else if (tpw <= 8) launch_fused<SRC, (T < 8 ? T : 8)>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
-    else if (tpw <= 12) launch_fused<SRC, (T < 12 ? T : 12)>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
-    else launch_fused<SRC, T>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
+    launch_resident<SRC, kMaxTpw<SRC>>(gm, grid, tpw, src_scale, ws, out, flags, num_cus, stream);
 }
 
 template <int SRC>
