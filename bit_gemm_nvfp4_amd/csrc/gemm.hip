@@ -21,7 +21,11 @@
 //   - NVFP4 operands (W, and A in the W4A4 form) are loaded two steps ahead into registers, one
 //     code dword (8 elements) and its scale byte per unit, spread evenly over all threads; the
 //     units of step s + 1 are expanded exactly and written to the other LDS stage between the
-//     matrix instructions of step s.  One barrier ends each step.
+//     matrix instructions of step s.  One barrier per step.
+//   - Wave tiles up to 64 x 96 keep all four 16-deep fragment slices of a step in registers and
+//     place the barrier after the second slice: the expansion goes between the matrix
+//     instructions of slices 0 and 1, and the first two slices of the next step are read under
+//     those of slices 2 and 3, so no fragment read waits at the start of a step.
 //   - The block scale byte is decoded by the hardware FP8 conversion (OCP e4m3).
 //   - W4A4 expands both operands to f16 instead of bf16: e2m1 x s lies in [2^-10, 2688] with at
 //     most 6 significant bits, so it is exact in f16 as well, and the f16 form needs half the
@@ -484,61 +488,113 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
 #pragma unroll
             for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
 
-    // prologue: steps 0 and 1 in flight, step 0 expanded
+    typedef typename std::conditional<A_Q, f16x8, bf16x8>::type frag_t;
+    auto mfma = [&](const frag_t &a, const frag_t &b, f32x16 &c) {
+        if constexpr (A_Q) c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+        else c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    };
+    // Register-resident slices: all four 16-deep fragment slices of a step in registers, when they
+    // fit beside the accumulators (wave tiles up to 64 x 96).
+    constexpr bool RESIDENT = TM * TN <= 6;
+    frag_t af[RESIDENT ? 4 : 2][TM], bfr[RESIDENT ? 4 : 2][TN];
+    auto read_frags = [&](int slot, int kk, int sa, int sw) {
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+            af[slot][i] = *reinterpret_cast<const frag_t *>(smem + sa * A_STAGE + offA[kk] + i * 32 * ROWB);
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+            bfr[slot][j] = *reinterpret_cast<const frag_t *>(smem + sw * W_STAGE + offB[kk] + j * 32 * ROWB);
+    };
+    auto mfmas = [&](int slot) {
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int j = 0; j < TN; j++) mfma(af[slot][i], bfr[slot][j], acc[i][j]);
+    };
+
+    // prologue: steps 0 and 1 in flight, step 0 expanded (and, register-resident, slices 0 and 1
+    // of step 0 read)
     issue(0, 0, 0);
     issue(1, 1, 1);
 #pragma unroll
     for (int u = 0; u < QD; u++) expand_unit(u, 0, 0, 0);
     end_step();
+    if constexpr (RESIDENT) {
+        read_frags(0, 0, 0, 0);
+        read_frags(1, 1, 0, 0);
+    }
 
-    // Step s (S = s mod 6, so stage indices are constants): issue the loads of step s + 2, then the
-    // four 16-deep slices of matrix work from stages s, with the expansion of step s + 1 spread
-    // between them.
+    // Step s (S = s mod 6, so stage indices are constants).
+    // Register-resident: issue the loads of step s + 2 and read slices 2 and 3 of step s; the
+    // matrix work of slices 0 and 1 with the expansion of step s + 1 placed between the
+    // instructions; the barrier (stage s + 1 complete); the matrix work of slices 2 and 3 with
+    // slices 0 and 1 of step s + 1 read between the instructions.  Every fragment read is thus
+    // issued at least six matrix instructions before its use, across the barrier too.
+    // Otherwise: issue the loads of step s + 2, then the four slices of step s with double-buffered
+    // fragments and the expansion of step s + 1 spread between them; the barrier ends the step.
     auto step = [&](auto Sc, int s) {
         constexpr int S = decltype(Sc)::value;
         constexpr int SA = A_Q ? S % 2 : S % 3;
         constexpr int SW = S % 2;
         constexpr int SN = (S + 1) % 2;
         issue(s + 2, (S + 2) % 3, S % 2);
-        typedef typename std::conditional<A_Q, f16x8, bf16x8>::type frag_t;
-        frag_t af[2][TM], bfr[2][TN];
-        auto load_frags = [&](int kk, int b) {
+        if constexpr (RESIDENT) {
+            constexpr int SAN = A_Q ? (S + 1) % 2 : (S + 1) % 3;
+            read_frags(2, 2, SA, SW);
+            read_frags(3, 3, SA, SW);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < TM; i++)
-                af[b][i] = *reinterpret_cast<const frag_t *>(smem + SA * A_STAGE + offA[kk] + i * 32 * ROWB);
+            for (int kk = 0; kk < 2; kk++) {
+                mfmas(kk);
 #pragma unroll
-            for (int j = 0; j < TN; j++)
-                bfr[b][j] = *reinterpret_cast<const frag_t *>(smem + SW * W_STAGE + offB[kk] + j * 32 * ROWB);
-        };
-        load_frags(0, 0);
+                for (int u = 0; u < QD; u++)
+                    if (u * 2 / QD == kk) expand_unit(u, SN, SN, SN);
+                // matrix instructions with up to five VALU between them, then the LDS writes
 #pragma unroll
-        for (int kk = 0; kk < 4; kk++) {
-            if (kk < 3) load_frags(kk + 1, (kk + 1) & 1);
-#pragma unroll
-            for (int i = 0; i < TM; i++)
-#pragma unroll
-                for (int j = 0; j < TN; j++) {
-                    if constexpr (A_Q)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[kk & 1][i], bfr[kk & 1][j], acc[i][j], 0, 0, 0);
-                    else
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][i], bfr[kk & 1][j], acc[i][j], 0, 0, 0);
+                for (int q = 0; q < TM * TN - 1; q++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
                 }
+                __builtin_amdgcn_sched_group_barrier(0x200, (QD + 1) / 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+            end_step();
 #pragma unroll
-            for (int u = 0; u < QD; u++)
-                if (u * 4 / QD == kk) expand_unit(u, SN, SN, SN);
-            // order within the slice: next fragments' reads, then matrix instructions with the
-            // expansion arithmetic placed between them, then the LDS writes
-            if (kk < 3) __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - 3, 0);
+            for (int kk = 2; kk < 4; kk++) {
+                mfmas(kk);
+                read_frags(kk - 2, kk - 2, SAN, SN);
+                // one fragment read after each of the first matrix instructions
+#pragma unroll
+                for (int q = 0; q < TM + TN; q++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - TM - TN, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            read_frags(0, 0, SA, SW);
+#pragma unroll
+            for (int kk = 0; kk < 4; kk++) {
+                if (kk < 3) read_frags((kk + 1) & 1, kk + 1, SA, SW);
+                mfmas(kk & 1);
+#pragma unroll
+                for (int u = 0; u < QD; u++)
+                    if (u * 4 / QD == kk) expand_unit(u, SN, SN, SN);
+                // order within the slice: next fragments' reads, then matrix instructions with the
+                // expansion arithmetic placed between them, then the LDS writes
+                if (kk < 3) __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - 3, 0);
+            }
+            end_step();
         }
-        end_step();
     };
 
     int s = 0;
@@ -555,8 +611,9 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
     if (s + 2 < nsteps) step(StepIdx<2>{}, s + 2);
     if (s + 3 < nsteps) step(StepIdx<3>{}, s + 3);
     if (s + 4 < nsteps) step(StepIdx<4>{}, s + 4);
-    // no direct-to-LDS load may still be writing when the workgroup's LDS is released
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+    // no direct-to-LDS load may still be writing (and no fragment read still pending) when the
+    // workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
     // ---- epilogue: multiply by the global scale(s), store fp32; a K slice of a split product
     // (w_g == nullptr) stores its raw partial sums into its own [M x ldc] plane of C instead ----
