@@ -175,6 +175,33 @@ def test_quantize_attention_weight_full(nv):
     assert np.array_equal(f32.view(np.uint32), oracle.dequantize(ref, "f32").view(np.uint32))
 
 
+# Tall tensors whose tile counts (64 blocks per tile, 3 tiles per 3072-wide row) give the
+# single-pass kernel 2, 4, 5, 8 and 12 resident tiles per wave at four workgroups per CU on a
+# 256-CU part, the largest residency for fp32, bf16, f16 and e4m3 sources respectively.
+@pytest.mark.parametrize("dtype,rows", [("f32", 2000), ("f32", 5000), ("bf16", 6000), ("f16", 10000),
+                                        ("e4m3", 15000)])
+def test_quantize_resident_tiles_per_wave(nv, dtype, rows):
+    cols = 3072
+    _note(f"quantize {dtype} {rows}x{cols}")
+    g = synth.rng(rows + 31)
+    x = (g.standard_t(5, size=(rows, cols)) * 0.02).astype(np.float32)
+    x[g.random((rows, cols)) < 0.01] = 0.0
+    if dtype == "f32":
+        xd, ref = to_dev_f32(x), oracle.quantize(x)[0]
+        _assert_q_equal(_quant(nv, xd), ref, f"{dtype} {rows}")
+    elif dtype == "bf16":
+        b = synth.bf16_bits(x)
+        _assert_q_equal(_quant(nv, to_dev_bf16(b)), oracle.quantize(b, oracle.BF16)[0], f"{dtype} {rows}")
+    elif dtype == "f16":
+        h = x.astype(np.float16).view(np.uint16)
+        _assert_q_equal(_quant(nv, to_dev_f16(h)), oracle.quantize(h, oracle.F16)[0], f"{dtype} {rows}")
+    else:
+        b, sc = synth.fp8_tensorwise(x)
+        ref, _ = oracle.quantize(b, oracle.E4M3, float(sc))
+        q = _quant(nv, to_dev_u8(b), src_scale=torch.tensor([sc], dtype=torch.float32, device=DEV))
+        _assert_q_equal(q, ref, f"{dtype} {rows}")
+
+
 # ------------------------------------------------------------------------------------------------
 # dequantize
 # ------------------------------------------------------------------------------------------------
