@@ -15,7 +15,8 @@ Inputs are resident in HBM before timing; the step rotates over several input se
 size exceeds the 256 MB Infinity Cache, so repeated steps do not hit in cache.  Each operation is
 bracketed by events on the stream it runs on; the dominant kernel's roofline uses those times.
 
-Prints one JSON line.  Flags: --gpus (1 only), --steps, --warmup, --no-cpu-baseline.
+Prints one JSON line.  Flags: --gpus (1 only), --steps, --warmup, --no-cpu-baseline, --peaks (adds the
+achievable peaks measured with library calls: a 1 GiB device copy and a bf16 matmul of the GEMM's shape).
 """
 import argparse
 import json
@@ -40,6 +41,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--peaks", action="store_true",
+                    help="also measure achievable peaks: HBM by a 1 GiB device-to-device copy, matrix cores by "
+                         "a bf16 torch.matmul of the attention-projection shape")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after the timed steps, copy a buffer of this many MiB three times (a plain copy of "
                          "known size, for scaling HBM byte counters)")
@@ -180,6 +184,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w_np)
+    if args.peaks:
+        out["achievable_peaks"] = achievable_peaks(dev)
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -211,6 +217,42 @@ def measured_traffic(op):
     if h.hexdigest() != fields.get(f"{op}.source_sha256"):
         return None
     return float(fields[f"{op}.bytes"])
+
+
+def achievable_peaks(dev):
+    """Achievable peaks on this GPU from library calls (no code of this repository): HBM read+write
+    rate of a 1 GiB device-to-device copy, and the bf16 matmul rate of torch (hipBLASLt) at the
+    attention-projection shape.  Event-timed medians over 20 runs after 3 warmups."""
+    import numpy as np
+    import torch
+
+    def timed(fn, n=20):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    copy_ms = timed(lambda: dst.copy_(src))
+    del src, dst
+    # the GEMM's own layout: A [M x K] times W [N x K] transposed (a 2-D product, no batching)
+    a = torch.randn(M_TOK, K_IN, device=dev, dtype=torch.bfloat16)
+    w = torch.randn(N_OUT, K_IN, device=dev, dtype=torch.bfloat16)
+    mm_ms = timed(lambda: torch.matmul(a, w.T))
+    return {"hbm_copy_GBps": round(2 * n / (copy_ms * 1e-3) / 1e9, 1), "hbm_copy_bytes": 2 * n,
+            "bf16_matmul_TFLOPs": round(2.0 * M_TOK * N_OUT * K_IN / (mm_ms * 1e-3) / 1e12, 1),
+            "bf16_matmul_shape": [M_TOK, N_OUT, K_IN]}
 
 
 def cpu_baseline(w_np):
