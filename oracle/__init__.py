@@ -65,6 +65,9 @@ def _load():
     lib.ref_e2m1_index_array.argtypes = [P, I64, P]
     lib.ref_e4m3_encode_array.argtypes = [P, I64, P]
     lib.ref_f32_to_bf16_array.argtypes = [P, I64, P]
+    lib.ref_fp8_scale.argtypes, lib.ref_fp8_scale.restype = [ctypes.c_float], ctypes.c_float
+    lib.ref_fp8_byte.argtypes, lib.ref_fp8_byte.restype = [ctypes.c_float, ctypes.c_float], I
+    lib.ref_quantize_fp8_f32.argtypes, lib.ref_quantize_fp8_f32.restype = [P, I64, I64, P, P, P], I
     _lib = lib
     return lib
 
@@ -168,6 +171,36 @@ def quantize(x: np.ndarray, dtype: int = F32, src_scale: float | None = None,
     return QTensor(codes, scales, g[0]), int(flags)
 
 
+def fp8_scale(amax: float) -> np.float32:
+    return np.float32(_load().ref_fp8_scale(float(amax)))
+
+
+def fp8_byte(v: float, scale: float) -> int:
+    return _load().ref_fp8_byte(float(v), float(scale))
+
+
+def quantize_fp8(x: np.ndarray, dtype: int = F32, src_scale: float | None = None,
+                 amax: float | None = None) -> tuple[np.ndarray, np.float32, int]:
+    """FP8 E4M3 tensorwise quantization ("Qwen3-VL-8B-Instruct-heretic-NVFP4", "Quantization
+    Details" and "Runtime / hardware"): scale = fl(amax / 448) (1 when amax = 0), byte = sign |
+    nearest E4M3 (ties to even, saturating) of fl(|v| / scale).  Returns (bytes [rows, cols] uint8,
+    scale, flags)."""
+    v = widen(x, dtype, src_scale)
+    rows, cols = v.shape
+    out = np.zeros((rows, cols), dtype=np.uint8)
+    sc = np.zeros(1, dtype=np.float32)
+    a = np.array([amax], dtype=np.float32) if amax is not None else None
+    flags = _load().ref_quantize_fp8_f32(_ptr(v), rows, cols, _ptr(a) if a is not None else None, _ptr(out),
+                                         _ptr(sc))
+    return out, sc[0], int(flags)
+
+
+def fp8_values(b: np.ndarray, scale: float) -> np.ndarray:
+    """Exact values e4m3(b) * scale of FP8 bytes, in float64."""
+    lut = np.array([_load().ref_e4m3_value(i & 0x7F) * (-1.0 if i & 0x80 else 1.0) for i in range(256)])
+    return lut[np.asarray(b, dtype=np.uint8)] * float(np.float32(scale))
+
+
 def dequantize(q: QTensor, out: str = "f32") -> np.ndarray:
     """Expand NVFP4 to 'f32', 'bf16' (uint16 bit patterns) or 'f64' (exact values)."""
     rows, cols = q.shape
@@ -205,6 +238,13 @@ def gemm_w4a16(a_bits: np.ndarray, w: QTensor) -> np.ndarray:
 def gemm_w4a4(a: QTensor, w: QTensor) -> np.ndarray:
     """Reference for the W4A4 GEMM: both operands expanded exactly from NVFP4."""
     return gemm_f64(dequantize(a, "f64"), dequantize(w, "f64"))
+
+
+def gemm_w4a8(a_fp8: np.ndarray, a_scale: float, w: QTensor) -> np.ndarray:
+    """Reference for the GEMM with FP8 activations ("Qwen3-VL-8B-Instruct-heretic-NVFP4", "Runtime /
+    hardware": FP4 weight times dynamically quantized FP8 activation): both operands expanded
+    exactly, contraction in float64."""
+    return gemm_f64(fp8_values(a_fp8, a_scale), dequantize(w, "f64"))
 
 
 def gemm_error(c: np.ndarray, cref: np.ndarray) -> float:

@@ -37,6 +37,11 @@
  *   R5  FP8 source: v = fl(e4m3(b) * src_scale), a missing scale meaning 1.0.
  *   R6  expansion: w = fl(e2m1 * s * g) with one rounding (e2m1 * s is exact).
  *   R7  percentile: nearest rank, k = clamp(ceil(p * n / 100), 1, n), over |x| per channel.
+ *   R8  FP8 tensorwise ([VL] "Quantization Details": float8_e4m3fn, tensorwise, round to
+ *       nearest; "Runtime / hardware": FP4 weights against dynamically quantized FP8
+ *       activations): scale = fl(amax / 448), 448 the largest E4M3, and 1 when amax = 0;
+ *       byte = sign bit of v | E4M3 nearest (ties to even, saturating at 448) of fl(|v| / scale).
+ *       Dequantized value = e4m3(byte) x scale.
  *
  * Arithmetic precision: every fp32 step above is carried out in IEEE binary32 (the pages fix
  * an FP32 global scale, so the decisions that pick codes are taken in fp32).  Grid rounding is
@@ -202,6 +207,35 @@ int ref_quantize_f32(const float *v, int64_t rows, int64_t cols, const float *am
             }
         }
     }
+    return flags;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* FP8 tensorwise quantization of fp32 values [rows x cols] (dense), R8.  Returns flags (bit0 =  */
+/* a non-finite input was seen).  amax_in: static amax (values beyond it saturate), or NULL.    */
+/* ------------------------------------------------------------------------------------------ */
+float ref_fp8_scale(float amax) { return amax == 0.0f ? 1.0f : amax / 448.0f; }
+
+int ref_fp8_byte(float v, float scale) {
+    int sign = signbit(v) ? 0x80 : 0;
+    float t = fabsf(v) / scale;
+    return sign | ref_e4m3_encode(t);
+}
+
+int ref_quantize_fp8_f32(const float *v, int64_t rows, int64_t cols, const float *amax_in, uint8_t *out,
+                         float *scale_out) {
+    int flags = 0;
+    int64_t n = rows * cols;
+    float amax = 0.0f;
+    for (int64_t i = 0; i < n; i++) {
+        if (!isfinite(v[i])) flags |= 1;
+        float a = fabsf(v[i]);
+        if (a > amax) amax = a;
+    }
+    if (amax_in) amax = *amax_in;
+    float scale = ref_fp8_scale(amax);
+    *scale_out = scale;
+    for (int64_t i = 0; i < n; i++) out[i] = (uint8_t)ref_fp8_byte(v[i], scale);
     return flags;
 }
 

@@ -396,3 +396,86 @@ def test_gemm_against_unquantized_tracks_weight_error():
     cerr = np.linalg.norm(cq - cu) / np.linalg.norm(cu)
     assert 0.07 < werr < 0.12
     assert 0.85 * werr < cerr < 1.15 * werr
+
+
+# ------------------------------------------------------------------------------------------------
+# FP8 tensorwise ("Qwen3-VL-8B-Instruct-heretic-NVFP4", "Quantization Details": float8_e4m3fn,
+# tensorwise, round to nearest; "Runtime / hardware": FP4 weight x dynamically quantized FP8
+# activation)
+# ------------------------------------------------------------------------------------------------
+def test_fp8_bytes_against_torch_division_and_cast():
+    # torch's float32 division and its float8_e4m3fn cast are an independent implementation of
+    # byte = nearest-even E4M3 of fl(v / scale); probes sit on grid points, midpoints and their
+    # neighbours after scaling, for several scales, both signs
+    vals = np.array([oracle.e4m3_value(i) for i in range(0x7F)], dtype=np.float64)
+    mids = (vals[1:] + vals[:-1]) / 2
+    rnd = np.random.default_rng(41)
+    for scale in [np.float32(1.0), np.float32(0.02 * 4.5 / 448), np.float32(3.7e-3), np.float32(1.2345e2)]:
+        q = []
+        for m in np.concatenate([vals, mids]):
+            m32 = np.float32(m * float(scale))
+            q += [m32, np.nextafter(m32, np.float32(0)), np.nextafter(m32, np.float32(1e30))]
+        q = np.array(q, dtype=np.float32)
+        q = np.concatenate([q, (float(scale) * 2.0 ** rnd.uniform(-12, 8.8, 50000)).astype(np.float32)])
+        q = np.concatenate([q, -q, np.array([0.0, -0.0], dtype=np.float32)])
+        tq = torch.from_numpy(q) / torch.tensor(scale, dtype=torch.float32)
+        keep = (tq.abs() < 464).numpy()
+        ref = tq[torch.from_numpy(keep)].to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        got = np.array([oracle.fp8_byte(float(v), float(scale)) for v in q[keep]], dtype=np.uint8)
+        assert np.array_equal(got, ref), f"scale {scale}"
+
+
+def test_fp8_scale_and_largest_element():
+    rnd = np.random.default_rng(42)
+    for shape in [(7, 48), (64, 256)]:
+        x = (rnd.standard_t(4, size=shape) * 0.02).astype(np.float32)
+        b, sc, flags = oracle.quantize_fp8(x)
+        amax = np.float32(np.abs(x).max())
+        assert flags == 0 and sc == np.float32(amax / np.float32(448))
+        i = np.unravel_index(np.argmax(np.abs(x)), shape)
+        assert b[i] & 0x7F == 0x7E  # |amax| / fl(amax / 448) rounds to 448
+        assert (b[i] & 0x80 != 0) == bool(x[i] < 0)
+        assert np.all((b & 0x7F) != 0x7F)  # no NaN byte is produced
+
+
+def test_fp8_round_trip_and_error_bound():
+    rnd = np.random.default_rng(43)
+    x = (rnd.standard_normal((32, 512)) * 0.05).astype(np.float32)
+    b, sc, _ = oracle.quantize_fp8(x)
+    v = oracle.fp8_values(b, sc)
+    # requantizing the dequantized values with the same scale reproduces the bytes
+    b2 = np.array([[oracle.fp8_byte(float(np.float32(t)), float(sc)) for t in row] for row in v], dtype=np.uint8)
+    assert np.array_equal(b2, b)
+    # nearest rounding: within half a grid step (relative 2^-4) in the normal range, 2^-10 * scale below it
+    err = np.abs(v - x.astype(np.float64))
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * float(sc)) * (1 + 1e-6)
+    assert np.all(err <= bound)
+
+
+def test_fp8_zero_tensor_static_amax_and_flags():
+    b, sc, flags = oracle.quantize_fp8(np.zeros((2, 32), dtype=np.float32))
+    assert sc == 1.0 and not b.any() and flags == 0
+    x = np.array([[0.5, -4.0, 2.0, -0.0] * 8], dtype=np.float32)
+    b, sc, _ = oracle.quantize_fp8(x, amax=1.0)
+    assert sc == np.float32(1.0 / 448)
+    assert b[0, 1] == 0xFE and b[0, 2] == 0x7E and b[0, 3] == 0x80  # beyond the static amax: saturate
+    x[0, 5] = np.nan
+    assert oracle.quantize_fp8(x)[2] & 1
+
+
+def test_gemm_w4a8_one_hot_and_definition():
+    rnd = np.random.default_rng(44)
+    q, _ = oracle.quantize(rnd.standard_normal((24, 64)).astype(np.float32))
+    eye = np.zeros((64, 64), dtype=np.float32)
+    eye[np.arange(64), np.arange(64)] = 1.0
+    b, sc, _ = oracle.quantize_fp8(eye)
+    c = oracle.gemm_w4a8(b, sc, q)
+    assert np.array_equal(c, oracle.dequantize(q, "f64").T * (448.0 * float(sc)))
+    xa = rnd.standard_normal((3, 64)).astype(np.float32)
+    ba, sa, _ = oracle.quantize_fp8(xa)
+    c = oracle.gemm_w4a8(ba, sa, q)
+    a = oracle.fp8_values(ba, sa)
+    w = oracle.dequantize(q, "f64")
+    for m in range(3):
+        for n in range(0, 24, 5):
+            assert c[m, n] == pytest.approx(sum(a[m, k] * w[n, k] for k in range(64)), rel=1e-14, abs=1e-300)
