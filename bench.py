@@ -11,6 +11,9 @@ One step runs every operation of the path once, at the Qwen-Image attention-proj
   gemm_w4a4    C = A_hat . W_hat^T, NVFP4 activations
   gemv_w4a16   the first 2 rows of A against W (memory-bound form)
   percentile   per-channel p99.9 and max of |A|
+The FP8 side path is timed after the step, in a loop of its own over the same inputs ("next_ops"):
+  act_quantize_fp8  A bf16 -> FP8 E4M3 tensorwise (dynamic amax)
+  gemm_w4a8    C = A_fp8 . W_hat^T, FP8 activations
 Inputs are resident in HBM before timing; the step rotates over several input sets whose total
 size exceeds the 256 MB Infinity Cache, so repeated steps do not hit in cache.  Each operation is
 bracketed by events on the stream it runs on; the dominant kernel's roofline uses those times.
@@ -88,13 +91,17 @@ def main():
     qws = torch.empty(nv.workspace_size(nv.OP_QUANTIZE, 0, 0), dtype=torch.uint8, device=dev)
     qws2 = torch.empty_like(qws)
     qws3 = torch.empty_like(qws)
+    qws4 = torch.empty_like(qws)
+    a8 = nv.FP8Tensor.empty(M_TOK, K_IN, dev)
+    c8 = torch.empty((M_TOK, N_OUT), dtype=torch.float32, device=dev)
 
     ops = ["quantize", "requantize", "dequantize", "act_quantize", "gemm_w4a16", "gemm_w4a4", "gemv_w4a16",
            "percentile"]
+    next_ops = ["act_quantize_fp8", "gemm_w4a8"]
     # kernels each op launches (the roofline is reported for the longest single-kernel op); the
     # percentile at p99.9 over 4096 rows takes the one-pass top-M path (selection + merge)
     n_kernels = {"quantize": 1, "requantize": 1, "dequantize": 1, "act_quantize": 1, "gemm_w4a16": 1,
-                 "gemm_w4a4": 1, "gemv_w4a16": 1, "percentile": 2}
+                 "gemm_w4a4": 1, "gemv_w4a16": 1, "percentile": 2, "act_quantize_fp8": 1, "gemm_w4a8": 1}
 
     def step(i, events=None):
         w, a, w8 = sets[i % nsets]
@@ -117,6 +124,15 @@ def main():
         nv.amax_percentile(a, 99.9, per_channel=True)
         if e: e[8].record()
 
+    def step_next(i, events=None):
+        w, a, w8 = sets[i % nsets]
+        e = events
+        if e: e[0].record()
+        nv.quantize_fp8(a, out=a8, workspace=qws4)
+        if e: e[1].record()
+        nv.gemm(a8, qw, out=c8)
+        if e: e[2].record()
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -130,6 +146,17 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     op_ms = {op: float(np.mean([evs[s][j].elapsed_time(evs[s][j + 1]) for s in range(args.steps)]))
              for j, op in enumerate(ops)}
+    # the FP8 side path, in its own loop (the step above stays the NVFP4 path alone)
+    for i in range(args.warmup):
+        step_next(i)
+    torch.cuda.synchronize()
+    evn = [[torch.cuda.Event(enable_timing=True) for _ in range(len(next_ops) + 1)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(args.warmup + i)
+        step_next(args.warmup + i, evn[i])
+    torch.cuda.synchronize()
+    op_ms.update({op: float(np.mean([evn[s][j].elapsed_time(evn[s][j + 1]) for s in range(args.steps)]))
+                  for j, op in enumerate(next_ops)})
 
     nW, nA = N_OUT * K_IN, M_TOK * K_IN
     work = {  # algorithmic bytes (codec / memory-bound ops) or flops (GEMMs)
@@ -141,13 +168,16 @@ def main():
         "gemm_w4a4": ("TFLOP/s", 2.0 * M_TOK * N_OUT * K_IN, BF16_MFMA_PEAK_TFLOPS),
         "gemv_w4a16": ("GB/s", nW * 0.5625 + GEMV_M * K_IN * 2 + GEMV_M * N_OUT * 4, HBM_PEAK_GBS),
         "percentile": ("GB/s", nA * 2.0, HBM_PEAK_GBS),
+        "act_quantize_fp8": ("GB/s", nA * 3.0 + 4, HBM_PEAK_GBS),
+        "gemm_w4a8": ("TFLOP/s", 2.0 * M_TOK * N_OUT * K_IN, BF16_MFMA_PEAK_TFLOPS),
     }
-    op_report = {}
-    for op in ops:
+    op_report, next_report = {}, {}
+    for op in ops + next_ops:
         unit, amount, peak = work[op]
         rate = amount / (op_ms[op] * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
-        op_report[op] = {"ms": round(op_ms[op], 5), "rate": round(rate, 2), "unit": unit,
-                         "frac_of_peak": round(rate / peak, 4), "kernels": n_kernels[op]}
+        (op_report if op in ops else next_report)[op] = {
+            "ms": round(op_ms[op], 5), "rate": round(rate, 2), "unit": unit, "frac_of_peak": round(rate / peak, 4),
+            "kernels": n_kernels[op]}
 
     gemm_ms = op_ms["gemm_w4a16"]
     dom = max((o for o in ops if n_kernels[o] == 1), key=lambda o: op_ms[o])
@@ -180,6 +210,7 @@ def main():
         },
         "gemm_tflops": round(2.0 * M_TOK * N_OUT * K_IN / (gemm_ms * 1e-3) / 1e12, 2),
         "ops": op_report,
+        "next_ops": next_report,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

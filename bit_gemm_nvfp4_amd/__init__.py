@@ -29,8 +29,8 @@ NVFP4_F32, NVFP4_BF16, NVFP4_F16, NVFP4_E4M3 = 0, 1, 2, 3
 OP_QUANTIZE, OP_DEQUANTIZE, OP_GEMM, OP_PERCENTILE = 0, 1, 2, 3
 STATUS_NAMES = ["NVFP4_OK", "NVFP4_ERR_NULL", "NVFP4_ERR_SHAPE", "NVFP4_ERR_ALIGN", "NVFP4_ERR_DTYPE",
                 "NVFP4_ERR_WORKSPACE", "NVFP4_ERR_ARG", "NVFP4_ERR_DEVICE", "NVFP4_ERR_LAUNCH"]
-EXPORTED = ["nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm", "amax_percentile", "nvfp4_workspace_size",
-            "nvfp4_status_string"]
+EXPORTED = ["nvfp4_quantize", "nvfp4_quantize_fp8", "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_gemm_fp8a",
+            "amax_percentile", "nvfp4_workspace_size", "nvfp4_status_string"]
 
 
 class CTensor(ctypes.Structure):
@@ -43,6 +43,10 @@ _P, _I64, _I32, _SZ, _D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.
 _PT = ctypes.POINTER(CTensor)
 lib.nvfp4_quantize.argtypes = [_P, _I32, _I64, _P, _P, _PT, _P, _P, _SZ, _P]
 lib.nvfp4_quantize.restype = _I32
+lib.nvfp4_quantize_fp8.argtypes = [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]
+lib.nvfp4_quantize_fp8.restype = _I32
+lib.nvfp4_gemm_fp8a.argtypes = [_P, _P, _I64, _I64, _PT, _P, _I64, _P, _SZ, _P]
+lib.nvfp4_gemm_fp8a.restype = _I32
 lib.nvfp4_dequantize.argtypes = [_PT, _P, _I32, _I64, _P]
 lib.nvfp4_dequantize.restype = _I32
 lib.nvfp4_gemm.argtypes = [_P, _PT, _I64, _I64, _PT, _P, _I64, _P, _SZ, _P]
@@ -105,6 +109,23 @@ class NVFP4Tensor:
         return CTensor(self.codes.data_ptr(), self.scales.data_ptr(), self.global_scale.data_ptr(), r, c)
 
 
+@dataclass
+class FP8Tensor:
+    """FP8 E4M3 tensor with one tensor scale: data [rows, cols] uint8 (E4M3 bit patterns), scale [1]
+    fp32; element value = e4m3(byte) x scale."""
+    data: torch.Tensor
+    scale: torch.Tensor
+
+    @property
+    def shape(self):
+        return tuple(self.data.shape)
+
+    @staticmethod
+    def empty(rows: int, cols: int, device) -> "FP8Tensor":
+        return FP8Tensor(torch.empty((rows, cols), dtype=torch.uint8, device=device),
+                         torch.empty(1, dtype=torch.float32, device=device))
+
+
 def workspace_size(op: int, rows: int, cols: int, k: int = 0) -> int:
     return int(lib.nvfp4_workspace_size(op, rows, cols, k))
 
@@ -137,6 +158,24 @@ def quantize(x: torch.Tensor, amax: torch.Tensor | None = None, src_scale: torch
     return out
 
 
+def quantize_fp8(x: torch.Tensor, amax: torch.Tensor | None = None, src_scale: torch.Tensor | None = None,
+                 flags: torch.Tensor | None = None, out: FP8Tensor | None = None,
+                 workspace: torch.Tensor | None = None) -> FP8Tensor:
+    """FP8 E4M3 tensorwise quantization of a 2-D device tensor (fp32, bf16, fp16 or E4M3 bytes):
+    scale = amax / 448 (run-time amax, or the static `amax`), bytes = nearest E4M3 of x / scale."""
+    assert x.dim() == 2 and x.is_cuda
+    rows, cols = x.shape
+    if out is None:
+        out = FP8Tensor.empty(rows, cols, x.device)
+    if workspace is None and amax is None:
+        workspace = _workspace(workspace_size(OP_QUANTIZE, rows, cols), x.device)
+    st = lib.nvfp4_quantize_fp8(_ptr(x), _DT[x.dtype], rows, cols, x.stride(0) if rows > 0 else cols, _ptr(src_scale),
+                                _ptr(amax), _ptr(out.data), _ptr(out.scale), _ptr(flags), _ptr(workspace),
+                                0 if workspace is None else workspace.numel(), _stream(x.device))
+    _check(st, "nvfp4_quantize_fp8")
+    return out
+
+
 def dequantize(q: NVFP4Tensor, dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
     """Expand NVFP4 to bf16 or fp32: w = e2m1 x block scale x global scale."""
     rows, cols = q.shape
@@ -149,10 +188,22 @@ def dequantize(q: NVFP4Tensor, dtype: torch.dtype = torch.bfloat16, out: torch.T
     return out
 
 
-def gemm(a: torch.Tensor | NVFP4Tensor, w: NVFP4Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
-    """C [M, N] fp32 = A . W_hat^T.  `a` is a bf16 [M, K] tensor (W4A16) or an NVFP4Tensor (W4A4)."""
+def gemm(a: torch.Tensor | NVFP4Tensor | FP8Tensor, w: NVFP4Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """C [M, N] fp32 = A . W_hat^T.  `a` is a bf16 [M, K] tensor (W4A16), an NVFP4Tensor (W4A4) or an
+    FP8Tensor (FP8 activations)."""
     n, k = w.shape
     device = w.codes.device
+    if isinstance(a, FP8Tensor):
+        m = a.shape[0]
+        if out is None:
+            out = torch.empty((m, n), dtype=torch.float32, device=device)
+        ws_bytes = workspace_size(OP_GEMM, m, n, k)
+        ws = _workspace(ws_bytes, device)
+        wct = w.c()
+        st = lib.nvfp4_gemm_fp8a(_ptr(a.data), _ptr(a.scale), m, a.data.stride(0) if m > 0 else k, ctypes.byref(wct),
+                                 _ptr(out), out.stride(0) if m > 0 else n, _ptr(ws), ws_bytes, _stream(device))
+        _check(st, "nvfp4_gemm_fp8a")
+        return out
     if isinstance(a, NVFP4Tensor):
         m = a.shape[0]
         a_ct, a_ptr, lda = ctypes.byref(a.c()), None, k

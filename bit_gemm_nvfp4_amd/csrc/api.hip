@@ -141,6 +141,30 @@ nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype x_dtype, int64_t ld_x, co
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
 }
 
+nvfp4_status nvfp4_quantize_fp8(const void *x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                                const float *src_scale, const float *amax_in, uint8_t *out, float *out_scale,
+                                int32_t *flags, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    const int eb = elem_bytes(x_dtype);
+    if (eb == 0) return NVFP4_ERR_DTYPE;
+    if (!out_scale) return NVFP4_ERR_NULL;
+    if (rows < 0 || cols < 0 || (cols % 16) != 0) return NVFP4_ERR_SHAPE;
+    nvfp4_status st = check_matrix(x, rows, cols, ld_x, eb);
+    if (st != NVFP4_OK) return st;
+    st = check_matrix(out, rows, cols, cols, 1);
+    if (st != NVFP4_OK) return st;
+    if (src_scale && x_dtype != NVFP4_E4M3) return NVFP4_ERR_ARG;
+    if (!aligned4(out_scale) || (src_scale && !aligned4(src_scale)) || (amax_in && !aligned4(amax_in)) ||
+        (flags && !aligned4(flags)))
+        return NVFP4_ERR_ALIGN;
+    if (!amax_in && (!workspace || workspace_bytes < kQuantizeWsBytes)) return NVFP4_ERR_WORKSPACE;
+    if (workspace && !aligned16(workspace)) return NVFP4_ERR_ALIGN;
+    const int cus = current_device_cus();
+    if (cus == 0) return NVFP4_ERR_DEVICE;
+    hipError_t e = launch_quantize_fp8(x, x_dtype, ld_x, rows, cols, src_scale, amax_in, out, out_scale, flags,
+                                       workspace, cus, stream);
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+}
+
 nvfp4_status nvfp4_dequantize(const nvfp4_tensor *in, void *out, nvfp4_dtype out_dtype, int64_t ld_out,
                               hipStream_t stream) {
     nvfp4_status st = check_qtensor(in);
@@ -177,6 +201,28 @@ nvfp4_status nvfp4_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, 
     if (cus == 0) return NVFP4_ERR_DEVICE;
     hipError_t e = (K == 0) ? launch_fill_zero_f32(c, M, N, ldc, stream)
                             : launch_gemm(a_bf16, a_q, M, lda, w, c, ldc, workspace, workspace_bytes, cus, stream);
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+}
+
+nvfp4_status nvfp4_gemm_fp8a(const uint8_t *a_fp8, const float *a_scale, int64_t M, int64_t lda,
+                             const nvfp4_tensor *w, float *c, int64_t ldc, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+    if (!a_scale) return NVFP4_ERR_NULL;
+    nvfp4_status st = check_qtensor(w);
+    if (st != NVFP4_OK) return st;
+    const int64_t N = w->rows, K = w->cols;
+    if (M < 0) return NVFP4_ERR_SHAPE;
+    st = check_matrix(a_fp8, M, K, lda, 1);
+    if (st != NVFP4_OK) return st;
+    st = check_matrix(c, M, N, ldc, 4, 4);
+    if (st != NVFP4_OK) return st;
+    if (!aligned4(a_scale)) return NVFP4_ERR_ALIGN;
+    if (workspace && !aligned16(workspace)) return NVFP4_ERR_ALIGN;
+    const int cus = current_device_cus();
+    if (cus == 0) return NVFP4_ERR_DEVICE;
+    hipError_t e = (K == 0) ? launch_fill_zero_f32(c, M, N, ldc, stream)
+                            : launch_gemm_fp8(a_fp8, a_scale, M, lda, w, c, ldc, workspace, workspace_bytes, cus,
+                                              stream);
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
 }
 

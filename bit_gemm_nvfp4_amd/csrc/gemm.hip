@@ -74,6 +74,30 @@ __device__ __forceinline__ u32x4 expand8_f16(uint32_t w, f16x2 s2) {
     return o;
 }
 
+// Activation operand of the tiled kernels.
+constexpr int kAmBf16 = 0;   // bf16 rows (W4A16)
+constexpr int kAmNvfp4 = 1;  // NVFP4 tensor (W4A4)
+constexpr int kAmFp8 = 2;    // E4M3 bytes with one tensor scale (FP8 activations)
+
+// Expand 8 E4M3 bytes (two dwords, element i in byte i) into 8 exact f16 values: e4m3 values have
+// at most 4 significant bits and lie in [2^-9, 448], inside f16's range.
+__device__ __forceinline__ u32x4 expand8_fp8_f16(u32x2 b) {
+    u32x4 o;
+    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b[0], 1.0f, false));
+    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b[0], 1.0f, true));
+    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b[1], 1.0f, false));
+    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b[1], 1.0f, true));
+    return o;
+}
+
+// The same 8 E4M3 values as exact bf16 (the high halves of their exact fp32 values).
+__device__ __forceinline__ u32x4 expand8_fp8_bf16(u32x2 b) {
+    const f32x2 f0 = __builtin_amdgcn_cvt_pk_f32_fp8(b[0], false), f1 = __builtin_amdgcn_cvt_pk_f32_fp8(b[0], true);
+    const f32x2 f2 = __builtin_amdgcn_cvt_pk_f32_fp8(b[1], false), f3 = __builtin_amdgcn_cvt_pk_f32_fp8(b[1], true);
+    return u32x4{pack_bf16_exact(f0[0], f0[1]), pack_bf16_exact(f1[0], f1[1]), pack_bf16_exact(f2[0], f2[1]),
+                 pack_bf16_exact(f3[0], f3[1])};
+}
+
 // Raw global data of one 32-element NVFP4 chunk (two blocks): 16 code bytes and 2 scale bytes.
 struct QChunk {
     u32x4 codes;
@@ -128,7 +152,7 @@ __device__ __forceinline__ void tile_coords(int id, int tiles_m, int tiles_n, in
     tn = r / gm;
 }
 
-template <int BM, int BN, int WM, int WN, bool A_Q>
+template <int BM, int BN, int WM, int WN, int AM>
 __global__ __launch_bounds__(64 * WM *WN) void k_gemm_tile(const __bf16 *__restrict__ A, int64_t lda,
                                                           const uint8_t *__restrict__ a_codes,
                                                           const uint8_t *__restrict__ a_scales,
@@ -137,6 +161,7 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_tile(const __bf16 *__restr
                                                           const uint8_t *__restrict__ w_scales,
                                                           const float *__restrict__ w_g, float *__restrict__ C,
                                                           int64_t ldc, int64_t M, int64_t N, int64_t K) {
+    constexpr bool A_Q = AM == kAmNvfp4, A_F8 = AM == kAmFp8;
     constexpr int NT = 64 * WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
     constexpr int TM = WTM / 32, TN = WTN / 32;   // 32x32 MFMA tiles per wave
@@ -164,14 +189,15 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_tile(const __bf16 *__restr
 
     // ---- register staging of one K step (two sets: loads run two steps ahead) ----
     struct Staging {
-        u32x4 a[A_Q ? 1 : A_BF_PASSES];
+        u32x4 a[AM == kAmBf16 ? A_BF_PASSES : 1];  // 8 bf16 values per pass
+        u32x2 a8[A_F8 ? A_BF_PASSES : 1];          // 8 E4M3 bytes per pass
         QChunk aq[A_Q ? A_Q_PASSES : 1];
         QChunk w[W_PASSES];
     };
     Staging st0, st1;
 
     auto load_step = [&](int64_t k0, Staging &st) {
-        if constexpr (!A_Q) {
+        if constexpr (AM == kAmBf16) {
 #pragma unroll
             for (int p = 0; p < A_BF_PASSES; p++) {
                 const int idx = p * NT + tid;
@@ -181,6 +207,18 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_tile(const __bf16 *__restr
                     st.a[p] = *reinterpret_cast<const u32x4 *>(A + gr * lda + gk);
                 } else {
                     st.a[p] = u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+        } else if constexpr (A_F8) {
+#pragma unroll
+            for (int p = 0; p < A_BF_PASSES; p++) {
+                const int idx = p * NT + tid;
+                const int r = idx / (kBK / 8), c8 = idx % (kBK / 8);
+                const int64_t gr = m0 + r, gk = k0 + c8 * 8;
+                if (gr < M && gk < K) {
+                    st.a8[p] = *reinterpret_cast<const u32x2 *>(a_codes + gr * lda + gk);
+                } else {
+                    st.a8[p] = u32x2{0u, 0u};
                 }
             }
         } else {
@@ -225,10 +263,14 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_tile(const __bf16 *__restr
     };
     auto store_unit = [&](int u, __bf16 *As, __bf16 *Bs, const Staging &st) {
         if (u < A_UNITS) {
-            if constexpr (!A_Q) {
+            if constexpr (AM == kAmBf16) {
                 const int idx = u * NT + tid;
                 const int r = idx / (kBK / 8), c8 = idx % (kBK / 8);
                 *reinterpret_cast<u32x4 *>(&As[r * kLdsRow + c8 * 8]) = st.a[u];
+            } else if constexpr (A_F8) {
+                const int idx = u * NT + tid;
+                const int r = idx / (kBK / 8), c8 = idx % (kBK / 8);
+                *reinterpret_cast<u32x4 *>(&As[r * kLdsRow + c8 * 8]) = expand8_fp8_bf16(st.a8[u]);
             } else {
                 const int p = u / 4, q = u % 4;
                 const int idx = p * NT + tid;
@@ -314,7 +356,7 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_tile(const __bf16 *__restr
 
     // ---- epilogue: multiply by the global scale(s), store fp32 ----
     const float gw = *w_g;
-    const float ga = A_Q ? *a_g : 1.0f;
+    const float ga = AM != kAmBf16 ? *a_g : 1.0f;
 #pragma unroll
     for (int i = 0; i < TM; i++) {
 #pragma unroll
@@ -325,7 +367,7 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_tile(const __bf16 *__restr
                 const int64_t row = m0 + wm * WTM + i * 32 + 8 * (e / 4) + 4 * (lane / 32) + (e % 4);
                 if (row < M && col < N) {
                     float v = acc[i][j][e];
-                    if (A_Q) v = v * ga;
+                    if (AM != kAmBf16) v = v * ga;
                     C[row * ldc + col] = v * gw;
                 }
             }
@@ -349,7 +391,7 @@ __device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, void *ld
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
 }
 
-template <int BM, int BN, int WM, int WN, bool A_Q>
+template <int BM, int BN, int WM, int WN, int AM>
 __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restrict__ A, int64_t lda,
                                                           const uint8_t *__restrict__ a_codes,
                                                           const uint8_t *__restrict__ a_scales,
@@ -359,21 +401,26 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
                                                           const float *__restrict__ w_g, float *__restrict__ C,
                                                           int64_t ldc, int64_t M, int64_t N, int64_t K,
                                                           int slice_steps) {
+    // A_X: activations expanded from registers into LDS as f16 (NVFP4 codes, or E4M3 bytes), with W
+    // expanded to f16 too; otherwise bf16 activations are copied straight into LDS.
+    constexpr bool A_Q = AM == kAmNvfp4, A_F8 = AM == kAmFp8, A_X = AM != kAmBf16;
     constexpr int NT = 64 * WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;    // wave tile
     constexpr int TM = WTM / 32, TN = WTN / 32;    // 32x32 MFMA tiles per wave
     constexpr int ROWB = kBK * 2;                  // LDS row: 64 16-bit values, no padding
     constexpr int A_STAGE = BM * ROWB, W_STAGE = BN * ROWB;
-    constexpr int NA = A_Q ? 2 : 3;                // A stages (three for the two-step-ahead DMA)
+    constexpr int NA = A_X ? 2 : 3;                // A stages (three for the two-step-ahead DMA)
     constexpr int W_OFF = NA * A_STAGE;
     constexpr int LDS_BYTES = W_OFF + 2 * W_STAGE;
     constexpr int WD = BN * 8 / NT;                // W code dwords per thread per step
-    constexpr int AD = A_Q ? BM * 8 / NT : 0;      // A code dwords per thread per step (W4A4)
+    constexpr int AD = A_X ? BM * 8 / NT : 0;      // A units (8 elements each) per thread per step
     constexpr int QD = AD + WD;                    // expansion units per thread per step
-    constexpr int A_DMA = A_Q ? 0 : BM / 8 / (WM * WN);  // 1 KiB direct-to-LDS loads per wave per step
-    constexpr int VM_STEP = A_DMA + 2 * QD;        // vector-memory instructions issued per step
+    constexpr int A_DMA = A_X ? 0 : BM / 8 / (WM * WN);  // 1 KiB direct-to-LDS loads per wave per step
+    // vector-memory instructions issued per step: an NVFP4 unit loads a code dword and a scale byte,
+    // an E4M3 unit one 8-byte load
+    constexpr int VM_STEP = A_DMA + 2 * WD + (A_F8 ? AD : 2 * AD);
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-    static_assert(BN * 8 % NT == 0 && BM * 8 % NT == 0 && (A_Q || BM / 8 % (WM * WN) == 0), "even split");
+    static_assert(BN * 8 % NT == 0 && BM * 8 % NT == 0 && (A_X || BM / 8 % (WM * WN) == 0), "even split");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
     static_assert(VM_STEP < 64, "vmcnt range");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
@@ -397,24 +444,26 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
     __amdgpu_buffer_rsrc_t ra = make_rsrc(A, 0);
     __amdgpu_buffer_rsrc_t rc[2], rs[2];  // NVFP4 codes / scales: [0] A (W4A4), [1] W
     rc[0] = rs[0] = make_rsrc(a_codes, 0);
-    if constexpr (!A_Q) {
+    if constexpr (AM == kAmBf16) {
         ra = make_rsrc(A + m0 * lda, ((mrows - 1) * lda + K) * 2);
-    } else {
+    } else if constexpr (A_Q) {
         rc[0] = make_rsrc(a_codes + m0 * (K / 2), mrows * (K / 2));
         rs[0] = make_rsrc(a_scales + m0 * (K / 16), mrows * (K / 16));
+    } else {
+        rc[0] = make_rsrc(a_codes + m0 * lda, (mrows - 1) * lda + K);  // E4M3 bytes, row stride lda
     }
     rc[1] = make_rsrc(w_codes + n0 * (K / 2), nrows * (K / 2));
     rs[1] = make_rsrc(w_scales + n0 * (K / 16), nrows * (K / 16));
 
-    // Expansion unit u of this thread: code dword d = tid + NT * j of the step's tile (row d / 8,
-    // dword d % 8), j = u for A (u < AD), u - AD for W.  LDS rows hold 16-byte chunks at chunk
-    // index (chunk ^ row % 8).
+    // Expansion unit u of this thread: 8-element chunk d = tid + NT * j of the step's tile (row d / 8,
+    // chunk d % 8: one NVFP4 code dword, or 8 E4M3 bytes), j = u for A (u < AD), u - AD for W.  LDS
+    // rows hold 16-byte chunks at chunk index (chunk ^ row % 8).
     uint32_t q_coff[QD], q_soff[QD], q_lds[QD];
 #pragma unroll
     for (int u = 0; u < QD; u++) {
         const int j = u < AD ? u : u - AD;
         const uint32_t d = (uint32_t)(tid + NT * j), row = d >> 3, c = d & 7;
-        q_coff[u] = row * (uint32_t)(K / 2) + c * 4;
+        q_coff[u] = (A_F8 && u < AD) ? row * (uint32_t)lda + c * 8 : row * (uint32_t)(K / 2) + c * 4;
         q_soff[u] = row * (uint32_t)(K / 16) + (c >> 1);
         q_lds[u] = (u < AD ? 0u : (uint32_t)W_OFF) + row * ROWB + ((c ^ (row & 7)) << 4);
     }
@@ -437,6 +486,7 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
     }
 
     uint32_t qc[2][QD], qs[2][QD];  // two register sets of code dwords and scale bytes
+    u32x2 qa8[2][A_F8 ? AD : 1];     // E4M3 activations: two register sets of 8-byte chunks
 
     // K slice of this workgroup (split-K: blockIdx.y; otherwise the whole of K)
     const int total_steps = (int)(K / kBK);
@@ -446,7 +496,7 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
     // Loads past the last step repeat it: harmless, and the loop body stays free of branches.
     auto issue = [&](int s, int a_stage, int r) {
         const uint32_t k0 = (uint32_t)((kbase + (s < last ? s : last)) * kBK);
-        if constexpr (!A_Q) {
+        if constexpr (!A_X) {
 #pragma unroll
             for (int b = 0; b < A_DMA; b++)
                 load_to_lds16(ra, smem + a_stage * A_STAGE + (wid * A_DMA + b) * 1024,
@@ -454,6 +504,10 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
         }
 #pragma unroll
         for (int u = 0; u < QD; u++) {
+            if (A_F8 && u < AD) {
+                qa8[r][A_F8 ? u : 0] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rc[0], q_coff[u], k0, 0));
+                continue;
+            }
             const int o = u < AD ? 0 : 1;
             qc[r][u] = __builtin_amdgcn_raw_buffer_load_b32(rc[o], q_coff[u], k0 / 2, 0);
             qs[r][u] = __builtin_amdgcn_raw_buffer_load_b8(rs[o], q_soff[u], k0 / 16, 0);
@@ -461,9 +515,13 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
     };
     auto expand_unit = [&](int u, int r, int a_stage, int w_stage) {
         const uint32_t base = u < AD ? (uint32_t)(a_stage * A_STAGE) : (uint32_t)(w_stage * W_STAGE);
+        if (A_F8 && u < AD) {
+            *reinterpret_cast<u32x4 *>(smem + base + q_lds[u]) = expand8_fp8_f16(qa8[r][A_F8 ? u : 0]);
+            return;
+        }
         const float sc = __builtin_amdgcn_cvt_f32_fp8((int)qs[r][u], 0);
         u32x4 v;
-        if constexpr (A_Q) {
+        if constexpr (A_X) {
             const _Float16 sh = (_Float16)sc;
             v = expand8_f16(qc[r][u], f16x2{sh, sh});
         } else {
@@ -488,9 +546,9 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
 #pragma unroll
             for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
 
-    typedef typename std::conditional<A_Q, f16x8, bf16x8>::type frag_t;
+    typedef typename std::conditional<A_X, f16x8, bf16x8>::type frag_t;
     auto mfma = [&](const frag_t &a, const frag_t &b, f32x16 &c) {
-        if constexpr (A_Q) c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+        if constexpr (A_X) c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
         else c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     };
     // Register-resident slices: all four 16-deep fragment slices of a step in registers, when they
@@ -534,12 +592,12 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
     // fragments and the expansion of step s + 1 spread between them; the barrier ends the step.
     auto step = [&](auto Sc, int s) {
         constexpr int S = decltype(Sc)::value;
-        constexpr int SA = A_Q ? S % 2 : S % 3;
+        constexpr int SA = A_X ? S % 2 : S % 3;
         constexpr int SW = S % 2;
         constexpr int SN = (S + 1) % 2;
         issue(s + 2, (S + 2) % 3, S % 2);
         if constexpr (RESIDENT) {
-            constexpr int SAN = A_Q ? (S + 1) % 2 : (S + 1) % 3;
+            constexpr int SAN = A_X ? (S + 1) % 2 : (S + 1) % 3;
             read_frags(2, 2, SA, SW);
             read_frags(3, 3, SA, SW);
             __builtin_amdgcn_sched_barrier(0);
@@ -619,7 +677,7 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
     // (w_g == nullptr) stores its raw partial sums into its own [M x ldc] plane of C instead ----
     const bool partial = w_g == nullptr;
     const float gw = partial ? 1.0f : *w_g;
-    const float ga = (A_Q && !partial) ? *a_g : 1.0f;
+    const float ga = (A_X && !partial) ? *a_g : 1.0f;
     float *Cs = C + (int64_t)blockIdx.y * M * ldc;
 #pragma unroll
     for (int i = 0; i < TM; i++) {
@@ -632,7 +690,7 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
                 if (row < M && col < N) {
                     float v = acc[i][j][e];
                     if (!partial) {
-                        if (A_Q) v = v * ga;
+                        if (A_X) v = v * ga;
                         v = v * gw;
                     }
                     Cs[row * ldc + col] = v;
@@ -966,43 +1024,50 @@ size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus) {
     return p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)N * 4 : 0;
 }
 
-template <int BM, int BN, int WM, int WN, bool A_Q>
-static void launch_tile(const void *a_bf16, int64_t lda, const nvfp4_tensor *a_q, int64_t M, const nvfp4_tensor *w,
-                        float *c, int64_t ldc, const GemmPlan &plan, float *partials, hipStream_t stream) {
+// Activation operand of the tiled launch: bf16 rows, an NVFP4 tensor, or E4M3 bytes.
+struct GemmA {
+    const void *bf16;       // kAmBf16: [M x K] bf16, row stride lda
+    const uint8_t *codes;   // kAmNvfp4: codes; kAmFp8: [M x K] E4M3 bytes, row stride lda
+    const uint8_t *scales;  // kAmNvfp4: block scales
+    const float *g;         // kAmNvfp4: global scale; kAmFp8: tensor scale
+    int64_t lda;
+};
+
+template <int BM, int BN, int WM, int WN, int AM>
+static void launch_tile(const GemmA &a, int64_t M, const nvfp4_tensor *w, float *c, int64_t ldc,
+                        const GemmPlan &plan, float *partials, hipStream_t stream) {
     const int64_t N = w->rows, K = w->cols;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    const uint8_t *ac = A_Q ? a_q->codes : nullptr;
-    const uint8_t *as = A_Q ? a_q->scales : nullptr;
-    const float *ag = A_Q ? a_q->global_scale : nullptr;
+    const int64_t lda = a.lda;
     // k_gemm_mfma addresses one tile's rows with 32-bit buffer offsets
     const int64_t lim = (int64_t)1 << 31;
-    const bool fits = (int64_t)(BM + 1) * (A_Q ? K / 2 : lda * 2) + K * 2 < lim && (int64_t)BN * (K / 2) < lim;
+    const int64_t a_row_bytes = AM == kAmBf16 ? lda * 2 : AM == kAmNvfp4 ? K / 2 : lda;
+    const bool fits = (int64_t)(BM + 1) * a_row_bytes + K * 2 < lim && (int64_t)BN * (K / 2) < lim;
     if (K % kBK == 0 && fits) {
         if (partials) {
             // K slices into their own planes of the workspace, then the ordered sum and scaling
-            hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, A_Q>), dim3((unsigned)tiles, (unsigned)plan.splits),
-                               dim3(64 * WM * WN), 0, stream, (const __bf16 *)a_bf16, lda, ac, as, ag, w->codes,
-                               w->scales, nullptr, partials, N, M, N, K, plan.slice_steps);
+            hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, AM>), dim3((unsigned)tiles, (unsigned)plan.splits),
+                               dim3(64 * WM * WN), 0, stream, (const __bf16 *)a.bf16, lda, a.codes, a.scales, a.g,
+                               w->codes, w->scales, nullptr, partials, N, M, N, K, plan.slice_steps);
             const int64_t total = M * N;
             const int64_t blocks = (total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536;
-            hipLaunchKernelGGL((k_splitk_reduce<A_Q>), dim3((unsigned)blocks), dim3(256), 0, stream, partials,
-                               plan.splits, M, N, N, ag, w->global_scale, c, ldc);
+            hipLaunchKernelGGL((k_splitk_reduce<AM != kAmBf16>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                               partials, plan.splits, M, N, N, a.g, w->global_scale, c, ldc);
             return;
         }
-        hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, A_Q>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0, stream,
-                           (const __bf16 *)a_bf16, lda, ac, as, ag, w->codes, w->scales, w->global_scale, c, ldc, M,
-                           N, K, (int)(K / kBK));
+        hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, AM>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0, stream,
+                           (const __bf16 *)a.bf16, lda, a.codes, a.scales, a.g, w->codes, w->scales,
+                           w->global_scale, c, ldc, M, N, K, (int)(K / kBK));
     } else {
-        hipLaunchKernelGGL((k_gemm_tile<BM, BN, WM, WN, A_Q>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0, stream,
-                           (const __bf16 *)a_bf16, lda, ac, as, ag, w->codes, w->scales, w->global_scale, c, ldc, M,
-                           N, K);
+        hipLaunchKernelGGL((k_gemm_tile<BM, BN, WM, WN, AM>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0, stream,
+                           (const __bf16 *)a.bf16, lda, a.codes, a.scales, a.g, w->codes, w->scales,
+                           w->global_scale, c, ldc, M, N, K);
     }
 }
 
-template <bool A_Q>
-static void launch_tiled(const void *a_bf16, int64_t lda, const nvfp4_tensor *a_q, int64_t M, const nvfp4_tensor *w,
-                         float *c, int64_t ldc, void *workspace, size_t workspace_bytes, int num_cus,
-                         hipStream_t stream) {
+template <int AM>
+static void launch_tiled(const GemmA &a, int64_t M, const nvfp4_tensor *w, float *c, int64_t ldc, void *workspace,
+                         size_t workspace_bytes, int num_cus, hipStream_t stream) {
     GemmPlan plan = plan_gemm(M, w->rows, w->cols, num_cus);
     float *partials = nullptr;
     if (plan.splits > 1) {
@@ -1013,10 +1078,10 @@ static void launch_tiled(const void *a_bf16, int64_t lda, const nvfp4_tensor *a_
             plan = GemmPlan{plan.cfg, 1, (int)(w->cols / kBK)};
     }
     switch (plan.cfg) {
-    case 0: launch_tile<256, 256, 4, 2, A_Q>(a_bf16, lda, a_q, M, w, c, ldc, plan, partials, stream); break;
-    case 1: launch_tile<256, 192, 4, 2, A_Q>(a_bf16, lda, a_q, M, w, c, ldc, plan, partials, stream); break;
-    case 2: launch_tile<128, 256, 2, 4, A_Q>(a_bf16, lda, a_q, M, w, c, ldc, plan, partials, stream); break;
-    default: launch_tile<128, 128, 2, 2, A_Q>(a_bf16, lda, a_q, M, w, c, ldc, plan, partials, stream); break;
+    case 0: launch_tile<256, 256, 4, 2, AM>(a, M, w, c, ldc, plan, partials, stream); break;
+    case 1: launch_tile<256, 192, 4, 2, AM>(a, M, w, c, ldc, plan, partials, stream); break;
+    case 2: launch_tile<128, 256, 2, 4, AM>(a, M, w, c, ldc, plan, partials, stream); break;
+    default: launch_tile<128, 128, 2, 2, AM>(a, M, w, c, ldc, plan, partials, stream); break;
     }
 }
 
@@ -1030,8 +1095,22 @@ hipError_t launch_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, i
         else launch_gemv<false>(M, a_bf16, lda, a_q, w, c, ldc, num_cus, stream);
         return hipGetLastError();
     }
-    if (a_q) launch_tiled<true>(a_bf16, lda, a_q, M, w, c, ldc, workspace, workspace_bytes, num_cus, stream);
-    else launch_tiled<false>(a_bf16, lda, a_q, M, w, c, ldc, workspace, workspace_bytes, num_cus, stream);
+    if (a_q) {
+        const GemmA a{nullptr, a_q->codes, a_q->scales, a_q->global_scale, K};
+        launch_tiled<kAmNvfp4>(a, M, w, c, ldc, workspace, workspace_bytes, num_cus, stream);
+    } else {
+        const GemmA a{a_bf16, nullptr, nullptr, nullptr, lda};
+        launch_tiled<kAmBf16>(a, M, w, c, ldc, workspace, workspace_bytes, num_cus, stream);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp8(const uint8_t *a_fp8, const float *a_scale, int64_t M, int64_t lda, const nvfp4_tensor *w,
+                           float *c, int64_t ldc, void *workspace, size_t workspace_bytes, int num_cus,
+                           hipStream_t stream) {
+    if (M == 0 || w->rows == 0) return hipGetLastError();
+    const GemmA a{nullptr, a_fp8, nullptr, a_scale, lda};
+    launch_tiled<kAmFp8>(a, M, w, c, ldc, workspace, workspace_bytes, num_cus, stream);
     return hipGetLastError();
 }
 

@@ -17,6 +17,11 @@ constexpr size_t kQuantizeWsBytes = 16384;
 hipError_t launch_quantize(const void *x, nvfp4_dtype dt, int64_t ld_x, const float *src_scale, const float *amax_in,
                            const nvfp4_tensor *out, int32_t *flags, void *workspace, int num_cus, hipStream_t stream);
 
+// FP8 E4M3 tensorwise: out [rows x cols] bytes (dense), *out_scale = the tensor scale.
+hipError_t launch_quantize_fp8(const void *x, nvfp4_dtype dt, int64_t ld_x, int64_t rows, int64_t cols,
+                               const float *src_scale, const float *amax_in, uint8_t *out, float *out_scale,
+                               int32_t *flags, void *workspace, int num_cus, hipStream_t stream);
+
 hipError_t launch_dequantize(const nvfp4_tensor *in, void *out, nvfp4_dtype out_dtype, int64_t ld_out, int num_cus,
                              hipStream_t stream);
 
@@ -34,6 +39,11 @@ size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus);
 hipError_t launch_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, int64_t lda, const nvfp4_tensor *w,
                        float *c, int64_t ldc, void *workspace, size_t workspace_bytes, int num_cus,
                        hipStream_t stream);
+
+// The GEMM with E4M3 activations [M x K] (row stride lda bytes) and one tensor scale.
+hipError_t launch_gemm_fp8(const uint8_t *a_fp8, const float *a_scale, int64_t M, int64_t lda, const nvfp4_tensor *w,
+                           float *c, int64_t ldc, void *workspace, size_t workspace_bytes, int num_cus,
+                           hipStream_t stream);
 
 size_t percentile_ws_bytes(int64_t cols, int per_channel);
 

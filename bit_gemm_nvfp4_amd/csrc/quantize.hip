@@ -15,6 +15,13 @@
 // integer max of magnitude bit patterns (non-negative floats order like their bit patterns; NaN
 // patterns sort above infinity, so a non-finite input shows up in it).
 //
+// FP8 tensorwise output ("Qwen3-VL-8B-Instruct-heretic-NVFP4", "Quantization Details": float8_e4m3fn,
+// tensorwise, round to nearest, for embed_tokens and lm_head; "Runtime / hardware": FP4 weights
+// against dynamically quantized FP8 activations), the same kernels with OUTF = kOutFp8:
+//   scale = fl(amax / 448) (1 when amax = 0); byte = sign | E4M3 nearest-even of fl(|v| / scale),
+//   saturating at 448.  The hardware packed conversion (v_cvt_pk_fp8_f32) rounds to nearest even;
+//   the quotient is clamped to +-448 first, so it never overflows.
+//
 // Launches (on the caller's stream): run-time amax -> k_quant_fused, one launch that reads the input
 // once (below); static amax -> k_encode, one pass.
 #include <hip/hip_runtime.h>
@@ -308,17 +315,82 @@ __device__ __forceinline__ float amax_from_bits(uint32_t bits, float sc, bool *n
     }
 }
 
+// Output formats of the quantize kernels.
+constexpr int kOutNvfp4 = 0;  // codes + block scales + global scale
+constexpr int kOutFp8 = 1;    // E4M3 bytes + one tensor scale
+
+// FP8 tensor scale from amax.
+__device__ __forceinline__ float fp8_scale(float amax) { return amax == 0.0f ? 1.0f : amax / 448.0f; }
+
+// Four quotients -> four E4M3 bytes (element i in byte i), each clamped to +-448 first.
+__device__ __forceinline__ uint32_t fp8_pack4(float q0, float q1, float q2, float q3) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(q0, -448.0f, 448.0f),
+                                            __builtin_amdgcn_fmed3f(q1, -448.0f, 448.0f), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(q2, -448.0f, 448.0f),
+                                        __builtin_amdgcn_fmed3f(q3, -448.0f, 448.0f), w, true);
+    return (uint32_t)w;
+}
+
+// Write one tile as FP8: vector vt = j * 64 + lane of the tile holds elements (blk0 * VPB + vt) * EPV
+// and becomes EPV bytes at the same element offset.  Each quotient is a correctly rounded fp32
+// division by the tensor scale.
+template <int SRC>
+__device__ __forceinline__ void tile_store_fp8(const TileRegs<SRC> &t, float scale, float sc, uint64_t tile,
+                                               uint64_t nblocks, uint8_t *__restrict__ out, int lane) {
+    constexpr int EPV = kEpv<SRC>;
+    constexpr int VPB = kVpb<SRC>;
+    const uint64_t blk0 = tile * 64;
+    const bool full = blk0 + 64 <= nblocks;  // wave-uniform
+    uint32_t w[VPB][EPV / 4];
+#pragma unroll
+    for (int j = 0; j < VPB; j++) {
+        float v[EPV];
+        widen<SRC>(t.raw[j], sc, v);
+#pragma unroll
+        for (int e = 0; e < EPV; e += 4)
+            w[j][e / 4] = fp8_pack4(v[e] / scale, v[e + 1] / scale, v[e + 2] / scale, v[e + 3] / scale);
+    }
+    uint8_t *dst = out + (blk0 * VPB + lane) * EPV;
+    auto store = [&](int j) {
+        uint8_t *d = dst + j * 64 * EPV;
+        if constexpr (EPV == 4) {
+            *reinterpret_cast<uint32_t *>(d) = w[j][0];
+        } else if constexpr (EPV == 8) {
+            *reinterpret_cast<u32x2 *>(d) = u32x2{w[j][0], w[j][1]};
+        } else {
+            *reinterpret_cast<u32x4 *>(d) = u32x4{w[j][0], w[j][1], w[j][2], w[j][3]};
+        }
+    };
+    if (full) {
+#pragma unroll
+        for (int j = 0; j < VPB; j++) store(j);
+    } else {
+#pragma unroll
+        for (int j = 0; j < VPB; j++)
+            if (blk0 + (j * 64 + lane) / VPB < nblocks) store(j);
+    }
+}
+
+// Largest magnitude pattern over the lane's vectors of a tile (no per-block reduction).
+template <int SRC>
+__device__ __forceinline__ uint32_t tile_lane_max(const TileRegs<SRC> &t) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < kVpb<SRC>; j++) m = max(m, vec_absmax_bits<SRC>(t.raw[j]));
+    return m;
+}
+
 // ---------------------------------------------------------------------------------------------
 // Static (calibrated) amax: the global scale is known up front, so one pass encodes.
 // ---------------------------------------------------------------------------------------------
-template <int SRC>
+template <int SRC, int OUTF>
 __global__ __launch_bounds__(256) void k_encode(TileGeom gm, const float *__restrict__ src_scale,
                                                 const float *__restrict__ amax_in, uint8_t *__restrict__ codes,
                                                 uint8_t *__restrict__ scales, float *__restrict__ g_out,
                                                 int32_t *__restrict__ flags) {
     const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const float sc = (SRC == NVFP4_E4M3 && src_scale) ? *src_scale : 1.0f;
-    const float g = *amax_in / 2688.0f;
+    const float g = OUTF == kOutFp8 ? fp8_scale(*amax_in) : *amax_in / 2688.0f;
     if (blockIdx.x == 0 && threadIdx.x == 0) *g_out = g;
     const float six_g = 6.0f * g;
     const uint64_t ntiles = (gm.nblocks + 63) / 64;
@@ -331,8 +403,14 @@ __global__ __launch_bounds__(256) void k_encode(TileGeom gm, const float *__rest
         const uint64_t next = tile + nwaves;
         TileRegs<SRC> nxt;
         if (next < ntiles) tile_load<SRC>(nxt, gm, next, lane);  // prefetch while encoding
-        const uint32_t bm = tile_block_max<SRC>(cur, lane);
-        tile_encode<SRC>(cur, bm, g, six_g, sc, tile, gm.nblocks, codes, scales, flags, lane);
+        if constexpr (OUTF == kOutFp8) {
+            // vectors past the end of the tensor were loaded as zeros
+            if (__any(block_nonfinite<SRC>(tile_lane_max<SRC>(cur), sc)) && lane == 0 && flags) atomicOr(flags, 1);
+            tile_store_fp8<SRC>(cur, g, sc, tile, gm.nblocks, codes, lane);
+        } else {
+            const uint32_t bm = tile_block_max<SRC>(cur, lane);
+            tile_encode<SRC>(cur, bm, g, six_g, sc, tile, gm.nblocks, codes, scales, flags, lane);
+        }
         if (next >= ntiles) break;
         tile = next;
         cur = nxt;
@@ -360,7 +438,7 @@ constexpr int kSlotBase = 16;       // workspace words before the 64-bit slots (
 constexpr int kFusedPerCu = 4;      // most workgroups per CU of the single-pass kernel
 constexpr uint32_t kPollLimit = 1u << 22;
 
-template <int SRC, int TPW, int PB>
+template <int SRC, int TPW, int PB, int OUTF>
 __global__ __launch_bounds__(256) void k_quant_fused(TileGeom gm, const float *__restrict__ src_scale,
                                                      uint32_t *__restrict__ ws, uint32_t epoch,
                                                      uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
@@ -374,7 +452,7 @@ __global__ __launch_bounds__(256) void k_quant_fused(TileGeom gm, const float *_
     uint64_t *slots = reinterpret_cast<uint64_t *>(ws + kSlotBase);
     uint64_t *result = reinterpret_cast<uint64_t *>(ws);
 
-    // ---- phase 1: load the resident tiles, block maxima, tensor maximum ----
+    // ---- phase 1: load the resident tiles, block maxima (NVFP4), tensor maximum ----
     TileRegs<SRC> t[TPW];
     uint32_t bm[TPW];
 #pragma unroll
@@ -382,8 +460,12 @@ __global__ __launch_bounds__(256) void k_quant_fused(TileGeom gm, const float *_
     uint32_t m = 0;
 #pragma unroll
     for (int s = 0; s < TPW; s++) {
-        bm[s] = tile_block_max<SRC>(t[s], lane);
-        m = max(m, bm[s]);
+        if constexpr (OUTF == kOutFp8) {
+            m = max(m, tile_lane_max<SRC>(t[s]));
+        } else {
+            bm[s] = tile_block_max<SRC>(t[s], lane);
+            m = max(m, bm[s]);
+        }
     }
     // tiles beyond the resident ones are streamed, PB loads in flight per wave
     for (uint64_t tile = wave + TPW * nwaves; tile < ntiles; tile += PB * nwaves) {
@@ -456,12 +538,30 @@ __global__ __launch_bounds__(256) void k_quant_fused(TileGeom gm, const float *_
     __syncthreads();
     m = amax_bits;
     bool nonfinite = false;
-    const float g = amax_from_bits<SRC>(m, sc, &nonfinite) / 2688.0f;
+    const float amax = amax_from_bits<SRC>(m, sc, &nonfinite);
+    const float g = OUTF == kOutFp8 ? fp8_scale(amax) : amax / 2688.0f;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         *g_out = g;
         if (nonfinite && flags) atomicOr(flags, 1);
     }
     const float six_g = 6.0f * g;
+    if constexpr (OUTF == kOutFp8) {
+        // ---- phase 2 (FP8): convert the resident tiles, then the streamed ones ----
+#pragma unroll
+        for (int s = 0; s < TPW; s++) {
+            const uint64_t tile = wave + s * nwaves;
+            if (tile < ntiles) tile_store_fp8<SRC>(t[s], g, sc, tile, gm.nblocks, codes, lane);
+        }
+        for (uint64_t tile = wave + TPW * nwaves; tile < ntiles; tile += PB * nwaves) {
+            TileRegs<SRC> o[PB];
+#pragma unroll
+            for (int b = 0; b < PB; b++) tile_load<SRC>(o[b], gm, tile + b * nwaves, lane);
+#pragma unroll
+            for (int b = 0; b < PB; b++)
+                if (tile + b * nwaves < ntiles) tile_store_fp8<SRC>(o[b], g, sc, tile + b * nwaves, gm.nblocks, codes, lane);
+        }
+        return;
+    }
 
     // ---- phase 2: encode the resident tiles, then the streamed ones ----
     // the per-block divisions of all resident tiles first (independent, so they overlap), then
@@ -518,13 +618,14 @@ constexpr int kStreamBatch = SRC == NVFP4_F32 ? 2 : 4;
 
 // Workgroups of k_quant_fused<SRC, TPW> that can be resident on one CU (at most kFusedPerCu),
 // from the runtime's occupancy calculation; computed once per instantiation.
-template <int SRC, int TPW, int PB>
+template <int SRC, int TPW, int PB, int OUTF>
 static int fused_per_cu() {
     static std::atomic<int> cached{0};
     int n = cached.load(std::memory_order_relaxed);
     if (n == 0) {
         int b = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_quant_fused<SRC, TPW, PB>, 256, 0) != hipSuccess || b < 1)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_quant_fused<SRC, TPW, PB, OUTF>, 256, 0) != hipSuccess ||
+            b < 1)
             b = 1;
         n = b < kFusedPerCu ? b : kFusedPerCu;
         cached.store(n, std::memory_order_relaxed);
@@ -534,58 +635,69 @@ static int fused_per_cu() {
 
 // The grid barrier needs every workgroup resident at once, so the grid never exceeds what the
 // CUs hold; waves then take more tiles than TPW and stream the rest.
-template <int SRC, int TPW, int PB = 1>
-static void launch_fused(const TileGeom &gm, int grid, const float *src_scale, uint32_t *ws, const nvfp4_tensor *out,
+// Output pointers of one quantize call: NVFP4 codes / block scales / global scale, or FP8 bytes (in
+// `codes`) and the tensor scale (in `scale`).
+struct QOut {
+    uint8_t *codes;
+    uint8_t *scales;
+    float *scale;
+};
+
+template <int SRC, int TPW, int OUTF, int PB = 1>
+static void launch_fused(const TileGeom &gm, int grid, const float *src_scale, uint32_t *ws, const QOut &out,
                          int32_t *flags, int num_cus, hipStream_t stream) {
-    const int cap = fused_per_cu<SRC, TPW, PB>() * num_cus;
+    const int cap = fused_per_cu<SRC, TPW, PB, OUTF>() * num_cus;
     if (grid > cap) grid = cap;
-    hipLaunchKernelGGL((k_quant_fused<SRC, TPW, PB>), dim3(grid), dim3(256), 0, stream, gm, src_scale, ws, next_epoch(),
-                       out->codes, out->scales, out->global_scale, flags);
+    hipLaunchKernelGGL((k_quant_fused<SRC, TPW, PB, OUTF>), dim3(grid), dim3(256), 0, stream, gm, src_scale, ws,
+                       next_epoch(), out.codes, out.scales, out.scale, flags);
 }
 
 // Resident launch: tiles per wave rounded up to a supported residency, at most T.
-template <int SRC, int T>
+template <int SRC, int OUTF, int T>
 static void launch_resident(const TileGeom &gm, int grid, uint64_t tpw, const float *src_scale, uint32_t *ws,
-                            const nvfp4_tensor *out, int32_t *flags, int num_cus, hipStream_t stream) {
-    if (tpw <= 1) launch_fused<SRC, 1>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
-    else if (tpw <= 2) launch_fused<SRC, 2>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
-    else if (tpw <= 3) launch_fused<SRC, 3>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
-    else if (tpw <= 4 || T < 5) launch_fused<SRC, (T < 4 ? T : 4)>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
-    else if (tpw <= 5 || T < 6) launch_fused<SRC, (T < 5 ? T : 5)>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
-    else if (tpw <= 6 || T < 8) launch_fused<SRC, (T < 6 ? T : 6)>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
-    else if (tpw <= 8 || T < 12) launch_fused<SRC, (T < 8 ? T : 8)>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
-    else if (tpw <= 12 || T < 16) launch_fused<SRC, (T < 12 ? T : 12)>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
-    else launch_fused<SRC, T>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
+                            const QOut &out, int32_t *flags, int num_cus, hipStream_t stream) {
+#define NVFP4_LAUNCH(T_) launch_fused<SRC, (T_), OUTF>(gm, grid, src_scale, ws, out, flags, num_cus, stream)
+    if (tpw <= 1) NVFP4_LAUNCH(1);
+    else if (tpw <= 2) NVFP4_LAUNCH(2);
+    else if (tpw <= 3) NVFP4_LAUNCH(3);
+    else if (tpw <= 4 || T < 5) NVFP4_LAUNCH(T < 4 ? T : 4);
+    else if (tpw <= 5 || T < 6) NVFP4_LAUNCH(T < 5 ? T : 5);
+    else if (tpw <= 6 || T < 8) NVFP4_LAUNCH(T < 6 ? T : 6);
+    else if (tpw <= 8 || T < 12) NVFP4_LAUNCH(T < 8 ? T : 8);
+    else if (tpw <= 12 || T < 16) NVFP4_LAUNCH(T < 12 ? T : 12);
+    else NVFP4_LAUNCH(T);
+#undef NVFP4_LAUNCH
 }
 
 // Tiles spread over all CUs: four workgroups each (four waves per SIMD hide each other's
 // latencies) when every wave's tiles then fit the smaller register budget, else two workgroups
 // each with up to kMaxTpw resident tiles; fewer workgroups for small tensors.  Beyond that the
 // streaming variant runs (the rest is read twice).
-template <int SRC>
-static void launch_fused_any(const TileGeom &gm, const float *src_scale, uint32_t *ws, const nvfp4_tensor *out,
+template <int SRC, int OUTF>
+static void launch_fused_any(const TileGeom &gm, const float *src_scale, uint32_t *ws, const QOut &out,
                              int32_t *flags, int num_cus, hipStream_t stream) {
     const uint64_t ntiles = (gm.nblocks + 63) / 64;
     if (4 * num_cus <= kMaxSlots) {
         const int grid4 = grid_for(ntiles, 4, 4 * num_cus);
         const uint64_t tpw4 = (ntiles + 4 * (uint64_t)grid4 - 1) / (4 * (uint64_t)grid4);
         if (tpw4 <= (uint64_t)kMaxTpw4<SRC>) {
-            launch_resident<SRC, kMaxTpw4<SRC>>(gm, grid4, tpw4, src_scale, ws, out, flags, num_cus, stream);
+            launch_resident<SRC, OUTF, kMaxTpw4<SRC>>(gm, grid4, tpw4, src_scale, ws, out, flags, num_cus, stream);
             return;
         }
     }
     const int grid = grid_for(ntiles, 4, 2 * num_cus);
     const uint64_t tpw = (ntiles + 4 * (uint64_t)grid - 1) / (4 * (uint64_t)grid);
     if (tpw > (uint64_t)kMaxTpw<SRC>) {
-        launch_fused<SRC, kStreamTpw<SRC>, kStreamBatch<SRC>>(gm, grid, src_scale, ws, out, flags, num_cus, stream);
+        launch_fused<SRC, kStreamTpw<SRC>, OUTF, kStreamBatch<SRC>>(gm, grid, src_scale, ws, out, flags, num_cus,
+                                                                   stream);
         return;
     }
-    launch_resident<SRC, kMaxTpw<SRC>>(gm, grid, tpw, src_scale, ws, out, flags, num_cus, stream);
+    launch_resident<SRC, OUTF, kMaxTpw<SRC>>(gm, grid, tpw, src_scale, ws, out, flags, num_cus, stream);
 }
 
-template <int SRC>
+template <int SRC, int OUTF>
 static hipError_t launch_quantize_t(const void *x, int64_t ld_x, int64_t rows, int64_t cols, const float *src_scale,
-                                    const float *amax_in, const nvfp4_tensor *out, int32_t *flags, uint32_t *ws,
+                                    const float *amax_in, const QOut &out, int32_t *flags, uint32_t *ws,
                                     int num_cus, hipStream_t stream) {
     constexpr int EB = SrcTraits<SRC>::kElemBytes;
     TileGeom gm;
@@ -596,29 +708,48 @@ static hipError_t launch_quantize_t(const void *x, int64_t ld_x, int64_t rows, i
     gm.contiguous = (ld_x == cols) ? 1 : 0;
     const uint64_t ntiles = (gm.nblocks + 63) / 64;
     if (!amax_in) {
-        launch_fused_any<SRC>(gm, src_scale, ws, out, flags, num_cus, stream);
+        launch_fused_any<SRC, OUTF>(gm, src_scale, ws, out, flags, num_cus, stream);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_encode<SRC>, dim3(grid_for(ntiles, 4, num_cus * 8)), dim3(256), 0, stream, gm, src_scale,
-                       amax_in, out->codes, out->scales, out->global_scale, flags);
+    hipLaunchKernelGGL((k_encode<SRC, OUTF>), dim3(grid_for(ntiles, 4, num_cus * 8)), dim3(256), 0, stream, gm,
+                       src_scale, amax_in, out.codes, out.scales, out.scale, flags);
     return hipGetLastError();
+}
+
+template <int OUTF>
+static hipError_t launch_quantize_any(const void *x, nvfp4_dtype dt, int64_t ld_x, int64_t rows, int64_t cols,
+                                      const float *src_scale, const float *amax_in, const QOut &out, int32_t *flags,
+                                      uint32_t *ws, int num_cus, hipStream_t stream) {
+    switch (dt) {
+    case NVFP4_F32:
+        return launch_quantize_t<NVFP4_F32, OUTF>(x, ld_x, rows, cols, src_scale, amax_in, out, flags, ws, num_cus,
+                                                  stream);
+    case NVFP4_BF16:
+        return launch_quantize_t<NVFP4_BF16, OUTF>(x, ld_x, rows, cols, src_scale, amax_in, out, flags, ws, num_cus,
+                                                   stream);
+    case NVFP4_F16:
+        return launch_quantize_t<NVFP4_F16, OUTF>(x, ld_x, rows, cols, src_scale, amax_in, out, flags, ws, num_cus,
+                                                  stream);
+    default:
+        return launch_quantize_t<NVFP4_E4M3, OUTF>(x, ld_x, rows, cols, src_scale, amax_in, out, flags, ws, num_cus,
+                                                   stream);
+    }
 }
 
 hipError_t launch_quantize(const void *x, nvfp4_dtype dt, int64_t ld_x, const float *src_scale, const float *amax_in,
                            const nvfp4_tensor *out, int32_t *flags, void *workspace, int num_cus,
                            hipStream_t stream) {
-    uint32_t *ws = reinterpret_cast<uint32_t *>(workspace);
-    const int64_t rows = out->rows, cols = out->cols;
-    switch (dt) {
-    case NVFP4_F32:
-        return launch_quantize_t<NVFP4_F32>(x, ld_x, rows, cols, src_scale, amax_in, out, flags, ws, num_cus, stream);
-    case NVFP4_BF16:
-        return launch_quantize_t<NVFP4_BF16>(x, ld_x, rows, cols, src_scale, amax_in, out, flags, ws, num_cus, stream);
-    case NVFP4_F16:
-        return launch_quantize_t<NVFP4_F16>(x, ld_x, rows, cols, src_scale, amax_in, out, flags, ws, num_cus, stream);
-    default:
-        return launch_quantize_t<NVFP4_E4M3>(x, ld_x, rows, cols, src_scale, amax_in, out, flags, ws, num_cus, stream);
-    }
+    const QOut o{out->codes, out->scales, out->global_scale};
+    return launch_quantize_any<kOutNvfp4>(x, dt, ld_x, out->rows, out->cols, src_scale, amax_in, o, flags,
+                                          reinterpret_cast<uint32_t *>(workspace), num_cus, stream);
+}
+
+hipError_t launch_quantize_fp8(const void *x, nvfp4_dtype dt, int64_t ld_x, int64_t rows, int64_t cols,
+                               const float *src_scale, const float *amax_in, uint8_t *out, float *out_scale,
+                               int32_t *flags, void *workspace, int num_cus, hipStream_t stream) {
+    const QOut o{out, nullptr, out_scale};
+    return launch_quantize_any<kOutFp8>(x, dt, ld_x, rows, cols, src_scale, amax_in, o, flags,
+                                        reinterpret_cast<uint32_t *>(workspace), num_cus, stream);
 }
 
 }  // namespace nvfp4

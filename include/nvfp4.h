@@ -100,6 +100,25 @@ nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype x_dtype, int64_t ld_x, co
                             size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * nvfp4_quantize_fp8 -- x [rows x cols] (row stride ld_x elements) -> FP8 E4M3 bytes out [rows x
+ * cols] (dense, row-major) and one fp32 tensor scale, for the layers kept in FP8 and for the FP8
+ * activations of nvfp4_gemm_fp8a ("Qwen3-VL-8B-Instruct-heretic-NVFP4", "Quantization Details":
+ * float8_e4m3fn, tensorwise, round to nearest, for embed_tokens and lm_head; "Runtime /
+ * hardware": FP4 weights against dynamically quantized FP8 activations):
+ *   1. widen to fp32 as nvfp4_quantize does (E4M3 source: times *src_scale, NULL meaning 1.0);
+ *   2. amax = max |v| over the tensor, or *amax_in (static; values beyond it saturate);
+ *   3. *out_scale = fl(amax / 448), 448 the largest E4M3 value; 1.0 when amax = 0;
+ *   4. byte = sign bit of v | E4M3 round-to-nearest-even of fl(|v| / scale), saturating at 448
+ *      (0x7E); value = e4m3(byte) x scale.
+ * cols % 16 == 0.  flags as for nvfp4_quantize; workspace of
+ * nvfp4_workspace_size(NVFP4_OP_QUANTIZE, rows, cols, 0) bytes when amax_in is NULL.
+ * src_scale, amax_in, out_scale, flags and workspace are device pointers.
+ */
+nvfp4_status nvfp4_quantize_fp8(const void *x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                                const float *src_scale, const float *amax_in, uint8_t *out, float *out_scale,
+                                int32_t *flags, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * nvfp4_dequantize -- the expander: NVFP4 `in` -> out [in->rows x in->cols] (row stride ld_out),
  * w = fl(e2m1 x s x g) in fp32 ("Qwen-Image NVFP4 on a 16 GB Ada GPU", section "Running the NVFP4
  * weights on Ada": each byte gives its two E2M1 values, each block's scale multiplies its 16
@@ -128,6 +147,19 @@ nvfp4_status nvfp4_dequantize(const nvfp4_tensor *in, void *out, nvfp4_dtype out
 nvfp4_status nvfp4_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, int64_t lda,
                         const nvfp4_tensor *w, float *c, int64_t ldc, void *workspace, size_t workspace_bytes,
                         hipStream_t stream);
+
+/*
+ * nvfp4_gemm_fp8a -- C [M x N] fp32 (row stride ldc) = A_hat . W_hat^T with FP8 activations: a_fp8
+ * [M x K] E4M3 bytes (row stride lda bytes, from nvfp4_quantize_fp8) with tensor scale *a_scale,
+ * and W an NVFP4 tensor [N x K] ("Qwen3-VL-8B-Instruct-heretic-NVFP4", "Runtime / hardware": FP4
+ * weight x dynamically quantized FP8 activation).  Both operands are expanded exactly to f16
+ * inside the kernel (e4m3 values and e2m1 x s both fit f16 exactly); products are summed in fp32
+ * and the sum is multiplied by *a_scale and the weight's global scale at the end.  workspace as
+ * for nvfp4_gemm (split-K partial sums; NULL runs the unsplit kernel).
+ */
+nvfp4_status nvfp4_gemm_fp8a(const uint8_t *a_fp8, const float *a_scale, int64_t M, int64_t lda,
+                             const nvfp4_tensor *w, float *c, int64_t ldc, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
 
 /*
  * amax_percentile -- calibration statistic: for each column c of x [rows x cols] (per_channel

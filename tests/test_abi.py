@@ -24,8 +24,9 @@ def nv():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == sorted(["nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm", "amax_percentile",
-                                            "nvfp4_workspace_size", "nvfp4_status_string"])
+    assert _declared_functions() == sorted(["nvfp4_quantize", "nvfp4_quantize_fp8", "nvfp4_dequantize", "nvfp4_gemm",
+                                            "nvfp4_gemm_fp8a", "amax_percentile", "nvfp4_workspace_size",
+                                            "nvfp4_status_string"])
 
 
 def test_library_exports_every_declared_symbol(nv):
@@ -107,6 +108,40 @@ def test_gemm_validation(nv):
     assert g(P(FAKE), None, -1, 128, ctypes.byref(w), P(FAKE), 64, None, 0, None) == 2
     assert g(P(FAKE), None, 8, 132, ctypes.byref(w), P(FAKE), 64, None, 0, None) == 3  # A rows 264 B
     assert g(P(FAKE), None, 8, 128, ctypes.byref(w), P(FAKE + 2), 64, None, 0, None) == 3  # C not 4-aligned
+
+
+def test_quantize_fp8_validation(nv):
+    q = nv.lib.nvfp4_quantize_fp8
+    P = ctypes.c_void_p
+    ws = nv.workspace_size(nv.OP_QUANTIZE, 4, 32)
+    assert q(P(FAKE), 9, 4, 32, 32, None, None, P(FAKE), P(FAKE), None, P(FAKE), ws, None) == 4  # dtype
+    assert q(None, 0, 4, 32, 32, None, None, P(FAKE), P(FAKE), None, P(FAKE), ws, None) == 1  # NULL x
+    assert q(P(FAKE), 0, 4, 32, 32, None, None, None, P(FAKE), None, P(FAKE), ws, None) == 1  # NULL out
+    assert q(P(FAKE), 0, 4, 32, 32, None, None, P(FAKE), None, None, P(FAKE), ws, None) == 1  # NULL scale out
+    assert q(P(FAKE), 0, 4, 24, 24, None, None, P(FAKE), P(FAKE), None, P(FAKE), ws, None) == 2  # cols % 16
+    assert q(P(FAKE), 0, 4, 32, 16, None, None, P(FAKE), P(FAKE), None, P(FAKE), ws, None) == 2  # ld < cols
+    assert q(P(FAKE), 0, -1, 32, 32, None, None, P(FAKE), P(FAKE), None, P(FAKE), ws, None) == 2
+    assert q(P(FAKE + 4), 0, 4, 32, 32, None, None, P(FAKE), P(FAKE), None, P(FAKE), ws, None) == 3  # x align
+    assert q(P(FAKE), 0, 4, 32, 32, None, None, P(FAKE + 8), P(FAKE), None, P(FAKE), ws, None) == 3  # out align
+    assert q(P(FAKE), 0, 4, 32, 32, None, None, P(FAKE), P(FAKE + 2), None, P(FAKE), ws, None) == 3
+    assert q(P(FAKE), 0, 4, 32, 32, P(FAKE), None, P(FAKE), P(FAKE), None, P(FAKE), ws, None) == 6  # src_scale
+    assert q(P(FAKE), 0, 4, 32, 32, None, None, P(FAKE), P(FAKE), None, None, 0, None) == 5  # workspace
+    assert q(P(FAKE), 0, 4, 32, 32, None, None, P(FAKE), P(FAKE), None, P(FAKE), ws - 1, None) == 5
+
+
+def test_gemm_fp8a_validation(nv):
+    g = nv.lib.nvfp4_gemm_fp8a
+    w = _qt(nv, 64, 128)
+    P = ctypes.c_void_p
+    assert g(P(FAKE), None, 8, 128, ctypes.byref(w), P(FAKE), 64, None, 0, None) == 1  # NULL a_scale
+    assert g(None, P(FAKE), 8, 128, ctypes.byref(w), P(FAKE), 64, None, 0, None) == 1  # NULL a
+    assert g(P(FAKE), P(FAKE), 8, 128, None, P(FAKE), 64, None, 0, None) == 1  # NULL w
+    assert g(P(FAKE), P(FAKE), 8, 64, ctypes.byref(w), P(FAKE), 64, None, 0, None) == 2  # lda < K
+    assert g(P(FAKE), P(FAKE), -1, 128, ctypes.byref(w), P(FAKE), 64, None, 0, None) == 2
+    assert g(P(FAKE), P(FAKE), 8, 136, ctypes.byref(w), P(FAKE), 64, None, 0, None) == 3  # A rows 136 B
+    assert g(P(FAKE), P(FAKE + 2), 8, 128, ctypes.byref(w), P(FAKE), 64, None, 0, None) == 3  # scale align
+    assert g(P(FAKE), P(FAKE), 8, 128, ctypes.byref(w), P(FAKE), 32, None, 0, None) == 2  # ldc < N
+    assert g(P(FAKE), P(FAKE), 8, 128, ctypes.byref(w), None, 64, None, 0, None) == 1  # NULL C
 
 
 def test_percentile_validation(nv):

@@ -432,3 +432,142 @@ def test_quantize_large_tensor_overflow_path(nv):
     q = _quant(nv, to_dev_f32(x))
     ref, _ = oracle.quantize(x)
     _assert_q_equal(q, ref, "large")
+
+
+# ------------------------------------------------------------------------------------------------
+# FP8 tensorwise quantizer and the GEMM with FP8 activations
+# ------------------------------------------------------------------------------------------------
+def _quant_fp8(nv, x, **kw):
+    flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+    q = nv.quantize_fp8(x, flags=flags, **kw)
+    f = int(flags.item())
+    assert f == 0, f"quantize_fp8 flags {f:#x}"
+    return q
+
+
+def _assert_fp8_equal(q, ref_bytes, ref_scale, what=""):
+    s = q.scale.cpu().numpy()[0]
+    assert s.view(np.uint32) == np.float32(ref_scale).view(np.uint32), f"{what} scale {s} vs {ref_scale}"
+    b = q.data.cpu().numpy()
+    bad = np.nonzero(b != ref_bytes)
+    assert bad[0].size == 0, (f"{what} {bad[0].size} bytes differ, first at {bad[0][0]},{bad[1][0]}: "
+                              f"{b[bad[0][0], bad[1][0]]:#x} vs {ref_bytes[bad[0][0], bad[1][0]]:#x}")
+
+
+def _fp8_case(x, dtype):
+    """(device tensor, oracle bytes, oracle scale) for fp32 values x given as dtype."""
+    if dtype == "f32":
+        return to_dev_f32(x), *oracle.quantize_fp8(x)[:2]
+    if dtype == "bf16":
+        b = synth.bf16_bits(x)
+        return to_dev_bf16(b), *oracle.quantize_fp8(b, oracle.BF16)[:2]
+    h = x.astype(np.float16).view(np.uint16)
+    return to_dev_f16(h), *oracle.quantize_fp8(h, oracle.F16)[:2]
+
+
+@pytest.mark.parametrize("shape", SHAPES + [(2000, 3072), (4096, 3072)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_quantize_fp8_shapes_dtypes(nv, shape, dtype):
+    rows, cols = shape
+    _note(f"quantize_fp8 {dtype} {shape}")
+    rng = np.random.default_rng(rows * 131 + cols)
+    x = (rng.standard_t(4, size=shape) * 10.0 ** rng.uniform(-3, 1)).astype(np.float32)
+    x[rng.random(shape) < 0.05] = 0.0
+    x[rng.random(shape) < 0.02] *= -0.0
+    xd, rb, rs = _fp8_case(x, dtype)
+    _assert_fp8_equal(_quant_fp8(nv, xd), rb, rs, f"{dtype} {shape}")
+    if rows > 1:
+        _assert_fp8_equal(_quant_fp8(nv, padded(xd, 16)), rb, rs, f"{dtype} {shape} strided")
+
+
+def test_quantize_fp8_from_fp8_static_zero_and_flags(nv):
+    _note("quantize_fp8: E4M3 source, static amax, zeros, non-finite")
+    rng = np.random.default_rng(8)
+    w = (rng.standard_normal((96, 512)) * 0.02).astype(np.float32)
+    b8, sc = synth.fp8_tensorwise(w)
+    rb, rs, _ = oracle.quantize_fp8(b8, oracle.E4M3, float(sc))
+    q = _quant_fp8(nv, to_dev_u8(b8), src_scale=torch.tensor([sc], dtype=torch.float32, device=DEV))
+    _assert_fp8_equal(q, rb, rs, "e4m3 source")
+    amax = np.float32(0.01)
+    rb, rs, _ = oracle.quantize_fp8(w, amax=float(amax))
+    q = nv.quantize_fp8(to_dev_f32(w), amax=torch.tensor([amax], dtype=torch.float32, device=DEV))
+    _assert_fp8_equal(q, rb, rs, "static amax")
+    z = np.zeros((33, 64), np.float32)
+    rb, rs, _ = oracle.quantize_fp8(z)
+    _assert_fp8_equal(_quant_fp8(nv, to_dev_f32(z)), rb, rs, "zeros")
+    w[5, 7] = np.inf
+    flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+    nv.quantize_fp8(to_dev_f32(w), flags=flags)
+    assert flags.item() & 1
+    flags.zero_()
+    nv.quantize_fp8(to_dev_f32(w), amax=torch.tensor([1.0], device=DEV), flags=flags)
+    assert flags.item() & 1
+
+
+def test_quantize_fp8_streamed_tensor(nv):
+    _note("quantize_fp8 16384 x 8192 fp32 (streaming path)")
+    rng = np.random.default_rng(78)
+    x = (rng.standard_normal((16384, 8192)) * 0.01).astype(np.float32)
+    x[99, 4321] = -0.5
+    rb, rs, _ = oracle.quantize_fp8(x)
+    _assert_fp8_equal(_quant_fp8(nv, to_dev_f32(x)), rb, rs, "large")
+
+
+# K % 64 != 0 takes k_gemm_tile; M <= 4 runs on the tiled kernels too (no GEMV form for FP8 A)
+@pytest.mark.parametrize("mnk", [(16, 64, 256), (1, 64, 128), (4, 100, 48), (5, 70, 80), (37, 129, 272),
+                                 (130, 257, 1024), (300, 200, 3072), (576, 16384, 64), (130, 1000, 128)])
+def test_gemm_fp8a(nv, mnk):
+    m, n, k = mnk
+    _note(f"gemm fp8a {mnk}")
+    q, ref = _rand_q(nv, n, k, seed=m * 13 + n)
+    x = np.random.default_rng(m * 7 + k).standard_normal((m, k)).astype(np.float32)
+    a8 = _quant_fp8(nv, to_dev_f32(x))
+    rb, rs, _ = oracle.quantize_fp8(x)
+    _assert_fp8_equal(a8, rb, rs, "activations")
+    c = nv.gemm(a8, q).cpu().numpy()
+    err = oracle.gemm_error(c, oracle.gemm_w4a8(rb, rs, ref))
+    assert err <= GEMM_TOL, err
+    if m > 1:  # strided A and C
+        import bit_gemm_nvfp4_amd as nvm
+        a = nvm.FP8Tensor(padded(a8.data, 16), a8.scale)
+        out = padded(torch.empty((m, n), dtype=torch.float32, device=DEV), 4)
+        nv.gemm(a, q, out=out)
+        assert np.array_equal(out.cpu().numpy(), c)
+
+
+def test_gemm_fp8a_one_hot_all_bytes(nv):
+    # every finite E4M3 byte times a one-hot row: C reproduces the exact products e4m3 x w_hat x scale
+    _note("gemm fp8a one-hot over all E4M3 bytes")
+    q, ref = _rand_q(nv, 64, 256, seed=7)
+    import bit_gemm_nvfp4_amd as nvm
+    bts = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], dtype=np.uint8)
+    a = np.zeros((bts.size, 256), dtype=np.uint8)
+    a[np.arange(bts.size), np.arange(bts.size) % 256] = bts
+    sc = np.float32(0.5)
+    a8 = nvm.FP8Tensor(to_dev_u8(a), torch.tensor([sc], dtype=torch.float32, device=DEV))
+    c = nv.gemm(a8, q).cpu().numpy()
+    cref = oracle.gemm_w4a8(a, sc, ref)
+    assert np.array_equal(c.astype(np.float64), cref.astype(np.float32).astype(np.float64))
+
+
+def test_gemm_fp8a_split_k_and_full(nv):
+    _note("gemm fp8a split-K 512x4096x12288, attention projection 4096x3072x3072 (sampled rows)")
+    m, n, k = 512, 4096, 12288
+    assert nv.workspace_size(nv.OP_GEMM, m, n, k) > 0
+    q, ref = _rand_q(nv, n, k, seed=5, sigma=0.015)
+    x = np.random.default_rng(6).standard_normal((m, k)).astype(np.float32)
+    a8 = _quant_fp8(nv, to_dev_f32(x))
+    rb, rs, _ = oracle.quantize_fp8(x)
+    _assert_fp8_equal(a8, rb, rs, "split-K activations")
+    assert oracle.gemm_error(nv.gemm(a8, q).cpu().numpy(), oracle.gemm_w4a8(rb, rs, ref)) <= GEMM_TOL
+    w = synth.attn_proj_weight()
+    ref, _ = oracle.quantize(w)
+    q = _quant(nv, to_dev_f32(w))
+    a_bits = synth.attn_proj_activations()
+    a8 = _quant_fp8(nv, to_dev_bf16(a_bits))
+    rb, rs, _ = oracle.quantize_fp8(a_bits, oracle.BF16)
+    _assert_fp8_equal(a8, rb, rs, "attention activations")
+    rows = np.random.default_rng(2).choice(4096, 256, replace=False)
+    c = nv.gemm(a8, q).cpu().numpy()[rows]
+    cref = oracle.gemm_f64(oracle.fp8_values(rb[rows], rs), oracle.dequantize(ref, "f64"))
+    assert oracle.gemm_error(c, cref) <= GEMM_TOL
