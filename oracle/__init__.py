@@ -65,6 +65,7 @@ def _load():
     lib.ref_e2m1_index_array.argtypes = [P, I64, P]
     lib.ref_e4m3_encode_array.argtypes = [P, I64, P]
     lib.ref_f32_to_bf16_array.argtypes = [P, I64, P]
+    lib.ref_matrix_stats.argtypes = [P, I64, I64, P, P, ctypes.c_float, I, P]
     lib.ref_fp8_scale.argtypes, lib.ref_fp8_scale.restype = [ctypes.c_float], ctypes.c_float
     lib.ref_fp8_byte.argtypes, lib.ref_fp8_byte.restype = [ctypes.c_float, ctypes.c_float], I
     lib.ref_quantize_fp8_f32.argtypes, lib.ref_quantize_fp8_f32.restype = [P, I64, I64, P, P, P], I
@@ -258,6 +259,25 @@ def gemm_error(c: np.ndarray, cref: np.ndarray) -> float:
     denom = np.maximum(np.abs(cref), floor)
     denom = np.where(denom == 0, 1.0, denom)
     return float(np.max(np.abs(c - cref) / denom))
+
+
+STAT_FIELDS = ("rel_error", "kurtosis", "block_max_over_std", "mean", "std", "max_abs", "blocks")
+
+
+def matrix_stats(w: np.ndarray, q: QTensor | None = None, dtype: int = F32) -> dict:
+    """Quality statistics of one matrix ("Qwen-Image NVFP4 on a 16 GB Ada GPU", section "Quality:
+    the error of each matrix"): the relative error ||W - W_hat|| / ||W|| (Frobenius, W_hat the exact
+    expansion of q), the excess kurtosis (population moments), and the mean over blocks of 64
+    consecutive elements of max|w| / std (population std of the block; blocks with std 0 left out)."""
+    v = widen(w, dtype)
+    rows, cols = v.shape
+    out = np.zeros(7, dtype=np.float64)
+    if q is not None:
+        codes, scales = np.ascontiguousarray(q.codes), np.ascontiguousarray(q.scales)
+        _load().ref_matrix_stats(_ptr(v), rows, cols, _ptr(codes), _ptr(scales), float(q.g), 1, _ptr(out))
+    else:
+        _load().ref_matrix_stats(_ptr(v), rows, cols, None, None, 0.0, 0, _ptr(out))
+    return dict(zip(STAT_FIELDS, out.tolist()))
 
 
 def rank(p: float, n: int) -> int:

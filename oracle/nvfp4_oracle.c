@@ -37,6 +37,11 @@
  *   R5  FP8 source: v = fl(e4m3(b) * src_scale), a missing scale meaning 1.0.
  *   R6  expansion: w = fl(e2m1 * s * g) with one rounding (e2m1 * s is exact).
  *   R7  percentile: nearest rank, k = clamp(ceil(p * n / 100), 1, n), over |x| per channel.
+ *   R9  matrix statistics ([ADA Error]): relative error = ||W - W_hat||_F / ||W||_F with W_hat the
+ *       exact expansion; kurtosis = excess kurtosis m4 / m2^2 - 3 with population central
+ *       moments; block ratio = mean over blocks of 64 consecutive elements (row-major order, the
+ *       last block possibly shorter) of max|w| / population std of the block, blocks with std 0
+ *       left out.
  *   R8  FP8 tensorwise ([VL] "Quantization Details": float8_e4m3fn, tensorwise, round to
  *       nearest; "Runtime / hardware": FP4 weights against dynamically quantized FP8
  *       activations): scale = fl(amax / 448), 448 the largest E4M3, and 1 when amax = 0;
@@ -328,6 +333,68 @@ void ref_amax_percentile(const float *x, int64_t rows, int64_t cols, double p, i
         if (out_max) out_max[0] = buf[n - 1];
         free(buf);
     }
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Quality statistics of one matrix ([ADA Error]; R9).  w: fp32 [rows x cols] dense; codes /    */
+/* scales / g: its NVFP4 form (used when has_q).  out[0] relative error (NaN without q),         */
+/* out[1] excess kurtosis, out[2] mean block ratio, out[3] mean, out[4] population std,          */
+/* out[5] max |w|, out[6] number of blocks in out[2].  Two passes, the plain definitions.        */
+/* ------------------------------------------------------------------------------------------ */
+void ref_matrix_stats(const float *w, int64_t rows, int64_t cols, const uint8_t *codes, const uint8_t *scales,
+                      float g, int has_q, double *out) {
+    int64_t n = rows * cols;
+    double sum = 0.0, amax = 0.0;
+    for (int64_t i = 0; i < n; i++) {
+        sum += (double)w[i];
+        if (fabs((double)w[i]) > amax) amax = fabs((double)w[i]);
+    }
+    double mu = sum / (double)n;
+    double m2 = 0.0, m4 = 0.0;
+    for (int64_t i = 0; i < n; i++) {
+        double d = (double)w[i] - mu;
+        m2 += d * d;
+        m4 += d * d * d * d;
+    }
+    m2 /= (double)n;
+    m4 /= (double)n;
+    out[1] = m4 / (m2 * m2) - 3.0;
+    out[3] = mu;
+    out[4] = sqrt(m2);
+    out[5] = amax;
+    if (has_q) {
+        double *wh = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        ref_dequantize_f64(codes, scales, g, rows, cols, wh);
+        double num = 0.0, den = 0.0;
+        for (int64_t i = 0; i < n; i++) {
+            double d = (double)w[i] - wh[i];
+            num += d * d;
+            den += (double)w[i] * (double)w[i];
+        }
+        out[0] = sqrt(num) / sqrt(den);
+        free(wh);
+    } else {
+        out[0] = NAN;
+    }
+    double rsum = 0.0;
+    int64_t cnt = 0;
+    for (int64_t b = 0; b < n; b += 64) {
+        int64_t e = b + 64 < n ? b + 64 : n;
+        double bs = 0.0, bmax = 0.0;
+        for (int64_t i = b; i < e; i++) {
+            bs += (double)w[i];
+            if (fabs((double)w[i]) > bmax) bmax = fabs((double)w[i]);
+        }
+        double bmu = bs / (double)(e - b), v = 0.0;
+        for (int64_t i = b; i < e; i++) v += ((double)w[i] - bmu) * ((double)w[i] - bmu);
+        double sd = sqrt(v / (double)(e - b));
+        if (sd > 0.0) {
+            rsum += bmax / sd;
+            cnt++;
+        }
+    }
+    out[2] = cnt > 0 ? rsum / (double)cnt : NAN;
+    out[6] = (double)cnt;
 }
 
 /* ------------------------------------------------------------------------------------------ */

@@ -479,3 +479,56 @@ def test_gemm_w4a8_one_hot_and_definition():
     for m in range(3):
         for n in range(0, 24, 5):
             assert c[m, n] == pytest.approx(sum(a[m, k] * w[n, k] for k in range(64)), rel=1e-14, abs=1e-300)
+
+
+# ------------------------------------------------------------------------------------------------
+# matrix statistics ("Qwen-Image NVFP4 on a 16 GB Ada GPU", section "Quality: the error of each
+# matrix": relative error of each matrix, kurtosis, max / std in blocks of 64)
+# ------------------------------------------------------------------------------------------------
+def test_stats_kurtosis_and_moments_against_scipy():
+    import scipy.stats
+    rnd = np.random.default_rng(51)
+    for x in [rnd.standard_normal((64, 512)), rnd.standard_t(3, (128, 256)) * 0.02, rnd.uniform(-1, 1, (32, 1024))]:
+        x = x.astype(np.float32)
+        st = oracle.matrix_stats(x)
+        xd = x.ravel().astype(np.float64)
+        assert st["kurtosis"] == pytest.approx(scipy.stats.kurtosis(xd, fisher=True, bias=True), rel=1e-10, abs=1e-12)
+        assert st["mean"] == pytest.approx(xd.mean(), rel=1e-12, abs=1e-15)
+        assert st["std"] == pytest.approx(xd.std(), rel=1e-12)
+        assert st["max_abs"] == np.abs(xd).max()
+    # uniform on [-1, 1]: excess kurtosis -6/5
+    big = rnd.uniform(-1, 1, (1024, 1024)).astype(np.float32)
+    assert oracle.matrix_stats(big)["kurtosis"] == pytest.approx(-1.2, abs=0.01)
+
+
+def test_stats_relative_error_against_numpy_norm():
+    rnd = np.random.default_rng(52)
+    w = (rnd.standard_normal((96, 768)) * 0.02).astype(np.float32)
+    q, _ = oracle.quantize(w)
+    wh = oracle.dequantize(q, "f64")
+    ref = np.linalg.norm(w.astype(np.float64) - wh) / np.linalg.norm(w.astype(np.float64))
+    assert oracle.matrix_stats(w, q)["rel_error"] == pytest.approx(ref, rel=1e-12)
+    assert np.isnan(oracle.matrix_stats(w)["rel_error"])
+    # Gaussian weights sit in the page's band for NVFP4 (median 9.47 %, all matrices 6.3 .. 9.6 %)
+    assert 0.08 < oracle.matrix_stats(w, q)["rel_error"] < 0.11
+
+
+def test_stats_block_ratio_closed_forms():
+    # one spike per block of 64: mean x/64, std x sqrt(63)/64, so max/std = 64/sqrt(63)
+    x = np.zeros((4, 128), dtype=np.float32)
+    x[:, 5] = 3.0
+    x[:, 64 + 17] = -0.25
+    st = oracle.matrix_stats(x)
+    assert st["blocks"] == 8 and st["block_max_over_std"] == pytest.approx(64 / math.sqrt(63), rel=1e-14)
+    # alternating +-a: std a, max a
+    y = np.tile(np.array([0.5, -0.5], dtype=np.float32), (8, 96))
+    assert oracle.matrix_stats(y)["block_max_over_std"] == pytest.approx(1.0, rel=1e-15)
+    # constant blocks have std 0 and are left out; a shorter last block counts with its own length
+    z = np.full((3, 48), 2.0, dtype=np.float32)  # 144 elements: blocks of 64, 64, 16
+    z[2, 32] = 0.0                                # inside the last block (elements 128..143)
+    st = oracle.matrix_stats(z)
+    assert st["blocks"] == 1
+    assert st["block_max_over_std"] == pytest.approx(2.0 / (math.sqrt(15) / 16 * 2.0), rel=1e-14)
+    # Gaussian blocks of 64: the page reports 2.61 for its non-modulation matrices
+    g = np.random.default_rng(53).standard_normal((256, 1024)).astype(np.float32)
+    assert 2.5 < oracle.matrix_stats(g)["block_max_over_std"] < 2.8
