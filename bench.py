@@ -14,6 +14,7 @@ One step runs every operation of the path once, at the Qwen-Image attention-proj
 The FP8 side path is timed after the step, in a loop of its own over the same inputs ("next_ops"):
   act_quantize_fp8  A bf16 -> FP8 E4M3 tensorwise (dynamic amax)
   gemm_w4a8    C = A_fp8 . W_hat^T, FP8 activations
+  weight_stats quality statistics of W and its NVFP4 form (relative error, kurtosis, block max/std)
 Inputs are resident in HBM before timing; the step rotates over several input sets whose total
 size exceeds the 256 MB Infinity Cache, so repeated steps do not hit in cache.  Each operation is
 bracketed by events on the stream it runs on; the dominant kernel's roofline uses those times.
@@ -94,14 +95,17 @@ def main():
     qws4 = torch.empty_like(qws)
     a8 = nv.FP8Tensor.empty(M_TOK, K_IN, dev)
     c8 = torch.empty((M_TOK, N_OUT), dtype=torch.float32, device=dev)
+    st_out = torch.empty(8, dtype=torch.float64, device=dev)
+    st_ws = torch.empty(nv.workspace_size(nv.OP_STATS, 0, 0), dtype=torch.uint8, device=dev)
 
     ops = ["quantize", "requantize", "dequantize", "act_quantize", "gemm_w4a16", "gemm_w4a4", "gemv_w4a16",
            "percentile"]
-    next_ops = ["act_quantize_fp8", "gemm_w4a8"]
+    next_ops = ["act_quantize_fp8", "gemm_w4a8", "weight_stats"]
     # kernels each op launches (the roofline is reported for the longest single-kernel op); the
     # percentile at p99.9 over 4096 rows takes the one-pass top-M path (selection + merge)
     n_kernels = {"quantize": 1, "requantize": 1, "dequantize": 1, "act_quantize": 1, "gemm_w4a16": 1,
-                 "gemm_w4a4": 1, "gemv_w4a16": 1, "percentile": 2, "act_quantize_fp8": 1, "gemm_w4a8": 1}
+                 "gemm_w4a4": 1, "gemv_w4a16": 1, "percentile": 2, "act_quantize_fp8": 1, "gemm_w4a8": 1,
+                 "weight_stats": 2}
 
     def step(i, events=None):
         w, a, w8 = sets[i % nsets]
@@ -132,6 +136,8 @@ def main():
         if e: e[1].record()
         nv.gemm(a8, qw, out=c8)
         if e: e[2].record()
+        nv.matrix_stats(w, qw, out=st_out, workspace=st_ws)
+        if e: e[3].record()
 
     for i in range(args.warmup):
         step(i)
@@ -170,6 +176,7 @@ def main():
         "percentile": ("GB/s", nA * 2.0, HBM_PEAK_GBS),
         "act_quantize_fp8": ("GB/s", nA * 3.0 + 4, HBM_PEAK_GBS),
         "gemm_w4a8": ("TFLOP/s", 2.0 * M_TOK * N_OUT * K_IN, BF16_MFMA_PEAK_TFLOPS),
+        "weight_stats": ("GB/s", nW * 4.5625 + 4, HBM_PEAK_GBS),
     }
     op_report, next_report = {}, {}
     for op in ops + next_ops:

@@ -26,11 +26,11 @@ lib = ctypes.CDLL(LIB_PATH)
 # C ABI declarations
 # ------------------------------------------------------------------------------------------------
 NVFP4_F32, NVFP4_BF16, NVFP4_F16, NVFP4_E4M3 = 0, 1, 2, 3
-OP_QUANTIZE, OP_DEQUANTIZE, OP_GEMM, OP_PERCENTILE = 0, 1, 2, 3
+OP_QUANTIZE, OP_DEQUANTIZE, OP_GEMM, OP_PERCENTILE, OP_STATS = 0, 1, 2, 3, 4
 STATUS_NAMES = ["NVFP4_OK", "NVFP4_ERR_NULL", "NVFP4_ERR_SHAPE", "NVFP4_ERR_ALIGN", "NVFP4_ERR_DTYPE",
                 "NVFP4_ERR_WORKSPACE", "NVFP4_ERR_ARG", "NVFP4_ERR_DEVICE", "NVFP4_ERR_LAUNCH"]
 EXPORTED = ["nvfp4_quantize", "nvfp4_quantize_fp8", "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_gemm_fp8a",
-            "amax_percentile", "nvfp4_workspace_size", "nvfp4_status_string"]
+            "nvfp4_matrix_stats", "amax_percentile", "nvfp4_workspace_size", "nvfp4_status_string"]
 
 
 class CTensor(ctypes.Structure):
@@ -47,6 +47,8 @@ lib.nvfp4_quantize_fp8.argtypes = [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _
 lib.nvfp4_quantize_fp8.restype = _I32
 lib.nvfp4_gemm_fp8a.argtypes = [_P, _P, _I64, _I64, _PT, _P, _I64, _P, _SZ, _P]
 lib.nvfp4_gemm_fp8a.restype = _I32
+lib.nvfp4_matrix_stats.argtypes = [_P, _I32, _I64, _I64, _I64, _PT, _P, _P, _SZ, _P]
+lib.nvfp4_matrix_stats.restype = _I32
 lib.nvfp4_dequantize.argtypes = [_PT, _P, _I32, _I64, _P]
 lib.nvfp4_dequantize.restype = _I32
 lib.nvfp4_gemm.argtypes = [_P, _PT, _I64, _I64, _PT, _P, _I64, _P, _SZ, _P]
@@ -240,3 +242,30 @@ def amax_percentile(x: torch.Tensor, p: float = 99.9, per_channel: bool = True,
                              _ptr(pct), _ptr(mx), _ptr(flags), _ptr(ws), ws_bytes, _stream(x.device))
     _check(st, "amax_percentile")
     return pct, mx
+
+
+STAT_FIELDS = ("rel_error", "kurtosis", "block_max_over_std", "mean", "std", "max_abs", "blocks")
+
+
+def matrix_stats(w: torch.Tensor, q: NVFP4Tensor | None = None, out: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None):
+    """Quality statistics of a 2-D weight (fp32, bf16 or fp16) and, if given, of its NVFP4 form:
+    relative error, excess kurtosis, mean block-of-64 max|w| / std, mean, std, max |w|, blocks.
+    Returns a dict (synchronising), or, when out (float64, >= 7 elements, on the device) is given,
+    out itself with the fields in STAT_FIELDS order and no synchronisation."""
+    assert w.dim() == 2 and w.is_cuda
+    rows, cols = w.shape
+    ret = out
+    if out is None:
+        out = torch.empty(8, dtype=torch.float64, device=w.device)
+    assert out.dtype == torch.float64 and out.is_contiguous() and out.numel() >= 7
+    ws_bytes = workspace_size(OP_STATS, 0, 0)
+    ws = workspace if workspace is not None else _workspace(ws_bytes, w.device)
+    qc = q.c() if q is not None else None
+    st = lib.nvfp4_matrix_stats(_ptr(w), _DT[w.dtype], rows, cols, w.stride(0), ctypes.byref(qc) if qc else None,
+                                _ptr(out), _ptr(ws), ws.numel() if workspace is not None else ws_bytes,
+                                _stream(w.device))
+    _check(st, "nvfp4_matrix_stats")
+    if ret is not None:
+        return ret
+    return dict(zip(STAT_FIELDS, out[:7].cpu().tolist()))

@@ -112,6 +112,7 @@ size_t nvfp4_workspace_size(int op, int64_t rows, int64_t cols, int64_t k) {
     switch (op) {
     case NVFP4_OP_QUANTIZE: return kQuantizeWsBytes;
     case NVFP4_OP_PERCENTILE: return cols >= 0 ? percentile_ws_bytes(cols, k ? 1 : 0) : 0;
+    case NVFP4_OP_STATS: return stats_ws_bytes();
     case NVFP4_OP_GEMM: {
         // planned for the current device's CU count (256, an MI355X, when none can be queried)
         const int cus = current_device_cus();
@@ -223,6 +224,28 @@ nvfp4_status nvfp4_gemm_fp8a(const uint8_t *a_fp8, const float *a_scale, int64_t
     hipError_t e = (K == 0) ? launch_fill_zero_f32(c, M, N, ldc, stream)
                             : launch_gemm_fp8(a_fp8, a_scale, M, lda, w, c, ldc, workspace, workspace_bytes, cus,
                                               stream);
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+}
+
+nvfp4_status nvfp4_matrix_stats(const void *w, nvfp4_dtype w_dtype, int64_t rows, int64_t cols, int64_t ld_w,
+                                const nvfp4_tensor *q, double *out, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+    if (w_dtype != NVFP4_F32 && w_dtype != NVFP4_BF16 && w_dtype != NVFP4_F16) return NVFP4_ERR_DTYPE;
+    if (!out) return NVFP4_ERR_NULL;
+    nvfp4_status st = check_matrix(w, rows, cols, ld_w, elem_bytes(w_dtype));
+    if (st != NVFP4_OK) return st;
+    if (rows < 1 || cols < 1 || (cols % 16) != 0) return NVFP4_ERR_SHAPE;
+    if (q) {
+        st = check_qtensor(q);
+        if (st != NVFP4_OK) return st;
+        if (q->rows != rows || q->cols != cols) return NVFP4_ERR_SHAPE;
+    }
+    if ((reinterpret_cast<uintptr_t>(out) & 7u) != 0) return NVFP4_ERR_ALIGN;
+    if (!workspace || workspace_bytes < stats_ws_bytes()) return NVFP4_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return NVFP4_ERR_ALIGN;
+    const int cus = current_device_cus();
+    if (cus == 0) return NVFP4_ERR_DEVICE;
+    hipError_t e = launch_stats(w, w_dtype, rows, cols, ld_w, q, out, workspace, cus, stream);
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
 }
 

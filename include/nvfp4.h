@@ -70,7 +70,7 @@ typedef struct {
 } nvfp4_tensor;
 
 /* Operation selectors for nvfp4_workspace_size. */
-enum { NVFP4_OP_QUANTIZE = 0, NVFP4_OP_DEQUANTIZE = 1, NVFP4_OP_GEMM = 2, NVFP4_OP_PERCENTILE = 3 };
+enum { NVFP4_OP_QUANTIZE = 0, NVFP4_OP_DEQUANTIZE = 1, NVFP4_OP_GEMM = 2, NVFP4_OP_PERCENTILE = 3, NVFP4_OP_STATS = 4 };
 
 /*
  * nvfp4_quantize -- x [out->rows x out->cols] (row stride ld_x elements) -> NVFP4 `out`.
@@ -175,6 +175,25 @@ nvfp4_status nvfp4_gemm_fp8a(const uint8_t *a_fp8, const float *a_scale, int64_t
 nvfp4_status amax_percentile(const void *x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
                              double p, int per_channel, float *out_pct, float *out_max, int32_t *flags,
                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * nvfp4_matrix_stats -- quality statistics of one weight matrix w [rows x cols] (row stride ld_w
+ * elements) and, when q is not NULL, of its NVFP4 form q ("Qwen-Image NVFP4 on a 16 GB Ada GPU",
+ * section "Quality: the error of each matrix": the relative error of each matrix, its kurtosis,
+ * the ratio of the maximum to the standard deviation in blocks of 64).  Writes 7 doubles to out:
+ *   out[0] ||w - w_hat||_F / ||w||_F, w_hat the exact expansion of q (NaN when q is NULL);
+ *   out[1] excess kurtosis m4 / m2^2 - 3, population central moments (from power sums in double);
+ *   out[2] mean over blocks of 64 consecutive elements in row-major order (the last one may be
+ *          shorter) of max |w| / population std of the block, blocks with std 0 left out (NaN if
+ *          none);
+ *   out[3] mean; out[4] population std; out[5] max |w|; out[6] number of blocks in out[2].
+ * w_dtype: NVFP4_F32, NVFP4_BF16 or NVFP4_F16; cols % 16 == 0; q, when given, has w's shape.
+ * out (8-byte aligned) and workspace (nvfp4_workspace_size(NVFP4_OP_STATS, 0, 0, 0) bytes) are
+ * device pointers.  The sums are reduced in a fixed order, so results repeat exactly on one device.
+ */
+nvfp4_status nvfp4_matrix_stats(const void *w, nvfp4_dtype w_dtype, int64_t rows, int64_t cols, int64_t ld_w,
+                                const nvfp4_tensor *q, double *out, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
 
 /* Workspace bytes an entry point needs (0 when none).  For NVFP4_OP_PERCENTILE the last argument
  * is per_channel; for NVFP4_OP_GEMM the arguments are (M, N, K), and the size is planned for the

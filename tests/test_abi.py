@@ -25,8 +25,8 @@ def nv():
 
 def test_header_declares_the_entry_points():
     assert _declared_functions() == sorted(["nvfp4_quantize", "nvfp4_quantize_fp8", "nvfp4_dequantize", "nvfp4_gemm",
-                                            "nvfp4_gemm_fp8a", "amax_percentile", "nvfp4_workspace_size",
-                                            "nvfp4_status_string"])
+                                            "nvfp4_gemm_fp8a", "nvfp4_matrix_stats", "amax_percentile",
+                                            "nvfp4_workspace_size", "nvfp4_status_string"])
 
 
 def test_library_exports_every_declared_symbol(nv):
@@ -142,6 +142,24 @@ def test_gemm_fp8a_validation(nv):
     assert g(P(FAKE), P(FAKE + 2), 8, 128, ctypes.byref(w), P(FAKE), 64, None, 0, None) == 3  # scale align
     assert g(P(FAKE), P(FAKE), 8, 128, ctypes.byref(w), P(FAKE), 32, None, 0, None) == 2  # ldc < N
     assert g(P(FAKE), P(FAKE), 8, 128, ctypes.byref(w), None, 64, None, 0, None) == 1  # NULL C
+
+
+def test_matrix_stats_validation(nv):
+    f = nv.lib.nvfp4_matrix_stats
+    P = ctypes.c_void_p
+    ws = nv.workspace_size(nv.OP_STATS, 0, 0)
+    assert ws > 0
+    q = _qt(nv, 4, 32)
+    assert f(P(FAKE), 3, 4, 32, 32, None, P(FAKE), P(FAKE), ws, None) == 4  # e4m3 input
+    assert f(P(FAKE), 0, 4, 32, 32, None, None, P(FAKE), ws, None) == 1  # NULL out
+    assert f(None, 0, 4, 32, 32, None, P(FAKE), P(FAKE), ws, None) == 1  # NULL w
+    assert f(P(FAKE), 0, 4, 24, 24, None, P(FAKE), P(FAKE), ws, None) == 2  # cols % 16
+    assert f(P(FAKE), 0, 0, 32, 32, None, P(FAKE), P(FAKE), ws, None) == 2  # no rows
+    bad = _qt(nv, 5, 32)
+    assert f(P(FAKE), 0, 4, 32, 32, ctypes.byref(bad), P(FAKE), P(FAKE), ws, None) == 2  # q shape
+    assert f(P(FAKE), 0, 4, 32, 32, ctypes.byref(q), P(FAKE + 4), P(FAKE), ws, None) == 3  # out align
+    assert f(P(FAKE), 0, 4, 32, 32, ctypes.byref(q), P(FAKE), P(FAKE), ws - 1, None) == 5  # workspace
+    assert f(P(FAKE), 0, 4, 32, 32, ctypes.byref(q), P(FAKE), None, ws, None) == 5
 
 
 def test_percentile_validation(nv):

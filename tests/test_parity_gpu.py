@@ -571,3 +571,102 @@ def test_gemm_fp8a_split_k_and_full(nv):
     c = nv.gemm(a8, q).cpu().numpy()[rows]
     cref = oracle.gemm_f64(oracle.fp8_values(rb[rows], rs), oracle.dequantize(ref, "f64"))
     assert oracle.gemm_error(c, cref) <= GEMM_TOL
+
+
+# ------------------------------------------------------------------------------------------------
+# per-matrix quality statistics
+# ------------------------------------------------------------------------------------------------
+# Both sides sum in double, in different orders; the oracle's sequential sums over n <= 6e7 terms
+# carry a relative error below n * 2^-53 < 1e-8, the kernel's tree sums far less.  The moments
+# behind the kurtosis are formed about the first element on the GPU and about the mean in the
+# oracle; for the inputs here the extra cancellation is a few units in the last place.  Maximum
+# and block count are exact; the ratio of a constant block is left out on both sides exactly.
+STAT_RTOL = 1e-8
+
+
+def _dev_q(nv, ref):
+    return nv.NVFP4Tensor(to_dev_u8(ref.codes), to_dev_u8(ref.scales),
+                          torch.tensor([ref.g], dtype=torch.float32, device=DEV))
+
+
+def _assert_stats(got, ref, what=""):
+    for k in ("max_abs", "blocks"):
+        assert got[k] == ref[k] or (math.isnan(got[k]) and math.isnan(ref[k])), f"{what} {k} {got[k]} vs {ref[k]}"
+    for k in ("rel_error", "block_max_over_std", "std"):
+        a, b = got[k], ref[k]
+        if math.isnan(b):
+            assert math.isnan(a), f"{what} {k} {a} vs NaN"
+        else:
+            assert abs(a - b) <= STAT_RTOL * abs(b), f"{what} {k} {a!r} vs {b!r}"
+    a, b = got["kurtosis"] + 3.0, ref["kurtosis"] + 3.0
+    if math.isnan(b):
+        assert math.isnan(a), f"{what} kurtosis {a} vs NaN"
+    else:
+        assert abs(a - b) <= STAT_RTOL * abs(b), f"{what} kurtosis {got['kurtosis']!r} vs {ref['kurtosis']!r}"
+    scale = abs(ref["mean"]) + ref["std"]
+    assert abs(got["mean"] - ref["mean"]) <= STAT_RTOL * scale, f"{what} mean {got['mean']!r} vs {ref['mean']!r}"
+
+
+def _stats_case(nv, x, dtype, with_q=True, pad=0):
+    """x: fp32 values; returns (device tensor in dtype, oracle source array, oracle dtype code)."""
+    if dtype == "f32":
+        src, code, dev = x, oracle.F32, to_dev_f32(x)
+    elif dtype == "bf16":
+        src = synth.bf16_bits(x)
+        code, dev = oracle.BF16, to_dev_bf16(src)
+    else:
+        src = x.astype(np.float16).view(np.uint16)
+        code, dev = oracle.F16, to_dev_f16(src)
+    if pad:
+        dev = padded(dev, pad)
+    ref_q = oracle.quantize(src, code)[0] if with_q else None
+    ref = oracle.matrix_stats(src, ref_q, code)
+    got = nv.matrix_stats(dev, _dev_q(nv, ref_q) if with_q else None)
+    return got, ref
+
+
+@pytest.mark.parametrize("shape", [(1, 16), (3, 48), (65, 1040), (300, 272), (129, 2048), (1000, 3072)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_matrix_stats_shapes_dtypes(nv, shape, dtype):
+    _note(f"matrix stats {dtype} {shape}")
+    g = synth.rng(shape[0] * 7 + shape[1])
+    x = (g.standard_t(4, size=shape) * 0.02).astype(np.float32)
+    got, ref = _stats_case(nv, x, dtype)
+    _assert_stats(got, ref, f"{dtype} {shape}")
+    got, ref = _stats_case(nv, x, dtype, with_q=False, pad=16)
+    assert math.isnan(got["rel_error"]) and math.isnan(ref["rel_error"])
+    _assert_stats(got, ref, f"{dtype} {shape} no q, strided")
+
+
+def test_matrix_stats_offset_constant_blocks_and_degenerate(nv):
+    _note("matrix stats: offset mean, constant blocks, constant matrix")
+    g = synth.rng(77)
+    # mean far from 0 relative to the spread (a norm-gain-like vector), and zero rows
+    x = (1.0 + 0.01 * g.standard_normal((257, 320))).astype(np.float32)
+    x[5] = 0.0
+    x[100:103] = 0.25
+    for dt in ("f32", "bf16"):
+        got, ref = _stats_case(nv, x, dt)
+        assert ref["blocks"] < 257 * 320 / 64
+        _assert_stats(got, ref, f"offset {dt}")
+    # a matrix whose first element is an outlier: the shift is far from the mean
+    y = (g.standard_normal((64, 512)) * 0.02).astype(np.float32)
+    y[0, 0] = 40.0
+    got, ref = _stats_case(nv, y, "f32")
+    _assert_stats(got, ref, "outlier first")
+    # constant matrix: no block counts, the moments are 0/0
+    z = np.full((8, 64), 0.5, dtype=np.float32)
+    got, ref = _stats_case(nv, z, "f32")
+    assert got["blocks"] == 0 and math.isnan(got["block_max_over_std"]) and math.isnan(got["kurtosis"])
+    _assert_stats(got, ref, "constant")
+    assert got["mean"] == 0.5 and got["std"] == 0.0
+
+
+def test_matrix_stats_full_sizes(nv):
+    _note("matrix stats: 18432x3072 bf16 modulation weight, 3072x3072 fp32 attention weight")
+    w = synth.modulation_weight()
+    got, ref = _stats_case(nv, w, "bf16")
+    _assert_stats(got, ref, "modulation bf16")
+    w = synth.attn_proj_weight()
+    got, ref = _stats_case(nv, w, "f32")
+    _assert_stats(got, ref, "attention f32")
