@@ -235,6 +235,7 @@ nvfp4_status nvfp4_matrix_stats(const void *w, nvfp4_dtype w_dtype, int64_t rows
     nvfp4_status st = check_matrix(w, rows, cols, ld_w, elem_bytes(w_dtype));
     if (st != NVFP4_OK) return st;
     if (rows < 1 || cols < 1 || (cols % 16) != 0) return NVFP4_ERR_SHAPE;
+    if (rows > 1 && ld_w != cols && cols > (int64_t(1) << 30)) return NVFP4_ERR_SHAPE;  // 32-bit column split
     if (q) {
         st = check_qtensor(q);
         if (st != NVFP4_OK) return st;

@@ -52,7 +52,7 @@ hipError_t launch_percentile(const void *x, nvfp4_dtype dt, int64_t rows, int64_
                              int num_cus, hipStream_t stream);
 
 // Matrix statistics: partial sums of at most kStatsMaxGroups workgroups in the workspace.
-constexpr int kStatsMaxGroups = 1024;
+constexpr int kStatsMaxGroups = 2048;
 size_t stats_ws_bytes();
 hipError_t launch_stats(const void *x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld_x,
                         const nvfp4_tensor *q, double *out, void *workspace, int num_cus, hipStream_t stream);

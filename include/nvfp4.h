@@ -187,7 +187,8 @@ nvfp4_status amax_percentile(const void *x, nvfp4_dtype x_dtype, int64_t rows, i
  *          shorter) of max |w| / population std of the block, blocks with std 0 left out (NaN if
  *          none);
  *   out[3] mean; out[4] population std; out[5] max |w|; out[6] number of blocks in out[2].
- * w_dtype: NVFP4_F32, NVFP4_BF16 or NVFP4_F16; cols % 16 == 0; q, when given, has w's shape.
+ * w_dtype: NVFP4_F32, NVFP4_BF16 or NVFP4_F16; cols % 16 == 0 (and cols <= 2^30 when the rows are
+ * not contiguous, ld_w != cols); q, when given, has w's shape.
  * out (8-byte aligned) and workspace (nvfp4_workspace_size(NVFP4_OP_STATS, 0, 0, 0) bytes) are
  * device pointers.  The sums are reduced in a fixed order, so results repeat exactly on one device.
  */
