@@ -9,7 +9,9 @@ this module only marshals numpy arrays into it.  The GEMM reference is the plain
 C = A_hat . W_hat^T evaluated in float64 with numpy's matmul over the exactly expanded operands
 ("Qwen-Image NVFP4 on a 16 GB Ada GPU", section "Running the NVFP4 weights on Ada": the weights are
 expanded before each multiply; activations are bf16, or NVFP4 for the W4A4 form named in section
-"What NVFP4 is and how it differs from NF4").
+"What NVFP4 is and how it differs from NF4").  With a low-rank branch (reading R10: "Qwen Image 2.1:
+INT4 + FP4", "What I quantized", FP4 weights with BF16 rank-128 branches) the same plain definition
+gains the term (A . V^T) . U^T, also in float64.
 """
 from __future__ import annotations
 
@@ -246,6 +248,20 @@ def gemm_w4a8(a_fp8: np.ndarray, a_scale: float, w: QTensor) -> np.ndarray:
     hardware": FP4 weight times dynamically quantized FP8 activation): both operands expanded
     exactly, contraction in float64."""
     return gemm_f64(fp8_values(a_fp8, a_scale), dequantize(w, "f64"))
+
+
+def gemm_lowrank(a_bits: np.ndarray, w: QTensor, v_bits: np.ndarray, u_bits: np.ndarray,
+                 a_q: QTensor | None = None) -> np.ndarray:
+    """Reference for the NVFP4 GEMM with a bf16 low-rank branch ("Qwen Image 2.1: INT4 + FP4",
+    "What I quantized": FP4 weights with BF16 rank-128 branches; reading R10): the weight is
+    W ~ W_hat + U . V with U [N x r] and V [r x K] kept in bf16, and the layer computes
+    C = A_hat . W_hat^T + (A . V^T) . U^T.  The branch takes the bf16 activations A (uint16 bits);
+    the main product takes A itself (W4A16) or its NVFP4 form a_q (W4A4).  Every product and sum in
+    float64 over the exact operand values."""
+    a = bf16_bits_to_f64(a_bits)
+    main = gemm_f64(dequantize(a_q, "f64") if a_q is not None else a, dequantize(w, "f64"))
+    t = gemm_f64(a, bf16_bits_to_f64(v_bits))  # T = A . V^T, [M x r]
+    return main + gemm_f64(t, bf16_bits_to_f64(u_bits))
 
 
 def gemm_error(c: np.ndarray, cref: np.ndarray) -> float:

@@ -47,6 +47,9 @@
  *       activations): scale = fl(amax / 448), 448 the largest E4M3, and 1 when amax = 0;
  *       byte = sign bit of v | E4M3 nearest (ties to even, saturating at 448) of fl(|v| / scale).
  *       Dequantized value = e4m3(byte) x scale.
+ *   R10 low-rank branch ("Qwen Image 2.1: INT4 + FP4", "What I quantized": FP4 weights with BF16
+ *       rank-128 branches): C = A_hat . W_hat^T + (A . V^T) . U^T with U [N x r], V [r x K] bf16
+ *       and the branch on the bf16 activations.  Plain float64 matrix products (Python side).
  *
  * Arithmetic precision: every fp32 step above is carried out in IEEE binary32 (the pages fix
  * an FP32 global scale, so the decisions that pick codes are taken in fp32).  Grid rounding is

@@ -335,6 +335,60 @@ def test_gemm_definition_brute_force_and_zero_weight():
     assert not oracle.gemm_w4a16(a_bits, qz).any()
 
 
+def _lowrank_case(m, n, k, r, seed):
+    rnd = np.random.default_rng(seed)
+    a_bits = oracle.f32_to_bf16_bits(rnd.standard_normal((m, k)).astype(np.float32))
+    q, _ = oracle.quantize((rnd.standard_normal((n, k)) * 0.02).astype(np.float32))
+    v_bits = oracle.f32_to_bf16_bits((rnd.standard_normal((r, k)) * 0.05).astype(np.float32))
+    u_bits = oracle.f32_to_bf16_bits((rnd.standard_normal((n, r)) * 0.05).astype(np.float32))
+    return a_bits, q, v_bits, u_bits
+
+
+def test_gemm_lowrank_brute_force_and_zero_branch():
+    a_bits, q, v_bits, u_bits = _lowrank_case(3, 5, 32, 4, 41)
+    c = oracle.gemm_lowrank(a_bits, q, v_bits, u_bits)
+    a = oracle.widen(a_bits, oracle.BF16).astype(np.float64)
+    w = oracle.dequantize(q, "f64")
+    v = oracle.widen(v_bits, oracle.BF16).astype(np.float64)
+    u = oracle.widen(u_bits, oracle.BF16).astype(np.float64)
+    for i in range(3):
+        for j in range(5):
+            main = math.fsum(a[i, kk] * w[j, kk] for kk in range(32))
+            branch = math.fsum(math.fsum(a[i, kk] * v[t, kk] for kk in range(32)) * u[j, t] for t in range(4))
+            assert c[i, j] == pytest.approx(main + branch, rel=1e-13, abs=1e-15)
+    # a zero branch leaves the plain W4A16 product, bit for bit
+    zv = np.zeros_like(v_bits)
+    assert np.array_equal(oracle.gemm_lowrank(a_bits, q, zv, u_bits), oracle.gemm_w4a16(a_bits, q))
+
+
+def test_gemm_lowrank_equals_product_with_the_rank_r_matrix():
+    # (A . V^T) . U^T = A . (U . V)^T: the branch as one product with the dense rank-r matrix U . V
+    a_bits, q, v_bits, u_bits = _lowrank_case(17, 40, 96, 16, 42)
+    a = oracle.widen(a_bits, oracle.BF16).astype(np.float64)
+    lr = oracle.widen(u_bits, oracle.BF16).astype(np.float64) @ oracle.widen(v_bits, oracle.BF16).astype(np.float64)
+    want = oracle.gemm_w4a16(a_bits, q) + np.einsum("mk,nk->mn", a, lr)
+    got = oracle.gemm_lowrank(a_bits, q, v_bits, u_bits)
+    assert np.max(np.abs(got - want)) <= 1e-12 * np.max(np.abs(want))
+    # one-hot: A = e_0, V = e_3 (row 0), U = e_7 (column 0) adds exactly 1 to C[0, 7]
+    a1 = np.zeros((1, 96), dtype=np.uint16)
+    a1[0, 3] = 0x3F80  # bf16 1.0
+    v1 = np.zeros((16, 96), dtype=np.uint16)
+    v1[0, 3] = 0x3F80
+    u1 = np.zeros((40, 16), dtype=np.uint16)
+    u1[7, 0] = 0x3F80
+    d = oracle.gemm_lowrank(a1, q, v1, u1) - oracle.gemm_w4a16(a1, q)
+    assert d[0, 7] == 1.0 and np.count_nonzero(d) == 1
+
+
+def test_gemm_lowrank_w4a4_main_product_uses_quantized_activations():
+    a_bits, q, v_bits, u_bits = _lowrank_case(6, 24, 64, 16, 43)
+    qa, _ = oracle.quantize(a_bits, oracle.BF16)
+    got = oracle.gemm_lowrank(a_bits, q, v_bits, u_bits, a_q=qa)
+    branch = oracle.gemm_lowrank(a_bits, q, v_bits, u_bits) - oracle.gemm_w4a16(a_bits, q)
+    want = oracle.gemm_w4a4(qa, q) + branch
+    assert np.max(np.abs(got - want)) <= 1e-13 * np.max(np.abs(want))
+
+
 def test_gemm_error_metric_floor():
     cref = np.array([[1.0, -1.0, 1e-9]])
     c = cref + np.array([[1e-4, 0, 5e-6]])
