@@ -26,11 +26,11 @@ lib = ctypes.CDLL(LIB_PATH)
 # C ABI declarations
 # ------------------------------------------------------------------------------------------------
 NVFP4_F32, NVFP4_BF16, NVFP4_F16, NVFP4_E4M3 = 0, 1, 2, 3
-OP_QUANTIZE, OP_DEQUANTIZE, OP_GEMM, OP_PERCENTILE, OP_STATS = 0, 1, 2, 3, 4
+OP_QUANTIZE, OP_DEQUANTIZE, OP_GEMM, OP_PERCENTILE, OP_STATS, OP_LOWRANK = 0, 1, 2, 3, 4, 5
 STATUS_NAMES = ["NVFP4_OK", "NVFP4_ERR_NULL", "NVFP4_ERR_SHAPE", "NVFP4_ERR_ALIGN", "NVFP4_ERR_DTYPE",
                 "NVFP4_ERR_WORKSPACE", "NVFP4_ERR_ARG", "NVFP4_ERR_DEVICE", "NVFP4_ERR_LAUNCH"]
 EXPORTED = ["nvfp4_quantize", "nvfp4_quantize_fp8", "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_gemm_fp8a",
-            "nvfp4_matrix_stats", "amax_percentile", "nvfp4_workspace_size", "nvfp4_status_string"]
+            "nvfp4_matrix_stats", "nvfp4_gemm_lowrank", "amax_percentile", "nvfp4_workspace_size", "nvfp4_status_string"]
 
 
 class CTensor(ctypes.Structure):
@@ -52,6 +52,8 @@ lib.nvfp4_matrix_stats.restype = _I32
 lib.nvfp4_dequantize.argtypes = [_PT, _P, _I32, _I64, _P]
 lib.nvfp4_dequantize.restype = _I32
 lib.nvfp4_gemm.argtypes = [_P, _PT, _I64, _I64, _PT, _P, _I64, _P, _SZ, _P]
+lib.nvfp4_gemm_lowrank.argtypes = [_P, _PT, _I64, _I64, _PT, _P, _P, _I64, _P, _I64, _P, _SZ, _P]
+lib.nvfp4_gemm_lowrank.restype = _I32
 lib.nvfp4_gemm.restype = _I32
 lib.amax_percentile.argtypes = [_P, _I32, _I64, _I64, _I64, _D, _I32, _P, _P, _P, _P, _SZ, _P]
 lib.amax_percentile.restype = _I32
@@ -225,6 +227,31 @@ def gemm(a: torch.Tensor | NVFP4Tensor | FP8Tensor, w: NVFP4Tensor, out: torch.T
     st = lib.nvfp4_gemm(a_ptr, a_ct, m, lda, ctypes.byref(wct), _ptr(out), out.stride(0) if m > 0 else n, _ptr(ws),
                         ws_bytes, _stream(device))
     _check(st, "nvfp4_gemm")
+    return out
+
+
+def gemm_lowrank(a: torch.Tensor, w: NVFP4Tensor, lr_down: torch.Tensor, lr_up: torch.Tensor,
+                 a_q: NVFP4Tensor | None = None, out: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """C [M, N] fp32 = A_hat . W_hat^T + (A . V^T) . U^T: the NVFP4 product plus a bf16 low-rank branch
+    of the weight.  `a` bf16 [M, K] (the branch's activations, and the main product's unless `a_q`, an
+    NVFP4Tensor [M, K], is given); lr_down V bf16 [r, K], lr_up U bf16 [N, r], both contiguous."""
+    n, k = w.shape
+    device = w.codes.device
+    assert a.dtype == torch.bfloat16 and a.dim() == 2 and a.shape[1] == k
+    assert lr_down.dtype == torch.bfloat16 and lr_up.dtype == torch.bfloat16
+    assert lr_down.is_contiguous() and lr_up.is_contiguous()
+    m, rank = a.shape[0], lr_down.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=device)
+    ws_bytes = workspace_size(OP_LOWRANK, m, n, k)
+    ws = workspace if workspace is not None else _workspace(ws_bytes, device)
+    wct = w.c()
+    a_ct = ctypes.byref(a_q.c()) if a_q is not None else None
+    st = lib.nvfp4_gemm_lowrank(_ptr(a), a_ct, m, a.stride(0) if m > 0 else k, ctypes.byref(wct), _ptr(lr_down),
+                                _ptr(lr_up), rank, _ptr(out), out.stride(0) if m > 0 else n, _ptr(ws),
+                                ws.numel() if workspace is not None else ws_bytes, _stream(device))
+    _check(st, "nvfp4_gemm_lowrank")
     return out
 
 

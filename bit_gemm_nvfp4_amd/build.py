@@ -26,7 +26,7 @@ FLAGS = [
     "-Wall", "-Wno-unused-result",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
-SOURCES = ["api.hip", "quantize.hip", "dequantize.hip", "gemm.hip", "percentile.hip", "stats.hip"]
+SOURCES = ["api.hip", "quantize.hip", "dequantize.hip", "gemm.hip", "percentile.hip", "stats.hip", "lowrank.hip"]
 
 
 def _compile(src: str) -> str:

@@ -113,6 +113,11 @@ size_t nvfp4_workspace_size(int op, int64_t rows, int64_t cols, int64_t k) {
     case NVFP4_OP_QUANTIZE: return kQuantizeWsBytes;
     case NVFP4_OP_PERCENTILE: return cols >= 0 ? percentile_ws_bytes(cols, k ? 1 : 0) : 0;
     case NVFP4_OP_STATS: return stats_ws_bytes();
+    case NVFP4_OP_LOWRANK: {
+        if (rows < 0 || cols < 0 || k < 0) return 0;
+        const int cus = current_device_cus();
+        return lowrank_t_bytes(rows) + gemm_ws_bytes(rows, cols, k, cus > 0 ? cus : 256);
+    }
     case NVFP4_OP_GEMM: {
         // planned for the current device's CU count (256, an MI355X, when none can be queried)
         const int cus = current_device_cus();
@@ -202,6 +207,39 @@ nvfp4_status nvfp4_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, 
     if (cus == 0) return NVFP4_ERR_DEVICE;
     hipError_t e = (K == 0) ? launch_fill_zero_f32(c, M, N, ldc, stream)
                             : launch_gemm(a_bf16, a_q, M, lda, w, c, ldc, workspace, workspace_bytes, cus, stream);
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+}
+
+nvfp4_status nvfp4_gemm_lowrank(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, int64_t lda,
+                                const nvfp4_tensor *w, const void *lr_down, const void *lr_up, int64_t rank, float *c,
+                                int64_t ldc, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    nvfp4_status st = check_qtensor(w);
+    if (st != NVFP4_OK) return st;
+    const int64_t N = w->rows, K = w->cols;
+    if (M < 0) return NVFP4_ERR_SHAPE;
+    if (rank < 16 || rank > 256 || rank % 16 != 0) return NVFP4_ERR_SHAPE;
+    if (!a_bf16 && M > 0) return NVFP4_ERR_NULL;  // the branch always takes the bf16 activations
+    st = check_matrix(a_bf16, M, K, lda, 2);
+    if (st != NVFP4_OK) return st;
+    if (a_q) {
+        st = check_qtensor(a_q);
+        if (st != NVFP4_OK) return st;
+        if (a_q->rows != M || a_q->cols != K) return NVFP4_ERR_SHAPE;
+    }
+    if (!lr_down || !lr_up) return NVFP4_ERR_NULL;
+    st = check_matrix(lr_down, rank, K, K, 2);
+    if (st != NVFP4_OK) return st;
+    st = check_matrix(lr_up, N, rank, rank, 2);
+    if (st != NVFP4_OK) return st;
+    st = check_matrix(c, M, N, ldc, 4, 4);
+    if (st != NVFP4_OK) return st;
+    if (!workspace || workspace_bytes < lowrank_t_bytes(M)) return NVFP4_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return NVFP4_ERR_ALIGN;
+    const int cus = current_device_cus();
+    if (cus == 0) return NVFP4_ERR_DEVICE;
+    hipError_t e = (K == 0) ? launch_fill_zero_f32(c, M, N, ldc, stream)
+                            : launch_gemm_lowrank(a_bf16, a_q, M, lda, w, lr_down, lr_up, (int)rank, c, ldc,
+                                                  workspace, workspace_bytes, cus, stream);
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
 }
 

@@ -44,6 +44,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "lowrank.h"
 
 namespace nvfp4 {
 
@@ -391,7 +392,7 @@ __device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, void *ld
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
 }
 
-template <int BM, int BN, int WM, int WN, int AM>
+template <int BM, int BN, int WM, int WN, int AM, bool LR = false>
 __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restrict__ A, int64_t lda,
                                                           const uint8_t *__restrict__ a_codes,
                                                           const uint8_t *__restrict__ a_scales,
@@ -400,7 +401,7 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
                                                           const uint8_t *__restrict__ w_scales,
                                                           const float *__restrict__ w_g, float *__restrict__ C,
                                                           int64_t ldc, int64_t M, int64_t N, int64_t K,
-                                                          int slice_steps) {
+                                                          int slice_steps, LrArgs lr) {
     // A_X: activations expanded from registers into LDS as f16 (NVFP4 codes, or E4M3 bytes), with W
     // expanded to f16 too; otherwise bf16 activations are copied straight into LDS.
     constexpr bool A_Q = AM == kAmNvfp4, A_F8 = AM == kAmFp8, A_X = AM != kAmBf16;
@@ -679,6 +680,33 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
     const float gw = partial ? 1.0f : *w_g;
     const float ga = (A_X && !partial) ? *a_g : 1.0f;
     float *Cs = C + (int64_t)blockIdx.y * M * ldc;
+    if constexpr (LR) {
+        // low-rank branch (unsplit products only): scale the sums first, with the same roundings as
+        // the store below, then add T . U^T on the matrix cores and store
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int j = 0; j < TN; j++)
+#pragma unroll
+                for (int e = 0; e < 16; e++) {
+                    float v = acc[i][j][e];
+                    if (A_X) v = v * ga;
+                    acc[i][j][e] = v * gw;
+                }
+        lr_branch<TM, TN>(acc, lr, M, N, m0 + wm * WTM, n0 + wn * WTN, lane);
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int j = 0; j < TN; j++) {
+                const int64_t col = n0 + wn * WTN + j * 32 + (lane % 32);
+#pragma unroll
+                for (int e = 0; e < 16; e++) {
+                    const int64_t row = m0 + wm * WTM + i * 32 + 8 * (e / 4) + 4 * (lane / 32) + (e % 4);
+                    if (row < M && col < N) C[row * ldc + col] = acc[i][j][e];
+                }
+            }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < TM; i++) {
 #pragma unroll
@@ -1033,9 +1061,10 @@ struct GemmA {
     int64_t lda;
 };
 
+// Returns true when the low-rank branch `lr` (if any) was added in the epilogue.
 template <int BM, int BN, int WM, int WN, int AM>
-static void launch_tile(const GemmA &a, int64_t M, const nvfp4_tensor *w, float *c, int64_t ldc,
-                        const GemmPlan &plan, float *partials, hipStream_t stream) {
+static bool launch_tile(const GemmA &a, int64_t M, const nvfp4_tensor *w, float *c, int64_t ldc,
+                        const GemmPlan &plan, float *partials, const LrArgs *lr, hipStream_t stream) {
     const int64_t N = w->rows, K = w->cols;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int64_t lda = a.lda;
@@ -1048,26 +1077,35 @@ static void launch_tile(const GemmA &a, int64_t M, const nvfp4_tensor *w, float 
             // K slices into their own planes of the workspace, then the ordered sum and scaling
             hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, AM>), dim3((unsigned)tiles, (unsigned)plan.splits),
                                dim3(64 * WM * WN), 0, stream, (const __bf16 *)a.bf16, lda, a.codes, a.scales, a.g,
-                               w->codes, w->scales, nullptr, partials, N, M, N, K, plan.slice_steps);
+                               w->codes, w->scales, nullptr, partials, N, M, N, K, plan.slice_steps, LrArgs{});
             const int64_t total = M * N;
             const int64_t blocks = (total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536;
             hipLaunchKernelGGL((k_splitk_reduce<AM != kAmBf16>), dim3((unsigned)blocks), dim3(256), 0, stream,
                                partials, plan.splits, M, N, N, a.g, w->global_scale, c, ldc);
-            return;
+            return false;
+        }
+        if (lr) {
+            if constexpr (AM != kAmFp8) {
+                hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, AM, true>), dim3((unsigned)tiles), dim3(64 * WM * WN),
+                                   0, stream, (const __bf16 *)a.bf16, lda, a.codes, a.scales, a.g, w->codes,
+                                   w->scales, w->global_scale, c, ldc, M, N, K, (int)(K / kBK), *lr);
+                return true;
+            }
         }
         hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, AM>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0, stream,
                            (const __bf16 *)a.bf16, lda, a.codes, a.scales, a.g, w->codes, w->scales,
-                           w->global_scale, c, ldc, M, N, K, (int)(K / kBK));
+                           w->global_scale, c, ldc, M, N, K, (int)(K / kBK), LrArgs{});
     } else {
         hipLaunchKernelGGL((k_gemm_tile<BM, BN, WM, WN, AM>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0, stream,
                            (const __bf16 *)a.bf16, lda, a.codes, a.scales, a.g, w->codes, w->scales,
                            w->global_scale, c, ldc, M, N, K);
     }
+    return false;
 }
 
 template <int AM>
-static void launch_tiled(const GemmA &a, int64_t M, const nvfp4_tensor *w, float *c, int64_t ldc, void *workspace,
-                         size_t workspace_bytes, int num_cus, hipStream_t stream) {
+static bool launch_tiled(const GemmA &a, int64_t M, const nvfp4_tensor *w, float *c, int64_t ldc, void *workspace,
+                         size_t workspace_bytes, int num_cus, hipStream_t stream, const LrArgs *lr = nullptr) {
     GemmPlan plan = plan_gemm(M, w->rows, w->cols, num_cus);
     float *partials = nullptr;
     if (plan.splits > 1) {
@@ -1078,10 +1116,10 @@ static void launch_tiled(const GemmA &a, int64_t M, const nvfp4_tensor *w, float
             plan = GemmPlan{plan.cfg, 1, (int)(w->cols / kBK)};
     }
     switch (plan.cfg) {
-    case 0: launch_tile<256, 256, 4, 2, AM>(a, M, w, c, ldc, plan, partials, stream); break;
-    case 1: launch_tile<256, 192, 4, 2, AM>(a, M, w, c, ldc, plan, partials, stream); break;
-    case 2: launch_tile<128, 256, 2, 4, AM>(a, M, w, c, ldc, plan, partials, stream); break;
-    default: launch_tile<128, 128, 2, 2, AM>(a, M, w, c, ldc, plan, partials, stream); break;
+    case 0: return launch_tile<256, 256, 4, 2, AM>(a, M, w, c, ldc, plan, partials, lr, stream);
+    case 1: return launch_tile<256, 192, 4, 2, AM>(a, M, w, c, ldc, plan, partials, lr, stream);
+    case 2: return launch_tile<128, 256, 2, 4, AM>(a, M, w, c, ldc, plan, partials, lr, stream);
+    default: return launch_tile<128, 128, 2, 2, AM>(a, M, w, c, ldc, plan, partials, lr, stream);
     }
 }
 
@@ -1102,6 +1140,34 @@ hipError_t launch_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, i
         const GemmA a{a_bf16, nullptr, nullptr, nullptr, lda};
         launch_tiled<kAmBf16>(a, M, w, c, ldc, workspace, workspace_bytes, num_cus, stream);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_lowrank(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, int64_t lda,
+                               const nvfp4_tensor *w, const void *v, const void *u, int r, float *c, int64_t ldc,
+                               void *workspace, size_t workspace_bytes, int num_cus, hipStream_t stream) {
+    const int64_t N = w->rows, K = w->cols;
+    if (M == 0 || N == 0) return hipGetLastError();
+    // T_hi, T_lo at the front of the workspace; the rest holds the product's split-K planes
+    const size_t tb = lowrank_t_bytes(M);
+    uint8_t *ws = reinterpret_cast<uint8_t *>(workspace);
+    hipError_t e = launch_lowrank_down(a_bf16, lda, v, M, K, r, ws, stream);
+    if (e != hipSuccess) return e;
+    const LrArgs lr{reinterpret_cast<const __bf16 *>(ws), reinterpret_cast<const __bf16 *>(u), r};
+    bool fused = false;
+    if (K == 0) {
+        launch_fill_zero_f32(c, M, N, ldc, stream);
+    } else if (gemv_applies(M, K)) {
+        if (a_q) launch_gemv<true>(M, a_bf16, lda, a_q, w, c, ldc, num_cus, stream);
+        else launch_gemv<false>(M, a_bf16, lda, a_q, w, c, ldc, num_cus, stream);
+    } else if (a_q) {
+        const GemmA a{nullptr, a_q->codes, a_q->scales, a_q->global_scale, K};
+        fused = launch_tiled<kAmNvfp4>(a, M, w, c, ldc, ws + tb, workspace_bytes - tb, num_cus, stream, &lr);
+    } else {
+        const GemmA a{a_bf16, nullptr, nullptr, nullptr, lda};
+        fused = launch_tiled<kAmBf16>(a, M, w, c, ldc, ws + tb, workspace_bytes - tb, num_cus, stream, &lr);
+    }
+    if (!fused) return launch_lowrank_up_add(ws, u, r, M, N, c, ldc, stream);
     return hipGetLastError();
 }
 

@@ -45,6 +45,18 @@ hipError_t launch_gemm_fp8(const uint8_t *a_fp8, const float *a_scale, int64_t M
                            float *c, int64_t ldc, void *workspace, size_t workspace_bytes, int num_cus,
                            hipStream_t stream);
 
+// The GEMM with a bf16 low-rank branch: C = A_hat . W_hat^T + (A . V^T) . U^T, V [r x K] and
+// U [N x r] bf16 (dense).  The workspace holds T = A . V^T as a bf16 pair (lowrank_t_bytes(M)
+// bytes), then the product's split-K planes (gemm_ws_bytes).
+size_t lowrank_t_bytes(int64_t M);
+hipError_t launch_gemm_lowrank(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, int64_t lda,
+                               const nvfp4_tensor *w, const void *v, const void *u, int r, float *c, int64_t ldc,
+                               void *workspace, size_t workspace_bytes, int num_cus, hipStream_t stream);
+hipError_t launch_lowrank_down(const void *a_bf16, int64_t lda, const void *v, int64_t M, int64_t K, int r,
+                               void *t, hipStream_t stream);
+hipError_t launch_lowrank_up_add(const void *t, const void *u, int r, int64_t M, int64_t N, float *c, int64_t ldc,
+                                 hipStream_t stream);
+
 size_t percentile_ws_bytes(int64_t cols, int per_channel);
 
 hipError_t launch_percentile(const void *x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld_x, uint32_t k,

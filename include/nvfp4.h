@@ -70,7 +70,14 @@ typedef struct {
 } nvfp4_tensor;
 
 /* Operation selectors for nvfp4_workspace_size. */
-enum { NVFP4_OP_QUANTIZE = 0, NVFP4_OP_DEQUANTIZE = 1, NVFP4_OP_GEMM = 2, NVFP4_OP_PERCENTILE = 3, NVFP4_OP_STATS = 4 };
+enum {
+    NVFP4_OP_QUANTIZE = 0,
+    NVFP4_OP_DEQUANTIZE = 1,
+    NVFP4_OP_GEMM = 2,
+    NVFP4_OP_PERCENTILE = 3,
+    NVFP4_OP_STATS = 4,
+    NVFP4_OP_LOWRANK = 5
+};
 
 /*
  * nvfp4_quantize -- x [out->rows x out->cols] (row stride ld_x elements) -> NVFP4 `out`.
@@ -147,6 +154,27 @@ nvfp4_status nvfp4_dequantize(const nvfp4_tensor *in, void *out, nvfp4_dtype out
 nvfp4_status nvfp4_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, int64_t lda,
                         const nvfp4_tensor *w, float *c, int64_t ldc, void *workspace, size_t workspace_bytes,
                         hipStream_t stream);
+
+/*
+ * nvfp4_gemm_lowrank -- C [M x N] fp32 (row stride ldc) = A_hat . W_hat^T + (A . V^T) . U^T: the
+ * NVFP4 product of nvfp4_gemm plus a bf16 low-rank branch of the weight, W ~ W_hat + U . V
+ * ("Qwen Image 2.1: INT4 + FP4", section "What I quantized": FP4 weights with BF16 rank-128
+ * branches).
+ *   a_bf16  [M x K] bf16, row stride lda: the activations of the branch, and of the main product
+ *           when a_q is NULL (W4A16); required (may be NULL only when M == 0);
+ *   a_q     NULL, or the NVFP4 activations [M x K] of a W4A4 main product;
+ *   lr_down V [rank x K] bf16, dense; lr_up U [N x rank] bf16, dense; 16 <= rank <= 256,
+ *           rank % 16 == 0 (NVFP4_ERR_SHAPE otherwise).
+ * T = A . V^T is summed in fp32 and carried as two bf16 planes (T_hi + T_lo, about 2^-17 relative);
+ * the up-projection runs in the GEMM's epilogue on the matrix cores when the product takes the
+ * unsplit tiled kernel, otherwise as a second pass that adds into C.
+ * workspace (device, 16-byte aligned): at least nvfp4_workspace_size(NVFP4_OP_LOWRANK, M, N, K)
+ * bytes -- T (M * 1 KiB) then the product's split-K planes; NVFP4_ERR_WORKSPACE when smaller than
+ * the T part (with less than the full size the product runs unsplit).
+ */
+nvfp4_status nvfp4_gemm_lowrank(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, int64_t lda,
+                                const nvfp4_tensor *w, const void *lr_down, const void *lr_up, int64_t rank, float *c,
+                                int64_t ldc, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * nvfp4_gemm_fp8a -- C [M x N] fp32 (row stride ldc) = A_hat . W_hat^T with FP8 activations: a_fp8

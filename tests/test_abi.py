@@ -25,7 +25,7 @@ def nv():
 
 def test_header_declares_the_entry_points():
     assert _declared_functions() == sorted(["nvfp4_quantize", "nvfp4_quantize_fp8", "nvfp4_dequantize", "nvfp4_gemm",
-                                            "nvfp4_gemm_fp8a", "nvfp4_matrix_stats", "amax_percentile",
+                                            "nvfp4_gemm_fp8a", "nvfp4_matrix_stats", "nvfp4_gemm_lowrank", "amax_percentile",
                                             "nvfp4_workspace_size", "nvfp4_status_string"])
 
 
@@ -160,6 +160,30 @@ def test_matrix_stats_validation(nv):
     assert f(P(FAKE), 0, 4, 32, 32, ctypes.byref(q), P(FAKE + 4), P(FAKE), ws, None) == 3  # out align
     assert f(P(FAKE), 0, 4, 32, 32, ctypes.byref(q), P(FAKE), P(FAKE), ws - 1, None) == 5  # workspace
     assert f(P(FAKE), 0, 4, 32, 32, ctypes.byref(q), P(FAKE), None, ws, None) == 5
+
+
+def test_gemm_lowrank_validation(nv):
+    f = nv.lib.nvfp4_gemm_lowrank
+    P = ctypes.c_void_p
+    w = _qt(nv, 64, 32)
+    ws = nv.workspace_size(nv.OP_LOWRANK, 8, 64, 32)
+    assert ws >= 8 * 1024  # T at rank 256: 8 rows x 1 KiB
+    ok = dict(a=P(FAKE), aq=None, M=8, lda=32, w=ctypes.byref(w), v=P(FAKE), u=P(FAKE), r=16, c=P(FAKE), ldc=64,
+              ws=P(FAKE), wsb=ws)
+
+    def call(**kw):
+        d = dict(ok, **kw)
+        return f(d["a"], d["aq"], d["M"], d["lda"], d["w"], d["v"], d["u"], d["r"], d["c"], d["ldc"], d["ws"],
+                 d["wsb"], None)
+    assert call(r=0) == 2 and call(r=24) == 2 and call(r=272) == 2  # rank: 16 .. 256, multiple of 16
+    assert call(a=None) == 1                                          # the branch needs the bf16 activations
+    assert call(v=None) == 1 and call(u=None) == 1
+    assert call(lda=16) == 2                                          # lda < K
+    assert call(v=P(FAKE + 8)) == 3                                   # alignment of V
+    assert call(ws=None) == 5 and call(wsb=8 * 1024 - 1) == 5         # T does not fit
+    bad = _qt(nv, 9, 32)
+    assert call(aq=ctypes.byref(bad)) == 2                            # a_q rows != M
+    assert call(M=-1) == 2
 
 
 def test_percentile_validation(nv):

@@ -670,3 +670,82 @@ def test_matrix_stats_full_sizes(nv):
     w = synth.attn_proj_weight()
     got, ref = _stats_case(nv, w, "f32")
     _assert_stats(got, ref, "attention f32")
+
+
+# ------------------------------------------------------------------------------------------------
+# NVFP4 GEMM with a bf16 low-rank branch: C = A_hat . W_hat^T + (A . V^T) . U^T
+# ------------------------------------------------------------------------------------------------
+def _lowrank_operands(m, n, k, r, seed):
+    g = synth.rng(seed)
+    a_bits = synth.bf16_bits(g.standard_normal((m, k)).astype(np.float32))
+    v_bits = synth.bf16_bits((g.standard_normal((r, k)) * 0.05).astype(np.float32))
+    u_bits = synth.bf16_bits((g.standard_normal((n, r)) * 0.05).astype(np.float32))
+    return a_bits, v_bits, u_bits
+
+
+# paths: fused epilogue of the tiled kernel (K % 64 == 0, unsplit), the GEMV for M <= 4, the
+# K % 64 != 0 kernel and split-K (the last three add the branch in a second pass); ranks 16 .. 256
+# including r % 32 == 16 and r > 128 (two column blocks of T)
+LOWRANK_SHAPES = [(16, 64, 256, 16), (1, 64, 128, 32), (3, 100, 4096, 128), (64, 96, 112, 48),
+                  (200, 300, 512, 128), (130, 1000, 128, 64), (256, 192, 1024, 256), (100, 1000, 4096, 128),
+                  (300, 520, 640, 144)]
+
+
+@pytest.mark.parametrize("mnkr", LOWRANK_SHAPES)
+@pytest.mark.parametrize("form", ["w4a16", "w4a4"])
+def test_gemm_lowrank(nv, mnkr, form):
+    m, n, k, r = mnkr
+    _note(f"gemm lowrank {form} {mnkr}")
+    q, ref = _rand_q(nv, n, k, seed=m * 13 + n + r)
+    a_bits, v_bits, u_bits = _lowrank_operands(m, n, k, r, seed=m + k + r)
+    a, v, u = to_dev_bf16(a_bits), to_dev_bf16(v_bits), to_dev_bf16(u_bits)
+    aq = aref = None
+    if form == "w4a4":
+        aq = _quant(nv, a)
+        aref, _ = oracle.quantize(a_bits, oracle.BF16)
+        _assert_q_equal(aq, aref, "activations")
+    c = nv.gemm_lowrank(a, q, v, u, a_q=aq).cpu().numpy()
+    cref = oracle.gemm_lowrank(a_bits, ref, v_bits, u_bits, a_q=aref)
+    err = oracle.gemm_error(c, cref)
+    assert err <= GEMM_TOL, err
+    if m > 1:  # strided A and C, and a workspace that holds T only (the product runs unsplit)
+        t_bytes = (m * 1024 + 255) // 256 * 256
+        ws = torch.empty(t_bytes, dtype=torch.uint8, device=DEV)
+        out = padded(torch.empty((m, n), dtype=torch.float32, device=DEV), 4)
+        nv.gemm_lowrank(padded(a, 8), q, v, u, a_q=aq, out=out, workspace=ws)
+        err2 = oracle.gemm_error(out.cpu().numpy(), cref)
+        assert err2 <= GEMM_TOL, err2
+
+
+def test_gemm_lowrank_zero_branch_is_plain_product(nv):
+    _note("gemm lowrank: zero branch, one-hot branch")
+    m, n, k, r = 300, 200, 1024, 128
+    q, ref = _rand_q(nv, n, k, seed=5)
+    a_bits, v_bits, u_bits = _lowrank_operands(m, n, k, r, seed=6)
+    a, v = to_dev_bf16(a_bits), to_dev_bf16(v_bits)
+    zu = torch.zeros((n, r), dtype=torch.bfloat16, device=DEV)
+    assert np.array_equal(nv.gemm_lowrank(a, q, v, zu).cpu().numpy(), nv.gemm(a, q).cpu().numpy())
+    # one-hot branch: V = e_k (row 0), U = e_0 for output column 7: adds A[:, 3] to column 7 exactly
+    v1 = np.zeros((r, k), np.uint16)
+    v1[0, 3] = 0x3F80
+    u1 = np.zeros((n, r), np.uint16)
+    u1[7, 0] = 0x3F80
+    d = nv.gemm_lowrank(a, q, to_dev_bf16(v1), to_dev_bf16(u1)).cpu().numpy() - nv.gemm(a, q).cpu().numpy()
+    want = np.zeros((m, n))
+    want[:, 7] = oracle.bf16_bits_to_f64(a_bits)[:, 3]
+    assert np.allclose(d, want, rtol=1e-6, atol=1e-6 * np.abs(nv.gemm(a, q).cpu().numpy()).max())
+
+
+def test_gemm_lowrank_attention_projection_full(nv):
+    m, n, k, r = 4096, 3072, 3072, 128
+    _note(f"gemm lowrank w4a16 {m}x{n}x{k} rank {r} (full)")
+    w = synth.attn_proj_weight()
+    a_bits = synth.attn_proj_activations()
+    ref, _ = oracle.quantize(w)
+    q = _quant(nv, to_dev_f32(w))
+    _assert_q_equal(q, ref, "attn weight")
+    _, v_bits, u_bits = _lowrank_operands(8, n, k, r, seed=2024)
+    c = nv.gemm_lowrank(to_dev_bf16(a_bits), q, to_dev_bf16(v_bits), to_dev_bf16(u_bits)).cpu().numpy()
+    err = oracle.gemm_error(c, oracle.gemm_lowrank(a_bits, ref, v_bits, u_bits))
+    _note(f"  floored max rel err {err:.3e}")
+    assert err <= GEMM_TOL
