@@ -15,6 +15,7 @@ The FP8 side path is timed after the step, in a loop of its own over the same in
   act_quantize_fp8  A bf16 -> FP8 E4M3 tensorwise (dynamic amax)
   gemm_w4a8    C = A_fp8 . W_hat^T, FP8 activations
   weight_stats quality statistics of W and its NVFP4 form (relative error, kurtosis, block max/std)
+  gemm_w4a16_lr128  C = A . W_hat^T + (A . V^T) . U^T with a bf16 rank-128 branch (V [128 x K], U [N x 128])
 Inputs are resident in HBM before timing; the step rotates over several input sets whose total
 size exceeds the 256 MB Infinity Cache, so repeated steps do not hit in cache.  Each operation is
 bracketed by events on the stream it runs on; the dominant kernel's roofline uses those times.
@@ -36,6 +37,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 M_TOK, N_OUT, K_IN = 4096, 3072, 3072
 GEMV_M = 2
+LR_RANK = 128  # rank of the bf16 low-rank branch ("FP4 with BF16 rank 128 branches")
 ROTATE_MIN_BYTES = 320 << 20
 
 
@@ -97,15 +99,20 @@ def main():
     c8 = torch.empty((M_TOK, N_OUT), dtype=torch.float32, device=dev)
     st_out = torch.empty(8, dtype=torch.float64, device=dev)
     st_ws = torch.empty(nv.workspace_size(nv.OP_STATS, 0, 0), dtype=torch.uint8, device=dev)
+    gl = torch.Generator(device="cpu").manual_seed(128)
+    lr_v = (torch.randn((LR_RANK, K_IN), generator=gl) * 0.05).to(torch.bfloat16).to(dev)
+    lr_u = (torch.randn((N_OUT, LR_RANK), generator=gl) * 0.05).to(torch.bfloat16).to(dev)
+    lr_ws = torch.empty(nv.workspace_size(nv.OP_LOWRANK, M_TOK, N_OUT, K_IN), dtype=torch.uint8, device=dev)
+    clr = torch.empty((M_TOK, N_OUT), dtype=torch.float32, device=dev)
 
     ops = ["quantize", "requantize", "dequantize", "act_quantize", "gemm_w4a16", "gemm_w4a4", "gemv_w4a16",
            "percentile"]
-    next_ops = ["act_quantize_fp8", "gemm_w4a8", "weight_stats"]
+    next_ops = ["act_quantize_fp8", "gemm_w4a8", "weight_stats", "gemm_w4a16_lr128"]
     # kernels each op launches (the roofline is reported for the longest single-kernel op); the
     # percentile at p99.9 over 4096 rows takes the one-pass top-M path (selection + merge)
     n_kernels = {"quantize": 1, "requantize": 1, "dequantize": 1, "act_quantize": 1, "gemm_w4a16": 1,
                  "gemm_w4a4": 1, "gemv_w4a16": 1, "percentile": 2, "act_quantize_fp8": 1, "gemm_w4a8": 1,
-                 "weight_stats": 2}
+                 "weight_stats": 2, "gemm_w4a16_lr128": 2}
 
     def step(i, events=None):
         w, a, w8 = sets[i % nsets]
@@ -138,6 +145,8 @@ def main():
         if e: e[2].record()
         nv.matrix_stats(w, qw, out=st_out, workspace=st_ws)
         if e: e[3].record()
+        nv.gemm_lowrank(a, qw, lr_v, lr_u, out=clr, workspace=lr_ws)
+        if e: e[4].record()
 
     for i in range(args.warmup):
         step(i)
@@ -177,6 +186,8 @@ def main():
         "act_quantize_fp8": ("GB/s", nA * 3.0 + 4, HBM_PEAK_GBS),
         "gemm_w4a8": ("TFLOP/s", 2.0 * M_TOK * N_OUT * K_IN, BF16_MFMA_PEAK_TFLOPS),
         "weight_stats": ("GB/s", nW * 4.5625 + 4, HBM_PEAK_GBS),
+        "gemm_w4a16_lr128": ("TFLOP/s", 2.0 * M_TOK * N_OUT * K_IN + 2.0 * M_TOK * LR_RANK * (K_IN + N_OUT),
+                             BF16_MFMA_PEAK_TFLOPS),
     }
     op_report, next_report = {}, {}
     for op in ops + next_ops:

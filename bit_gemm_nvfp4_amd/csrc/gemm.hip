@@ -693,7 +693,65 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
                     if (A_X) v = v * ga;
                     acc[i][j][e] = v * gw;
                 }
-        lr_branch<TM, TN>(acc, lr, M, N, m0 + wm * WTM, n0 + wn * WTN, lane);
+        // T . U^T in chunks of kLrChunk ranks: the tile's rows of T_hi, T_lo and U are staged in LDS
+        // (free once the main loop is done) by all threads at once, then read as fragments
+        constexpr int LROW = kLrChunk + 8;  // padded bf16 row: fragment reads spread over the banks
+        constexpr int LR_UNITS = (2 * BM + BN) * (kLrChunk / 8);  // 16-byte units per chunk
+        static_assert((2 * BM + BN) * LROW * 2 <= LDS_BYTES, "LDS for the low-rank chunk");
+        static_assert(BM * 8 % NT == 0, "one staging region per pass of the threads");
+        __bf16 *lt = reinterpret_cast<__bf16 *>(smem);
+        const int r = lr.r;
+        // the tile's rows of T_hi, T_lo and U: rows past M or N fall outside and read as zero
+        const __amdgpu_buffer_rsrc_t rt[3] = {lr_rsrc(lr.t + m0 * r, mrows * r * 2),
+                                              lr_rsrc(lr.t + M * (int64_t)r + m0 * r, mrows * r * 2),
+                                              lr_rsrc(lr.u + n0 * r, nrows * r * 2)};
+        constexpr int LR_PER = (LR_UNITS + NT - 1) / NT;
+        for (int rc0 = 0; rc0 < r; rc0 += kLrChunk) {
+            // all of this thread's loads first (no branches around them), then the LDS writes
+            bf16x8 v[LR_PER];
+#pragma unroll
+            for (int q = 0; q < LR_PER; q++) {
+                const int d = tid + q * NT;
+                const int row = d / (kLrChunk / 8), c8 = (d % (kLrChunk / 8)) * 8;  // LDS row, rank offset
+                // the region (T_hi, T_lo, U) is the same for all threads of one q: BM * 8 % NT == 0
+                const int which = q * NT < BM * 8 ? 0 : q * NT < 2 * BM * 8 ? 1 : 2;
+                const int lrow = row - which * BM;
+                const bool in = d < LR_UNITS && rc0 + c8 < r;
+                const uint32_t o = in ? (uint32_t)(lrow * r + rc0 + c8) * 2 : kLrOob;
+                v[q] = lr_load(which == 0 ? rt[0] : which == 1 ? rt[1] : rt[2], o);
+            }
+            __syncthreads();  // the previous reads of LDS (main loop or chunk) are done
+#pragma unroll
+            for (int q = 0; q < LR_PER; q++) {
+                const int d = tid + q * NT;
+                if (d < LR_UNITS) {
+                    const int row = d / (kLrChunk / 8), c8 = (d % (kLrChunk / 8)) * 8;
+                    *reinterpret_cast<bf16x8 *>(lt + row * LROW + c8) = v[q];
+                }
+            }
+            __syncthreads();
+            const int kend = (r - rc0) < kLrChunk ? (r - rc0) : kLrChunk;
+            for (int kk = 0; kk < kend; kk += 16) {
+                bf16x8 ah[TM], al[TM], bu[TN];
+                const int kc = kk + (lane >> 5) * 8;
+#pragma unroll
+                for (int i = 0; i < TM; i++) {
+                    const int row = wm * WTM + i * 32 + (lane & 31);
+                    ah[i] = *reinterpret_cast<const bf16x8 *>(lt + row * LROW + kc);
+                    al[i] = *reinterpret_cast<const bf16x8 *>(lt + (BM + row) * LROW + kc);
+                }
+#pragma unroll
+                for (int j = 0; j < TN; j++)
+                    bu[j] = *reinterpret_cast<const bf16x8 *>(lt + (2 * BM + wn * WTN + j * 32 + (lane & 31)) * LROW + kc);
+#pragma unroll
+                for (int i = 0; i < TM; i++)
+#pragma unroll
+                    for (int j = 0; j < TN; j++) {
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bu[j], acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bu[j], acc[i][j], 0, 0, 0);
+                    }
+            }
+        }
 #pragma unroll
         for (int i = 0; i < TM; i++)
 #pragma unroll
