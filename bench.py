@@ -16,6 +16,8 @@ The FP8 side path is timed after the step, in a loop of its own over the same in
   gemm_w4a8    C = A_fp8 . W_hat^T, FP8 activations
   weight_stats quality statistics of W and its NVFP4 form (relative error, kurtosis, block max/std)
   gemm_w4a16_lr128  C = A . W_hat^T + (A . V^T) . U^T with a bf16 rank-128 branch (V [128 x K], U [N x 128])
+  gemm_w4a4_qa C = A_hat . W_hat^T with A quantized under a static amax (p99.9 calibration) by the same call
+               (at N = 3072 the library picks a quantize pass + the W4A4 kernel over the fused kernel)
 Inputs are resident in HBM before timing; the step rotates over several input sets whose total
 size exceeds the 256 MB Infinity Cache, so repeated steps do not hit in cache.  Each operation is
 bracketed by events on the stream it runs on; the dominant kernel's roofline uses those times.
@@ -104,15 +106,19 @@ def main():
     lr_u = (torch.randn((N_OUT, LR_RANK), generator=gl) * 0.05).to(torch.bfloat16).to(dev)
     lr_ws = torch.empty(nv.workspace_size(nv.OP_LOWRANK, M_TOK, N_OUT, K_IN), dtype=torch.uint8, device=dev)
     clr = torch.empty((M_TOK, N_OUT), dtype=torch.float32, device=dev)
+    # static activation amax, calibrated once: max over channels of the per-channel p99.9 of |A|
+    qa_amax = nv.amax_percentile(sets[0][1], 99.9, per_channel=True)[0].max().reshape(1).contiguous()
+    qa_ws = torch.empty(max(nv.workspace_size(nv.OP_GEMM_QA, M_TOK, N_OUT, K_IN), 1), dtype=torch.uint8, device=dev)
+    cqa = torch.empty((M_TOK, N_OUT), dtype=torch.float32, device=dev)
 
     ops = ["quantize", "requantize", "dequantize", "act_quantize", "gemm_w4a16", "gemm_w4a4", "gemv_w4a16",
            "percentile"]
-    next_ops = ["act_quantize_fp8", "gemm_w4a8", "weight_stats", "gemm_w4a16_lr128"]
+    next_ops = ["act_quantize_fp8", "gemm_w4a8", "weight_stats", "gemm_w4a16_lr128", "gemm_w4a4_qa"]
     # kernels each op launches (the roofline is reported for the longest single-kernel op); the
     # percentile at p99.9 over 4096 rows takes the one-pass top-M path (selection + merge)
     n_kernels = {"quantize": 1, "requantize": 1, "dequantize": 1, "act_quantize": 1, "gemm_w4a16": 1,
                  "gemm_w4a4": 1, "gemv_w4a16": 1, "percentile": 2, "act_quantize_fp8": 1, "gemm_w4a8": 1,
-                 "weight_stats": 2, "gemm_w4a16_lr128": 2}
+                 "weight_stats": 2, "gemm_w4a16_lr128": 2, "gemm_w4a4_qa": 2}
 
     def step(i, events=None):
         w, a, w8 = sets[i % nsets]
@@ -147,6 +153,8 @@ def main():
         if e: e[3].record()
         nv.gemm_lowrank(a, qw, lr_v, lr_u, out=clr, workspace=lr_ws)
         if e: e[4].record()
+        nv.gemm_qa(a, qw, qa_amax, out=cqa, workspace=qa_ws)
+        if e: e[5].record()
 
     for i in range(args.warmup):
         step(i)
@@ -188,6 +196,7 @@ def main():
         "weight_stats": ("GB/s", nW * 4.5625 + 4, HBM_PEAK_GBS),
         "gemm_w4a16_lr128": ("TFLOP/s", 2.0 * M_TOK * N_OUT * K_IN + 2.0 * M_TOK * LR_RANK * (K_IN + N_OUT),
                              BF16_MFMA_PEAK_TFLOPS),
+        "gemm_w4a4_qa": ("TFLOP/s", 2.0 * M_TOK * N_OUT * K_IN, BF16_MFMA_PEAK_TFLOPS),
     }
     op_report, next_report = {}, {}
     for op in ops + next_ops:

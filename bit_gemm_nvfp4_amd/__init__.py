@@ -26,11 +26,11 @@ lib = ctypes.CDLL(LIB_PATH)
 # C ABI declarations
 # ------------------------------------------------------------------------------------------------
 NVFP4_F32, NVFP4_BF16, NVFP4_F16, NVFP4_E4M3 = 0, 1, 2, 3
-OP_QUANTIZE, OP_DEQUANTIZE, OP_GEMM, OP_PERCENTILE, OP_STATS, OP_LOWRANK = 0, 1, 2, 3, 4, 5
+OP_QUANTIZE, OP_DEQUANTIZE, OP_GEMM, OP_PERCENTILE, OP_STATS, OP_LOWRANK, OP_GEMM_QA = 0, 1, 2, 3, 4, 5, 6
 STATUS_NAMES = ["NVFP4_OK", "NVFP4_ERR_NULL", "NVFP4_ERR_SHAPE", "NVFP4_ERR_ALIGN", "NVFP4_ERR_DTYPE",
                 "NVFP4_ERR_WORKSPACE", "NVFP4_ERR_ARG", "NVFP4_ERR_DEVICE", "NVFP4_ERR_LAUNCH"]
 EXPORTED = ["nvfp4_quantize", "nvfp4_quantize_fp8", "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_gemm_fp8a",
-            "nvfp4_matrix_stats", "nvfp4_gemm_lowrank", "amax_percentile", "nvfp4_workspace_size", "nvfp4_status_string"]
+            "nvfp4_matrix_stats", "nvfp4_gemm_lowrank", "nvfp4_gemm_qa", "amax_percentile", "nvfp4_workspace_size", "nvfp4_status_string"]
 
 
 class CTensor(ctypes.Structure):
@@ -54,6 +54,8 @@ lib.nvfp4_dequantize.restype = _I32
 lib.nvfp4_gemm.argtypes = [_P, _PT, _I64, _I64, _PT, _P, _I64, _P, _SZ, _P]
 lib.nvfp4_gemm_lowrank.argtypes = [_P, _PT, _I64, _I64, _PT, _P, _P, _I64, _P, _I64, _P, _SZ, _P]
 lib.nvfp4_gemm_lowrank.restype = _I32
+lib.nvfp4_gemm_qa.argtypes = [_P, _P, _I64, _I64, _PT, _P, _I64, _P, _SZ, _P]
+lib.nvfp4_gemm_qa.restype = _I32
 lib.nvfp4_gemm.restype = _I32
 lib.amax_percentile.argtypes = [_P, _I32, _I64, _I64, _I64, _D, _I32, _P, _P, _P, _P, _SZ, _P]
 lib.amax_percentile.restype = _I32
@@ -227,6 +229,27 @@ def gemm(a: torch.Tensor | NVFP4Tensor | FP8Tensor, w: NVFP4Tensor, out: torch.T
     st = lib.nvfp4_gemm(a_ptr, a_ct, m, lda, ctypes.byref(wct), _ptr(out), out.stride(0) if m > 0 else n, _ptr(ws),
                         ws_bytes, _stream(device))
     _check(st, "nvfp4_gemm")
+    return out
+
+
+def gemm_qa(a: torch.Tensor, w: NVFP4Tensor, amax: torch.Tensor, out: torch.Tensor | None = None,
+            workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """C [M, N] fp32 = A_hat . W_hat^T with A (bf16 [M, K]) quantized to NVFP4 inside the GEMM under
+    the static amax (a float32 device tensor of one element)."""
+    n, k = w.shape
+    device = w.codes.device
+    assert a.dtype == torch.bfloat16 and a.dim() == 2 and a.shape[1] == k
+    assert amax.dtype == torch.float32 and amax.is_cuda and amax.numel() == 1
+    m = a.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=device)
+    ws_bytes = workspace_size(OP_GEMM_QA, m, n, k)
+    ws = workspace if workspace is not None else _workspace(ws_bytes, device)
+    wct = w.c()
+    st = lib.nvfp4_gemm_qa(_ptr(a), _ptr(amax), m, a.stride(0) if m > 0 else k, ctypes.byref(wct), _ptr(out),
+                           out.stride(0) if m > 0 else n, _ptr(ws), ws.numel() if workspace is not None else ws_bytes,
+                           _stream(device))
+    _check(st, "nvfp4_gemm_qa")
     return out
 
 

@@ -66,6 +66,16 @@ int elem_bytes(nvfp4_dtype dt) {
 
 // Shape and alignment checks shared by every NVFP4 tensor argument.
 // codes and scales may be NULL only for a tensor with no elements; global_scale is always required.
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+constexpr int64_t kQaFusedMaxN = 512;  // widest N that nvfp4_gemm_qa runs with the fused kernel
+
+// Workspace of the unfused form of nvfp4_gemm_qa: the NVFP4 activations (codes, scales, scale).
+size_t qa_ws_bytes(int64_t M, int64_t K) {
+    if (M <= 0 || K <= 0) return 0;
+    return align256((size_t)M * (size_t)(K / 2)) + align256((size_t)M * (size_t)(K / 16)) + 256;
+}
+
 nvfp4_status check_qtensor(const nvfp4_tensor *t) {
     if (!t || !t->global_scale) return NVFP4_ERR_NULL;
     if (t->rows < 0 || t->cols < 0 || (t->cols % 16) != 0) return NVFP4_ERR_SHAPE;
@@ -113,6 +123,14 @@ size_t nvfp4_workspace_size(int op, int64_t rows, int64_t cols, int64_t k) {
     case NVFP4_OP_QUANTIZE: return kQuantizeWsBytes;
     case NVFP4_OP_PERCENTILE: return cols >= 0 ? percentile_ws_bytes(cols, k ? 1 : 0) : 0;
     case NVFP4_OP_STATS: return stats_ws_bytes();
+    case NVFP4_OP_GEMM_QA: {
+        if (rows < 0 || cols < 0 || k < 0) return 0;
+        const int cus = current_device_cus();
+        const int c2 = cus > 0 ? cus : 256;
+        const size_t fused = gemm_ws_bytes(rows, cols, k, c2, kFirstQuantTileCfg);
+        const size_t two_step = qa_ws_bytes(rows, k) + gemm_ws_bytes(rows, cols, k, c2);
+        return fused > two_step ? fused : two_step;
+    }
     case NVFP4_OP_LOWRANK: {
         if (rows < 0 || cols < 0 || k < 0) return 0;
         const int cus = current_device_cus();
@@ -240,6 +258,44 @@ nvfp4_status nvfp4_gemm_lowrank(const void *a_bf16, const nvfp4_tensor *a_q, int
     hipError_t e = (K == 0) ? launch_fill_zero_f32(c, M, N, ldc, stream)
                             : launch_gemm_lowrank(a_bf16, a_q, M, lda, w, lr_down, lr_up, (int)rank, c, ldc,
                                                   workspace, workspace_bytes, cus, stream);
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+}
+
+nvfp4_status nvfp4_gemm_qa(const void *a_bf16, const float *a_amax, int64_t M, int64_t lda, const nvfp4_tensor *w,
+                           float *c, int64_t ldc, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    nvfp4_status st = check_qtensor(w);
+    if (st != NVFP4_OK) return st;
+    const int64_t N = w->rows, K = w->cols;
+    if (M < 0) return NVFP4_ERR_SHAPE;
+    if (!a_amax) return NVFP4_ERR_NULL;
+    if (!aligned4(a_amax)) return NVFP4_ERR_ALIGN;
+    st = check_matrix(a_bf16, M, K, lda, 2);
+    if (st != NVFP4_OK) return st;
+    st = check_matrix(c, M, N, ldc, 4, 4);
+    if (st != NVFP4_OK) return st;
+    if (workspace && !aligned16(workspace)) return NVFP4_ERR_ALIGN;
+    // Fused only where it is not slower: each N tile quantizes its A rows again, so beyond two
+    // 256-wide N tiles the separate quantize pass plus the W4A4 kernel wins (measured on MI355X:
+    // equal at N = 256 .. 512, 1.1x slower fused at N = 1024, 1.85x at N = 3072).
+    const bool fused = gemm_qa_fusable(M, K, lda) && N <= kQaFusedMaxN;
+    if (!fused && M > 0 && K > 0 && (!workspace || workspace_bytes < qa_ws_bytes(M, K))) return NVFP4_ERR_WORKSPACE;
+    const int cus = current_device_cus();
+    if (cus == 0) return NVFP4_ERR_DEVICE;
+    hipError_t e;
+    if (K == 0 || M == 0) {
+        e = launch_fill_zero_f32(c, M, N, ldc, stream);
+    } else if (fused) {
+        e = launch_gemm_qa_fused(a_bf16, a_amax, M, lda, w, c, ldc, workspace, workspace_bytes, cus, stream);
+    } else {
+        // quantize A with the static amax into the workspace, then the W4A4 product
+        uint8_t *ws = reinterpret_cast<uint8_t *>(workspace);
+        const size_t qb = qa_ws_bytes(M, K);
+        const size_t cb = align256((size_t)M * (size_t)(K / 2)), sb = align256((size_t)M * (size_t)(K / 16));
+        const nvfp4_tensor aq{ws, ws + cb, reinterpret_cast<float *>(ws + cb + sb), M, K};
+        e = launch_quantize(a_bf16, NVFP4_BF16, lda, nullptr, a_amax, &aq, nullptr, nullptr, cus, stream);
+        if (e == hipSuccess)
+            e = launch_gemm(nullptr, &aq, M, K, w, c, ldc, ws + qb, workspace_bytes - qb, cus, stream);
+    }
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
 }
 

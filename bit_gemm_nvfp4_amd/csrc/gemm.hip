@@ -79,6 +79,38 @@ __device__ __forceinline__ u32x4 expand8_f16(uint32_t w, f16x2 s2) {
 constexpr int kAmBf16 = 0;   // bf16 rows (W4A16)
 constexpr int kAmNvfp4 = 1;  // NVFP4 tensor (W4A4)
 constexpr int kAmFp8 = 2;    // E4M3 bytes with one tensor scale (FP8 activations)
+constexpr int kAmQuant = 3;  // bf16 rows quantized to NVFP4 in the kernel with a static amax (W4A4)
+
+// Quantize one unit of 8 bf16 activations to NVFP4 with the static global scale g (six_g = fl(6 g))
+// and return their exact values e2m1 x s as 8 f16.  The unit's 16-element block is completed by
+// the neighbouring lane (lane ^ 1), which holds the other 8 elements: the block amax is exchanged
+// with one DPP move.  The steps and roundings are those of the quantize kernel (block scale byte
+// = nearest E4M3 of fl(bamax / six_g), r = fl(1 / fl(s g)), code = nearest E2M1 of fl(v r), zero
+// kept at zero), so the values equal the expansion of what nvfp4_quantize with this amax stores.
+__device__ __forceinline__ u32x4 quant8_f16(u32x4 raw, float g, float six_g) {
+    float v[8];
+    uint32_t bm = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        v[2 * i] = u2f(raw[i] << 16);
+        v[2 * i + 1] = u2f(raw[i] & 0xFFFF0000u);
+        const uint32_t m0 = (raw[i] << 16) & 0x7FFFFFFFu, m1 = raw[i] & 0x7FFF0000u;
+        bm = bm > m0 ? bm : m0;
+        bm = bm > m1 ? bm : m1;
+    }
+    const uint32_t bo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)bm, 0xB1, 0xF, 0xF, false);  // lane ^ 1
+    bm = bm > bo ? bm : bo;
+    const float q = u2f(bm) / six_g;
+    const uint32_t sbyte = g != 0.0f ? e4m3_from_f32(q) : 0u;
+    const float s = e4m3_to_f32(sbyte);
+    const float rd = 1.0f / (s * g);
+    const float r = s == 0.0f ? 0.0f : rd;
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) y[e] = v[e] == 0.0f ? v[e] : v[e] * r;
+    const _Float16 sh = (_Float16)s;
+    return expand8_f16(fp4_pack8(y), f16x2{sh, sh});
+}
 
 // Expand 8 E4M3 bytes (two dwords, element i in byte i) into 8 exact f16 values: e4m3 values have
 // at most 4 significant bits and lie in [2^-9, 448], inside f16's range.
@@ -404,7 +436,7 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
                                                           int slice_steps, LrArgs lr) {
     // A_X: activations expanded from registers into LDS as f16 (NVFP4 codes, or E4M3 bytes), with W
     // expanded to f16 too; otherwise bf16 activations are copied straight into LDS.
-    constexpr bool A_Q = AM == kAmNvfp4, A_F8 = AM == kAmFp8, A_X = AM != kAmBf16;
+    constexpr bool A_Q = AM == kAmNvfp4, A_F8 = AM == kAmFp8, A_QS = AM == kAmQuant, A_X = AM != kAmBf16;
     constexpr int NT = 64 * WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;    // wave tile
     constexpr int TM = WTM / 32, TN = WTN / 32;    // 32x32 MFMA tiles per wave
@@ -419,7 +451,7 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
     constexpr int A_DMA = A_X ? 0 : BM / 8 / (WM * WN);  // 1 KiB direct-to-LDS loads per wave per step
     // vector-memory instructions issued per step: an NVFP4 unit loads a code dword and a scale byte,
     // an E4M3 unit one 8-byte load
-    constexpr int VM_STEP = A_DMA + 2 * WD + (A_F8 ? AD : 2 * AD);
+    constexpr int VM_STEP = A_DMA + 2 * WD + (A_F8 || A_QS ? AD : 2 * AD);
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert(BN * 8 % NT == 0 && BM * 8 % NT == 0 && (A_X || BM / 8 % (WM * WN) == 0), "even split");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
@@ -450,6 +482,8 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
     } else if constexpr (A_Q) {
         rc[0] = make_rsrc(a_codes + m0 * (K / 2), mrows * (K / 2));
         rs[0] = make_rsrc(a_scales + m0 * (K / 16), mrows * (K / 16));
+    } else if constexpr (A_QS) {
+        rc[0] = make_rsrc(A + m0 * lda, ((mrows - 1) * lda + K) * 2);  // bf16 rows, quantized here
     } else {
         rc[0] = make_rsrc(a_codes + m0 * lda, (mrows - 1) * lda + K);  // E4M3 bytes, row stride lda
     }
@@ -464,7 +498,9 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
     for (int u = 0; u < QD; u++) {
         const int j = u < AD ? u : u - AD;
         const uint32_t d = (uint32_t)(tid + NT * j), row = d >> 3, c = d & 7;
-        q_coff[u] = (A_F8 && u < AD) ? row * (uint32_t)lda + c * 8 : row * (uint32_t)(K / 2) + c * 4;
+        q_coff[u] = (A_F8 && u < AD)    ? row * (uint32_t)lda + c * 8
+                    : (A_QS && u < AD) ? (row * (uint32_t)lda + c * 8) * 2
+                                       : row * (uint32_t)(K / 2) + c * 4;
         q_soff[u] = row * (uint32_t)(K / 16) + (c >> 1);
         q_lds[u] = (u < AD ? 0u : (uint32_t)W_OFF) + row * ROWB + ((c ^ (row & 7)) << 4);
     }
@@ -488,6 +524,10 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
 
     uint32_t qc[2][QD], qs[2][QD];  // two register sets of code dwords and scale bytes
     u32x2 qa8[2][A_F8 ? AD : 1];     // E4M3 activations: two register sets of 8-byte chunks
+    u32x4 qa16[2][A_QS ? AD : 1];    // bf16 activations to quantize: two register sets of 16 bytes
+    // static amax -> global scale of the quantized activations (as the quantize kernel forms it)
+    const float qs_g = A_QS ? *a_g / 2688.0f : 0.0f;
+    const float qs_six_g = 6.0f * qs_g;
 
     // K slice of this workgroup (split-K: blockIdx.y; otherwise the whole of K)
     const int total_steps = (int)(K / kBK);
@@ -509,6 +549,10 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
                 qa8[r][A_F8 ? u : 0] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rc[0], q_coff[u], k0, 0));
                 continue;
             }
+            if (A_QS && u < AD) {
+                qa16[r][A_QS ? u : 0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc[0], q_coff[u], k0 * 2, 0));
+                continue;
+            }
             const int o = u < AD ? 0 : 1;
             qc[r][u] = __builtin_amdgcn_raw_buffer_load_b32(rc[o], q_coff[u], k0 / 2, 0);
             qs[r][u] = __builtin_amdgcn_raw_buffer_load_b8(rs[o], q_soff[u], k0 / 16, 0);
@@ -518,6 +562,10 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
         const uint32_t base = u < AD ? (uint32_t)(a_stage * A_STAGE) : (uint32_t)(w_stage * W_STAGE);
         if (A_F8 && u < AD) {
             *reinterpret_cast<u32x4 *>(smem + base + q_lds[u]) = expand8_fp8_f16(qa8[r][A_F8 ? u : 0]);
+            return;
+        }
+        if (A_QS && u < AD) {
+            *reinterpret_cast<u32x4 *>(smem + base + q_lds[u]) = quant8_f16(qa16[r][A_QS ? u : 0], qs_g, qs_six_g);
             return;
         }
         const float sc = __builtin_amdgcn_cvt_f32_fp8((int)qs[r][u], 0);
@@ -678,7 +726,7 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
     // (w_g == nullptr) stores its raw partial sums into its own [M x ldc] plane of C instead ----
     const bool partial = w_g == nullptr;
     const float gw = partial ? 1.0f : *w_g;
-    const float ga = (A_X && !partial) ? *a_g : 1.0f;
+    const float ga = (A_X && !partial) ? (A_QS ? qs_g : *a_g) : 1.0f;
     float *Cs = C + (int64_t)blockIdx.y * M * ldc;
     if constexpr (LR) {
         // low-rank branch (unsplit products only): scale the sums first, with the same roundings as
@@ -787,14 +835,15 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
 }
 
 // Sum of the split-K partial planes P[s] ([M x ldp] each) in slice order, times the global
-// scale(s): C = ((sum_s P[s]) * g_a) * g_w.  One thread per output element.
-template <bool A_Q>
+// scale(s): C = ((sum_s P[s]) * g_a) * g_w.  One thread per output element.  GA: 0 no activation
+// scale, 1 *a_g is g_a, 2 *a_g is a static amax (g_a = fl(amax / 2688)).
+template <int GA>
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__ P, int splits, int64_t M, int64_t N,
                                                        int64_t ldp, const float *__restrict__ a_g,
                                                        const float *__restrict__ w_g, float *__restrict__ C,
                                                        int64_t ldc) {
     const float gw = *w_g;
-    const float ga = A_Q ? *a_g : 1.0f;
+    const float ga = GA == 1 ? *a_g : GA == 2 ? *a_g / 2688.0f : 1.0f;
     const int64_t total = M * N;
     const int64_t plane = M * ldp;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
@@ -802,7 +851,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__
         const float *p = P + r * ldp + c;
         float v = p[0];
         for (int s = 1; s < splits; s++) v += p[(int64_t)s * plane];
-        if (A_Q) v = v * ga;
+        if (GA) v = v * ga;
         C[r * ldc + c] = v * gw;
     }
 }
@@ -1079,12 +1128,12 @@ constexpr double kUsPerTileStep = 2.0;      // one 256 x 256 x 64 step on one CU
 constexpr double kReduceBytesPerUs = 4.0e6;  // HBM rate of the partial-sum pass
 constexpr int kMaxSplits = 8;
 
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int num_cus) {
-    GemmPlan best{0, 1, (int)((K + kBK - 1) / kBK)};
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int num_cus, int first_cfg) {
+    GemmPlan best{first_cfg, 1, (int)((K + kBK - 1) / kBK)};
     double best_cost = 1e300;
     const int64_t steps = (K + kBK - 1) / kBK;
     const bool splittable = K % kBK == 0;
-    for (int i = 0; i < (int)(sizeof(kTiles) / sizeof(kTiles[0])); i++) {
+    for (int i = first_cfg; i < (int)(sizeof(kTiles) / sizeof(kTiles[0])); i++) {
         const TileCfg &t = kTiles[i];
         const double tiles = (double)((M + t.bm - 1) / t.bm) * (double)((N + t.bn - 1) / t.bn);
         const double slots = (double)num_cus * t.per_cu;
@@ -1104,9 +1153,9 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int num_cus) {
     return best;
 }
 
-size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus) {
+size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus, int first_cfg) {
     if (M <= 0 || N <= 0 || K <= 0 || gemv_applies(M, K)) return 0;
-    const GemmPlan p = plan_gemm(M, N, K, num_cus);
+    const GemmPlan p = plan_gemm(M, N, K, num_cus, first_cfg);
     return p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)N * 4 : 0;
 }
 
@@ -1128,7 +1177,7 @@ static bool launch_tile(const GemmA &a, int64_t M, const nvfp4_tensor *w, float 
     const int64_t lda = a.lda;
     // k_gemm_mfma addresses one tile's rows with 32-bit buffer offsets
     const int64_t lim = (int64_t)1 << 31;
-    const int64_t a_row_bytes = AM == kAmBf16 ? lda * 2 : AM == kAmNvfp4 ? K / 2 : lda;
+    const int64_t a_row_bytes = (AM == kAmBf16 || AM == kAmQuant) ? lda * 2 : AM == kAmNvfp4 ? K / 2 : lda;
     const bool fits = (int64_t)(BM + 1) * a_row_bytes + K * 2 < lim && (int64_t)BN * (K / 2) < lim;
     if (K % kBK == 0 && fits) {
         if (partials) {
@@ -1138,12 +1187,13 @@ static bool launch_tile(const GemmA &a, int64_t M, const nvfp4_tensor *w, float 
                                w->codes, w->scales, nullptr, partials, N, M, N, K, plan.slice_steps, LrArgs{});
             const int64_t total = M * N;
             const int64_t blocks = (total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536;
-            hipLaunchKernelGGL((k_splitk_reduce<AM != kAmBf16>), dim3((unsigned)blocks), dim3(256), 0, stream,
+            hipLaunchKernelGGL((k_splitk_reduce<AM == kAmBf16 ? 0 : AM == kAmQuant ? 2 : 1>), dim3((unsigned)blocks),
+                               dim3(256), 0, stream,
                                partials, plan.splits, M, N, N, a.g, w->global_scale, c, ldc);
             return false;
         }
         if (lr) {
-            if constexpr (AM != kAmFp8) {
+            if constexpr (AM == kAmBf16 || AM == kAmNvfp4) {
                 hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, AM, true>), dim3((unsigned)tiles), dim3(64 * WM * WN),
                                    0, stream, (const __bf16 *)a.bf16, lda, a.codes, a.scales, a.g, w->codes,
                                    w->scales, w->global_scale, c, ldc, M, N, K, (int)(K / kBK), *lr);
@@ -1153,7 +1203,7 @@ static bool launch_tile(const GemmA &a, int64_t M, const nvfp4_tensor *w, float 
         hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, AM>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0, stream,
                            (const __bf16 *)a.bf16, lda, a.codes, a.scales, a.g, w->codes, w->scales,
                            w->global_scale, c, ldc, M, N, K, (int)(K / kBK), LrArgs{});
-    } else {
+    } else if constexpr (AM != kAmQuant) {  // the fused quantization runs only where K % 64 == 0
         hipLaunchKernelGGL((k_gemm_tile<BM, BN, WM, WN, AM>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0, stream,
                            (const __bf16 *)a.bf16, lda, a.codes, a.scales, a.g, w->codes, w->scales,
                            w->global_scale, c, ldc, M, N, K);
@@ -1161,10 +1211,15 @@ static bool launch_tile(const GemmA &a, int64_t M, const nvfp4_tensor *w, float 
     return false;
 }
 
+// Tiles with 256 rows hold the quantizing A path's extra registers only by spilling: that form
+// plans over the 128-row shapes.
+template <int AM>
+constexpr int first_tile_cfg() { return AM == kAmQuant ? kFirstQuantTileCfg : 0; }
+
 template <int AM>
 static bool launch_tiled(const GemmA &a, int64_t M, const nvfp4_tensor *w, float *c, int64_t ldc, void *workspace,
                          size_t workspace_bytes, int num_cus, hipStream_t stream, const LrArgs *lr = nullptr) {
-    GemmPlan plan = plan_gemm(M, w->rows, w->cols, num_cus);
+    GemmPlan plan = plan_gemm(M, w->rows, w->cols, num_cus, first_tile_cfg<AM>());
     float *partials = nullptr;
     if (plan.splits > 1) {
         // split-K needs its partial planes; without room for them the product runs unsplit
@@ -1173,12 +1228,12 @@ static bool launch_tiled(const GemmA &a, int64_t M, const nvfp4_tensor *w, float
         else
             plan = GemmPlan{plan.cfg, 1, (int)(w->cols / kBK)};
     }
-    switch (plan.cfg) {
-    case 0: return launch_tile<256, 256, 4, 2, AM>(a, M, w, c, ldc, plan, partials, lr, stream);
-    case 1: return launch_tile<256, 192, 4, 2, AM>(a, M, w, c, ldc, plan, partials, lr, stream);
-    case 2: return launch_tile<128, 256, 2, 4, AM>(a, M, w, c, ldc, plan, partials, lr, stream);
-    default: return launch_tile<128, 128, 2, 2, AM>(a, M, w, c, ldc, plan, partials, lr, stream);
+    if constexpr (first_tile_cfg<AM>() == 0) {
+        if (plan.cfg == 0) return launch_tile<256, 256, 4, 2, AM>(a, M, w, c, ldc, plan, partials, lr, stream);
+        if (plan.cfg == 1) return launch_tile<256, 192, 4, 2, AM>(a, M, w, c, ldc, plan, partials, lr, stream);
     }
+    if (plan.cfg == 2) return launch_tile<128, 256, 2, 4, AM>(a, M, w, c, ldc, plan, partials, lr, stream);
+    return launch_tile<128, 128, 2, 2, AM>(a, M, w, c, ldc, plan, partials, lr, stream);
 }
 
 hipError_t launch_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, int64_t lda, const nvfp4_tensor *w,
@@ -1226,6 +1281,22 @@ hipError_t launch_gemm_lowrank(const void *a_bf16, const nvfp4_tensor *a_q, int6
         fused = launch_tiled<kAmBf16>(a, M, w, c, ldc, ws + tb, workspace_bytes - tb, num_cus, stream, &lr);
     }
     if (!fused) return launch_lowrank_up_add(ws, u, r, M, N, c, ldc, stream);
+    return hipGetLastError();
+}
+
+// Whether the product with activations quantized in the kernel can run fused: the tiled kernel
+// with K % 64 == 0 and 32-bit tile offsets.  Elsewhere the caller quantizes into the workspace
+// first.
+bool gemm_qa_fusable(int64_t M, int64_t K, int64_t lda) {
+    if (M <= 0 || K <= 0 || K % kBK != 0 || gemv_applies(M, K)) return false;
+    return (int64_t)(256 + 1) * lda * 2 + K * 2 < ((int64_t)1 << 31);
+}
+
+hipError_t launch_gemm_qa_fused(const void *a_bf16, const float *amax, int64_t M, int64_t lda, const nvfp4_tensor *w,
+                                float *c, int64_t ldc, void *workspace, size_t workspace_bytes, int num_cus,
+                                hipStream_t stream) {
+    const GemmA a{a_bf16, nullptr, nullptr, amax, lda};
+    launch_tiled<kAmQuant>(a, M, w, c, ldc, workspace, workspace_bytes, num_cus, stream);
     return hipGetLastError();
 }
 

@@ -32,9 +32,12 @@ struct GemmPlan {
     int splits;
     int slice_steps;
 };
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int num_cus);
+// first_cfg: the first shape of the table the plan may use (the quantizing A path starts at the
+// 128-row shapes, kFirstQuantTileCfg).
+constexpr int kFirstQuantTileCfg = 2;
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int num_cus, int first_cfg = 0);
 // Workspace bytes the plan for this problem uses (its split-K partial planes), 0 if none.
-size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus);
+size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus, int first_cfg = 0);
 
 hipError_t launch_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, int64_t lda, const nvfp4_tensor *w,
                        float *c, int64_t ldc, void *workspace, size_t workspace_bytes, int num_cus,
@@ -56,6 +59,13 @@ hipError_t launch_lowrank_down(const void *a_bf16, int64_t lda, const void *v, i
                                void *t, hipStream_t stream);
 hipError_t launch_lowrank_up_add(const void *t, const void *u, int r, int64_t M, int64_t N, float *c, int64_t ldc,
                                  hipStream_t stream);
+
+// W4A4 with the activations quantized in the GEMM (static amax): whether the fused kernel applies,
+// and its launch (C = A_hat . W_hat^T, A_hat the NVFP4 quantization of A with amax *amax).
+bool gemm_qa_fusable(int64_t M, int64_t K, int64_t lda);
+hipError_t launch_gemm_qa_fused(const void *a_bf16, const float *amax, int64_t M, int64_t lda, const nvfp4_tensor *w,
+                                float *c, int64_t ldc, void *workspace, size_t workspace_bytes, int num_cus,
+                                hipStream_t stream);
 
 size_t percentile_ws_bytes(int64_t cols, int per_channel);
 

@@ -76,7 +76,8 @@ enum {
     NVFP4_OP_GEMM = 2,
     NVFP4_OP_PERCENTILE = 3,
     NVFP4_OP_STATS = 4,
-    NVFP4_OP_LOWRANK = 5
+    NVFP4_OP_LOWRANK = 5,
+    NVFP4_OP_GEMM_QA = 6
 };
 
 /*
@@ -154,6 +155,26 @@ nvfp4_status nvfp4_dequantize(const nvfp4_tensor *in, void *out, nvfp4_dtype out
 nvfp4_status nvfp4_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, int64_t lda,
                         const nvfp4_tensor *w, float *c, int64_t ldc, void *workspace, size_t workspace_bytes,
                         hipStream_t stream);
+
+/*
+ * nvfp4_gemm_qa -- C [M x N] fp32 (row stride ldc) = A_hat . W_hat^T, the W4A4 product with the
+ * activations quantized inside the GEMM: A_hat is the NVFP4 form of a_bf16 [M x K] (bf16, row stride
+ * lda) under the static (calibrated) amax *a_amax -- exactly what nvfp4_quantize(amax_in = a_amax)
+ * would store -- so no activation-quantize launch precedes the product ("Qwen3-VL-8B-Instruct-
+ * heretic-NVFP4", "Quantization Details": NVFP4 activations with a per-tensor amax;
+ * "Qwen-Rapid-AIO-NVFP4", "Recommended Model": static per-layer amax from p99.9 calibration; with
+ * a static amax the quantization of a tile needs nothing outside the tile).  Values above the amax
+ * saturate.  Each workgroup quantizes the A rows of its tile in its staging path (the block scale,
+ * the codes and their exact f16 values; see nvfp4_quantize for the steps).
+ * The fused kernel runs when K % 64 == 0, M > 4 and N <= 512 (every N tile quantizes its rows of A
+ * again, so for wider products a separate quantize pass into the workspace followed by the W4A4
+ * kernel is faster and is what runs); otherwise NVFP4_ERR_WORKSPACE if the workspace is NULL or
+ * smaller than the quantized activations.
+ * a_amax: device pointer to one float (>= 0; 0 gives C = 0).  Inputs must be finite (no flag).
+ * workspace: nvfp4_workspace_size(NVFP4_OP_GEMM_QA, M, N, K) bytes covers either form.
+ */
+nvfp4_status nvfp4_gemm_qa(const void *a_bf16, const float *a_amax, int64_t M, int64_t lda, const nvfp4_tensor *w,
+                           float *c, int64_t ldc, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * nvfp4_gemm_lowrank -- C [M x N] fp32 (row stride ldc) = A_hat . W_hat^T + (A . V^T) . U^T: the

@@ -25,7 +25,8 @@ def nv():
 
 def test_header_declares_the_entry_points():
     assert _declared_functions() == sorted(["nvfp4_quantize", "nvfp4_quantize_fp8", "nvfp4_dequantize", "nvfp4_gemm",
-                                            "nvfp4_gemm_fp8a", "nvfp4_matrix_stats", "nvfp4_gemm_lowrank", "amax_percentile",
+                                            "nvfp4_gemm_fp8a", "nvfp4_matrix_stats", "nvfp4_gemm_lowrank", "nvfp4_gemm_qa",
+                                            "amax_percentile",
                                             "nvfp4_workspace_size", "nvfp4_status_string"])
 
 
@@ -184,6 +185,23 @@ def test_gemm_lowrank_validation(nv):
     bad = _qt(nv, 9, 32)
     assert call(aq=ctypes.byref(bad)) == 2                            # a_q rows != M
     assert call(M=-1) == 2
+
+
+def test_gemm_qa_validation(nv):
+    f = nv.lib.nvfp4_gemm_qa
+    P = ctypes.c_void_p
+    w = _qt(nv, 64, 128)
+    w_odd = _qt(nv, 64, 48)  # K % 64 != 0: the unfused form, which needs the workspace
+    ws = nv.workspace_size(nv.OP_GEMM_QA, 8, 64, 48)
+    assert ws >= 8 * 24 + 8 * 3  # codes and scales of the quantized activations
+    assert f(P(FAKE), None, 8, 128, ctypes.byref(w), P(FAKE), 64, None, 0, None) == 1        # amax NULL
+    assert f(P(FAKE), P(FAKE + 2), 8, 128, ctypes.byref(w), P(FAKE), 64, None, 0, None) == 3  # amax align
+    assert f(None, P(FAKE), 8, 128, ctypes.byref(w), P(FAKE), 64, None, 0, None) == 1        # A NULL
+    assert f(P(FAKE), P(FAKE), 8, 64, ctypes.byref(w), P(FAKE), 64, None, 0, None) == 2      # lda < K
+    assert f(P(FAKE), P(FAKE), 8, 128, ctypes.byref(w), P(FAKE), 32, None, 0, None) == 2     # ldc < N
+    assert f(P(FAKE), P(FAKE), -1, 128, ctypes.byref(w), P(FAKE), 64, None, 0, None) == 2
+    assert f(P(FAKE), P(FAKE), 8, 48, ctypes.byref(w_odd), P(FAKE), 64, None, 0, None) == 5  # unfused, no ws
+    assert f(P(FAKE), P(FAKE), 8, 48, ctypes.byref(w_odd), P(FAKE), 64, P(FAKE), 8, None) == 5
 
 
 def test_percentile_validation(nv):

@@ -749,3 +749,84 @@ def test_gemm_lowrank_attention_projection_full(nv):
     err = oracle.gemm_error(c, oracle.gemm_lowrank(a_bits, ref, v_bits, u_bits))
     _note(f"  floored max rel err {err:.3e}")
     assert err <= GEMM_TOL
+
+
+# ------------------------------------------------------------------------------------------------
+# W4A4 with the activation quantization inside the GEMM (static amax)
+# ------------------------------------------------------------------------------------------------
+# fused where K % 64 == 0, M > 4 and N <= 512 (128-row tiles, split-K for few tiles); elsewhere
+# (M <= 4, K % 64 != 0, wider N) A is quantized into the workspace first.  The reference quantizes
+# A with the same static amax in the oracle and contracts the exact operands in float64.
+QA_SHAPES = [(16, 64, 256), (2, 300, 1024), (64, 96, 112), (200, 300, 512), (100, 500, 4096), (2048, 384, 3072),
+             (130, 1000, 128), (100, 1000, 4096), (512, 12288, 4096), (300, 520, 640)]
+
+
+@pytest.mark.parametrize("mnk", QA_SHAPES)
+def test_gemm_qa(nv, mnk):
+    m, n, k = mnk
+    _note(f"gemm qa (static amax) {mnk}")
+    q, ref = _rand_q(nv, n, k, seed=m * 11 + n, sigma=0.015)
+    a_bits = synth.bf16_bits(np.random.default_rng(m * 5 + k).standard_normal((m, k)).astype(np.float32))
+    amax = np.float32(0.8 * np.abs(oracle.bf16_bits_to_f64(a_bits)).max())  # static amax below max: clipping
+    aref, _ = oracle.quantize(a_bits, oracle.BF16, amax=float(amax))
+    cref = oracle.gemm_w4a4(aref, ref)
+    amax_d = torch.tensor([amax], dtype=torch.float32, device=DEV)
+    c = nv.gemm_qa(to_dev_bf16(a_bits), q, amax_d).cpu().numpy()
+    err = oracle.gemm_error(c, cref)
+    assert err <= GEMM_TOL, err
+    if m > 1:  # strided A and C
+        out = padded(torch.empty((m, n), dtype=torch.float32, device=DEV), 4)
+        nv.gemm_qa(padded(to_dev_bf16(a_bits), 8), q, amax_d, out=out)
+        assert oracle.gemm_error(out.cpu().numpy(), cref) <= GEMM_TOL
+
+
+def test_gemm_qa_exact_cases(nv):
+    _note("gemm qa: one-hot rows, amax 0, values equal to the separate quantize")
+    n, k = 192, 320
+    q, ref = _rand_q(nv, n, k, seed=17)
+    # one-hot rows with amax 1 (the quantized activations are 6 x 448 x g = 2688 fl(1/2688), one
+    # ulp from 1): each output is one product, so it matches the float64 reference to the two fp32
+    # roundings of the scale factors (K = 336: the unfused form; K = 256: fused)
+    for kk in (336, 256):
+        qk, refk = _rand_q(nv, n, kk, seed=18 + kk)
+        eye = np.zeros((kk, kk), np.float32)
+        eye[np.arange(kk), np.arange(kk)] = 1.0
+        eb = synth.bf16_bits(eye)
+        one = torch.tensor([1.0], dtype=torch.float32, device=DEV)
+        c = nv.gemm_qa(to_dev_bf16(eb), qk, one).cpu().numpy()
+        aref, _ = oracle.quantize(eb, oracle.BF16, amax=1.0)
+        assert np.max(np.abs(oracle.dequantize(aref, "f64") - np.eye(kk))) <= 2.0 ** -24
+        cref = oracle.gemm_w4a4(aref, refk)
+        assert np.all(np.abs(c - cref) <= 2.5e-7 * np.abs(cref)), kk
+    # amax 0: every code is 0, C = 0
+    a_bits = synth.bf16_bits(np.random.default_rng(3).standard_normal((64, k)).astype(np.float32))
+    zero = torch.zeros(1, dtype=torch.float32, device=DEV)
+    assert not nv.gemm_qa(to_dev_bf16(a_bits), q, zero).cpu().numpy().any()
+    # the fused form (N = 512) against the separate quantize + W4A4 product on the GPU (same operand
+    # values, different summation order): within the fp32 accumulation error
+    k2 = 1024
+    q2, _ = _rand_q(nv, 512, k2, seed=19)
+    a2 = synth.bf16_bits(np.random.default_rng(4).standard_normal((300, k2)).astype(np.float32))
+    amax = torch.tensor([2.5], dtype=torch.float32, device=DEV)
+    c_fused = nv.gemm_qa(to_dev_bf16(a2), q2, amax).cpu().numpy()
+    aq = _quant(nv, to_dev_bf16(a2), amax=amax)
+    c_two = nv.gemm(aq, q2).cpu().numpy()
+    assert oracle.gemm_error(c_fused, c_two) <= 1e-5
+
+
+def test_gemm_qa_attention_projection_full(nv):
+    _note("gemm qa 4096x3072x3072 (full), static amax = p99.9 of |A| per channel, max over channels")
+    w = synth.attn_proj_weight()
+    a_bits = synth.attn_proj_activations()
+    ref, _ = oracle.quantize(w)
+    q = _quant(nv, to_dev_f32(w))
+    _assert_q_equal(q, ref, "attn weight")
+    pct, _ = nv.amax_percentile(to_dev_bf16(a_bits), 99.9, per_channel=True)
+    amax = pct.max().reshape(1)
+    aref, _ = oracle.quantize(a_bits, oracle.BF16, amax=float(amax.item()))
+    rows = np.random.default_rng(2).choice(4096, 256, replace=False)
+    c = nv.gemm_qa(to_dev_bf16(a_bits), q, amax).cpu().numpy()[rows]
+    cref = oracle.gemm_f64(oracle.dequantize(aref, "f64")[rows], oracle.dequantize(ref, "f64"))
+    err = oracle.gemm_error(c, cref)
+    _note(f"  floored max rel err {err:.3e}")
+    assert err <= GEMM_TOL
