@@ -18,12 +18,13 @@ constexpr int kLrDownBM = 64;   // rows of A per workgroup
 constexpr int kLrDownBN = 32;   // columns of T per workgroup
 constexpr int kLrDownKC = 128;  // K per staged chunk
 constexpr int kLrDownRow = kLrDownKC + 8;  // padded LDS row (bf16): fragment reads spread over banks
+constexpr int kLrDownSPW = kLrDownKC / 16 / 4;  // 16-deep slices of a chunk per wave
 
 // A workgroup (4 waves) computes a 64 x 32 block of T over the whole of K.  Chunks of 128 of K of
 // its A rows and V rows are loaded with whole 16-byte pieces per lane (rows read contiguously),
 // staged in LDS (two buffers: the next chunk's loads are in flight while the current one is
-// multiplied), and read back as matrix fragments; wave w multiplies the 16-deep slices 2w, 2w + 1
-// of each chunk into its own two 32 x 32 accumulators, and the four waves' sums are added in LDS
+// multiplied), and read back as matrix fragments; wave w multiplies its quarter of each chunk's
+// 16-deep slices into its own two 32 x 32 accumulators, and the four waves' sums are added in LDS
 // in wave order (fixed, so the result does not depend on timing).  Workgroups that share rows of
 // A are numbered to land on one XCD at about the same time, so those rows come from its L2.
 __global__ __launch_bounds__(256) void k_lr_down(const __bf16 *__restrict__ A, int64_t lda,
@@ -32,6 +33,8 @@ __global__ __launch_bounds__(256) void k_lr_down(const __bf16 *__restrict__ A, i
     constexpr int A_UNITS = kLrDownBM * (kLrDownKC / 8) / 256;  // 16-byte pieces per thread per chunk
     constexpr int V_UNITS = kLrDownBN * (kLrDownKC / 8) / 256;
     constexpr int STAGE = (kLrDownBM + kLrDownBN) * kLrDownRow;   // bf16 per LDS buffer
+    static_assert(A_UNITS * 256 == kLrDownBM * (kLrDownKC / 8) && V_UNITS * 256 == kLrDownBN * (kLrDownKC / 8),
+                  "the pieces of a chunk cover the tile's rows exactly");
     __shared__ __attribute__((aligned(16))) __bf16 lds[2 * STAGE > 4 * 2 * 16 * 64 * 2 ? 2 * STAGE : 4 * 2 * 16 * 64 * 2];
     const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, kh = (lane >> 5) * 8;
@@ -46,24 +49,25 @@ __global__ __launch_bounds__(256) void k_lr_down(const __bf16 *__restrict__ A, i
     const int vrows = (r - c0) < kLrDownBN ? (r - c0) : kLrDownBN;
     const __amdgpu_buffer_rsrc_t ra = lr_rsrc(A + m0 * lda, ((mrows - 1) * lda + K) * 2);
     const __amdgpu_buffer_rsrc_t rv = lr_rsrc(V + (int64_t)c0 * K, (int64_t)vrows * K * 2);
-    // this thread's pieces: piece u = tid + 256 q -> row u / 16, 8 elements at (u % 16) * 8
+    // this thread's pieces: piece u = tid + 256 q -> row u / (KC / 8), 8 elements at (u % (KC / 8)) * 8
     uint32_t a_off[A_UNITS], v_off[V_UNITS], a_lds[A_UNITS], v_lds[V_UNITS];
     uint32_t a_k[A_UNITS], v_k[V_UNITS];
 #pragma unroll
     for (int q = 0; q < A_UNITS; q++) {
-        const int u = tid + 256 * q, row = u / 16, c8 = (u % 16) * 8;
+        const int u = tid + 256 * q, row = u / (kLrDownKC / 8), c8 = (u % (kLrDownKC / 8)) * 8;
         a_off[q] = (uint32_t)(row * lda + c8) * 2;
         a_k[q] = (uint32_t)c8;
         a_lds[q] = (uint32_t)(row * kLrDownRow + c8);
     }
 #pragma unroll
     for (int q = 0; q < V_UNITS; q++) {
-        const int u = tid + 256 * q, row = u / 16, c8 = (u % 16) * 8;
+        const int u = tid + 256 * q, row = u / (kLrDownKC / 8), c8 = (u % (kLrDownKC / 8)) * 8;
         v_off[q] = (uint32_t)((int64_t)row * K + c8) * 2;
         v_k[q] = (uint32_t)c8;
         v_lds[q] = (uint32_t)((kLrDownBM + row) * kLrDownRow + c8);
     }
-    // four register sets of loads: three chunks stay in flight while one is multiplied
+    // four register sets of loads: three chunks stay in flight while one is multiplied (eight
+    // sets, or chunks of 256, measured no faster)
     constexpr int NSET = 4;
     bf16x8 ga[NSET][A_UNITS], gv[NSET][V_UNITS];
     // chunks past K load zeros, so the loads carry no branches (and the waits stay exact)
@@ -88,8 +92,8 @@ __global__ __launch_bounds__(256) void k_lr_down(const __bf16 *__restrict__ A, i
     auto mma = [&](int buf) {
         const __bf16 *st = lds + buf * STAGE;
 #pragma unroll
-        for (int s = 0; s < 2; s++) {
-            const int kk = (2 * wid + s) * 16 + kh;
+        for (int s = 0; s < kLrDownSPW; s++) {
+            const int kk = (kLrDownSPW * wid + s) * 16 + kh;
             const bf16x8 fv = *reinterpret_cast<const bf16x8 *>(st + (kLrDownBM + l32) * kLrDownRow + kk);
 #pragma unroll
             for (int i = 0; i < 2; i++) {
@@ -98,25 +102,23 @@ __global__ __launch_bounds__(256) void k_lr_down(const __bf16 *__restrict__ A, i
             }
         }
     };
-    // chunk c is multiplied from LDS buffer c % 2 and was loaded into register set c % 4
+    // chunk c is multiplied from LDS buffer c % 2 and was loaded into register set c % NSET
     const int64_t nchunks = (K + kLrDownKC - 1) / kLrDownKC;
 #pragma unroll
     for (int set = 0; set < NSET; set++) load(set, (int64_t)set * kLrDownKC);
     store(0, 0);
     load(0, (int64_t)NSET * kLrDownKC);
     __syncthreads();
-    auto step = [&](int64_t c, int set_next) {  // set_next = (c + 1) % 4
+    auto step = [&](int64_t c, int set_next) {  // set_next = (c + 1) % NSET
         mma((int)(c & 1));
         store(set_next, (int)((c + 1) & 1));
         load(set_next, (c + 1 + NSET) * kLrDownKC);
         __syncthreads();
     };
-    // whole rounds of four: chunks past the end are zeros (no branches, so the waits stay exact)
-    for (int64_t c = 0; c < nchunks; c += 4) {
-        step(c, 1);
-        step(c + 1, 2);
-        step(c + 2, 3);
-        step(c + 3, 0);
+    // whole rounds of NSET: chunks past the end are zeros (no branches, so the waits stay exact)
+    for (int64_t c = 0; c < nchunks; c += NSET) {
+#pragma unroll
+        for (int i = 0; i < NSET; i++) step(c + i, (i + 1) % NSET);
     }
     // the four waves' partial tiles, as [wave][tile][element][lane], summed in wave order
     float *red = reinterpret_cast<float *>(lds);
