@@ -90,7 +90,8 @@ nvfp4_status check_qtensor(const nvfp4_tensor *t) {
 // pointer may be NULL only when the matrix has no elements.
 nvfp4_status check_matrix(const void *p, int64_t rows, int64_t cols, int64_t ld, int eb, int align = 16) {
     if (rows < 0 || cols < 0 || ld < cols) return NVFP4_ERR_SHAPE;
-    if (!p && rows != 0 && cols != 0) return NVFP4_ERR_NULL;
+    if (rows == 0 || cols == 0) return NVFP4_OK;  // no element is addressed
+    if (!p) return NVFP4_ERR_NULL;
     if ((reinterpret_cast<uintptr_t>(p) % align) != 0 || (rows > 1 && ((ld * eb) % align) != 0))
         return NVFP4_ERR_ALIGN;
     return NVFP4_OK;
@@ -236,7 +237,7 @@ nvfp4_status nvfp4_gemm_lowrank(const void *a_bf16, const nvfp4_tensor *a_q, int
     const int64_t N = w->rows, K = w->cols;
     if (M < 0) return NVFP4_ERR_SHAPE;
     if (rank < 16 || rank > 256 || rank % 16 != 0) return NVFP4_ERR_SHAPE;
-    if (!a_bf16 && M > 0) return NVFP4_ERR_NULL;  // the branch always takes the bf16 activations
+    if (!a_bf16 && M > 0 && K > 0) return NVFP4_ERR_NULL;  // the branch always takes the bf16 activations
     st = check_matrix(a_bf16, M, K, lda, 2);
     if (st != NVFP4_OK) return st;
     if (a_q) {
@@ -244,19 +245,18 @@ nvfp4_status nvfp4_gemm_lowrank(const void *a_bf16, const nvfp4_tensor *a_q, int
         if (st != NVFP4_OK) return st;
         if (a_q->rows != M || a_q->cols != K) return NVFP4_ERR_SHAPE;
     }
-    if (!lr_down || !lr_up) return NVFP4_ERR_NULL;
     st = check_matrix(lr_down, rank, K, K, 2);
     if (st != NVFP4_OK) return st;
     st = check_matrix(lr_up, N, rank, rank, 2);
     if (st != NVFP4_OK) return st;
     st = check_matrix(c, M, N, ldc, 4, 4);
     if (st != NVFP4_OK) return st;
-    if (!workspace || workspace_bytes < lowrank_t_bytes(M)) return NVFP4_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return NVFP4_ERR_ALIGN;
+    if (M > 0 && K > 0 && (!workspace || workspace_bytes < lowrank_t_bytes(M))) return NVFP4_ERR_WORKSPACE;
+    if (workspace && !aligned16(workspace)) return NVFP4_ERR_ALIGN;
     const int cus = current_device_cus();
     if (cus == 0) return NVFP4_ERR_DEVICE;
-    hipError_t e = (K == 0) ? launch_fill_zero_f32(c, M, N, ldc, stream)
-                            : launch_gemm_lowrank(a_bf16, a_q, M, lda, w, lr_down, lr_up, (int)rank, c, ldc,
+    hipError_t e = (K == 0 || M == 0) ? launch_fill_zero_f32(c, M, N, ldc, stream)
+                                      : launch_gemm_lowrank(a_bf16, a_q, M, lda, w, lr_down, lr_up, (int)rank, c, ldc,
                                                   workspace, workspace_bytes, cus, stream);
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
 }

@@ -182,7 +182,7 @@ nvfp4_status nvfp4_gemm_qa(const void *a_bf16, const float *a_amax, int64_t M, i
  * ("Qwen Image 2.1: INT4 + FP4", section "What I quantized": FP4 weights with BF16 rank-128
  * branches).
  *   a_bf16  [M x K] bf16, row stride lda: the activations of the branch, and of the main product
- *           when a_q is NULL (W4A16); required (may be NULL only when M == 0);
+ *           when a_q is NULL (W4A16); required (may be NULL only when M == 0 or K == 0);
  *   a_q     NULL, or the NVFP4 activations [M x K] of a W4A4 main product;
  *   lr_down V [rank x K] bf16, dense; lr_up U [N x rank] bf16, dense; 16 <= rank <= 256,
  *           rank % 16 == 0 (NVFP4_ERR_SHAPE otherwise).
@@ -191,7 +191,8 @@ nvfp4_status nvfp4_gemm_qa(const void *a_bf16, const float *a_amax, int64_t M, i
  * unsplit tiled kernel, otherwise as a second pass that adds into C.
  * workspace (device, 16-byte aligned): at least nvfp4_workspace_size(NVFP4_OP_LOWRANK, M, N, K)
  * bytes -- T (M * 1 KiB) then the product's split-K planes; NVFP4_ERR_WORKSPACE when smaller than
- * the T part (with less than the full size the product runs unsplit).
+ * the T part (with less than the full size the product runs unsplit).  M == 0 or K == 0 needs no
+ * workspace (C = 0 when K == 0).
  */
 nvfp4_status nvfp4_gemm_lowrank(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, int64_t lda,
                                 const nvfp4_tensor *w, const void *lr_down, const void *lr_up, int64_t rank, float *c,

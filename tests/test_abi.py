@@ -178,7 +178,7 @@ def test_gemm_lowrank_validation(nv):
                  d["wsb"], None)
     assert call(r=0) == 2 and call(r=24) == 2 and call(r=272) == 2  # rank: 16 .. 256, multiple of 16
     assert call(a=None) == 1                                          # the branch needs the bf16 activations
-    assert call(v=None) == 1 and call(u=None) == 1
+    assert call(v=None) == 1 and call(u=None) == 1                    # V, U NULL with elements
     assert call(lda=16) == 2                                          # lda < K
     assert call(v=P(FAKE + 8)) == 3                                   # alignment of V
     assert call(ws=None) == 5 and call(wsb=8 * 1024 - 1) == 5         # T does not fit

@@ -830,3 +830,26 @@ def test_gemm_qa_attention_projection_full(nv):
     err = oracle.gemm_error(c, cref)
     _note(f"  floored max rel err {err:.3e}")
     assert err <= GEMM_TOL
+
+
+def test_gemm_lowrank_and_qa_empty(nv):
+    _note("gemm lowrank / qa: M = 0 and K = 0")
+    import bit_gemm_nvfp4_amd as nvm
+    q, _ = _rand_q(nv, 40, 64, seed=1)
+    v = torch.zeros((16, 64), dtype=torch.bfloat16, device=DEV)
+    u = torch.zeros((40, 16), dtype=torch.bfloat16, device=DEV)
+    a0 = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
+    assert nv.gemm_lowrank(a0, q, v, u).shape == (0, 40)
+    amax = torch.ones(1, dtype=torch.float32, device=DEV)
+    assert nv.gemm_qa(a0, q, amax).shape == (0, 40)
+    # K = 0: C = 0
+    w0 = nvm.NVFP4Tensor(torch.zeros((5, 0), dtype=torch.uint8, device=DEV),
+                         torch.zeros((5, 0), dtype=torch.uint8, device=DEV), torch.ones(1, device=DEV))
+    a = torch.zeros((3, 0), dtype=torch.bfloat16, device=DEV)
+    out = torch.full((3, 5), 7.0, device=DEV)
+    nv.gemm_lowrank(a, w0, torch.zeros((16, 0), dtype=torch.bfloat16, device=DEV),
+                    torch.zeros((5, 16), dtype=torch.bfloat16, device=DEV), out=out)
+    assert not out.cpu().numpy().any()
+    out.fill_(7.0)
+    nv.gemm_qa(a, w0, amax, out=out)
+    assert not out.cpu().numpy().any()
