@@ -42,12 +42,16 @@ __global__ void k_pct_init(uint32_t *ws, int64_t nch, uint32_t k) {
         ws[i] = (i >= nch && i < 2 * nch) ? k : 0u;
 }
 
-// One workgroup per (64 channels, row chunk).  Every lane loads 16 bytes of a row (8 bf16 / fp16
-// or 4 fp32 channels), so one wave load covers whole 128- or 256-byte row segments of several rows;
-// U rows are in flight per lane (rows past the chunk are masked).  Counters live in LDS as
-// [digit][channel] (64 KB, two workgroups per CU).  DT: NVFP4_F32 (31-bit keys), NVFP4_BF16 or
+// One workgroup of 8 waves per (256 channels, row chunk).  Every lane loads 16 bytes of a row (8 bf16 /
+// fp16 or 4 fp32 channels), so one wave load covers whole 512-byte (bf16) or 1 KB (fp32) row segments:
+// wide enough for the DRAM pages, where 64-channel strips of a 6 KB row read at about 2.8 TB/s.
+// U rows are in flight per lane (rows past the chunk are masked).  Counters live in LDS as 16-bit
+// halves of [digit][channel] words (128 KB; a chunk has at most 65535 rows, so no half overflows),
+// which also halves the lanes that add into one bank.  DT: NVFP4_F32 (31-bit keys), NVFP4_BF16 or
 // NVFP4_F16 (15-bit keys).
-constexpr int kPctThreads = 256;
+constexpr int kPctThreads = 512;
+constexpr int kPctChannels = 256;   // channels per workgroup of the histogram pass
+constexpr int kPctMaxRowsPerWg = 65535;
 
 template <int DT, int U>
 __global__ __launch_bounds__(kPctThreads) void k_pct_hist(const uint8_t *__restrict__ x, int64_t rows, int64_t cols,
@@ -55,17 +59,18 @@ __global__ __launch_bounds__(kPctThreads) void k_pct_hist(const uint8_t *__restr
                                                           int shift, int dbits, int first_pass,
                                                           uint32_t *__restrict__ ws) {
     constexpr int EPL = (DT == NVFP4_F32) ? 4 : 8;  // channels per lane (one 16-byte load)
-    constexpr int LPR = 64 / EPL;                    // lanes per 64-channel row segment
+    constexpr int WCH = kPctChannels;
+    constexpr int LPR = WCH / EPL;                   // lanes per row segment of the workgroup's channels
     constexpr int RPW = 64 / LPR;                    // rows per wave load
+    static_assert(LPR <= 64 && 64 % LPR == 0, "a wave covers whole row segments");
     constexpr int NW = kPctThreads / 64;
     constexpr int STEP = NW * RPW;                   // rows per workgroup load step
-    constexpr int WCH = 64;
-    __shared__ uint32_t hist[256 * WCH];
+    __shared__ uint32_t hist[256 * WCH / 2];         // two 16-bit counters per word
     const int64_t nch = per_channel ? cols : 1;
     uint32_t *prefix = ws, *maxkey = ws + 2 * nch, *ghist = ws + 3 * nch;
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    for (int i = tid; i < 256 * WCH / 4; i += kPctThreads) reinterpret_cast<u32x4 *>(hist)[i] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = tid; i < 256 * WCH / 8; i += kPctThreads) reinterpret_cast<u32x4 *>(hist)[i] = u32x4{0u, 0u, 0u, 0u};
 
     const int64_t c0 = (int64_t)blockIdx.x * WCH;
     const int64_t r0 = (int64_t)blockIdx.y * rows_per_wg;
@@ -98,7 +103,10 @@ __global__ __launch_bounds__(kPctThreads) void k_pct_hist(const uint8_t *__restr
 #pragma unroll
         for (int j = 0; j < EPL; j++) {
             if (first_pass) mk[j] = max(mk[j], key[j]);
-            if ((key[j] >> hs) == pre[j]) atomicAdd(&hist[((key[j] >> shift) & dmask) * WCH + lc + j], 1u);
+            if ((key[j] >> hs) == pre[j]) {
+                const int i = (int)((key[j] >> shift) & dmask) * WCH + lc + j;
+                atomicAdd(&hist[i >> 1], 1u << ((i & 1) * 16));
+            }
         }
     };
     if (active) {
@@ -129,17 +137,19 @@ __global__ __launch_bounds__(kPctThreads) void k_pct_hist(const uint8_t *__restr
     }
     __syncthreads();
     const int nbins = 1 << dbits;
+    auto count = [&](int i) { return (hist[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu; };
     if (per_channel) {
         for (int i = tid; i < nbins * WCH; i += kPctThreads) {
-            const uint32_t cnt = hist[i];
+            const uint32_t cnt = count(i);
             const int64_t ch = c0 + (i % WCH);
             if (cnt && ch < cols) atomicAdd(&ghist[ch * 256 + i / WCH], cnt);
         }
     } else {
-        // the whole tensor is one channel: add up the local channels of each bin first
+        // the whole tensor is one channel: add up the local channels of each bin first (each lane
+        // starts at its own channel, so the lanes of a wave read different banks)
         for (int b = tid; b < nbins; b += kPctThreads) {
             uint32_t cnt = 0;
-            for (int c = 0; c < WCH; c++) cnt += hist[b * WCH + c];
+            for (int c = 0; c < WCH; c++) cnt += count(b * WCH + ((c + b) & (WCH - 1)));
             if (cnt) atomicAdd(&ghist[b], cnt);
         }
     }
@@ -417,7 +427,7 @@ static hipError_t launch_pct_t(const void *x, int64_t rows, int64_t cols, int64_
                                float *out_pct, float *out_max, int32_t *flags, uint32_t *ws, int num_cus,
                                hipStream_t stream) {
     constexpr int EB = (DT == NVFP4_F32) ? 4 : 2;
-    constexpr int WCH = 64;
+    constexpr int WCH = kPctChannels;
     constexpr int KEYBITS = (DT == NVFP4_F32) ? 31 : 15;
     const int64_t nch = per_channel ? cols : 1;
     if (per_channel) {
@@ -436,32 +446,41 @@ static hipError_t launch_pct_t(const void *x, int64_t rows, int64_t cols, int64_
     }
     hipLaunchKernelGGL(k_pct_init, dim3((unsigned)((nch * 259 + 255) / 256 < 4096 ? (nch * 259 + 255) / 256 : 4096)),
                        dim3(256), 0, stream, ws, nch, k);
-    // Enough workgroups to cover the CUs twice, but at least 1024 rows each: every workgroup pays for
-    // clearing and merging 64 channels x 256 counters, which few rows would not amortize.  Long
-    // chunks keep 16 rows in flight per lane, short ones 4.
+    // A workgroup per CU (its 128 KB of counters fill most of the LDS), but at least 1024 rows each:
+    // every workgroup pays for clearing and merging 256 channels x 256 counters, which few rows would
+    // not amortize; and at most 65535 rows, so the 16-bit counters cannot overflow.  Long chunks keep
+    // 16 rows in flight per lane, short ones 4.  Counts and maxima add up across launches, so rows
+    // beyond what one grid of 65535 chunks holds go to further launches over later rows.
     const int64_t cgroups = (cols + WCH - 1) / WCH;
-    const int64_t target = (int64_t)num_cus * 2;
-    int64_t rchunks = (target + cgroups - 1) / cgroups;
-    const int64_t max_chunks = (rows + 1023) / 1024;
-    if (rchunks > max_chunks) rchunks = max_chunks;
-    if (rchunks < 1) rchunks = 1;
-    if (rchunks > 65535) rchunks = 65535;
-    const int rows_per_wg = (int)((rows + rchunks - 1) / rchunks);
-    rchunks = (rows + rows_per_wg - 1) / rows_per_wg;
-    const bool deep = rows_per_wg >= 8192;
+    const int64_t seg_max = (int64_t)kPctMaxRowsPerWg * 65535;
+    auto hist_pass = [&](int shift, int dbits, int first_pass) {
+        for (int64_t s0 = 0; s0 < rows; s0 += seg_max) {
+            const int64_t srows = (rows - s0) < seg_max ? (rows - s0) : seg_max;
+            int64_t rchunks = (int64_t)num_cus / cgroups;  // one round of workgroups: no straggler round
+            const int64_t max_chunks = (srows + 1023) / 1024;
+            if (rchunks > max_chunks) rchunks = max_chunks;
+            const int64_t min_chunks = (srows + kPctMaxRowsPerWg - 1) / kPctMaxRowsPerWg;
+            if (rchunks < min_chunks) rchunks = min_chunks;
+            if (rchunks < 1) rchunks = 1;
+            const int rows_per_wg = (int)((srows + rchunks - 1) / rchunks);
+            rchunks = (srows + rows_per_wg - 1) / rows_per_wg;
+            const uint8_t *xs = (const uint8_t *)x + s0 * ld_x * EB;
+            if (rows_per_wg >= 8192)
+                hipLaunchKernelGGL((k_pct_hist<DT, 16>), dim3((unsigned)cgroups, (unsigned)rchunks), dim3(kPctThreads),
+                                   0, stream, xs, srows, cols, ld_x * EB, per_channel, rows_per_wg, shift, dbits,
+                                   first_pass, ws);
+            else
+                hipLaunchKernelGGL((k_pct_hist<DT, 4>), dim3((unsigned)cgroups, (unsigned)rchunks), dim3(kPctThreads),
+                                   0, stream, xs, srows, cols, ld_x * EB, per_channel, rows_per_wg, shift, dbits,
+                                   first_pass, ws);
+        }
+    };
     int consumed = 0;
     bool first = true;
     while (consumed < KEYBITS) {
         const int dbits = (KEYBITS - consumed) >= 8 ? 8 : (KEYBITS - consumed);
         const int shift = KEYBITS - consumed - dbits;
-        if (deep)
-            hipLaunchKernelGGL((k_pct_hist<DT, 16>), dim3((unsigned)cgroups, (unsigned)rchunks), dim3(kPctThreads), 0,
-                               stream, (const uint8_t *)x, rows, cols, ld_x * EB, per_channel, rows_per_wg, shift,
-                               dbits, first ? 1 : 0, ws);
-        else
-            hipLaunchKernelGGL((k_pct_hist<DT, 4>), dim3((unsigned)cgroups, (unsigned)rchunks), dim3(kPctThreads), 0,
-                               stream, (const uint8_t *)x, rows, cols, ld_x * EB, per_channel, rows_per_wg, shift,
-                               dbits, first ? 1 : 0, ws);
+        hist_pass(shift, dbits, first ? 1 : 0);
         consumed += dbits;
         const int last = consumed == KEYBITS;
         hipLaunchKernelGGL(k_pct_select<DT>, dim3((unsigned)((nch + 3) / 4)), dim3(256), 0, stream, ws, nch, dbits,

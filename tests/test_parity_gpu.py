@@ -387,6 +387,39 @@ def test_percentile_calibration_full_rows(nv):
     assert np.array_equal(pct.cpu().numpy(), rp) and np.array_equal(mx.cpu().numpy(), rm)
 
 
+def test_percentile_long_row_chunks(nv):
+    # 2.1 M rows on 16 channels: the histogram pass gives each workgroup over 8192 rows (16 rows in
+    # flight per lane), with a ragged last chunk
+    _note("percentile 2100000 x 16 bf16")
+    x = synth.calib_activations(rows=2_100_000, cols=16, seed=5001)
+    xd = to_dev_bf16(x)
+    for p, per_channel in [(99.9, True), (50.0, True), (99.9, False)]:
+        pct, mx = nv.amax_percentile(xd, p, per_channel)
+        rp, rm = oracle.amax_percentile(x, p, per_channel, dtype=oracle.BF16)
+        assert np.array_equal(pct.cpu().numpy(), rp), (p, per_channel)
+        assert np.array_equal(mx.cpu().numpy(), rm), (p, per_channel)
+
+
+def test_percentile_counter_capacity(nv):
+    # 65535 x 256 + 1000 rows that are all 1.0 but for +-2.0 in the last 100 rows: with 256 row
+    # chunks a chunk would count more than 65535 equal keys of one channel, so the launch must cut
+    # the rows finer.  The answer is known in closed form: the m-th largest |x| of a channel is 2.0
+    # for m <= 100 and 1.0 beyond (m > 16 keeps it on the histogram path).
+    rows, cols = 65535 * 256 + 1000, 16
+    _note(f"percentile {rows} x {cols} bf16, counter capacity")
+    x = torch.full((rows, cols), 1.0, dtype=torch.bfloat16, device=DEV)
+    x[-100:, 0::2] = -2.0
+    x[-100:, 1::2] = 2.0
+    for n, per_channel, m_two in [(rows, True, 100), (rows * cols, False, 100 * cols)]:
+        for m in [m_two // 2, m_two, m_two + 1, 3 * m_two]:
+            p = 100.0 * (n - m + 0.5) / n  # nearest rank n - m + 1: the m-th largest
+            pct, mx = nv.amax_percentile(x, p, per_channel)
+            want = 2.0 if m <= m_two else 1.0
+            assert torch.all(pct == want).item(), (per_channel, m, pct[:4].tolist())
+            assert torch.all(mx == 2.0).item(), (per_channel, m)
+    del x
+
+
 # shapes that select each of the GEMM kernel's tile configurations (256x256, 256x192, 128x256,
 # 128x128), with aligned and ragged K and ragged M / N edges
 @pytest.mark.parametrize("mnk", [(576, 16384, 64), (448, 16512, 64), (130, 1000, 128), (704, 10880, 128),
