@@ -418,39 +418,38 @@ __global__ __launch_bounds__(256) void k_encode(TileGeom gm, const float *__rest
 }
 
 // ---------------------------------------------------------------------------------------------
-// Single-pass path: one launch of at most four workgroups per CU, small enough that every workgroup
-// is resident at once on an otherwise idle GPU.  Each wave loads its TPW tiles and keeps them in
-// registers while the grid agrees on amax, then encodes them from registers, so the input crosses
-// HBM once.  Tiles beyond the register capacity are streamed for the maximum and read again for
-// the encode.
+// Single-pass path: one launch of one workgroup of NWV waves per CU (16 waves: four per SIMD, with
+// at most 128 VGPRs; 8 waves: two per SIMD), so that every workgroup is resident at once on an
+// otherwise idle GPU.  Each wave loads its TPW tiles and keeps them in registers while the grid
+// agrees on amax, then encodes them from registers, so the input crosses HBM once.  Tiles beyond
+// the register capacity are streamed for the maximum and read again for the encode.
 //
 // Agreement on amax: every workgroup publishes one 64-bit word (call epoch << 32 | its partial
-// maximum) in its workspace slot; workgroup 0 polls all slots until each carries this call's
-// epoch, then publishes (epoch << 32 | tensor maximum) in a result word that the other workgroups
-// poll.  The payload travels inside the atomic word, so relaxed device-scope atomics suffice (no
-// cache maintenance in the loop).  The epoch differs between calls, so the workspace needs no
-// clearing and earlier contents are ignored.  The polls are bounded: if other work kept some
-// workgroups from being scheduled for that long, bit 1 of `flags` is set and the outputs are
-// invalid, instead of a hang.
+// maximum) in its workspace slot, then polls all slots until each carries this call's epoch and
+// takes the maximum of their payloads.  Every workgroup reads every slot (one per CU, so a poll
+// moves a few KB), so the maximum reaches all of them one memory round trip after the last slot
+// is written, with no relay through a leader.  The payload travels inside the atomic word, so
+// relaxed device-scope atomics suffice (no cache maintenance in the loop).  The epoch differs
+// between calls, so the workspace needs no clearing and earlier contents are ignored.  The polls
+// are bounded: if other work kept some workgroups from being scheduled for that long, bit 1 of
+// `flags` is set and the outputs are invalid, instead of a hang.
 // ---------------------------------------------------------------------------------------------
 constexpr int kSlotBase = 16;       // workspace words before the 64-bit slots (8-byte aligned)
 
-constexpr int kFusedPerCu = 4;      // most workgroups per CU of the single-pass kernel
 constexpr uint32_t kPollLimit = 1u << 22;
 
-template <int SRC, int TPW, int PB, int OUTF>
-__global__ __launch_bounds__(256) void k_quant_fused(TileGeom gm, const float *__restrict__ src_scale,
-                                                     uint32_t *__restrict__ ws, uint32_t epoch,
-                                                     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
-                                                     float *__restrict__ g_out, int32_t *__restrict__ flags) {
-    __shared__ uint32_t red[4];
+template <int SRC, int TPW, int PB, int OUTF, int NWV>
+__global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const float *__restrict__ src_scale,
+                                                          uint32_t *__restrict__ ws, uint32_t epoch,
+                                                          uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
+                                                          float *__restrict__ g_out, int32_t *__restrict__ flags) {
+    __shared__ uint32_t red[NWV];
     __shared__ uint32_t amax_bits;
     const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint64_t ntiles = (gm.nblocks + 63) / 64;
-    const uint64_t wave = (uint64_t)blockIdx.x * 4 + wid, nwaves = (uint64_t)gridDim.x * 4;
+    const uint64_t wave = (uint64_t)blockIdx.x * NWV + wid, nwaves = (uint64_t)gridDim.x * NWV;
     const float sc = (SRC == NVFP4_E4M3 && src_scale) ? *src_scale : 1.0f;
     uint64_t *slots = reinterpret_cast<uint64_t *>(ws + kSlotBase);
-    uint64_t *result = reinterpret_cast<uint64_t *>(ws);
 
     // ---- phase 1: load the resident tiles, block maxima (NVFP4), tensor maximum ----
     TileRegs<SRC> t[TPW];
@@ -482,55 +481,39 @@ __global__ __launch_bounds__(256) void k_quant_fused(TileGeom gm, const float *_
     __syncthreads();
     if (wid == 0) {
         if (lane == 0) {
-            const uint32_t wgmax = max(max(red[0], red[1]), max(red[2], red[3]));
+            uint32_t wgmax = 0;
+#pragma unroll
+            for (int i = 0; i < NWV; i++) wgmax = max(wgmax, red[i]);
             __hip_atomic_store(&slots[blockIdx.x], ((uint64_t)epoch << 32) | wgmax, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
-        // ---- workgroup 0 waits for every slot of this call and publishes the maximum in the
-        // result word; the others wait for the result word only (one load per poll, so the
-        // polling adds almost no memory traffic while other workgroups still stream input) ----
+        // ---- wait for every slot of this call; all loads of a chunk of 8 slots per lane in
+        // flight at once ----
+        const uint32_t G = gridDim.x;
         uint32_t a = 0;
-        if (blockIdx.x == 0) {
-            // all loads of a chunk of 8 slots per lane in flight at once
-            const uint32_t G = gridDim.x;
-            for (uint32_t it = 0;; it++) {
-                bool ready = true;
-                a = 0;
-                for (uint32_t base = 0; base < G; base += 512) {
-                    uint64_t v[8];
+        for (uint32_t it = 0;; it++) {
+            bool ready = true;
+            a = 0;
+            for (uint32_t base = 0; base < G; base += 512) {
+                uint64_t v[8];
 #pragma unroll
-                    for (int k = 0; k < 8; k++) {
-                        const uint32_t i = base + (uint32_t)lane + 64u * k;
-                        v[k] = i < G ? __hip_atomic_load(&slots[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                     : (uint64_t)epoch << 32;
-                    }
+                for (int k = 0; k < 8; k++) {
+                    const uint32_t i = base + (uint32_t)lane + 64u * k;
+                    v[k] = i < G ? __hip_atomic_load(&slots[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                 : (uint64_t)epoch << 32;
+                }
 #pragma unroll
-                    for (int k = 0; k < 8; k++) {
-                        if ((uint32_t)(v[k] >> 32) != epoch) ready = false;
-                        a = max(a, (uint32_t)v[k]);
-                    }
+                for (int k = 0; k < 8; k++) {
+                    if ((uint32_t)(v[k] >> 32) != epoch) ready = false;
+                    a = max(a, (uint32_t)v[k]);
                 }
-                if (__all(ready)) break;
-                if (it >= kPollLimit) {
-                    if (lane == 0 && flags) atomicOr(flags, 2);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
             }
-            a = wave_max_u32(a);
-            if (lane == 0)
-                __hip_atomic_store(result, ((uint64_t)epoch << 32) | a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            for (uint32_t it = 0;; it++) {
-                const uint64_t v = __hip_atomic_load(result, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                a = (uint32_t)v;
-                if ((uint32_t)(v >> 32) == epoch) break;
-                if (it >= kPollLimit) {
-                    if (lane == 0 && flags) atomicOr(flags, 2);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
+            if (__all(ready)) break;
+            if (it >= kPollLimit) {
+                if (lane == 0 && flags) atomicOr(flags, 2);
+                break;
             }
+            __builtin_amdgcn_s_sleep(1);
         }
         a = wave_max_u32(a);
         if (lane == 0) amax_bits = a;
@@ -601,8 +584,8 @@ static uint32_t next_epoch() {
     return counter.fetch_add(0x61C88647u, std::memory_order_relaxed) | 1u;
 }
 
-// Largest residency (tiles per wave) whose registers still leave room for four workgroups per CU
-// (at most 128 VGPRs), and for two.
+// Largest residency (tiles per wave) whose registers still leave room for four waves per SIMD (at
+// most 128 VGPRs), and for two.
 template <int SRC>
 constexpr int kMaxTpw4 = SRC == NVFP4_F32 ? 4 : SRC == NVFP4_BF16 ? 5 : SRC == NVFP4_F16 ? 8 : 12;
 template <int SRC>
@@ -616,18 +599,19 @@ constexpr int kStreamTpw = SRC == NVFP4_F32 ? 4 : SRC == NVFP4_BF16 ? 6 : SRC ==
 template <int SRC>
 constexpr int kStreamBatch = SRC == NVFP4_F32 ? 2 : 4;
 
-// Workgroups of k_quant_fused<SRC, TPW> that can be resident on one CU (at most kFusedPerCu),
-// from the runtime's occupancy calculation; computed once per instantiation.
-template <int SRC, int TPW, int PB, int OUTF>
+// Workgroups of k_quant_fused<SRC, TPW, PB, OUTF, NWV> that can be resident on one CU (at least
+// one is assumed), from the runtime's occupancy calculation; computed once per instantiation.
+template <int SRC, int TPW, int PB, int OUTF, int NWV>
 static int fused_per_cu() {
     static std::atomic<int> cached{0};
     int n = cached.load(std::memory_order_relaxed);
     if (n == 0) {
         int b = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_quant_fused<SRC, TPW, PB, OUTF>, 256, 0) != hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_quant_fused<SRC, TPW, PB, OUTF, NWV>, NWV * 64, 0) !=
+                hipSuccess ||
             b < 1)
             b = 1;
-        n = b < kFusedPerCu ? b : kFusedPerCu;
+        n = b;
         cached.store(n, std::memory_order_relaxed);
     }
     return n;
@@ -643,20 +627,20 @@ struct QOut {
     float *scale;
 };
 
-template <int SRC, int TPW, int OUTF, int PB = 1>
+template <int SRC, int TPW, int OUTF, int NWV, int PB = 1>
 static void launch_fused(const TileGeom &gm, int grid, const float *src_scale, uint32_t *ws, const QOut &out,
                          int32_t *flags, int num_cus, hipStream_t stream) {
-    const int cap = fused_per_cu<SRC, TPW, PB, OUTF>() * num_cus;
+    const int cap = fused_per_cu<SRC, TPW, PB, OUTF, NWV>() * num_cus;
     if (grid > cap) grid = cap;
-    hipLaunchKernelGGL((k_quant_fused<SRC, TPW, PB, OUTF>), dim3(grid), dim3(256), 0, stream, gm, src_scale, ws,
-                       next_epoch(), out.codes, out.scales, out.scale, flags);
+    hipLaunchKernelGGL((k_quant_fused<SRC, TPW, PB, OUTF, NWV>), dim3(grid), dim3(NWV * 64), 0, stream, gm,
+                       src_scale, ws, next_epoch(), out.codes, out.scales, out.scale, flags);
 }
 
 // Resident launch: tiles per wave rounded up to a supported residency, at most T.
-template <int SRC, int OUTF, int T>
+template <int SRC, int OUTF, int NWV, int T>
 static void launch_resident(const TileGeom &gm, int grid, uint64_t tpw, const float *src_scale, uint32_t *ws,
                             const QOut &out, int32_t *flags, int num_cus, hipStream_t stream) {
-#define NVFP4_LAUNCH(T_) launch_fused<SRC, (T_), OUTF>(gm, grid, src_scale, ws, out, flags, num_cus, stream)
+#define NVFP4_LAUNCH(T_) launch_fused<SRC, (T_), OUTF, NWV>(gm, grid, src_scale, ws, out, flags, num_cus, stream)
     if (tpw <= 1) NVFP4_LAUNCH(1);
     else if (tpw <= 2) NVFP4_LAUNCH(2);
     else if (tpw <= 3) NVFP4_LAUNCH(3);
@@ -669,30 +653,29 @@ static void launch_resident(const TileGeom &gm, int grid, uint64_t tpw, const fl
 #undef NVFP4_LAUNCH
 }
 
-// Tiles spread over all CUs: four workgroups each (four waves per SIMD hide each other's
-// latencies) when every wave's tiles then fit the smaller register budget, else two workgroups
-// each with up to kMaxTpw resident tiles; fewer workgroups for small tensors.  Beyond that the
-// streaming variant runs (the rest is read twice).
+// Tiles spread over all CUs: one workgroup of 16 waves each (four waves per SIMD hide each other's
+// latencies) when every wave's tiles then fit the smaller register budget, else 8 waves each with up
+// to kMaxTpw resident tiles; fewer workgroups for small tensors.  Beyond that the streaming variant
+// runs (the rest is read twice).
 template <int SRC, int OUTF>
 static void launch_fused_any(const TileGeom &gm, const float *src_scale, uint32_t *ws, const QOut &out,
                              int32_t *flags, int num_cus, hipStream_t stream) {
     const uint64_t ntiles = (gm.nblocks + 63) / 64;
-    if (4 * num_cus <= kMaxSlots) {
-        const int grid4 = grid_for(ntiles, 4, 4 * num_cus);
-        const uint64_t tpw4 = (ntiles + 4 * (uint64_t)grid4 - 1) / (4 * (uint64_t)grid4);
-        if (tpw4 <= (uint64_t)kMaxTpw4<SRC>) {
-            launch_resident<SRC, OUTF, kMaxTpw4<SRC>>(gm, grid4, tpw4, src_scale, ws, out, flags, num_cus, stream);
-            return;
-        }
-    }
-    const int grid = grid_for(ntiles, 4, 2 * num_cus);
-    const uint64_t tpw = (ntiles + 4 * (uint64_t)grid - 1) / (4 * (uint64_t)grid);
-    if (tpw > (uint64_t)kMaxTpw<SRC>) {
-        launch_fused<SRC, kStreamTpw<SRC>, OUTF, kStreamBatch<SRC>>(gm, grid, src_scale, ws, out, flags, num_cus,
-                                                                   stream);
+    const int max_grid = num_cus < kMaxSlots ? num_cus : kMaxSlots;
+    const int grid16 = grid_for(ntiles, 16, max_grid);
+    const uint64_t tpw16 = (ntiles + 16 * (uint64_t)grid16 - 1) / (16 * (uint64_t)grid16);
+    if (tpw16 <= (uint64_t)kMaxTpw4<SRC>) {
+        launch_resident<SRC, OUTF, 16, kMaxTpw4<SRC>>(gm, grid16, tpw16, src_scale, ws, out, flags, max_grid, stream);
         return;
     }
-    launch_resident<SRC, OUTF, kMaxTpw<SRC>>(gm, grid, tpw, src_scale, ws, out, flags, num_cus, stream);
+    const int grid = grid_for(ntiles, 8, max_grid);
+    const uint64_t tpw = (ntiles + 8 * (uint64_t)grid - 1) / (8 * (uint64_t)grid);
+    if (tpw > (uint64_t)kMaxTpw<SRC>) {
+        launch_fused<SRC, kStreamTpw<SRC>, OUTF, 8, kStreamBatch<SRC>>(gm, grid, src_scale, ws, out, flags, max_grid,
+                                                                      stream);
+        return;
+    }
+    launch_resident<SRC, OUTF, 8, kMaxTpw<SRC>>(gm, grid, tpw, src_scale, ws, out, flags, max_grid, stream);
 }
 
 template <int SRC, int OUTF>

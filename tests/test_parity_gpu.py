@@ -176,7 +176,7 @@ def test_quantize_attention_weight_full(nv):
 
 
 # Tall tensors whose tile counts (64 blocks per tile, 3 tiles per 3072-wide row) give the
-# single-pass kernel 2, 4, 5, 8 and 12 resident tiles per wave at four workgroups per CU on a
+# single-pass kernel 2, 4, 5, 8 and 12 resident tiles per wave at four waves per SIMD on a
 # 256-CU part, the largest residency for fp32, bf16, f16 and e4m3 sources respectively.
 @pytest.mark.parametrize("dtype,rows", [("f32", 2000), ("f32", 5000), ("bf16", 6000), ("f16", 10000),
                                         ("e4m3", 15000)])
