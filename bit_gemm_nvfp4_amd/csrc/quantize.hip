@@ -228,7 +228,9 @@ __device__ __forceinline__ BlockScale block_scale(uint32_t bm, float g, float si
 // Write one tile: the scale bytes (lane L: block L) and the codes, each lane converting its own
 // vectors with its block's reciprocal.  The conversions take one of two wave-uniform paths: the
 // plain one, or, when some block's reciprocal overflowed, one that keeps zeros at zero.  Tiles
-// wholly inside the tensor store without per-lane bounds checks.
+// wholly inside the tensor store without per-lane bounds checks.  The stores are non-temporal:
+// little of the output is read back soon, and the kernel ends about 0.5 us sooner when the L2
+// holds no dirty output lines to write back at its end.
 template <int SRC>
 __device__ __forceinline__ void tile_store(const TileRegs<SRC> &t, BlockScale b, float sc, uint64_t tile,
                                            uint64_t nblocks, uint8_t *__restrict__ codes,
@@ -238,7 +240,7 @@ __device__ __forceinline__ void tile_store(const TileRegs<SRC> &t, BlockScale b,
     constexpr int BPL = 64 / VPB;
     const uint64_t blk0 = tile * 64;
     const bool full = blk0 + 64 <= nblocks;  // wave-uniform
-    if (full || blk0 + lane < nblocks) scales[blk0 + lane] = (uint8_t)b.sbyte;
+    if (full || blk0 + lane < nblocks) __builtin_nontemporal_store((uint8_t)b.sbyte, scales + blk0 + lane);
     float rj[VPB];
 #pragma unroll
     for (int j = 0; j < VPB; j++) rj[j] = VPB == 1 ? b.r : __shfl(b.r, j * BPL + lane / VPB, 64);
@@ -270,11 +272,11 @@ __device__ __forceinline__ void tile_store(const TileRegs<SRC> &t, BlockScale b,
     uint8_t *dst = codes + (blk0 * VPB + lane) * (EPV / 2);
     auto store = [&](int j) {
         if constexpr (EPV == 4) {
-            *reinterpret_cast<uint16_t *>(dst + j * 64 * (EPV / 2)) = (uint16_t)out[j][0];
+            __builtin_nontemporal_store((uint16_t)out[j][0], reinterpret_cast<uint16_t *>(dst + j * 64 * (EPV / 2)));
         } else if constexpr (EPV == 8) {
-            *reinterpret_cast<uint32_t *>(dst + j * 64 * (EPV / 2)) = out[j][0];
+            __builtin_nontemporal_store(out[j][0], reinterpret_cast<uint32_t *>(dst + j * 64 * (EPV / 2)));
         } else {
-            *reinterpret_cast<u32x2 *>(dst + j * 64 * (EPV / 2)) = u32x2{out[j][0], out[j][1]};
+            __builtin_nontemporal_store(u32x2{out[j][0], out[j][1]}, reinterpret_cast<u32x2 *>(dst + j * 64 * (EPV / 2)));
         }
     };
     if (full) {
@@ -354,11 +356,11 @@ __device__ __forceinline__ void tile_store_fp8(const TileRegs<SRC> &t, float sca
     auto store = [&](int j) {
         uint8_t *d = dst + j * 64 * EPV;
         if constexpr (EPV == 4) {
-            *reinterpret_cast<uint32_t *>(d) = w[j][0];
+            __builtin_nontemporal_store(w[j][0], reinterpret_cast<uint32_t *>(d));
         } else if constexpr (EPV == 8) {
-            *reinterpret_cast<u32x2 *>(d) = u32x2{w[j][0], w[j][1]};
+            __builtin_nontemporal_store(u32x2{w[j][0], w[j][1]}, reinterpret_cast<u32x2 *>(d));
         } else {
-            *reinterpret_cast<u32x4 *>(d) = u32x4{w[j][0], w[j][1], w[j][2], w[j][3]};
+            __builtin_nontemporal_store(u32x4{w[j][0], w[j][1], w[j][2], w[j][3]}, reinterpret_cast<u32x4 *>(d));
         }
     };
     if (full) {
