@@ -264,7 +264,7 @@ __device__ __forceinline__ void topm_insert(uint32_t (&L)[M], uint32_t k) {
 // magnitude bits, XOR-complemented when `invert` (then the lists hold the smallest originals).
 // The waves' lists are then merged pairwise through LDS in three rounds.
 constexpr int kTopmWaves = 8;
-constexpr int kTopmU = 8;
+constexpr int kTopmU = 4;
 
 template <int DT, int M>
 __global__ __launch_bounds__(64 * kTopmWaves) void k_pct_topm(const uint8_t *__restrict__ x, int64_t rows,
@@ -403,9 +403,10 @@ static bool launch_topm(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
     constexpr int CPL = DT != NVFP4_F32 ? 4 : 2;
     constexpr int EB = DT == NVFP4_F32 ? 4 : 2;
     const int64_t cgroups = (cols + 64 * CPL - 1) / (64 * CPL);
-    // two workgroups per CU, at least 64 rows each; the lists must fit the workspace and the
-    // final wave (one lane per list)
-    int64_t rchunks = ((int64_t)num_cus * 2 + cgroups - 1) / cgroups;
+    // one round of workgroups, at most one per CU (a second partial round, or more lists for the
+    // final merge, measured slower), at least 64 rows each; the lists must fit the workspace and
+    // the final wave (one lane per list)
+    int64_t rchunks = (int64_t)num_cus / cgroups;
     const int64_t by_rows = (rows + 63) / 64;
     int64_t by_ws = 259 / (M + 1);
     if (by_ws > 64) by_ws = 64;
@@ -438,9 +439,18 @@ static hipError_t launch_pct_t(const void *x, int64_t rows, int64_t cols, int64_
         if (m <= (uint32_t)kTopmMax) {
             const int inv = top ? 0 : 1;
             bool done;
-            if (m <= 4) done = launch_topm<DT, 4>(x, rows, cols, ld_x, m, inv, out_pct, out_max, flags, ws, num_cus, stream);
-            else if (m <= 8) done = launch_topm<DT, 8>(x, rows, cols, ld_x, m, inv, out_pct, out_max, flags, ws, num_cus, stream);
-            else done = launch_topm<DT, 16>(x, rows, cols, ld_x, m, inv, out_pct, out_max, flags, ws, num_cus, stream);
+            // lists of exactly m keys up to 6 (each key costs 2 M compare-exchange VALU), then 8, 12, 16
+#define NVFP4_TOPM(M_) launch_topm<DT, (M_)>(x, rows, cols, ld_x, m, inv, out_pct, out_max, flags, ws, num_cus, stream)
+            if (m <= 1) done = NVFP4_TOPM(1);
+            else if (m <= 2) done = NVFP4_TOPM(2);
+            else if (m <= 3) done = NVFP4_TOPM(3);
+            else if (m <= 4) done = NVFP4_TOPM(4);
+            else if (m <= 5) done = NVFP4_TOPM(5);
+            else if (m <= 6) done = NVFP4_TOPM(6);
+            else if (m <= 8) done = NVFP4_TOPM(8);
+            else if (m <= 12) done = NVFP4_TOPM(12);
+            else done = NVFP4_TOPM(16);
+#undef NVFP4_TOPM
             if (done) return hipGetLastError();
         }
     }

@@ -369,6 +369,28 @@ def test_percentile(nv, dtype, shape):
         assert np.array_equal(pct.cpu().numpy(), rp)
 
 
+# the m-th largest and m-th smallest of 4096-row channels for m = 1..17: every list length of the
+# one-pass path (1-6, 8, 12, 16) at and just past its bucket edge, and the radix path beyond 16
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 13, 16, 17])
+def test_percentile_rank_near_ends(nv, dtype, m):
+    rows, cols = 4096, 64
+    _note(f"percentile {dtype} rank {m} from either end")
+    x = np.random.default_rng(900 + m).standard_t(3, size=(rows, cols)).astype(np.float32)
+    if dtype == "bf16":
+        src, odt = synth.bf16_bits(x), oracle.BF16
+        xd = to_dev_bf16(src)
+    else:
+        src, odt = x, oracle.F32
+        xd = to_dev_f32(src)
+    for k in (rows - m + 1, m):
+        p = 100.0 * (k - 0.5) / rows  # nearest rank k
+        pct, mx = nv.amax_percentile(xd, p)
+        rp, rm = oracle.amax_percentile(src, p, dtype=odt)
+        assert np.array_equal(pct.cpu().numpy(), rp), (m, k)
+        assert np.array_equal(mx.cpu().numpy(), rm), (m, k)
+
+
 def test_percentile_attention_activations_full(nv):
     # the activations of the attention projection, per-channel p99.9 (the 5th largest of 4096)
     _note("percentile 4096 x 3072 bf16")
