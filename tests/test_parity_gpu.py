@@ -325,6 +325,54 @@ def test_gemm_attention_projection_full(nv):
     assert oracle.gemm_error(c4, c4ref) <= GEMM_TOL
 
 
+def test_mlp_w4a4_chain_full(nv):
+    # the Qwen3-VL-8B text MLP at full size: gate / up 12288 x 4096 and down 4096 x 12288 NVFP4
+    # weights, 512 tokens of bf16 activations quantized with their run-time amax, W4A4 products.
+    # The intermediate between the projections (SiLU(gate) * up, rounded to bf16) is test glue,
+    # formed from the oracle's gate and up outputs; both sides quantize and project it.
+    _note("Qwen3-VL MLP chain 512 x 4096 -> 12288 -> 4096, W4A4")
+    wg, wu, wd = synth.mlp_weights()
+    qs, refs = [], []
+    for w in (wg, wu, wd):
+        ref, _ = oracle.quantize(w)
+        q = _quant(nv, to_dev_f32(w))
+        _assert_q_equal(q, ref, f"mlp weight {w.shape}")
+        qs.append(q)
+        refs.append(ref)
+    a_bits = synth.mlp_activations()
+    aq = _quant(nv, to_dev_bf16(a_bits))
+    aref, _ = oracle.quantize(a_bits, oracle.BF16)
+    _assert_q_equal(aq, aref, "mlp activations")
+    gate_ref = oracle.gemm_w4a4(aref, refs[0])
+    up_ref = oracle.gemm_w4a4(aref, refs[1])
+    assert oracle.gemm_error(nv.gemm(aq, qs[0]).cpu().numpy(), gate_ref) <= GEMM_TOL
+    assert oracle.gemm_error(nv.gemm(aq, qs[1]).cpu().numpy(), up_ref) <= GEMM_TOL
+    h_bits = synth.bf16_bits((gate_ref / (1.0 + np.exp(-gate_ref)) * up_ref).astype(np.float32))
+    hq = _quant(nv, to_dev_bf16(h_bits))
+    href, _ = oracle.quantize(h_bits, oracle.BF16)
+    _assert_q_equal(hq, href, "mlp intermediate")
+    down = nv.gemm(hq, qs[2]).cpu().numpy()
+    assert oracle.gemm_error(down, oracle.gemm_w4a4(href, refs[2])) <= GEMM_TOL
+
+
+# one block of the 60-block layer stack: its six FP8 weights requantized (bit-exact), then each
+# one's W4A16 product at M = 4096, checked on 64 sampled rows
+@pytest.mark.parametrize("j", range(6))
+def test_stack_block_requantize_and_gemm(nv, j):
+    block = 37
+    _note(f"stack block {block} weight {j}")
+    b, sc = synth.stack_weight_fp8(block, j)
+    ref, _ = oracle.quantize(b, oracle.E4M3, float(sc))
+    q = _quant(nv, to_dev_u8(b), src_scale=torch.tensor([sc], dtype=torch.float32, device=DEV))
+    _assert_q_equal(q, ref, f"stack {block}.{j}")
+    k = b.shape[1]
+    a_bits = synth.bf16_bits(synth.rng(5500 + j).standard_normal((4096, k)).astype(np.float32))
+    c = nv.gemm(to_dev_bf16(a_bits), q)
+    rows = np.sort(synth.rng(5600 + j).choice(4096, 64, replace=False))
+    cs = c[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    assert oracle.gemm_error(cs, oracle.gemm_w4a16(a_bits[rows], ref)) <= GEMM_TOL
+
+
 def test_gemv_modulation_full(nv):
     _note("gemv M=2 over 18432x3072")
     w = synth.modulation_weight()
