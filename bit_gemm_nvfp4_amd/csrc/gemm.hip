@@ -34,10 +34,10 @@
 // Workgroup ids are remapped so that the workgroups the hardware places on one XCD (ids congruent
 // mod 8) take neighbouring tiles that share W columns in that XCD's L2.
 //
-// k_gemv: for M <= 4 the product is bound by streaming W once from HBM.  A (expanded to bf16) sits
-// in LDS; each lane takes whole 16-element blocks of a W row, forms the 16-term dot products with
-// bf16 dot2 instructions and applies the block scale once per block; a wave reduction finishes
-// each row.  A wave works on two rows at once with all their loads issued ahead of the arithmetic.
+// k_gemv: for M <= 4 the product is bound by streaming W once from HBM.  A (bf16, or NVFP4 / E4M3
+// activations expanded exactly to bf16) sits in LDS; each lane takes whole 16-element blocks of a W
+// row, forms the 16-term dot products with bf16 dot2 instructions and applies the block scale once
+// per block; a wave reduction finishes each row.  A wave works on two rows at once with all their loads issued ahead of the arithmetic.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -859,7 +859,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__
 // ------------------------------------------------------------------------------------------------
 // GEMV, M <= 4
 // ------------------------------------------------------------------------------------------------
-template <int MM, bool A_Q>
+template <int MM, int AM>
 __global__ __launch_bounds__(256) void k_gemv(const __bf16 *__restrict__ A, int64_t lda,
                                               const uint8_t *__restrict__ a_codes,
                                               const uint8_t *__restrict__ a_scales, const float *__restrict__ a_g,
@@ -898,22 +898,24 @@ __global__ __launch_bounds__(256) void k_gemv(const __bf16 *__restrict__ A, int6
         load_batch(rows, 0);
     }
 
-    // stage A (expanded exactly to bf16 for the W4A4 form) in LDS
+    // stage A (expanded exactly to bf16 for NVFP4 and E4M3 activations) in LDS
     for (int64_t i = tid; i < MM * (K / 8); i += blockDim.x) {
         const int64_t m = i / (K / 8), c8 = i % (K / 8);
         u32x4 v;
-        if constexpr (!A_Q) {
+        if constexpr (AM == kAmBf16) {
             v = *reinterpret_cast<const u32x4 *>(A + m * lda + c8 * 8);
-        } else {
+        } else if constexpr (AM == kAmNvfp4) {
             const uint32_t w = *reinterpret_cast<const uint32_t *>(a_codes + m * (K / 2) + c8 * 4);
             v = expand8(w, e4m3_to_f32(a_scales[m * (K / 16) + c8 / 2]));
+        } else {
+            v = expand8_fp8_bf16(*reinterpret_cast<const u32x2 *>(a_codes + m * lda + c8 * 8));
         }
         *reinterpret_cast<u32x4 *>(&a_lds[m * kp + c8 * 4]) = v;
     }
     __syncthreads();
 
     const float gw = *w_g;
-    const float ga = A_Q ? *a_g : 1.0f;
+    const float ga = AM != kAmBf16 ? *a_g : 1.0f;
     for (; n < N; n += 2 * nwaves) {
         const int64_t rows[2] = {n, (n + nwaves) < N ? (n + nwaves) : n};
         float acc[2][MM];
@@ -956,7 +958,7 @@ __global__ __launch_bounds__(256) void k_gemv(const __bf16 *__restrict__ A, int6
                 const float t = wave_sum_f32(acc[h][m]);
                 if (lane == 0) {
                     float v = t;
-                    if (A_Q) v = v * ga;
+                    if (AM != kAmBf16) v = v * ga;
                     C[m * ldc + rows[h]] = v * gw;
                 }
             }
@@ -965,9 +967,10 @@ __global__ __launch_bounds__(256) void k_gemv(const __bf16 *__restrict__ A, int6
 }
 
 // k_gemv_reg: the same product for K <= 4096 without LDS.  Lane l works on blocks l + 64 u (u < UB) of
-// every row it visits, so it loads those blocks of A (expanded to bf16 for W4A4) into registers
-// once; a wave then streams pairs of W rows with all their loads issued ahead of the arithmetic.
-template <int MM, bool A_Q, int UB>
+// every row it visits, so it loads those blocks of A (expanded to bf16 for NVFP4 and E4M3
+// activations) into registers once; a wave then streams pairs of W rows with all their loads
+// issued ahead of the arithmetic.
+template <int MM, int AM, int UB>
 __global__ __launch_bounds__(256) void k_gemv_reg(const __bf16 *__restrict__ A, int64_t lda,
                                                   const uint8_t *__restrict__ a_codes,
                                                   const uint8_t *__restrict__ a_scales, const float *__restrict__ a_g,
@@ -1002,19 +1005,23 @@ __global__ __launch_bounds__(256) void k_gemv_reg(const __bf16 *__restrict__ A, 
     for (int m = 0; m < MM; m++)
 #pragma unroll
         for (int u = 0; u < UB; u++) {
-            if constexpr (!A_Q) {
+            if constexpr (AM == kAmBf16) {
                 const u32x4 *ap = reinterpret_cast<const u32x4 *>(A + m * lda + blk[u] * 16);
                 av[m][u][0] = ap[0];
                 av[m][u][1] = ap[1];
-            } else {
+            } else if constexpr (AM == kAmNvfp4) {
                 const u32x2 c = *reinterpret_cast<const u32x2 *>(a_codes + m * (K / 2) + blk[u] * 8);
                 const float s = __builtin_amdgcn_cvt_f32_fp8((int)a_scales[m * nblk + blk[u]], 0);
                 av[m][u][0] = expand8(c[0], s);
                 av[m][u][1] = expand8(c[1], s);
+            } else {
+                const u32x4 b = *reinterpret_cast<const u32x4 *>(a_codes + m * lda + blk[u] * 16);
+                av[m][u][0] = expand8_fp8_bf16(u32x2{b[0], b[1]});
+                av[m][u][1] = expand8_fp8_bf16(u32x2{b[2], b[3]});
             }
         }
     const float gw = *w_g;
-    const float ga = A_Q ? *a_g : 1.0f;
+    const float ga = AM != kAmBf16 ? *a_g : 1.0f;
     for (int64_t n = wave; n < N; n += 2 * nwaves) {
         const int64_t rows[2] = {n, (n + nwaves) < N ? (n + nwaves) : n};
         load_rows(rows);
@@ -1053,7 +1060,7 @@ __global__ __launch_bounds__(256) void k_gemv_reg(const __bf16 *__restrict__ A, 
                 const float t = wave_sum_f32(acc[h][m]);
                 if (lane == 0) {
                     float v = t;
-                    if (A_Q) v = v * ga;
+                    if (AM != kAmBf16) v = v * ga;
                     C[m * ldc + rows[h]] = v * gw;
                 }
             }
@@ -1064,48 +1071,56 @@ __global__ __launch_bounds__(256) void k_gemv_reg(const __bf16 *__restrict__ A, 
 // ------------------------------------------------------------------------------------------------
 // host launchers
 // ------------------------------------------------------------------------------------------------
+// Activation operand of the launchers: bf16 rows, an NVFP4 tensor, or E4M3 bytes.
+struct GemmA {
+    const void *bf16;       // kAmBf16: [M x K] bf16, row stride lda
+    const uint8_t *codes;   // kAmNvfp4: codes; kAmFp8: [M x K] E4M3 bytes, row stride lda
+    const uint8_t *scales;  // kAmNvfp4: block scales
+    const float *g;         // kAmNvfp4: global scale; kAmFp8: tensor scale
+    int64_t lda;
+};
+
 size_t gemv_lds_bytes(int64_t M, int64_t K) { return (size_t)M * (size_t)K * 2; }
 
 bool gemv_applies(int64_t M, int64_t K) { return M >= 1 && M <= 4 && gemv_lds_bytes(M, K) <= 64 * 1024; }
 
-template <int MM, bool A_Q, int UB>
-static void launch_gemv_reg(const void *a_bf16, int64_t lda, const nvfp4_tensor *a_q, const nvfp4_tensor *w,
-                            float *c, int64_t ldc, int num_cus, hipStream_t stream) {
+template <int MM, int AM, int UB>
+static void launch_gemv_reg(const GemmA &a, const nvfp4_tensor *w, float *c, int64_t ldc, int num_cus,
+                            hipStream_t stream) {
     const int64_t N = w->rows, K = w->cols;
     int64_t grid = (N + 7) / 8;  // one pass of two rows per wave, at most 16 workgroups per CU
     if (grid > (int64_t)num_cus * 16) grid = (int64_t)num_cus * 16;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((k_gemv_reg<MM, A_Q, UB>), dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16 *)a_bf16,
-                       lda, A_Q ? a_q->codes : nullptr, A_Q ? a_q->scales : nullptr, A_Q ? a_q->global_scale : nullptr,
-                       w->codes, w->scales, w->global_scale, c, ldc, N, K);
+    hipLaunchKernelGGL((k_gemv_reg<MM, AM, UB>), dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16 *)a.bf16,
+                       a.lda, a.codes, a.scales, a.g, w->codes, w->scales, w->global_scale, c, ldc, N, K);
 }
 
-template <int MM, bool A_Q>
-static void launch_gemv_t(const void *a_bf16, int64_t lda, const nvfp4_tensor *a_q, const nvfp4_tensor *w, float *c,
-                          int64_t ldc, int num_cus, hipStream_t stream) {
+template <int MM, int AM>
+static void launch_gemv_t(const GemmA &a, const nvfp4_tensor *w, float *c, int64_t ldc, int num_cus,
+                          hipStream_t stream) {
     const int64_t N = w->rows, K = w->cols;
     const int64_t ub = (K / 16 + 63) / 64;  // blocks per lane
-    if (ub <= 1) return launch_gemv_reg<MM, A_Q, 1>(a_bf16, lda, a_q, w, c, ldc, num_cus, stream);
-    if (ub <= 2) return launch_gemv_reg<MM, A_Q, 2>(a_bf16, lda, a_q, w, c, ldc, num_cus, stream);
-    if (ub <= 3) return launch_gemv_reg<MM, A_Q, 3>(a_bf16, lda, a_q, w, c, ldc, num_cus, stream);
-    if (ub <= 4) return launch_gemv_reg<MM, A_Q, 4>(a_bf16, lda, a_q, w, c, ldc, num_cus, stream);
+    if (ub <= 1) return launch_gemv_reg<MM, AM, 1>(a, w, c, ldc, num_cus, stream);
+    if (ub <= 2) return launch_gemv_reg<MM, AM, 2>(a, w, c, ldc, num_cus, stream);
+    if (ub <= 3) return launch_gemv_reg<MM, AM, 3>(a, w, c, ldc, num_cus, stream);
+    if (ub <= 4) return launch_gemv_reg<MM, AM, 4>(a, w, c, ldc, num_cus, stream);
     // a wave takes two rows per pass, one pass per wave up to 16 workgroups per CU
     int64_t grid = (N + 7) / 8;
     if (grid > (int64_t)num_cus * 16) grid = (int64_t)num_cus * 16;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((k_gemv<MM, A_Q>), dim3((unsigned)grid), dim3(256), gemv_lds_bytes(MM, K), stream,
-                       (const __bf16 *)a_bf16, lda, A_Q ? a_q->codes : nullptr, A_Q ? a_q->scales : nullptr,
-                       A_Q ? a_q->global_scale : nullptr, w->codes, w->scales, w->global_scale, c, ldc, N, K);
+    hipLaunchKernelGGL((k_gemv<MM, AM>), dim3((unsigned)grid), dim3(256), gemv_lds_bytes(MM, K), stream,
+                       (const __bf16 *)a.bf16, a.lda, a.codes, a.scales, a.g, w->codes, w->scales, w->global_scale, c,
+                       ldc, N, K);
 }
 
-template <bool A_Q>
-static void launch_gemv(int64_t M, const void *a_bf16, int64_t lda, const nvfp4_tensor *a_q, const nvfp4_tensor *w,
-                        float *c, int64_t ldc, int num_cus, hipStream_t stream) {
+template <int AM>
+static void launch_gemv(int64_t M, const GemmA &a, const nvfp4_tensor *w, float *c, int64_t ldc, int num_cus,
+                        hipStream_t stream) {
     switch (M) {
-    case 1: launch_gemv_t<1, A_Q>(a_bf16, lda, a_q, w, c, ldc, num_cus, stream); break;
-    case 2: launch_gemv_t<2, A_Q>(a_bf16, lda, a_q, w, c, ldc, num_cus, stream); break;
-    case 3: launch_gemv_t<3, A_Q>(a_bf16, lda, a_q, w, c, ldc, num_cus, stream); break;
-    default: launch_gemv_t<4, A_Q>(a_bf16, lda, a_q, w, c, ldc, num_cus, stream); break;
+    case 1: launch_gemv_t<1, AM>(a, w, c, ldc, num_cus, stream); break;
+    case 2: launch_gemv_t<2, AM>(a, w, c, ldc, num_cus, stream); break;
+    case 3: launch_gemv_t<3, AM>(a, w, c, ldc, num_cus, stream); break;
+    default: launch_gemv_t<4, AM>(a, w, c, ldc, num_cus, stream); break;
     }
 }
 
@@ -1158,15 +1173,6 @@ size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus, int first_cfg
     const GemmPlan p = plan_gemm(M, N, K, num_cus, first_cfg);
     return p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)N * 4 : 0;
 }
-
-// Activation operand of the tiled launch: bf16 rows, an NVFP4 tensor, or E4M3 bytes.
-struct GemmA {
-    const void *bf16;       // kAmBf16: [M x K] bf16, row stride lda
-    const uint8_t *codes;   // kAmNvfp4: codes; kAmFp8: [M x K] E4M3 bytes, row stride lda
-    const uint8_t *scales;  // kAmNvfp4: block scales
-    const float *g;         // kAmNvfp4: global scale; kAmFp8: tensor scale
-    int64_t lda;
-};
 
 // Returns true when the low-rank branch `lr` (if any) was added in the epilogue.
 template <int BM, int BN, int WM, int WN, int AM>
@@ -1241,17 +1247,14 @@ hipError_t launch_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, i
                        hipStream_t stream) {
     const int64_t K = w->cols;
     if (M == 0 || w->rows == 0) return hipGetLastError();
-    if (gemv_applies(M, K)) {
-        if (a_q) launch_gemv<true>(M, a_bf16, lda, a_q, w, c, ldc, num_cus, stream);
-        else launch_gemv<false>(M, a_bf16, lda, a_q, w, c, ldc, num_cus, stream);
-        return hipGetLastError();
-    }
     if (a_q) {
         const GemmA a{nullptr, a_q->codes, a_q->scales, a_q->global_scale, K};
-        launch_tiled<kAmNvfp4>(a, M, w, c, ldc, workspace, workspace_bytes, num_cus, stream);
+        if (gemv_applies(M, K)) launch_gemv<kAmNvfp4>(M, a, w, c, ldc, num_cus, stream);
+        else launch_tiled<kAmNvfp4>(a, M, w, c, ldc, workspace, workspace_bytes, num_cus, stream);
     } else {
         const GemmA a{a_bf16, nullptr, nullptr, nullptr, lda};
-        launch_tiled<kAmBf16>(a, M, w, c, ldc, workspace, workspace_bytes, num_cus, stream);
+        if (gemv_applies(M, K)) launch_gemv<kAmBf16>(M, a, w, c, ldc, num_cus, stream);
+        else launch_tiled<kAmBf16>(a, M, w, c, ldc, workspace, workspace_bytes, num_cus, stream);
     }
     return hipGetLastError();
 }
@@ -1271,8 +1274,9 @@ hipError_t launch_gemm_lowrank(const void *a_bf16, const nvfp4_tensor *a_q, int6
     if (K == 0) {
         launch_fill_zero_f32(c, M, N, ldc, stream);
     } else if (gemv_applies(M, K)) {
-        if (a_q) launch_gemv<true>(M, a_bf16, lda, a_q, w, c, ldc, num_cus, stream);
-        else launch_gemv<false>(M, a_bf16, lda, a_q, w, c, ldc, num_cus, stream);
+        if (a_q) launch_gemv<kAmNvfp4>(M, GemmA{nullptr, a_q->codes, a_q->scales, a_q->global_scale, K}, w, c, ldc,
+                                       num_cus, stream);
+        else launch_gemv<kAmBf16>(M, GemmA{a_bf16, nullptr, nullptr, nullptr, lda}, w, c, ldc, num_cus, stream);
     } else if (a_q) {
         const GemmA a{nullptr, a_q->codes, a_q->scales, a_q->global_scale, K};
         fused = launch_tiled<kAmNvfp4>(a, M, w, c, ldc, ws + tb, workspace_bytes - tb, num_cus, stream, &lr);
@@ -1305,7 +1309,8 @@ hipError_t launch_gemm_fp8(const uint8_t *a_fp8, const float *a_scale, int64_t M
                            hipStream_t stream) {
     if (M == 0 || w->rows == 0) return hipGetLastError();
     const GemmA a{nullptr, a_fp8, nullptr, a_scale, lda};
-    launch_tiled<kAmFp8>(a, M, w, c, ldc, workspace, workspace_bytes, num_cus, stream);
+    if (gemv_applies(M, w->cols)) launch_gemv<kAmFp8>(M, a, w, c, ldc, num_cus, stream);
+    else launch_tiled<kAmFp8>(a, M, w, c, ldc, workspace, workspace_bytes, num_cus, stream);
     return hipGetLastError();
 }
 

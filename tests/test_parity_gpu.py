@@ -373,6 +373,20 @@ def test_stack_block_requantize_and_gemm(nv, j):
     assert oracle.gemm_error(cs, oracle.gemm_w4a16(a_bits[rows], ref)) <= GEMM_TOL
 
 
+def test_gemv_fp8a_modulation_full(nv):
+    # the modulation GEMV with its two activation rows as FP8 (dynamic tensor scale)
+    _note("gemv fp8a M=2 over 18432x3072")
+    w = synth.modulation_weight()
+    ref, _ = oracle.quantize(w)
+    q = _quant(nv, to_dev_f32(w))
+    a_bits = synth.modulation_activations()
+    a8 = _quant_fp8(nv, to_dev_bf16(a_bits))
+    rb, rs, _ = oracle.quantize_fp8(a_bits, oracle.BF16)
+    _assert_fp8_equal(a8, rb, rs, "activations")
+    c = nv.gemm(a8, q).cpu().numpy()
+    assert oracle.gemm_error(c, oracle.gemm_w4a8(rb, rs, ref)) <= GEMM_TOL
+
+
 def test_gemv_modulation_full(nv):
     _note("gemv M=2 over 18432x3072")
     w = synth.modulation_weight()
@@ -616,9 +630,10 @@ def test_quantize_fp8_streamed_tensor(nv):
     _assert_fp8_equal(_quant_fp8(nv, to_dev_f32(x)), rb, rs, "large")
 
 
-# K % 64 != 0 takes k_gemm_tile; M <= 4 runs on the tiled kernels too (no GEMV form for FP8 A)
+# K % 64 != 0 takes k_gemm_tile; M <= 4 the GEMV forms (A in registers for K <= 4096, in LDS beyond)
 @pytest.mark.parametrize("mnk", [(16, 64, 256), (1, 64, 128), (4, 100, 48), (5, 70, 80), (37, 129, 272),
-                                 (130, 257, 1024), (300, 200, 3072), (576, 16384, 64), (130, 1000, 128)])
+                                 (130, 257, 1024), (300, 200, 3072), (576, 16384, 64), (130, 1000, 128),
+                                 (2, 300, 4608), (3, 1000, 3072), (4, 257, 8192)])
 def test_gemm_fp8a(nv, mnk):
     m, n, k = mnk
     _note(f"gemm fp8a {mnk}")
@@ -651,6 +666,10 @@ def test_gemm_fp8a_one_hot_all_bytes(nv):
     c = nv.gemm(a8, q).cpu().numpy()
     cref = oracle.gemm_w4a8(a, sc, ref)
     assert np.array_equal(c.astype(np.float64), cref.astype(np.float32).astype(np.float64))
+    # the same rows four at a time through the GEMV form
+    cv = np.concatenate([nv.gemm(nvm.FP8Tensor(to_dev_u8(np.ascontiguousarray(a[i:i + 4])), a8.scale), q).cpu().numpy()
+                         for i in range(0, bts.size, 4)])
+    assert np.array_equal(cv.astype(np.float64), cref.astype(np.float32).astype(np.float64))
 
 
 def test_gemm_fp8a_split_k_and_full(nv):
