@@ -426,25 +426,28 @@ __global__ __launch_bounds__(256) void k_encode(TileGeom gm, const float *__rest
 // agrees on amax, then encodes them from registers, so the input crosses HBM once.  Tiles beyond
 // the register capacity are streamed for the maximum and read again for the encode.
 //
-// Agreement on amax: every workgroup publishes one 64-bit word (call epoch << 32 | its partial
-// maximum) in its workspace slot, then polls all slots until each carries this call's epoch and
+// Agreement on amax: every workgroup publishes one 64-bit word (call tag << 32 | its partial
+// maximum) in its workspace slot, then polls all slots until each carries this call's tag and
 // takes the maximum of their payloads.  Every workgroup reads every slot (one per CU, so a poll
 // moves a few KB), so the maximum reaches all of them one memory round trip after the last slot
 // is written, with no relay through a leader.  The payload travels inside the atomic word, so
-// relaxed device-scope atomics suffice (no cache maintenance in the loop).  The epoch differs
-// between calls, so the workspace needs no clearing and earlier contents are ignored.  The polls
-// are bounded: if other work kept some workgroups from being scheduled for that long, bit 1 of
-// `flags` is set and the outputs are invalid, instead of a hang.
+// relaxed device-scope atomics suffice (no cache maintenance in the loop).  The call tag is one
+// more than the tag word at the head of the workspace, which workgroup 0 advances once every slot
+// has been seen (by then every workgroup has read it); so each call tags its slots differently from
+// the last one on this workspace, the workspace needs no clearing, and a launch captured in a HIP
+// graph (same kernel arguments on every replay) still works.  The polls are bounded: if other work
+// kept some workgroups from being scheduled for that long, bit 1 of `flags` is set and the outputs
+// are invalid, instead of a hang.
 // ---------------------------------------------------------------------------------------------
-constexpr int kSlotBase = 16;       // workspace words before the 64-bit slots (8-byte aligned)
+constexpr int kSlotBase = 16;       // workspace words before the 64-bit slots; word 0 is the tag word
 
 constexpr uint32_t kPollLimit = 1u << 22;
 
 template <int SRC, int TPW, int PB, int OUTF, int NWV>
 __global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const float *__restrict__ src_scale,
-                                                          uint32_t *__restrict__ ws, uint32_t epoch,
-                                                          uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
-                                                          float *__restrict__ g_out, int32_t *__restrict__ flags) {
+                                                          uint32_t *__restrict__ ws, uint8_t *__restrict__ codes,
+                                                          uint8_t *__restrict__ scales, float *__restrict__ g_out,
+                                                          int32_t *__restrict__ flags) {
     __shared__ uint32_t red[NWV];
     __shared__ uint32_t amax_bits;
     const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -452,6 +455,7 @@ __global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const flo
     const uint64_t wave = (uint64_t)blockIdx.x * NWV + wid, nwaves = (uint64_t)gridDim.x * NWV;
     const float sc = (SRC == NVFP4_E4M3 && src_scale) ? *src_scale : 1.0f;
     uint64_t *slots = reinterpret_cast<uint64_t *>(ws + kSlotBase);
+    const uint32_t epoch = __hip_atomic_load(ws, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;  // call tag
 
     // ---- phase 1: load the resident tiles, block maxima (NVFP4), tensor maximum ----
     TileRegs<SRC> t[TPW];
@@ -519,6 +523,8 @@ __global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const flo
         }
         a = wave_max_u32(a);
         if (lane == 0) amax_bits = a;
+        // every workgroup has read the tag word before publishing its slot: advance it
+        if (blockIdx.x == 0 && lane == 0) __hip_atomic_store(ws, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     m = amax_bits;
@@ -580,12 +586,6 @@ static int grid_for(uint64_t work_items, int per_block, int max_blocks) {
     return (int)b;
 }
 
-// A different value for every call (the barrier's epoch); starts from an arbitrary point.
-static uint32_t next_epoch() {
-    static std::atomic<uint32_t> counter{0x9E3779B9u};
-    return counter.fetch_add(0x61C88647u, std::memory_order_relaxed) | 1u;
-}
-
 // Largest residency (tiles per wave) whose registers still leave room for four waves per SIMD (at
 // most 128 VGPRs), and for two.
 template <int SRC>
@@ -635,7 +635,7 @@ static void launch_fused(const TileGeom &gm, int grid, const float *src_scale, u
     const int cap = fused_per_cu<SRC, TPW, PB, OUTF, NWV>() * num_cus;
     if (grid > cap) grid = cap;
     hipLaunchKernelGGL((k_quant_fused<SRC, TPW, PB, OUTF, NWV>), dim3(grid), dim3(NWV * 64), 0, stream, gm,
-                       src_scale, ws, next_epoch(), out.codes, out.scales, out.scale, flags);
+                       src_scale, ws, out.codes, out.scales, out.scale, flags);
 }
 
 // Resident launch: tiles per wave rounded up to a supported residency, at most T.

@@ -100,7 +100,9 @@ enum {
  * amax_in NULL for the run-time amax; flags nullable (bit 0 = non-finite input seen; bit 1 = the
  * run-time amax could not be agreed because other work kept part of the grid off the GPU for a
  * bounded wait; outputs are unspecified when either is set); workspace of
- * nvfp4_workspace_size(NVFP4_OP_QUANTIZE, rows, cols, 0) bytes.
+ * nvfp4_workspace_size(NVFP4_OP_QUANTIZE, rows, cols, 0) bytes (run-time amax only).  The
+ * workspace carries a call counter from one call to the next: it may hold anything before its
+ * first use and needs no clearing, and the call may be captured in a HIP graph and replayed.
  * src_scale, amax_in, flags and workspace are device pointers.
  */
 nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype x_dtype, int64_t ld_x, const float *src_scale,

@@ -165,6 +165,39 @@ def test_requantize_modulation_fp8(nv):
     _assert_q_equal(q, ref, "modulation fp8")
 
 
+def test_quantize_replayed_from_hip_graph(nv):
+    # run-time amax quantizes (NVFP4 and FP8) captured once in a HIP graph and replayed on new
+    # inputs whose amax differs each time: the replays reuse the kernel arguments, so each call's
+    # grid agreement must be told apart through its workspace, not its arguments
+    rows, cols = 1024, 3072
+    _note(f"quantize + quantize_fp8 replayed from a HIP graph, {rows}x{cols}")
+    x = torch.zeros((rows, cols), dtype=torch.float32, device=DEV)
+    q = nv.NVFP4Tensor.empty(rows, cols, DEV)
+    q8 = nv.FP8Tensor.empty(rows, cols, DEV)
+    ws = torch.empty(nv.workspace_size(nv.OP_QUANTIZE, rows, cols), dtype=torch.uint8, device=DEV)
+    ws8 = torch.empty_like(ws)
+    flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+    nv.quantize(x, out=q, workspace=ws, flags=flags)
+    nv.quantize_fp8(x, out=q8, workspace=ws8, flags=flags)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        nv.quantize(x, out=q, workspace=ws, flags=flags)
+        nv.quantize_fp8(x, out=q8, workspace=ws8, flags=flags)
+    for i in range(5):
+        xi = (np.random.default_rng(700 + i).standard_normal((rows, cols)) * 10.0 ** (i - 2)).astype(np.float32)
+        xi[i * 100, 7 * i] = 40.0 * 10.0 ** (i - 2)
+        x.copy_(torch.from_numpy(xi))
+        flags.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(flags.item()) == 0, f"replay {i}"
+        _assert_q_equal(q, oracle.quantize(xi)[0], f"replay {i}")
+        rb, rs, _ = oracle.quantize_fp8(xi)
+        _assert_fp8_equal(q8, rb, rs, f"fp8 replay {i}")
+
+
 def test_quantize_attention_weight_full(nv):
     _note("quantize 3072x3072 fp32 attention weight")
     w = synth.attn_proj_weight()
