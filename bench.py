@@ -22,6 +22,9 @@ Inputs are resident in HBM before timing; the step rotates over several input se
 size exceeds the 256 MB Infinity Cache, so repeated steps do not hit in cache.  Each operation is
 bracketed by events on the stream it runs on; the dominant kernel's roofline uses those times.
 
+The JSON line also carries "graph": the step and the quantize alone captured in HIP graphs and
+replayed (no eager dispatch gaps between kernels), for information.
+
 Prints one JSON line.  Flags: --gpus (1 only), --steps, --warmup, --no-cpu-baseline, --peaks (adds the
 achievable peaks measured with library calls: a 1 GiB device copy and a bf16 matmul of the GEMM's shape).
 """
@@ -181,7 +184,41 @@ def main():
     op_ms.update({op: float(np.mean([evn[s][j].elapsed_time(evn[s][j + 1]) for s in range(args.steps)]))
                   for j, op in enumerate(next_ops)})
 
+    def graph_rates():
+        """The step, and the quantize alone, captured in HIP graphs (one call per rotating input set)
+        and replayed: the same kernels without the eager stream's dispatch gaps.  Informational; the
+        headline stays the eager figure."""
+        try:
+            graphs = []
+            for body in (lambda: [step(i) for i in range(nsets)],
+                         lambda: [nv.quantize(sets[i][0], out=qw, workspace=qws) for i in range(nsets)]):
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    body()
+                graphs.append(g)
+            res = []
+            for g in graphs:
+                g.replay()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                reps = 10
+                e0.record()
+                for _ in range(reps):
+                    g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                res.append(e0.elapsed_time(e1) / (reps * nsets))
+            return {"ms_per_step": round(res[0], 4),
+                    "quantize_ms": round(res[1], 5),
+                    "quantize_GBps": round((nW * 4.5625 + 4) / (res[1] * 1e-3) / 1e9, 2),
+                    "note": "each replayed graph holds one call per rotating input set; times per call"}
+        except Exception as exc:  # capture is informational: report, do not fail the run
+            return {"error": f"{type(exc).__name__}: {exc}"[:200]}
+
     nW, nA = N_OUT * K_IN, M_TOK * K_IN
+    graph = graph_rates()
+
     work = {  # algorithmic bytes (codec / memory-bound ops) or flops (GEMMs)
         "quantize": ("GB/s", nW * 4.5625 + 4, HBM_PEAK_GBS),
         "requantize": ("GB/s", nW * 1.5625 + 4, HBM_PEAK_GBS),
@@ -239,6 +276,7 @@ def main():
         "ops": op_report,
         "next_ops": next_report,
         "roofline": roofline,
+        "graph": graph,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w_np)
