@@ -25,7 +25,10 @@
  *     (NVFP4_ERR_ALIGN otherwise);
  *   - the library checks once per device that it runs on gfx950 (NVFP4_ERR_DEVICE otherwise);
  *   - the calls are thread-safe; calls that share a workspace buffer must be ordered by the
- *     caller (same stream, or events).
+ *     caller (same stream, or events);
+ *   - every call may be captured in a HIP graph and replayed: the library enqueues kernels only
+ *     (no allocation, memset, copy or host synchronization), and no per-call value is frozen into
+ *     the kernel arguments.
  */
 #ifndef NVFP4_H
 #define NVFP4_H

@@ -198,6 +198,59 @@ def test_quantize_replayed_from_hip_graph(nv):
         _assert_fp8_equal(q8, rb, rs, f"fp8 replay {i}")
 
 
+def test_whole_path_replayed_from_hip_graph(nv):
+    # every entry point captured once in one HIP graph and replayed on new inputs (written between
+    # replays by ordinary stream work); each replay's outputs equal, bit for bit, those of eager
+    # calls on the same inputs
+    n, k, m, r = 384, 1024, 200, 64
+    _note("whole path replayed from a HIP graph")
+    w = torch.zeros((n, k), dtype=torch.float32, device=DEV)
+    w8 = torch.zeros((n, k), dtype=torch.uint8, device=DEV)
+    a = torch.zeros((m, k), dtype=torch.bfloat16, device=DEV)
+    sc = torch.tensor([0.01], dtype=torch.float32, device=DEV)
+    amax = torch.tensor([4.0], dtype=torch.float32, device=DEV)
+    gl = torch.Generator(device="cpu").manual_seed(11)
+    v_lr = (torch.randn((r, k), generator=gl) * 0.05).to(torch.bfloat16).to(DEV)
+    u_lr = (torch.randn((n, r), generator=gl) * 0.05).to(torch.bfloat16).to(DEV)
+    st_out = torch.zeros(8, dtype=torch.float64, device=DEV)  # matrix_stats syncs unless given `out`
+
+    def path():
+        qw = nv.quantize(w)
+        qw8 = nv.quantize(w8, src_scale=sc)
+        qa = nv.quantize(a)
+        a8 = nv.quantize_fp8(a)
+        pct, mx = nv.amax_percentile(a, 99.9)
+        return [qw.codes, qw.scales, qw.global_scale, qw8.codes, qw8.scales, qw8.global_scale,
+                qa.codes, qa.scales, qa.global_scale, a8.data, a8.scale, nv.dequantize(qw),
+                nv.gemm(a, qw), nv.gemm(qa, qw), nv.gemm(a[:2], qw), nv.gemm(a8, qw), nv.gemm(a8.__class__(
+                    a8.data[:3], a8.scale), qw), pct, mx, nv.matrix_stats(w, qw, out=st_out)[:7],
+                nv.gemm_lowrank(a, qw, v_lr, u_lr), nv.gemm_qa(a, qw, amax)]
+
+    def refill(seed):
+        g = torch.Generator(device="cpu").manual_seed(seed)
+        w.copy_(torch.randn((n, k), generator=g) * 0.02)
+        b = torch.randint(0, 256, (n, k), generator=g, dtype=torch.int32).to(torch.uint8)
+        w8.copy_(torch.where((b & 0x7F) == 0x7F, b - 1, b))
+        a.copy_((torch.randn((m, k), generator=g) * (1 + seed % 3)).to(torch.bfloat16))
+
+    refill(0)
+    path()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = path()
+    for seed in (1, 2, 3):
+        refill(seed)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in outs]
+        want = path()
+        torch.cuda.synchronize()
+        for i, (x, y) in enumerate(zip(got, want)):
+            assert torch.equal(x, y), f"replay {seed}: output {i} differs from the eager call"
+
+
 def test_quantize_attention_weight_full(nv):
     _note("quantize 3072x3072 fp32 attention weight")
     w = synth.attn_proj_weight()
