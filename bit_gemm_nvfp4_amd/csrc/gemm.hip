@@ -34,7 +34,7 @@
 // Workgroup ids are remapped so that the workgroups the hardware places on one XCD (ids congruent
 // mod 8) take neighbouring tiles that share W columns in that XCD's L2.
 //
-// k_gemv: for M <= 4 the product is bound by streaming W once from HBM.  A (bf16, or NVFP4 / E4M3
+// k_gemv: for M <= 5 the product is bound by streaming W once from HBM.  A (bf16, or NVFP4 / E4M3
 // activations expanded exactly to bf16) sits in LDS; each lane takes whole 16-element blocks of a W
 // row, forms the 16-term dot products with bf16 dot2 instructions and applies the block scale once
 // per block; a wave reduction finishes each row.  A wave works on two rows at once with all their loads issued ahead of the arithmetic.
@@ -857,7 +857,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__
 }
 
 // ------------------------------------------------------------------------------------------------
-// GEMV, M <= 4
+// GEMV, M <= 5
 // ------------------------------------------------------------------------------------------------
 template <int MM, int AM>
 __global__ __launch_bounds__(256) void k_gemv(const __bf16 *__restrict__ A, int64_t lda,
@@ -1082,7 +1082,11 @@ struct GemmA {
 
 size_t gemv_lds_bytes(int64_t M, int64_t K) { return (size_t)M * (size_t)K * 2; }
 
-bool gemv_applies(int64_t M, int64_t K) { return M >= 1 && M <= 4 && gemv_lds_bytes(M, K) <= 64 * 1024; }
+// M <= 4: A in registers (K <= 4096) or LDS; M = 5: A in LDS.  Beyond that the dot products (8 per
+// 16-element block and row of A) outweigh the stream of W: at M = 8 the LDS form measured 19.3 us
+// against 22.5 us tiled at N = K = 3072, but 48.6 against 37.8 us at N = 18432, so the tiled kernels
+// run from M = 6.
+bool gemv_applies(int64_t M, int64_t K) { return M >= 1 && M <= 5 && gemv_lds_bytes(M, K) <= 64 * 1024; }
 
 template <int MM, int AM, int UB>
 static void launch_gemv_reg(const GemmA &a, const nvfp4_tensor *w, float *c, int64_t ldc, int num_cus,
@@ -1100,10 +1104,12 @@ static void launch_gemv_t(const GemmA &a, const nvfp4_tensor *w, float *c, int64
                           hipStream_t stream) {
     const int64_t N = w->rows, K = w->cols;
     const int64_t ub = (K / 16 + 63) / 64;  // blocks per lane
-    if (ub <= 1) return launch_gemv_reg<MM, AM, 1>(a, w, c, ldc, num_cus, stream);
-    if (ub <= 2) return launch_gemv_reg<MM, AM, 2>(a, w, c, ldc, num_cus, stream);
-    if (ub <= 3) return launch_gemv_reg<MM, AM, 3>(a, w, c, ldc, num_cus, stream);
-    if (ub <= 4) return launch_gemv_reg<MM, AM, 4>(a, w, c, ldc, num_cus, stream);
+    if constexpr (MM <= 4) {  // beyond 4 rows the register form would hold too many blocks of A per lane
+        if (ub <= 1) return launch_gemv_reg<MM, AM, 1>(a, w, c, ldc, num_cus, stream);
+        if (ub <= 2) return launch_gemv_reg<MM, AM, 2>(a, w, c, ldc, num_cus, stream);
+        if (ub <= 3) return launch_gemv_reg<MM, AM, 3>(a, w, c, ldc, num_cus, stream);
+        if (ub <= 4) return launch_gemv_reg<MM, AM, 4>(a, w, c, ldc, num_cus, stream);
+    }
     // a wave takes two rows per pass, one pass per wave up to 16 workgroups per CU
     int64_t grid = (N + 7) / 8;
     if (grid > (int64_t)num_cus * 16) grid = (int64_t)num_cus * 16;
@@ -1120,7 +1126,8 @@ static void launch_gemv(int64_t M, const GemmA &a, const nvfp4_tensor *w, float 
     case 1: launch_gemv_t<1, AM>(a, w, c, ldc, num_cus, stream); break;
     case 2: launch_gemv_t<2, AM>(a, w, c, ldc, num_cus, stream); break;
     case 3: launch_gemv_t<3, AM>(a, w, c, ldc, num_cus, stream); break;
-    default: launch_gemv_t<4, AM>(a, w, c, ldc, num_cus, stream); break;
+    case 4: launch_gemv_t<4, AM>(a, w, c, ldc, num_cus, stream); break;
+    default: launch_gemv_t<5, AM>(a, w, c, ldc, num_cus, stream); break;
     }
 }
 

@@ -4,7 +4,7 @@
 //
 // k_lr_down: T = A . V^T [M x r] on the bf16 matrix cores, written as the bf16 pair T_hi, T_lo
 //   (64 x 32 blocks of T, operands staged in LDS with contiguous row reads).
-// k_lr_up_add: C += T . U^T for products that do not take the fused epilogue (the GEMV for M <= 4,
+// k_lr_up_add: C += T . U^T for products that do not take the fused epilogue (the GEMV for M <= 5,
 //   K % 64 != 0, split-K): a 32 x 128 tile per workgroup, then a read-modify-write of C.
 #include <hip/hip_runtime.h>
 

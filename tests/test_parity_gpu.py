@@ -324,10 +324,11 @@ def _rand_q(nv, rows, cols, seed, sigma=0.02):
 
 
 # M <= 4 takes the GEMV kernels: A in registers up to K = 4096 (here 16 .. 4096), A in LDS beyond
-# (6144, 8192)
+# (6144, 8192); M = 5 the LDS form; M >= 6 the tiled kernels
 @pytest.mark.parametrize("mnk", [(16, 64, 256), (1, 64, 128), (2, 100, 48), (3, 33, 4096), (4, 17, 16),
                                  (5, 70, 80), (37, 129, 272), (130, 257, 1024), (256, 128, 64), (300, 200, 3072),
-                                 (2, 300, 8192), (4, 129, 6144)])
+                                 (2, 300, 8192), (4, 129, 6144), (6, 1000, 3072), (7, 65, 4096), (8, 300, 4096),
+                                 (8, 64, 8192), (9, 100, 1024)])
 def test_gemm_w4a16(nv, mnk):
     m, n, k = mnk
     _note(f"gemm w4a16 {mnk}")
@@ -344,7 +345,7 @@ def test_gemm_w4a16(nv, mnk):
 
 
 @pytest.mark.parametrize("mnk", [(16, 64, 256), (2, 300, 1024), (4, 64, 16), (64, 96, 112), (200, 300, 512),
-                                 (2, 100, 8192)])
+                                 (2, 100, 8192), (5, 200, 2048), (8, 100, 4096)])
 def test_gemm_w4a4(nv, mnk):
     m, n, k = mnk
     _note(f"gemm w4a4 {mnk}")
@@ -719,7 +720,7 @@ def test_quantize_fp8_streamed_tensor(nv):
 # K % 64 != 0 takes k_gemm_tile; M <= 4 the GEMV forms (A in registers for K <= 4096, in LDS beyond)
 @pytest.mark.parametrize("mnk", [(16, 64, 256), (1, 64, 128), (4, 100, 48), (5, 70, 80), (37, 129, 272),
                                  (130, 257, 1024), (300, 200, 3072), (576, 16384, 64), (130, 1000, 128),
-                                 (2, 300, 4608), (3, 1000, 3072), (4, 257, 8192)])
+                                 (2, 300, 4608), (3, 1000, 3072), (4, 257, 8192), (6, 300, 3072), (8, 129, 4096)])
 def test_gemm_fp8a(nv, mnk):
     m, n, k = mnk
     _note(f"gemm fp8a {mnk}")
@@ -896,7 +897,7 @@ def _lowrank_operands(m, n, k, r, seed):
 # including r % 32 == 16 and r > 128 (two column blocks of T)
 LOWRANK_SHAPES = [(16, 64, 256, 16), (1, 64, 128, 32), (3, 100, 4096, 128), (64, 96, 112, 48),
                   (200, 300, 512, 128), (130, 1000, 128, 64), (256, 192, 1024, 256), (100, 1000, 4096, 128),
-                  (300, 520, 640, 144)]
+                  (300, 520, 640, 144), (7, 300, 3072, 128)]
 
 
 @pytest.mark.parametrize("mnkr", LOWRANK_SHAPES)
@@ -966,7 +967,7 @@ def test_gemm_lowrank_attention_projection_full(nv):
 # (M <= 4, K % 64 != 0, wider N) A is quantized into the workspace first.  The reference quantizes
 # A with the same static amax in the oracle and contracts the exact operands in float64.
 QA_SHAPES = [(16, 64, 256), (2, 300, 1024), (64, 96, 112), (200, 300, 512), (100, 500, 4096), (2048, 384, 3072),
-             (130, 1000, 128), (100, 1000, 4096), (512, 12288, 4096), (300, 520, 640)]
+             (130, 1000, 128), (100, 1000, 4096), (512, 12288, 4096), (300, 520, 640), (8, 300, 3072)]
 
 
 @pytest.mark.parametrize("mnk", QA_SHAPES)
