@@ -96,10 +96,8 @@ def main():
     c16 = torch.empty((M_TOK, N_OUT), dtype=torch.float32, device=dev)
     c4 = torch.empty((M_TOK, N_OUT), dtype=torch.float32, device=dev)
     cv = torch.empty((GEMV_M, N_OUT), dtype=torch.float32, device=dev)
-    qws = torch.empty(nv.workspace_size(nv.OP_QUANTIZE, 0, 0), dtype=torch.uint8, device=dev)
-    qws2 = torch.empty_like(qws)
-    qws3 = torch.empty_like(qws)
-    qws4 = torch.empty_like(qws)
+    qws, qws2, qws3, qws4 = (nv.quantize_workspace(dev) for _ in range(4))
+    qflags = torch.zeros(1, dtype=torch.int32, device=dev)
     a8 = nv.FP8Tensor.empty(M_TOK, K_IN, dev)
     c8 = torch.empty((M_TOK, N_OUT), dtype=torch.float32, device=dev)
     st_out = torch.empty(8, dtype=torch.float64, device=dev)
@@ -127,13 +125,13 @@ def main():
         w, a, w8 = sets[i % nsets]
         e = events
         if e: e[0].record()
-        nv.quantize(w, out=qw, workspace=qws)
+        nv.quantize(w, out=qw, workspace=qws, flags=qflags)
         if e: e[1].record()
-        nv.quantize(w8, src_scale=src_scale, out=qw8, workspace=qws2)
+        nv.quantize(w8, src_scale=src_scale, out=qw8, workspace=qws2, flags=qflags)
         if e: e[2].record()
         nv.dequantize(qw, out=wd)
         if e: e[3].record()
-        nv.quantize(a, out=qa, workspace=qws3)
+        nv.quantize(a, out=qa, workspace=qws3, flags=qflags)
         if e: e[4].record()
         nv.gemm(a, qw, out=c16)
         if e: e[5].record()
@@ -148,7 +146,7 @@ def main():
         w, a, w8 = sets[i % nsets]
         e = events
         if e: e[0].record()
-        nv.quantize_fp8(a, out=a8, workspace=qws4)
+        nv.quantize_fp8(a, out=a8, workspace=qws4, flags=qflags)
         if e: e[1].record()
         nv.gemm(a8, qw, out=c8)
         if e: e[2].record()
@@ -191,7 +189,7 @@ def main():
         try:
             graphs = []
             for body in (lambda: [step(i) for i in range(nsets)],
-                         lambda: [nv.quantize(sets[i][0], out=qw, workspace=qws) for i in range(nsets)]):
+                         lambda: [nv.quantize(sets[i][0], out=qw, workspace=qws, flags=qflags) for i in range(nsets)]):
                 torch.cuda.synchronize()
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g):
@@ -218,6 +216,7 @@ def main():
 
     nW, nA = N_OUT * K_IN, M_TOK * K_IN
     graph = graph_rates()
+    nv.check_flags(qflags, "quantizers of the timed steps")
 
     work = {  # algorithmic bytes (codec / memory-bound ops) or flops (GEMMs)
         "quantize": ("GB/s", nW * 4.5625 + 4, HBM_PEAK_GBS),

@@ -122,6 +122,7 @@ const char *nvfp4_status_string(nvfp4_status s) {
 size_t nvfp4_workspace_size(int op, int64_t rows, int64_t cols, int64_t k) {
     switch (op) {
     case NVFP4_OP_QUANTIZE: return kQuantizeWsBytes;
+    case NVFP4_OP_AMAX: return kAmaxWsBytes;
     case NVFP4_OP_PERCENTILE: return cols >= 0 ? percentile_ws_bytes(cols, k ? 1 : 0) : 0;
     case NVFP4_OP_STATS: return stats_ws_bytes();
     case NVFP4_OP_GEMM_QA: {
@@ -163,6 +164,26 @@ nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype x_dtype, int64_t ld_x, co
     const int cus = current_device_cus();
     if (cus == 0) return NVFP4_ERR_DEVICE;
     hipError_t e = launch_quantize(x, x_dtype, ld_x, src_scale, amax_in, out, flags, workspace, cus, stream);
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+}
+
+nvfp4_status nvfp4_tensor_amax(const void *x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                               const float *src_scale, float *amax_out, int32_t *flags, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+    const int eb = elem_bytes(x_dtype);
+    if (eb == 0) return NVFP4_ERR_DTYPE;
+    if (!amax_out) return NVFP4_ERR_NULL;
+    if (rows < 0 || cols < 0 || (cols % 16) != 0) return NVFP4_ERR_SHAPE;
+    nvfp4_status st = check_matrix(x, rows, cols, ld_x, eb);
+    if (st != NVFP4_OK) return st;
+    if (src_scale && x_dtype != NVFP4_E4M3) return NVFP4_ERR_ARG;
+    if (!aligned4(amax_out) || (src_scale && !aligned4(src_scale)) || (flags && !aligned4(flags)))
+        return NVFP4_ERR_ALIGN;
+    if (!workspace || workspace_bytes < kAmaxWsBytes) return NVFP4_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return NVFP4_ERR_ALIGN;
+    const int cus = current_device_cus();
+    if (cus == 0) return NVFP4_ERR_DEVICE;
+    hipError_t e = launch_amax(x, x_dtype, ld_x, rows, cols, src_scale, amax_out, flags, workspace, cus, stream);
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
 }
 

@@ -55,7 +55,8 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) { return __builtin_amdg
 // ---------------------------------------------------------------------------------------------
 // Two fp32 -> two E2M1 codes written into byte SEL of `word` (first value in the low nibble).
 // With scale 1.0 the instruction is a plain round-to-nearest-even conversion that saturates at
-// +-6 and keeps the sign of zero; the exhaustive conversion test pins this against the oracle.
+// +-6 and keeps the sign of zero.  The GPU tests pin this against the oracle on every fp32 value in
+// [0, 6], every E2M1 midpoint and its neighbours, and values above 6.
 template <int SEL>
 __device__ __forceinline__ uint32_t fp4_pk(uint32_t word, float a, float b) {
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, a, b, 1.0f, SEL);

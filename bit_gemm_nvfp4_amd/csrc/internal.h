@@ -17,6 +17,13 @@ constexpr size_t kQuantizeWsBytes = 16384;
 hipError_t launch_quantize(const void *x, nvfp4_dtype dt, int64_t ld_x, const float *src_scale, const float *amax_in,
                            const nvfp4_tensor *out, int32_t *flags, void *workspace, int num_cus, hipStream_t stream);
 
+// Run-time amax as a pass of its own: *amax_out = max |v| (fp32; E4M3 source: the largest byte's
+// value times *src_scale), from per-workgroup partial maxima in the workspace (kAmaxWsBytes).
+constexpr int kAmaxMaxParts = 2048;
+constexpr size_t kAmaxWsBytes = kAmaxMaxParts * 4;
+hipError_t launch_amax(const void *x, nvfp4_dtype dt, int64_t ld_x, int64_t rows, int64_t cols, const float *src_scale,
+                       float *amax_out, int32_t *flags, void *workspace, int num_cus, hipStream_t stream);
+
 // FP8 E4M3 tensorwise: out [rows x cols] bytes (dense), *out_scale = the tensor scale.
 hipError_t launch_quantize_fp8(const void *x, nvfp4_dtype dt, int64_t ld_x, int64_t rows, int64_t cols,
                                const float *src_scale, const float *amax_in, uint8_t *out, float *out_scale,

@@ -431,15 +431,27 @@ __global__ __launch_bounds__(256) void k_encode(TileGeom gm, const float *__rest
 // takes the maximum of their payloads.  Every workgroup reads every slot (one per CU, so a poll
 // moves a few KB), so the maximum reaches all of them one memory round trip after the last slot
 // is written, with no relay through a leader.  The payload travels inside the atomic word, so
-// relaxed device-scope atomics suffice (no cache maintenance in the loop).  The call tag is one
-// more than the tag word at the head of the workspace, which workgroup 0 advances once every slot
-// has been seen (by then every workgroup has read it); so each call tags its slots differently from
-// the last one on this workspace, the workspace needs no clearing, and a launch captured in a HIP
-// graph (same kernel arguments on every replay) still works.  The polls are bounded: if other work
-// kept some workgroups from being scheduled for that long, bit 1 of `flags` is set and the outputs
-// are invalid, instead of a hang.
+// relaxed device-scope atomics suffice (no cache maintenance in the loop).
+//
+// Call tags: the tag of a call is one more than the tag word (workspace word 0).  Each workgroup
+// reads the tag word and then counts itself in an arrival counter (word 1, ordered after the read
+// by release semantics); the workgroup that arrives last has seen every other workgroup's read, so
+// at its end it advances the tag word to this call's tag and clears the counter.  The next call on
+// the workspace, which the stream (or the caller's events) starts only after every workgroup of
+// this one has finished, therefore tags its slots differently, with no clearing between calls, and
+// a launch captured in a HIP graph (same kernel arguments on every replay) still works.  The
+// workspace must hold zeros before its first use.  What breaks that contract is reported rather
+// than trusted: a slot that already carries this call's tag when a workgroup publishes, or an
+// arrival count beyond the grid, sets bit 2 of `flags`.
+//
+// The polls are bounded: if other work kept some workgroups from being scheduled for that long,
+// bit 1 of `flags` is set and the outputs are invalid, instead of a hang.  Late workgroups still
+// take part in the protocol when they run (they read the same tag, find every slot of the call
+// published, and the last of them advances the tag), so the next call starts from a clean state.
 // ---------------------------------------------------------------------------------------------
-constexpr int kSlotBase = 16;       // workspace words before the 64-bit slots; word 0 is the tag word
+constexpr int kSlotBase = 16;  // workspace words before the 64-bit slots
+constexpr int kTagWord = 0;    // tag of the last completed call
+constexpr int kArriveWord = 1; // workgroups of the running call that have read the tag word
 
 constexpr uint32_t kPollLimit = 1u << 22;
 
@@ -455,7 +467,15 @@ __global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const flo
     const uint64_t wave = (uint64_t)blockIdx.x * NWV + wid, nwaves = (uint64_t)gridDim.x * NWV;
     const float sc = (SRC == NVFP4_E4M3 && src_scale) ? *src_scale : 1.0f;
     uint64_t *slots = reinterpret_cast<uint64_t *>(ws + kSlotBase);
-    const uint32_t epoch = __hip_atomic_load(ws, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;  // call tag
+    // call tag and arrival count (wave 0, lane 0; the release orders the tag read before the count)
+    uint32_t epoch = 0, arrived = 0;
+    if (wid == 0) {
+        if (lane == 0) {
+            epoch = __hip_atomic_load(ws + kTagWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+            arrived = __hip_atomic_fetch_add(ws + kArriveWord, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        epoch = (uint32_t)__shfl((int)epoch, 0, 64);
+    }
 
     // ---- phase 1: load the resident tiles, block maxima (NVFP4), tensor maximum ----
     TileRegs<SRC> t[TPW];
@@ -490,8 +510,13 @@ __global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const flo
             uint32_t wgmax = 0;
 #pragma unroll
             for (int i = 0; i < NWV; i++) wgmax = max(wgmax, red[i]);
-            __hip_atomic_store(&slots[blockIdx.x], ((uint64_t)epoch << 32) | wgmax, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+            const uint64_t prev = __hip_atomic_exchange(&slots[blockIdx.x], ((uint64_t)epoch << 32) | wgmax,
+                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // a slot already tagged for this call, or more arrivals than workgroups: the workspace
+            // was not zeroed before first use, or was shared by overlapping calls
+            if ((uint32_t)(prev >> 32) == epoch || arrived >= gridDim.x) {
+                if (flags) atomicOr(flags, 4);
+            }
         }
         // ---- wait for every slot of this call; all loads of a chunk of 8 slots per lane in
         // flight at once ----
@@ -523,8 +548,12 @@ __global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const flo
         }
         a = wave_max_u32(a);
         if (lane == 0) amax_bits = a;
-        // every workgroup has read the tag word before publishing its slot: advance it
-        if (blockIdx.x == 0 && lane == 0) __hip_atomic_store(ws, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // the last workgroup to arrive: every workgroup has read the tag word, so advance it and
+        // clear the counter for the next call
+        if (lane == 0 && arrived == gridDim.x - 1) {
+            __hip_atomic_store(ws + kArriveWord, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(ws + kTagWord, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     __syncthreads();
     m = amax_bits;
@@ -576,6 +605,56 @@ __global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const flo
                 tile_encode<SRC, false>(o[b], tile_block_max<SRC>(o[b], lane), g, six_g, sc, tb, gm.nblocks, codes,
                                         scales, flags, lane);
         }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Run-time amax as a pass of its own (the two-launch form): per-workgroup maxima of the magnitude
+// bit patterns into the workspace, then one workgroup reduces them and writes amax as fp32.  No
+// workgroup waits for another, so it makes no assumption about which kernels share the GPU.
+// ---------------------------------------------------------------------------------------------
+template <int SRC>
+__global__ __launch_bounds__(256) void k_amax_partial(TileGeom gm, uint32_t *__restrict__ partial) {
+    __shared__ uint32_t red[4];
+    const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint64_t ntiles = (gm.nblocks + 63) / 64;
+    const uint64_t nwaves = (uint64_t)gridDim.x * 4;
+    uint32_t m = 0;
+    uint64_t tile = (uint64_t)blockIdx.x * 4 + wid;
+    // two tiles in flight per wave
+    for (; tile + nwaves < ntiles; tile += 2 * nwaves) {
+        TileRegs<SRC> a, b;
+        tile_load<SRC>(a, gm, tile, lane);
+        tile_load<SRC>(b, gm, tile + nwaves, lane);
+        m = max(m, max(tile_lane_max<SRC>(a), tile_lane_max<SRC>(b)));
+    }
+    if (tile < ntiles) {
+        TileRegs<SRC> a;
+        tile_load<SRC>(a, gm, tile, lane);
+        m = max(m, tile_lane_max<SRC>(a));
+    }
+    m = wave_max_u32(m);
+    if (lane == 0) red[wid] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) partial[blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
+template <int SRC>
+__global__ __launch_bounds__(256) void k_amax_final(const uint32_t *__restrict__ partial, int nparts,
+                                                    const float *__restrict__ src_scale, float *__restrict__ amax_out,
+                                                    int32_t *__restrict__ flags) {
+    __shared__ uint32_t red[4];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < nparts; i += 256) m = max(m, partial[i]);
+    m = wave_max_u32(m);
+    if (lane == 0) red[wid] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const float sc = (SRC == NVFP4_E4M3 && src_scale) ? *src_scale : 1.0f;
+        bool nonfinite = false;
+        *amax_out = amax_from_bits<SRC>(max(max(red[0], red[1]), max(red[2], red[3])), sc, &nonfinite);
+        if (nonfinite && flags) atomicOr(flags, 1);
     }
 }
 
@@ -699,6 +778,35 @@ static hipError_t launch_quantize_t(const void *x, int64_t ld_x, int64_t rows, i
     hipLaunchKernelGGL((k_encode<SRC, OUTF>), dim3(grid_for(ntiles, 4, num_cus * 8)), dim3(256), 0, stream, gm,
                        src_scale, amax_in, out.codes, out.scales, out.scale, flags);
     return hipGetLastError();
+}
+
+template <int SRC>
+static hipError_t launch_amax_t(const void *x, int64_t ld_x, int64_t rows, int64_t cols, const float *src_scale,
+                                float *amax_out, int32_t *flags, uint32_t *ws, int num_cus, hipStream_t stream) {
+    TileGeom gm;
+    gm.x = (const uint8_t *)x;
+    gm.nblocks = (uint64_t)rows * (uint64_t)(cols / 16);
+    gm.vpr = (uint32_t)(cols / 16) * (uint32_t)kVpb<SRC>;
+    gm.ld_bytes = ld_x * SrcTraits<SRC>::kElemBytes;
+    gm.contiguous = (ld_x == cols) ? 1 : 0;
+    const uint64_t ntiles = (gm.nblocks + 63) / 64;
+    const int cap = num_cus * 4 < kAmaxMaxParts ? num_cus * 4 : kAmaxMaxParts;
+    const int grid = grid_for(ntiles, 8, cap);  // about 8 tiles per workgroup (2 per wave) at least
+    hipLaunchKernelGGL((k_amax_partial<SRC>), dim3(grid), dim3(256), 0, stream, gm, ws);
+    hipLaunchKernelGGL((k_amax_final<SRC>), dim3(1), dim3(256), 0, stream, (const uint32_t *)ws, grid, src_scale,
+                       amax_out, flags);
+    return hipGetLastError();
+}
+
+hipError_t launch_amax(const void *x, nvfp4_dtype dt, int64_t ld_x, int64_t rows, int64_t cols, const float *src_scale,
+                       float *amax_out, int32_t *flags, void *workspace, int num_cus, hipStream_t stream) {
+    uint32_t *ws = reinterpret_cast<uint32_t *>(workspace);
+    switch (dt) {
+    case NVFP4_F32: return launch_amax_t<NVFP4_F32>(x, ld_x, rows, cols, src_scale, amax_out, flags, ws, num_cus, stream);
+    case NVFP4_BF16: return launch_amax_t<NVFP4_BF16>(x, ld_x, rows, cols, src_scale, amax_out, flags, ws, num_cus, stream);
+    case NVFP4_F16: return launch_amax_t<NVFP4_F16>(x, ld_x, rows, cols, src_scale, amax_out, flags, ws, num_cus, stream);
+    default: return launch_amax_t<NVFP4_E4M3>(x, ld_x, rows, cols, src_scale, amax_out, flags, ws, num_cus, stream);
+    }
 }
 
 template <int OUTF>

@@ -80,7 +80,8 @@ enum {
     NVFP4_OP_PERCENTILE = 3,
     NVFP4_OP_STATS = 4,
     NVFP4_OP_LOWRANK = 5,
-    NVFP4_OP_GEMM_QA = 6
+    NVFP4_OP_GEMM_QA = 6,
+    NVFP4_OP_AMAX = 7
 };
 
 /*
@@ -101,16 +102,41 @@ enum {
  *   6. pack two codes per byte, low nibble first.
  * Arguments: x_dtype any of nvfp4_dtype; src_scale only for NVFP4_E4M3 (must be > 0 if given);
  * amax_in NULL for the run-time amax; flags nullable (bit 0 = non-finite input seen; bit 1 = the
- * run-time amax could not be agreed because other work kept part of the grid off the GPU for a
- * bounded wait; outputs are unspecified when either is set); workspace of
- * nvfp4_workspace_size(NVFP4_OP_QUANTIZE, rows, cols, 0) bytes (run-time amax only).  The
- * workspace carries a call counter from one call to the next: it may hold anything before its
- * first use and needs no clearing, and the call may be captured in a HIP graph and replayed.
+ * run-time amax could not be agreed within a bounded wait; bit 2 = the workspace was not in the
+ * state the previous call left it in; outputs are unspecified when any is set); workspace of
+ * nvfp4_workspace_size(NVFP4_OP_QUANTIZE, rows, cols, 0) bytes (run-time amax only).
+ * Run-time amax in one launch: every workgroup keeps its part of the input on chip while the grid
+ * agrees on amax through the workspace, so the input crosses HBM once.  Preconditions:
+ *   - the workspace holds zeros before its first use (it then carries a call counter from one call
+ *     to the next and needs no further clearing; the call may be captured in a HIP graph and
+ *     replayed); a workspace that was not zeroed, or is used by overlapping calls, sets bit 2;
+ *   - no kernel of another stream holds compute units while the call runs: the launch uses as
+ *     many workgroups as the GPU holds at once, and each waits for all the others.  Work that keeps
+ *     some of them off the GPU for the bounded wait sets bit 1.  Callers that overlap streams use
+ *     the two-launch form instead: nvfp4_tensor_amax, then this call with amax_in = its output
+ *     (identical codes, scale bytes and global scale, no co-residency needed).
  * src_scale, amax_in, flags and workspace are device pointers.
  */
 nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype x_dtype, int64_t ld_x, const float *src_scale,
                             const float *amax_in, const nvfp4_tensor *out, int32_t *flags, void *workspace,
                             size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * nvfp4_tensor_amax -- *amax_out = max |v| over x [rows x cols] (row stride ld_x elements), v the
+ * source value widened as nvfp4_quantize step 1 does (E4M3 source: times *src_scale, NULL meaning
+ * 1.0; "Qwen3-VL-8B-Instruct-heretic-NVFP4", "Quantization Details": a per-tensor amax taken at
+ * run time).  The first launch of the two-launch run-time quantize: passing amax_out as amax_in to
+ * nvfp4_quantize or nvfp4_quantize_fp8 gives exactly the outputs of their one-launch run-time form,
+ * without its requirement that the whole grid be resident at once.  Two kernels: per-workgroup
+ * maxima into the workspace, then one workgroup reduces them.  A non-finite value ORs bit 0 into
+ * the optional *flags.  cols % 16 == 0; rows == 0 gives 0.  workspace of
+ * nvfp4_workspace_size(NVFP4_OP_AMAX, rows, cols, 0) bytes (needs no initialization; not the
+ * workspace of a run-time-amax quantize, whose contents carry from call to call).
+ * src_scale, amax_out, flags and workspace are device pointers.
+ */
+nvfp4_status nvfp4_tensor_amax(const void *x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                               const float *src_scale, float *amax_out, int32_t *flags, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream);
 
 /*
  * nvfp4_quantize_fp8 -- x [rows x cols] (row stride ld_x elements) -> FP8 E4M3 bytes out [rows x
@@ -123,8 +149,9 @@ nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype x_dtype, int64_t ld_x, co
  *   3. *out_scale = fl(amax / 448), 448 the largest E4M3 value; 1.0 when amax = 0;
  *   4. byte = sign bit of v | E4M3 round-to-nearest-even of fl(|v| / scale), saturating at 448
  *      (0x7E); value = e4m3(byte) x scale.
- * cols % 16 == 0.  flags as for nvfp4_quantize; workspace of
- * nvfp4_workspace_size(NVFP4_OP_QUANTIZE, rows, cols, 0) bytes when amax_in is NULL.
+ * cols % 16 == 0.  flags, workspace and the preconditions of the one-launch run-time amax as for
+ * nvfp4_quantize (workspace of nvfp4_workspace_size(NVFP4_OP_QUANTIZE, rows, cols, 0) bytes, zeroed
+ * before first use, when amax_in is NULL).
  * src_scale, amax_in, out_scale, flags and workspace are device pointers.
  */
 nvfp4_status nvfp4_quantize_fp8(const void *x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols, int64_t ld_x,

@@ -24,7 +24,8 @@ def nv():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == sorted(["nvfp4_quantize", "nvfp4_quantize_fp8", "nvfp4_dequantize", "nvfp4_gemm",
+    assert _declared_functions() == sorted(["nvfp4_quantize", "nvfp4_quantize_fp8", "nvfp4_tensor_amax",
+                                            "nvfp4_dequantize", "nvfp4_gemm",
                                             "nvfp4_gemm_fp8a", "nvfp4_matrix_stats", "nvfp4_gemm_lowrank", "nvfp4_gemm_qa",
                                             "amax_percentile",
                                             "nvfp4_workspace_size", "nvfp4_status_string"])
@@ -77,6 +78,24 @@ def test_quantize_validation(nv):
     assert q(P(FAKE), 0, 32, None, None, ctypes.byref(t), None, P(FAKE), ws - 1, None) == 5
     unal = _qt(nv, 4, 32, codes=FAKE + 8)
     assert q(P(FAKE), 0, 32, None, None, ctypes.byref(unal), None, P(FAKE), 256, None) == 3
+
+
+def test_tensor_amax_validation(nv):
+    f = nv.lib.nvfp4_tensor_amax
+    P = ctypes.c_void_p
+    ws = nv.workspace_size(nv.OP_AMAX, 4, 32)
+    assert ws >= 4 * 256
+    assert f(P(FAKE), 9, 4, 32, 32, None, P(FAKE), None, P(FAKE), ws, None) == 4  # dtype
+    assert f(None, 0, 4, 32, 32, None, P(FAKE), None, P(FAKE), ws, None) == 1  # NULL x
+    assert f(P(FAKE), 0, 4, 32, 32, None, None, None, P(FAKE), ws, None) == 1  # NULL amax_out
+    assert f(P(FAKE), 0, 4, 24, 24, None, P(FAKE), None, P(FAKE), ws, None) == 2  # cols % 16
+    assert f(P(FAKE), 0, 4, 32, 16, None, P(FAKE), None, P(FAKE), ws, None) == 2  # ld < cols
+    assert f(P(FAKE), 0, -1, 32, 32, None, P(FAKE), None, P(FAKE), ws, None) == 2
+    assert f(P(FAKE + 4), 0, 4, 32, 32, None, P(FAKE), None, P(FAKE), ws, None) == 3  # x align
+    assert f(P(FAKE), 0, 4, 32, 32, None, P(FAKE + 2), None, P(FAKE), ws, None) == 3  # amax align
+    assert f(P(FAKE), 0, 4, 32, 32, P(FAKE), P(FAKE), None, P(FAKE), ws, None) == 6  # src_scale w/o e4m3
+    assert f(P(FAKE), 0, 4, 32, 32, None, P(FAKE), None, None, ws, None) == 5  # workspace
+    assert f(P(FAKE), 0, 4, 32, 32, None, P(FAKE), None, P(FAKE), ws - 1, None) == 5
 
 
 def test_dequantize_validation(nv):
@@ -218,6 +237,18 @@ def test_percentile_validation(nv):
     assert f(P(FAKE), 1, 10, 32, 32, 99.9, 1, None, None, None, P(FAKE), ws, None) == 1
     assert f(P(FAKE), 1, 10, 32, 32, 99.9, 1, P(FAKE), None, None, P(FAKE), 100, None) == 5
     assert f(P(FAKE), 1, 10, 32, 32, 99.9, 1, P(FAKE), None, None, None, ws, None) == 5
+
+
+def test_binding_rejects_column_strided_views(nv):
+    # the C ABI takes a row stride only, so the binding refuses views whose rows are not contiguous
+    import torch
+    x = torch.zeros((4, 64), dtype=torch.float32)
+    with pytest.raises(AssertionError):
+        nv._row_stride(x[:, ::2], "x")
+    with pytest.raises(AssertionError):
+        nv._row_stride(x, "x", cols=32)
+    assert nv._row_stride(x[1:3], "x") == 64 and nv._row_stride(x[:1], "x") == 64
+    assert nv._row_stride(torch.zeros((8, 128))[:, :64], "x") == 128
 
 
 def test_valid_call_without_gpu_reports_device(nv):

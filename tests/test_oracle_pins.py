@@ -177,6 +177,18 @@ def test_f32_to_bf16_against_torch():
     assert np.array_equal(oracle.f32_to_bf16_bits(x), want)
 
 
+def test_widen_bf16_against_torch():
+    # every bf16 bit pattern widens to the fp32 value torch gives it (NaN patterns stay NaN)
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(4096, 16)
+    got = oracle.widen(h, oracle.BF16)
+    want = torch.from_numpy(h.view(np.int16)).view(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    m = ~np.isnan(want)
+    assert np.array_equal(got[m].view(np.uint32), want[m].view(np.uint32))
+    # and the bf16 -> f64 helper the GEMM references use agrees with it
+    assert np.array_equal(oracle.bf16_bits_to_f64(h)[m], want[m].astype(np.float64))
+
+
 def test_widen_f16_against_numpy():
     h = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(4096, 16)
     got = oracle.widen(h, oracle.F16)

@@ -174,8 +174,8 @@ def test_quantize_replayed_from_hip_graph(nv):
     x = torch.zeros((rows, cols), dtype=torch.float32, device=DEV)
     q = nv.NVFP4Tensor.empty(rows, cols, DEV)
     q8 = nv.FP8Tensor.empty(rows, cols, DEV)
-    ws = torch.empty(nv.workspace_size(nv.OP_QUANTIZE, rows, cols), dtype=torch.uint8, device=DEV)
-    ws8 = torch.empty_like(ws)
+    ws = nv.quantize_workspace(DEV)
+    ws8 = nv.quantize_workspace(DEV)
     flags = torch.zeros(1, dtype=torch.int32, device=DEV)
     nv.quantize(x, out=q, workspace=ws, flags=flags)
     nv.quantize_fp8(x, out=q8, workspace=ws8, flags=flags)
