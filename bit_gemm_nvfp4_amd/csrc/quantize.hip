@@ -433,25 +433,24 @@ __global__ __launch_bounds__(256) void k_encode(TileGeom gm, const float *__rest
 // is written, with no relay through a leader.  The payload travels inside the atomic word, so
 // relaxed device-scope atomics suffice (no cache maintenance in the loop).
 //
-// Call tags: the tag of a call is one more than the tag word (workspace word 0).  Each workgroup
-// reads the tag word and then counts itself in an arrival counter (word 1, ordered after the read
-// by release semantics); the workgroup that arrives last has seen every other workgroup's read, so
-// at its end it advances the tag word to this call's tag and clears the counter.  The next call on
-// the workspace, which the stream (or the caller's events) starts only after every workgroup of
-// this one has finished, therefore tags its slots differently, with no clearing between calls, and
-// a launch captured in a HIP graph (same kernel arguments on every replay) still works.  The
-// workspace must hold zeros before its first use.  What breaks that contract is reported rather
-// than trusted: a slot that already carries this call's tag when a workgroup publishes, or an
-// arrival count beyond the grid, sets bit 2 of `flags`.
+// Call tags: the tag of a call is one more than the tag word (workspace word 0), which every
+// workgroup reads before it publishes (the tag is part of the published word).  A workgroup whose
+// poll found every slot carrying the tag knows that every workgroup has read the tag word, so it
+// stores the call's tag there (all such stores write the same value).  The next call on the
+// workspace, which the stream (or the caller's events) starts only after every workgroup of this
+// one has finished, therefore tags its slots differently, with no clearing between calls, and a
+// launch captured in a HIP graph (same kernel arguments on every replay) still works.  A slot that
+// already carries the call's tag when its workgroup publishes (a workspace that was not zeroed
+// before first use, or calls that overlapped on it) would let the polls pass early; the publish is
+// an exchange, so that case is seen and sets bit 2 of `flags`.
 //
 // The polls are bounded: if other work kept some workgroups from being scheduled for that long,
-// bit 1 of `flags` is set and the outputs are invalid, instead of a hang.  Late workgroups still
-// take part in the protocol when they run (they read the same tag, find every slot of the call
-// published, and the last of them advances the tag), so the next call starts from a clean state.
+// bit 1 of `flags` is set and the outputs are invalid, instead of a hang.  Workgroups that time out
+// leave the tag word alone; the late workgroups then read the same tag, find every slot of the call
+// published, and store the tag, so the next call starts from a consistent state.
 // ---------------------------------------------------------------------------------------------
 constexpr int kSlotBase = 16;  // workspace words before the 64-bit slots
 constexpr int kTagWord = 0;    // tag of the last completed call
-constexpr int kArriveWord = 1; // workgroups of the running call that have read the tag word
 
 constexpr uint32_t kPollLimit = 1u << 22;
 
@@ -467,15 +466,9 @@ __global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const flo
     const uint64_t wave = (uint64_t)blockIdx.x * NWV + wid, nwaves = (uint64_t)gridDim.x * NWV;
     const float sc = (SRC == NVFP4_E4M3 && src_scale) ? *src_scale : 1.0f;
     uint64_t *slots = reinterpret_cast<uint64_t *>(ws + kSlotBase);
-    // call tag and arrival count (wave 0, lane 0; the release orders the tag read before the count)
-    uint32_t epoch = 0, arrived = 0;
-    if (wid == 0) {
-        if (lane == 0) {
-            epoch = __hip_atomic_load(ws + kTagWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-            arrived = __hip_atomic_fetch_add(ws + kArriveWord, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        epoch = (uint32_t)__shfl((int)epoch, 0, 64);
-    }
+    // call tag (wave 0); the publish below depends on it, so the read precedes the publish
+    uint32_t epoch = 0;
+    if (wid == 0) epoch = __hip_atomic_load(ws + kTagWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
 
     // ---- phase 1: load the resident tiles, block maxima (NVFP4), tensor maximum ----
     TileRegs<SRC> t[TPW];
@@ -512,16 +505,15 @@ __global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const flo
             for (int i = 0; i < NWV; i++) wgmax = max(wgmax, red[i]);
             const uint64_t prev = __hip_atomic_exchange(&slots[blockIdx.x], ((uint64_t)epoch << 32) | wgmax,
                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            // a slot already tagged for this call, or more arrivals than workgroups: the workspace
-            // was not zeroed before first use, or was shared by overlapping calls
-            if ((uint32_t)(prev >> 32) == epoch || arrived >= gridDim.x) {
-                if (flags) atomicOr(flags, 4);
-            }
+            // a slot already tagged for this call: the workspace was not zeroed before first use, or
+            // was shared by overlapping calls
+            if ((uint32_t)(prev >> 32) == epoch && flags) atomicOr(flags, 4);
         }
         // ---- wait for every slot of this call; all loads of a chunk of 8 slots per lane in
         // flight at once ----
         const uint32_t G = gridDim.x;
         uint32_t a = 0;
+        bool agreed = false;
         for (uint32_t it = 0;; it++) {
             bool ready = true;
             a = 0;
@@ -539,7 +531,10 @@ __global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const flo
                     a = max(a, (uint32_t)v[k]);
                 }
             }
-            if (__all(ready)) break;
+            if (__all(ready)) {
+                agreed = true;
+                break;
+            }
             if (it >= kPollLimit) {
                 if (lane == 0 && flags) atomicOr(flags, 2);
                 break;
@@ -548,12 +543,8 @@ __global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const flo
         }
         a = wave_max_u32(a);
         if (lane == 0) amax_bits = a;
-        // the last workgroup to arrive: every workgroup has read the tag word, so advance it and
-        // clear the counter for the next call
-        if (lane == 0 && arrived == gridDim.x - 1) {
-            __hip_atomic_store(ws + kArriveWord, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(ws + kTagWord, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        // every slot carried this call's tag, so every workgroup has read the tag word: advance it
+        if (lane == 0 && agreed) __hip_atomic_store(ws + kTagWord, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     m = amax_bits;
