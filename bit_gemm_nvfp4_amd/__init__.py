@@ -25,7 +25,7 @@ NVFP4_F32, NVFP4_BF16, NVFP4_F16, NVFP4_E4M3 = 0, 1, 2, 3
 OP_QUANTIZE, OP_DEQUANTIZE, OP_GEMM, OP_PERCENTILE, OP_STATS, OP_LOWRANK, OP_GEMM_QA, OP_AMAX = 0, 1, 2, 3, 4, 5, 6, 7
 STATUS_NAMES = ["NVFP4_OK", "NVFP4_ERR_NULL", "NVFP4_ERR_SHAPE", "NVFP4_ERR_ALIGN", "NVFP4_ERR_DTYPE",
                 "NVFP4_ERR_WORKSPACE", "NVFP4_ERR_ARG", "NVFP4_ERR_DEVICE", "NVFP4_ERR_LAUNCH"]
-EXPORTED = ["nvfp4_quantize", "nvfp4_quantize_fp8", "nvfp4_tensor_amax", "nvfp4_dequantize", "nvfp4_gemm",
+EXPORTED = ["nvfp4_quantize", "nvfp4_quantize_noalloc", "nvfp4_quantize_fp8", "nvfp4_tensor_amax", "nvfp4_dequantize", "nvfp4_gemm",
             "nvfp4_gemm_fp8a", "nvfp4_matrix_stats", "nvfp4_gemm_lowrank", "nvfp4_gemm_qa", "amax_percentile",
             "nvfp4_workspace_size", "nvfp4_status_string"]
 # bits of the quantize `flags` word
@@ -42,6 +42,7 @@ _P, _I64, _I32, _SZ, _D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.
 _PT = ctypes.POINTER(CTensor)
 _SIGNATURES = {
     "nvfp4_quantize": [_P, _I32, _I64, _P, _P, _PT, _P, _P, _SZ, _P],
+    "nvfp4_quantize_noalloc": [_P, _I32, _I64, _P, _P, _PT, _P, _P],
     "nvfp4_quantize_fp8": [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "nvfp4_tensor_amax": [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P],
     "nvfp4_gemm_fp8a": [_P, _P, _I64, _I64, _PT, _P, _I64, _P, _SZ, _P],
@@ -257,6 +258,22 @@ def quantize(x: torch.Tensor, amax: torch.Tensor | None = None, src_scale: torch
     out.flags = flags
     if check:
         check_flags(flags, "nvfp4_quantize")
+    return out
+
+
+def quantize_noalloc(x: torch.Tensor, out: NVFP4Tensor, amax: torch.Tensor | None = None,
+                     src_scale: torch.Tensor | None = None, flags: torch.Tensor | None = None) -> NVFP4Tensor:
+    """quantize() for callers that cannot allocate: the outputs (and the optional flags word) come
+    from the caller, and the run-time amax agreement uses the library's own per-GPU scratch instead of
+    a workspace.  Nothing is allocated.  Calls that overlap on one GPU race on that scratch."""
+    ld = _rows(x, "x")
+    rows, cols = x.shape
+    assert out.shape == (rows, cols), f"out: shape {out.shape}, expected {(rows, cols)}"
+    ct = out.c()
+    st = load_library().nvfp4_quantize_noalloc(_ptr(x), _DT[x.dtype], ld, _ptr(src_scale), _ptr(amax),
+                                               ctypes.byref(ct), _ptr(flags), _stream(x.device))
+    _check(st, "nvfp4_quantize_noalloc")
+    out.flags = flags
     return out
 
 

@@ -97,6 +97,27 @@ nvfp4_status check_matrix(const void *p, int64_t rows, int64_t cols, int64_t ld,
     return NVFP4_OK;
 }
 
+// Scratch of nvfp4_quantize_noalloc: the run-time amax agreement's tag word and slots, one array
+// per GPU for the life of the process.  Zero-initialized when the code object loads, which is the
+// state the agreement needs before its first use; each call leaves it consistent for the next.
+// The host sees only a stand-in for this name: kernels get the device address from
+// hipGetSymbolAddress (scratch_address below).
+static __device__ __align__(256) uint8_t scratch[kQuantizeWsBytes];
+
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array, looked up once per device; NULL on failure.
+void *scratch_address() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    void *q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+    g_scratch_ptr[dev].store(q, std::memory_order_release);
+    return q;
+}
+
 }  // namespace
 }  // namespace nvfp4
 
@@ -164,6 +185,32 @@ nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype x_dtype, int64_t ld_x, co
     const int cus = current_device_cus();
     if (cus == 0) return NVFP4_ERR_DEVICE;
     hipError_t e = launch_quantize(x, x_dtype, ld_x, src_scale, amax_in, out, flags, workspace, cus, stream);
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+}
+
+nvfp4_status nvfp4_quantize_noalloc(const void *x, nvfp4_dtype x_dtype, int64_t ld_x, const float *src_scale,
+                                    const float *amax_in, const nvfp4_tensor *out, int32_t *flags,
+                                    hipStream_t stream) {
+    const int eb = elem_bytes(x_dtype);
+    if (eb == 0) return NVFP4_ERR_DTYPE;
+    nvfp4_status st = check_qtensor(out);
+    if (st != NVFP4_OK) return st;
+    st = check_matrix(x, out->rows, out->cols, ld_x, eb);
+    if (st != NVFP4_OK) return st;
+    if (src_scale && x_dtype != NVFP4_E4M3) return NVFP4_ERR_ARG;
+    if ((src_scale && !aligned4(src_scale)) || (amax_in && !aligned4(amax_in)) || (flags && !aligned4(flags)))
+        return NVFP4_ERR_ALIGN;
+    // the scratch holds the run-time amax agreement of any size (the grid is capped at its slots)
+    static_assert(sizeof(scratch) >= kQuantizeWsBytes, "scratch smaller than the quantize workspace");
+    if (nvfp4_workspace_size(NVFP4_OP_QUANTIZE, out->rows, out->cols, 0) > sizeof(scratch)) return NVFP4_ERR_WORKSPACE;
+    const int cus = current_device_cus();
+    if (cus == 0) return NVFP4_ERR_DEVICE;
+    void *ws = nullptr;
+    if (!amax_in) {
+        ws = scratch_address();
+        if (!ws) return NVFP4_ERR_DEVICE;
+    }
+    hipError_t e = launch_quantize(x, x_dtype, ld_x, src_scale, amax_in, out, flags, ws, cus, stream);
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
 }
 

@@ -122,6 +122,23 @@ nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype x_dtype, int64_t ld_x, co
                             size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * nvfp4_quantize_noalloc -- nvfp4_quantize without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, steps, results and flags as nvfp4_quantize; the run-time amax
+ * agreement uses a scratch array inside the library instead of the caller's workspace: 16 KiB of
+ * device memory per GPU the library runs on, held until the process ends, zeroed when the library
+ * is loaded and left consistent by every call.  Every tensor size fits it.  The call allocates
+ * nothing (no hipMalloc, no library routine that allocates).  All calls on one GPU share that GPU's
+ * scratch: calls that overlap on one GPU (different streams with no ordering between them) race on
+ * it; such a race is reported in flags bit 2 when it is seen, and the outputs are then invalid.
+ * The static-amax form (amax_in not NULL) uses no scratch.  NVFP4_ERR_DEVICE also when the scratch
+ * address cannot be obtained.
+ */
+nvfp4_status nvfp4_quantize_noalloc(const void *x, nvfp4_dtype x_dtype, int64_t ld_x, const float *src_scale,
+                                    const float *amax_in, const nvfp4_tensor *out, int32_t *flags,
+                                    hipStream_t stream);
+
+/*
  * nvfp4_tensor_amax -- *amax_out = max |v| over x [rows x cols] (row stride ld_x elements), v the
  * source value widened as nvfp4_quantize step 1 does (E4M3 source: times *src_scale, NULL meaning
  * 1.0; "Qwen3-VL-8B-Instruct-heretic-NVFP4", "Quantization Details": a per-tensor amax taken at

@@ -24,7 +24,8 @@ def nv():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == sorted(["nvfp4_quantize", "nvfp4_quantize_fp8", "nvfp4_tensor_amax",
+    assert _declared_functions() == sorted(["nvfp4_quantize", "nvfp4_quantize_noalloc", "nvfp4_quantize_fp8",
+                                            "nvfp4_tensor_amax",
                                             "nvfp4_dequantize", "nvfp4_gemm",
                                             "nvfp4_gemm_fp8a", "nvfp4_matrix_stats", "nvfp4_gemm_lowrank", "nvfp4_gemm_qa",
                                             "amax_percentile",
@@ -78,6 +79,19 @@ def test_quantize_validation(nv):
     assert q(P(FAKE), 0, 32, None, None, ctypes.byref(t), None, P(FAKE), ws - 1, None) == 5
     unal = _qt(nv, 4, 32, codes=FAKE + 8)
     assert q(P(FAKE), 0, 32, None, None, ctypes.byref(unal), None, P(FAKE), 256, None) == 3
+
+
+def test_quantize_noalloc_validation(nv):
+    q = nv.lib.nvfp4_quantize_noalloc
+    t = _qt(nv, 4, 32)
+    P = ctypes.c_void_p
+    assert q(P(FAKE), 9, 32, None, None, ctypes.byref(t), None, None) == 4  # dtype
+    assert q(None, 0, 32, None, None, ctypes.byref(t), None, None) == 1  # NULL x
+    assert q(P(FAKE), 0, 32, None, None, None, None, None) == 1  # NULL out
+    assert q(P(FAKE), 0, 16, None, None, ctypes.byref(t), None, None) == 2  # ld < cols
+    assert q(P(FAKE + 4), 0, 32, None, None, ctypes.byref(t), None, None) == 3  # align
+    assert q(P(FAKE), 0, 32, P(FAKE), None, ctypes.byref(t), None, None) == 6  # scale without e4m3
+    assert q(P(FAKE), 0, 32, None, None, ctypes.byref(t), P(FAKE + 2), None) == 3  # flags align
 
 
 def test_tensor_amax_validation(nv):
@@ -261,3 +275,4 @@ def test_valid_call_without_gpu_reports_device(nv):
     P = ctypes.c_void_p
     ws = nv.workspace_size(nv.OP_QUANTIZE, 4, 32)
     assert nv.lib.nvfp4_quantize(P(FAKE), 0, 32, None, None, ctypes.byref(t), None, P(FAKE), ws, None) == 7
+    assert nv.lib.nvfp4_quantize_noalloc(P(FAKE), 0, 32, None, None, ctypes.byref(t), None, None) == 7
