@@ -433,30 +433,39 @@ __global__ __launch_bounds__(256) void k_encode(TileGeom gm, const float *__rest
 // is written, with no relay through a leader.  The payload travels inside the atomic word, so
 // relaxed device-scope atomics suffice (no cache maintenance in the loop).
 //
-// Call tags: the tag of a call is one more than the tag word (workspace word 0), which every
-// workgroup reads before it publishes (the tag is part of the published word).  A workgroup whose
-// poll found every slot carrying the tag knows that every workgroup has read the tag word, so it
-// stores the call's tag there (all such stores write the same value).  The next call on the
+// Call tags: each workgroup slot has a tag record next to it, which the workgroup sets to the
+// call's tag once its poll has found every slot carrying that tag.  A call's tag is one more than
+// the largest tag record.  Every workgroup reads the records before it publishes (the tag is part
+// of the published word) and a record is only written after every slot of the call is published,
+// so all workgroups of a call read the same records and agree on the tag; the next call on the
 // workspace, which the stream (or the caller's events) starts only after every workgroup of this
-// one has finished, therefore tags its slots differently, with no clearing between calls, and a
-// launch captured in a HIP graph (same kernel arguments on every replay) still works.  A slot that
-// already carries the call's tag when its workgroup publishes (a workspace that was not zeroed
-// before first use, or calls that overlapped on it) would let the polls pass early; the publish is
-// an exchange, so that case is seen and sets bit 2 of `flags`.
+// one has finished, gets a larger one.  Nothing is cleared between calls, and a launch captured in
+// a HIP graph (same kernel arguments on every replay) still works.  The records are written at
+// distinct addresses, and the publish is a plain store, so nothing on the path to the agreement
+// waits on a contended address.
 //
 // The polls are bounded: if other work kept some workgroups from being scheduled for that long,
 // bit 1 of `flags` is set and the outputs are invalid, instead of a hang.  Workgroups that time out
-// leave the tag word alone; the late workgroups then read the same tag, find every slot of the call
-// published, and store the tag, so the next call starts from a consistent state.
+// write no record; the late workgroups read the same records, find every slot of the call
+// published, and write theirs, so the next call still gets a new tag.  A workgroup whose own slot
+// already carries the call's tag before it publishes (a workspace that was not zeroed before first
+// use, or calls that overlapped on it) sets bit 2 of `flags`: the polls may then have passed early.
 // ---------------------------------------------------------------------------------------------
-constexpr int kSlotBase = 16;  // workspace words before the 64-bit slots
-constexpr int kTagWord = 0;    // tag of the last completed call
+constexpr int kHeadWords = 16;  // reserved workspace words
+// Workgroup slots of the workspace: kHeadWords words, one 32-bit tag record per slot, then one
+// 64-bit slot per workgroup (16 KiB hold 1360: several workgroups per CU on any current part).
+constexpr int kMaxSlots = (int)((kQuantizeWsBytes - kHeadWords * 4) / 12);
+constexpr size_t kSlotByteOffset = (kHeadWords * 4 + kMaxSlots * 4 + 7) / 8 * 8;
+static_assert(kSlotByteOffset + kMaxSlots * 8 <= kQuantizeWsBytes, "quantize workspace layout");
+// The largest grid of the single-pass kernel on a device: one workgroup per CU, within the slots.
+constexpr int max_grid_for(int num_cus) { return num_cus < kMaxSlots ? num_cus : kMaxSlots; }
 
 constexpr uint32_t kPollLimit = 1u << 22;
 
 template <int SRC, int TPW, int PB, int OUTF, int NWV>
 __global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const float *__restrict__ src_scale,
-                                                          uint32_t *__restrict__ ws, uint8_t *__restrict__ codes,
+                                                          uint32_t *__restrict__ ws, int nrec,
+                                                          uint8_t *__restrict__ codes,
                                                           uint8_t *__restrict__ scales, float *__restrict__ g_out,
                                                           int32_t *__restrict__ flags) {
     __shared__ uint32_t red[NWV];
@@ -465,10 +474,20 @@ __global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const flo
     const uint64_t ntiles = (gm.nblocks + 63) / 64;
     const uint64_t wave = (uint64_t)blockIdx.x * NWV + wid, nwaves = (uint64_t)gridDim.x * NWV;
     const float sc = (SRC == NVFP4_E4M3 && src_scale) ? *src_scale : 1.0f;
-    uint64_t *slots = reinterpret_cast<uint64_t *>(ws + kSlotBase);
-    // call tag (wave 0); the publish below depends on it, so the read precedes the publish
-    uint32_t epoch = 0;
-    if (wid == 0) epoch = __hip_atomic_load(ws + kTagWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    uint32_t *records = ws + kHeadWords;
+    uint64_t *slots = reinterpret_cast<uint64_t *>(reinterpret_cast<uint8_t *>(ws) + kSlotByteOffset);
+    // tag records (wave 0): issued first, used after the tiles are in, so their latency is hidden.
+    // nrec (the largest grid this device runs, the same for every call on it) bounds the records
+    // any call on this workspace can have written.
+    uint32_t rec[4] = {0u, 0u, 0u, 0u};
+    uint64_t own_prev = 0;
+    if (wid == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; k++)
+            if (lane + 64 * k < nrec)
+                rec[k] = __hip_atomic_load(&records[lane + 64 * k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) own_prev = __hip_atomic_load(&slots[blockIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 
     // ---- phase 1: load the resident tiles, block maxima (NVFP4), tensor maximum ----
     TileRegs<SRC> t[TPW];
@@ -497,17 +516,26 @@ __global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const flo
     }
     m = wave_max_u32(m);
     if (lane == 0) red[wid] = m;
+    // the call's tag: one more than the largest tag record (all workgroups read the same records,
+    // since none is written before every slot of the call is published)
+    uint32_t epoch = 0;
+    if (wid == 0) {
+        uint32_t t = max(max(rec[0], rec[1]), max(rec[2], rec[3]));
+        for (int i = 256 + lane; i < nrec; i += 64)  // parts with more than 256 workgroups
+            t = max(t, __hip_atomic_load(&records[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        epoch = wave_max_u32(t) + 1u;
+    }
     __syncthreads();
     if (wid == 0) {
         if (lane == 0) {
             uint32_t wgmax = 0;
 #pragma unroll
             for (int i = 0; i < NWV; i++) wgmax = max(wgmax, red[i]);
-            const uint64_t prev = __hip_atomic_exchange(&slots[blockIdx.x], ((uint64_t)epoch << 32) | wgmax,
-                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            // a slot already tagged for this call: the workspace was not zeroed before first use, or
-            // was shared by overlapping calls
-            if ((uint32_t)(prev >> 32) == epoch && flags) atomicOr(flags, 4);
+            __hip_atomic_store(&slots[blockIdx.x], ((uint64_t)epoch << 32) | wgmax, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            // its own slot already tagged for this call: the workspace was not zeroed before first
+            // use, or was shared by overlapping calls
+            if ((uint32_t)(own_prev >> 32) == epoch && flags) atomicOr(flags, 4);
         }
         // ---- wait for every slot of this call; all loads of a chunk of 8 slots per lane in
         // flight at once ----
@@ -543,8 +571,9 @@ __global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const flo
         }
         a = wave_max_u32(a);
         if (lane == 0) amax_bits = a;
-        // every slot carried this call's tag, so every workgroup has read the tag word: advance it
-        if (lane == 0 && agreed) __hip_atomic_store(ws + kTagWord, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // every slot carried this call's tag, so every workgroup has read the records: write this one
+        if (lane == 0 && agreed)
+            __hip_atomic_store(&records[blockIdx.x], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     m = amax_bits;
@@ -662,8 +691,6 @@ template <int SRC>
 constexpr int kMaxTpw4 = SRC == NVFP4_F32 ? 4 : SRC == NVFP4_BF16 ? 5 : SRC == NVFP4_F16 ? 8 : 12;
 template <int SRC>
 constexpr int kMaxTpw = SRC == NVFP4_F32 ? 6 : SRC == NVFP4_BF16 ? 8 : SRC == NVFP4_F16 ? 12 : 16;
-// Workgroup slots the quantize workspace holds.
-constexpr int kMaxSlots = (int)((kQuantizeWsBytes - kSlotBase * 4) / 8);
 // For tensors beyond the residency: fewer resident tiles, so that the streamed rest can keep
 // kStreamBatch loads in flight per wave within the same register budget.
 template <int SRC>
@@ -704,8 +731,10 @@ static void launch_fused(const TileGeom &gm, int grid, const float *src_scale, u
                          int32_t *flags, int num_cus, hipStream_t stream) {
     const int cap = fused_per_cu<SRC, TPW, PB, OUTF, NWV>() * num_cus;
     if (grid > cap) grid = cap;
+    // every launch on this device stays within max_grid_for(num_cus) workgroups, so that many tag
+    // records cover every record a call on this workspace can have written
     hipLaunchKernelGGL((k_quant_fused<SRC, TPW, PB, OUTF, NWV>), dim3(grid), dim3(NWV * 64), 0, stream, gm,
-                       src_scale, ws, out.codes, out.scales, out.scale, flags);
+                       src_scale, ws, max_grid_for(num_cus), out.codes, out.scales, out.scale, flags);
 }
 
 // Resident launch: tiles per wave rounded up to a supported residency, at most T.
@@ -733,7 +762,7 @@ template <int SRC, int OUTF>
 static void launch_fused_any(const TileGeom &gm, const float *src_scale, uint32_t *ws, const QOut &out,
                              int32_t *flags, int num_cus, hipStream_t stream) {
     const uint64_t ntiles = (gm.nblocks + 63) / 64;
-    const int max_grid = num_cus < kMaxSlots ? num_cus : kMaxSlots;
+    const int max_grid = max_grid_for(num_cus);
     const int grid16 = grid_for(ntiles, 16, max_grid);
     const uint64_t tpw16 = (ntiles + 16 * (uint64_t)grid16 - 1) / (16 * (uint64_t)grid16);
     if (tpw16 <= (uint64_t)kMaxTpw4<SRC>) {
