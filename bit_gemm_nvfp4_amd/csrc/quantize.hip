@@ -462,14 +462,17 @@ constexpr int max_grid_for(int num_cus) { return num_cus < kMaxSlots ? num_cus :
 
 constexpr uint32_t kPollLimit = 1u << 22;
 
-template <int SRC, int TPW, int PB, int OUTF, int NWV>
+template <int SRC, int TPW, int PB, int OUTF, int NWV, int LPW>
 __global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const float *__restrict__ src_scale,
                                                           uint32_t *__restrict__ ws, int nrec,
                                                           uint8_t *__restrict__ codes,
                                                           uint8_t *__restrict__ scales, float *__restrict__ g_out,
                                                           int32_t *__restrict__ flags) {
+    constexpr int VPB = kVpb<SRC>;
     __shared__ uint32_t red[NWV];
     __shared__ uint32_t amax_bits;
+    // LDS-resident tiles: LPW per wave, each lane's vectors at [wave][tile][vector][lane]
+    __shared__ u32x4 lds_tiles[LPW > 0 ? NWV * LPW * VPB * 64 : 1];
     const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint64_t ntiles = (gm.nblocks + 63) / 64;
     const uint64_t wave = (uint64_t)blockIdx.x * NWV + wid, nwaves = (uint64_t)gridDim.x * NWV;
@@ -490,11 +493,35 @@ __global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const flo
     }
 
     // ---- phase 1: load the resident tiles, block maxima (NVFP4), tensor maximum ----
+    // Tile s of the wave is tile wave + s * nwaves of the tensor: s < TPW stay in registers,
+    // TPW <= s < TPW + LPW are kept in LDS, the rest is streamed.  The LDS tiles pass through the
+    // register tiles first, in rounds of TPW.
     TileRegs<SRC> t[TPW];
     uint32_t bm[TPW];
+    uint32_t bm_lds[LPW > 0 ? LPW : 1];
+    uint32_t m = 0;
+    u32x4 *my_lds = lds_tiles + (size_t)wid * (LPW > 0 ? LPW : 0) * VPB * 64;
+#pragma unroll
+    for (int r0 = 0; r0 < LPW; r0 += TPW) {
+#pragma unroll
+        for (int i = 0; i < TPW; i++)
+            if (r0 + i < LPW) tile_load<SRC>(t[i], gm, wave + (TPW + r0 + i) * nwaves, lane);
+#pragma unroll
+        for (int i = 0; i < TPW; i++) {
+            if (r0 + i < LPW) {
+                if constexpr (OUTF == kOutFp8) {
+                    m = max(m, tile_lane_max<SRC>(t[i]));
+                } else {
+                    bm_lds[r0 + i] = tile_block_max<SRC>(t[i], lane);
+                    m = max(m, bm_lds[r0 + i]);
+                }
+#pragma unroll
+                for (int j = 0; j < VPB; j++) my_lds[((r0 + i) * VPB + j) * 64 + lane] = t[i].raw[j];
+            }
+        }
+    }
 #pragma unroll
     for (int s = 0; s < TPW; s++) tile_load<SRC>(t[s], gm, wave + s * nwaves, lane);
-    uint32_t m = 0;
 #pragma unroll
     for (int s = 0; s < TPW; s++) {
         if constexpr (OUTF == kOutFp8) {
@@ -505,7 +532,7 @@ __global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const flo
         }
     }
     // tiles beyond the resident ones are streamed, PB loads in flight per wave
-    for (uint64_t tile = wave + TPW * nwaves; tile < ntiles; tile += PB * nwaves) {
+    for (uint64_t tile = wave + (TPW + LPW) * nwaves; tile < ntiles; tile += PB * nwaves) {
         TileRegs<SRC> o[PB];
 #pragma unroll
         for (int b = 0; b < PB; b++) tile_load<SRC>(o[b], gm, tile + b * nwaves, lane);
@@ -592,7 +619,16 @@ __global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const flo
             const uint64_t tile = wave + s * nwaves;
             if (tile < ntiles) tile_store_fp8<SRC>(t[s], g, sc, tile, gm.nblocks, codes, lane);
         }
-        for (uint64_t tile = wave + TPW * nwaves; tile < ntiles; tile += PB * nwaves) {
+#pragma unroll
+        for (int l = 0; l < LPW; l++) {
+            const uint64_t tile = wave + (TPW + l) * nwaves;
+            if (tile < ntiles) {
+#pragma unroll
+                for (int j = 0; j < VPB; j++) t[0].raw[j] = my_lds[(l * VPB + j) * 64 + lane];
+                tile_store_fp8<SRC>(t[0], g, sc, tile, gm.nblocks, codes, lane);
+            }
+        }
+        for (uint64_t tile = wave + (TPW + LPW) * nwaves; tile < ntiles; tile += PB * nwaves) {
             TileRegs<SRC> o[PB];
 #pragma unroll
             for (int b = 0; b < PB; b++) tile_load<SRC>(o[b], gm, tile + b * nwaves, lane);
@@ -614,7 +650,18 @@ __global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const flo
         const uint64_t tile = wave + s * nwaves;
         if (tile < ntiles) tile_store<SRC>(t[s], bs[s], sc, tile, gm.nblocks, codes, scales, lane);
     }
-    for (uint64_t tile = wave + TPW * nwaves; tile < ntiles; tile += PB * nwaves) {
+    // then the LDS tiles, each through a register tile
+#pragma unroll
+    for (int l = 0; l < LPW; l++) {
+        const uint64_t tile = wave + (TPW + l) * nwaves;
+        if (tile < ntiles) {
+#pragma unroll
+            for (int j = 0; j < VPB; j++) t[0].raw[j] = my_lds[(l * VPB + j) * 64 + lane];
+            tile_store<SRC>(t[0], block_scale<SRC>(bm_lds[l], g, six_g, sc), sc, tile, gm.nblocks, codes, scales,
+                            lane);
+        }
+    }
+    for (uint64_t tile = wave + (TPW + LPW) * nwaves; tile < ntiles; tile += PB * nwaves) {
         TileRegs<SRC> o[PB];
 #pragma unroll
         for (int b = 0; b < PB; b++) tile_load<SRC>(o[b], gm, tile + b * nwaves, lane);
@@ -686,27 +733,27 @@ static int grid_for(uint64_t work_items, int per_block, int max_blocks) {
 }
 
 // Largest residency (tiles per wave) whose registers still leave room for four waves per SIMD (at
-// most 128 VGPRs), and for two.
+// most 128 VGPRs).
 template <int SRC>
 constexpr int kMaxTpw4 = SRC == NVFP4_F32 ? 4 : SRC == NVFP4_BF16 ? 5 : SRC == NVFP4_F16 ? 8 : 12;
+// With part of the tiles in LDS (16 waves sharing the 160 KiB, less 1 KiB for the reductions):
+// register tiles and LDS tiles per wave, the register tiles fewer where the LDS tiles' block maxima
+// would push the wave past 128 VGPRs.  Tensors beyond that keep the same residency and stream the
+// rest (read once for the maximum, again for the encode), one tile in flight per wave.
 template <int SRC>
-constexpr int kMaxTpw = SRC == NVFP4_F32 ? 6 : SRC == NVFP4_BF16 ? 8 : SRC == NVFP4_F16 ? 12 : 16;
-// For tensors beyond the residency: fewer resident tiles, so that the streamed rest can keep
-// kStreamBatch loads in flight per wave within the same register budget.
+constexpr int kTpw16L = SRC == NVFP4_F32 ? 4 : SRC == NVFP4_BF16 ? 4 : SRC == NVFP4_F16 ? 8 : 8;
 template <int SRC>
-constexpr int kStreamTpw = SRC == NVFP4_F32 ? 4 : SRC == NVFP4_BF16 ? 6 : SRC == NVFP4_F16 ? 8 : 16;
-template <int SRC>
-constexpr int kStreamBatch = SRC == NVFP4_F32 ? 2 : 4;
+constexpr int kLds16 = (159 * 1024 / 16) / (1024 * SrcTraits<SRC>::kElemBytes);
 
-// Workgroups of k_quant_fused<SRC, TPW, PB, OUTF, NWV> that can be resident on one CU (at least
-// one is assumed), from the runtime's occupancy calculation; computed once per instantiation.
-template <int SRC, int TPW, int PB, int OUTF, int NWV>
+// Workgroups of k_quant_fused<SRC, TPW, PB, OUTF, NWV, LPW> that can be resident on one CU (at
+// least one is assumed), from the runtime's occupancy calculation; computed once per instantiation.
+template <int SRC, int TPW, int PB, int OUTF, int NWV, int LPW>
 static int fused_per_cu() {
     static std::atomic<int> cached{0};
     int n = cached.load(std::memory_order_relaxed);
     if (n == 0) {
         int b = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_quant_fused<SRC, TPW, PB, OUTF, NWV>, NWV * 64, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_quant_fused<SRC, TPW, PB, OUTF, NWV, LPW>, NWV * 64, 0) !=
                 hipSuccess ||
             b < 1)
             b = 1;
@@ -726,14 +773,14 @@ struct QOut {
     float *scale;
 };
 
-template <int SRC, int TPW, int OUTF, int NWV, int PB = 1>
+template <int SRC, int TPW, int OUTF, int NWV, int PB = 1, int LPW = 0>
 static void launch_fused(const TileGeom &gm, int grid, const float *src_scale, uint32_t *ws, const QOut &out,
                          int32_t *flags, int num_cus, hipStream_t stream) {
-    const int cap = fused_per_cu<SRC, TPW, PB, OUTF, NWV>() * num_cus;
+    const int cap = fused_per_cu<SRC, TPW, PB, OUTF, NWV, LPW>() * num_cus;
     if (grid > cap) grid = cap;
     // every launch on this device stays within max_grid_for(num_cus) workgroups, so that many tag
     // records cover every record a call on this workspace can have written
-    hipLaunchKernelGGL((k_quant_fused<SRC, TPW, PB, OUTF, NWV>), dim3(grid), dim3(NWV * 64), 0, stream, gm,
+    hipLaunchKernelGGL((k_quant_fused<SRC, TPW, PB, OUTF, NWV, LPW>), dim3(grid), dim3(NWV * 64), 0, stream, gm,
                        src_scale, ws, max_grid_for(num_cus), out.codes, out.scales, out.scale, flags);
 }
 
@@ -754,10 +801,9 @@ static void launch_resident(const TileGeom &gm, int grid, uint64_t tpw, const fl
 #undef NVFP4_LAUNCH
 }
 
-// Tiles spread over all CUs: one workgroup of 16 waves each (four waves per SIMD hide each other's
-// latencies) when every wave's tiles then fit the smaller register budget, else 8 waves each with up
-// to kMaxTpw resident tiles; fewer workgroups for small tensors.  Beyond that the streaming variant
-// runs (the rest is read twice).
+// Tiles spread over all CUs, one workgroup of 16 waves each (four waves per SIMD hide each other's
+// latencies): all tiles in registers when they fit the 128-VGPR budget (fewer workgroups for small
+// tensors), else part of them in LDS; beyond that residency the rest is streamed (read twice).
 template <int SRC, int OUTF>
 static void launch_fused_any(const TileGeom &gm, const float *src_scale, uint32_t *ws, const QOut &out,
                              int32_t *flags, int num_cus, hipStream_t stream) {
@@ -769,14 +815,7 @@ static void launch_fused_any(const TileGeom &gm, const float *src_scale, uint32_
         launch_resident<SRC, OUTF, 16, kMaxTpw4<SRC>>(gm, grid16, tpw16, src_scale, ws, out, flags, max_grid, stream);
         return;
     }
-    const int grid = grid_for(ntiles, 8, max_grid);
-    const uint64_t tpw = (ntiles + 8 * (uint64_t)grid - 1) / (8 * (uint64_t)grid);
-    if (tpw > (uint64_t)kMaxTpw<SRC>) {
-        launch_fused<SRC, kStreamTpw<SRC>, OUTF, 8, kStreamBatch<SRC>>(gm, grid, src_scale, ws, out, flags, max_grid,
-                                                                      stream);
-        return;
-    }
-    launch_resident<SRC, OUTF, 8, kMaxTpw<SRC>>(gm, grid, tpw, src_scale, ws, out, flags, max_grid, stream);
+    launch_fused<SRC, kTpw16L<SRC>, OUTF, 16, 1, kLds16<SRC>>(gm, grid16, src_scale, ws, out, flags, max_grid, stream);
 }
 
 template <int SRC, int OUTF>

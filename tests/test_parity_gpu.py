@@ -263,9 +263,13 @@ def test_quantize_attention_weight_full(nv):
 
 # Tall tensors whose tile counts (64 blocks per tile, 3 tiles per 3072-wide row) give the
 # single-pass kernel 2, 4, 5, 8 and 12 resident tiles per wave at four waves per SIMD on a
-# 256-CU part, the largest residency for fp32, bf16, f16 and e4m3 sources respectively.
+# 256-CU part, the largest register residency for fp32, bf16, f16 and e4m3 sources respectively;
+# then part of the tiles in LDS (fp32 7000, bf16 9000, f16 14000, e4m3 22000 rows); then more than
+# registers and LDS hold, the rest streamed (fp32 18432, bf16 12000, f16 17000, e4m3 24000 rows).
 @pytest.mark.parametrize("dtype,rows", [("f32", 2000), ("f32", 5000), ("bf16", 6000), ("f16", 10000),
-                                        ("e4m3", 15000)])
+                                        ("e4m3", 15000), ("f32", 7000), ("bf16", 9000), ("f16", 14000),
+                                        ("e4m3", 22000), ("f32", 18432), ("bf16", 12000), ("f16", 17000),
+                                        ("e4m3", 24000)])
 def test_quantize_resident_tiles_per_wave(nv, dtype, rows):
     cols = 3072
     _note(f"quantize {dtype} {rows}x{cols}")
@@ -706,6 +710,21 @@ def test_quantize_fp8_from_fp8_static_zero_and_flags(nv):
     flags.zero_()
     nv.quantize_fp8(to_dev_f32(w), amax=torch.tensor([1.0], device=DEV), flags=flags)
     assert flags.item() & 1
+
+
+@pytest.mark.parametrize("dtype,rows", [("f32", 6000), ("bf16", 12000)])
+def test_quantize_fp8_lds_and_streamed_tiles(nv, dtype, rows):
+    # the FP8 output of the single-pass kernel with part of the tiles in LDS (fp32 6000 rows), and
+    # with the rest streamed (bf16 12000 rows)
+    _note(f"quantize_fp8 {dtype} {rows}x3072")
+    x = (np.random.default_rng(rows).standard_normal((rows, 3072)) * 0.02).astype(np.float32)
+    if dtype == "f32":
+        xd, xh, odt = to_dev_f32(x), x, oracle.F32
+    else:
+        xh = synth.bf16_bits(x)
+        xd, odt = to_dev_bf16(xh), oracle.BF16
+    rb, rs, _ = oracle.quantize_fp8(xh, odt)
+    _assert_fp8_equal(_quant_fp8(nv, xd), rb, rs, f"{dtype} {rows}")
 
 
 def test_quantize_fp8_streamed_tensor(nv):
