@@ -100,21 +100,40 @@ __device__ __forceinline__ void fp4_unpack8_bf16x2(uint32_t w, bf16x2 *v) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Wave reductions (64 lanes).
+// Wave reductions (64 lanes): DPP moves within each row of 16 lanes (lanes i ^ 1, i ^ 2, then the
+// half-row and row mirrors), then one lane of each of the four rows read into a scalar.  The result
+// is the same in every lane, and the order of the operations is fixed.
 // ---------------------------------------------------------------------------------------------
+// Every pattern used reads a lane of the same row, so no lane takes the bound-control zero; written
+// this way, the move folds into the add or max that consumes it (one DPP instruction per step).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within each 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within each 16
+
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int l) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        uint32_t w = (uint32_t)__shfl_xor((int)v, o, kWave);
-        v = v > w ? v : w;
-    }
-    return v;
+    v = max(v, dpp_u32<kDppXor1>(v));
+    v = max(v, dpp_u32<kDppXor2>(v));
+    v = max(v, dpp_u32<kDppHalfMirror>(v));
+    v = max(v, dpp_u32<kDppMirror>(v));
+    return max(max(readlane_u32(v, 0), readlane_u32(v, 16)), max(readlane_u32(v, 32), readlane_u32(v, 48)));
 }
 
 __device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    v += u2f(dpp_u32<kDppXor1>(f2u(v)));
+    v += u2f(dpp_u32<kDppXor2>(f2u(v)));
+    v += u2f(dpp_u32<kDppHalfMirror>(f2u(v)));
+    v += u2f(dpp_u32<kDppMirror>(f2u(v)));
+    return (u2f(readlane_u32(f2u(v), 0)) + u2f(readlane_u32(f2u(v), 16))) +
+           (u2f(readlane_u32(f2u(v), 32)) + u2f(readlane_u32(f2u(v), 48)));
 }
 
 // Pack two fp32 values that are exactly representable in bf16 (the decoded e2m1 x s products)

@@ -40,6 +40,8 @@
 // per block; a wave reduction finishes each row.  A wave works on two rows at once with all their loads issued ahead of the arithmetic.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include <type_traits>
 
 #include "common.h"
@@ -968,8 +970,8 @@ __global__ __launch_bounds__(256) void k_gemv(const __bf16 *__restrict__ A, int6
 
 // k_gemv_reg: the same product for K <= 4096 without LDS.  Lane l works on blocks l + 64 u (u < UB) of
 // every row it visits, so it loads those blocks of A (expanded to bf16 for NVFP4 and E4M3
-// activations) into registers once; a wave then streams pairs of W rows with all their loads
-// issued ahead of the arithmetic.
+// activations) into registers once; a wave then streams pairs of W rows, the loads of its next pair
+// issued before the arithmetic of the current one (two register buffers, used alternately).
 template <int MM, int AM, int UB>
 __global__ __launch_bounds__(256) void k_gemv_reg(const __bf16 *__restrict__ A, int64_t lda,
                                                   const uint8_t *__restrict__ a_codes,
@@ -979,26 +981,38 @@ __global__ __launch_bounds__(256) void k_gemv_reg(const __bf16 *__restrict__ A, 
                                                   float *__restrict__ C, int64_t ldc, int64_t N, int64_t K) {
     const int lane = threadIdx.x & 63;
     const int64_t nblk = K / 16;
-    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    // wave-uniform indices, so that row addresses are scalar and each lane adds a 32-bit offset
+    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
     // lanes past the last block use the last block and add nothing
-    int64_t blk[UB];
+    uint32_t blk[UB];
 #pragma unroll
     for (int u = 0; u < UB; u++) {
         const int64_t b = lane + 64 * u;
-        blk[u] = b < nblk ? b : nblk - 1;
+        blk[u] = (uint32_t)(b < nblk ? b : nblk - 1);
     }
-    u32x2 cw[2][UB];
-    uint32_t sb[2][UB];
-    auto load_rows = [&](const int64_t (&rows)[2]) {
+    struct RowPair {
+        int64_t rows[2];
+        u32x2 cw[2][UB];
+        uint32_t sb[2][UB];
+    };
+    // the pair of rows a wave takes at position n (the second one is n + nwaves, or n again)
+    auto load_pair = [&](RowPair &p, int64_t n) {
+        p.rows[0] = n;
+        p.rows[1] = (n + nwaves) < N ? (n + nwaves) : n;
 #pragma unroll
-        for (int h = 0; h < 2; h++)
+        for (int h = 0; h < 2; h++) {
+            const uint8_t *cr = w_codes + p.rows[h] * (K / 2);
+            const uint8_t *sr = w_scales + p.rows[h] * nblk;
 #pragma unroll
             for (int u = 0; u < UB; u++) {
-                cw[h][u] = *reinterpret_cast<const u32x2 *>(w_codes + rows[h] * (K / 2) + blk[u] * 8);
-                sb[h][u] = w_scales[rows[h] * nblk + blk[u]];
+                p.cw[h][u] = *reinterpret_cast<const u32x2 *>(cr + blk[u] * 8u);
+                p.sb[h][u] = sr[blk[u]];
             }
+        }
     };
+    RowPair buf[2];
+    if (wave < N) load_pair(buf[0], wave);
     // A's blocks of this lane, 16 bf16 each
     u32x4 av[MM][UB][2];
 #pragma unroll
@@ -1006,25 +1020,23 @@ __global__ __launch_bounds__(256) void k_gemv_reg(const __bf16 *__restrict__ A, 
 #pragma unroll
         for (int u = 0; u < UB; u++) {
             if constexpr (AM == kAmBf16) {
-                const u32x4 *ap = reinterpret_cast<const u32x4 *>(A + m * lda + blk[u] * 16);
+                const u32x4 *ap = reinterpret_cast<const u32x4 *>(A + m * lda + blk[u] * 16u);
                 av[m][u][0] = ap[0];
                 av[m][u][1] = ap[1];
             } else if constexpr (AM == kAmNvfp4) {
-                const u32x2 c = *reinterpret_cast<const u32x2 *>(a_codes + m * (K / 2) + blk[u] * 8);
+                const u32x2 c = *reinterpret_cast<const u32x2 *>(a_codes + m * (K / 2) + blk[u] * 8u);
                 const float s = __builtin_amdgcn_cvt_f32_fp8((int)a_scales[m * nblk + blk[u]], 0);
                 av[m][u][0] = expand8(c[0], s);
                 av[m][u][1] = expand8(c[1], s);
             } else {
-                const u32x4 b = *reinterpret_cast<const u32x4 *>(a_codes + m * lda + blk[u] * 16);
+                const u32x4 b = *reinterpret_cast<const u32x4 *>(a_codes + m * lda + blk[u] * 16u);
                 av[m][u][0] = expand8_fp8_bf16(u32x2{b[0], b[1]});
                 av[m][u][1] = expand8_fp8_bf16(u32x2{b[2], b[3]});
             }
         }
     const float gw = *w_g;
     const float ga = AM != kAmBf16 ? *a_g : 1.0f;
-    for (int64_t n = wave; n < N; n += 2 * nwaves) {
-        const int64_t rows[2] = {n, (n + nwaves) < N ? (n + nwaves) : n};
-        load_rows(rows);
+    auto compute = [&](const RowPair &p) {
         float acc[2][MM];
 #pragma unroll
         for (int h = 0; h < 2; h++)
@@ -1035,10 +1047,10 @@ __global__ __launch_bounds__(256) void k_gemv_reg(const __bf16 *__restrict__ A, 
             const bool live = lane + 64 * u < nblk;
 #pragma unroll
             for (int h = 0; h < 2; h++) {
-                const float sc = __builtin_amdgcn_cvt_f32_fp8((int)sb[h][u], 0);
+                const float sc = __builtin_amdgcn_cvt_f32_fp8((int)p.sb[h][u], 0);
                 bf16x2 wv[8];
-                fp4_unpack8_bf16x2(cw[h][u][0], wv);
-                fp4_unpack8_bf16x2(cw[h][u][1], wv + 4);
+                fp4_unpack8_bf16x2(p.cw[h][u][0], wv);
+                fp4_unpack8_bf16x2(p.cw[h][u][1], wv + 4);
 #pragma unroll
                 for (int m = 0; m < MM; m++) {
                     const u32x4 a0 = av[m][u][0], a1 = av[m][u][1];
@@ -1054,17 +1066,24 @@ __global__ __launch_bounds__(256) void k_gemv_reg(const __bf16 *__restrict__ A, 
         }
 #pragma unroll
         for (int h = 0; h < 2; h++) {
-            if (h == 1 && rows[1] == rows[0]) break;
+            if (h == 1 && p.rows[1] == p.rows[0]) break;
 #pragma unroll
             for (int m = 0; m < MM; m++) {
-                const float t = wave_sum_f32(acc[h][m]);
-                if (lane == 0) {
-                    float v = t;
-                    if (AM != kAmBf16) v = v * ga;
-                    C[m * ldc + rows[h]] = v * gw;
-                }
+                float v = wave_sum_f32(acc[h][m]);
+                if (AM != kAmBf16) v = v * ga;
+                if (lane == 0) C[m * ldc + p.rows[h]] = v * gw;
             }
         }
+    };
+    // pairs n = wave, wave + 2 nwaves, ...: load the next pair into the other buffer, then compute
+    for (int64_t n = wave; n < N; n += 4 * nwaves) {
+        const int64_t n1 = n + 2 * nwaves;
+        if (n1 < N) load_pair(buf[1], n1);
+        compute(buf[0]);
+        if (n1 >= N) break;
+        const int64_t n2 = n1 + 2 * nwaves;
+        if (n2 < N) load_pair(buf[0], n2);
+        compute(buf[1]);
     }
 }
 
@@ -1082,6 +1101,23 @@ struct GemmA {
 
 size_t gemv_lds_bytes(int64_t M, int64_t K) { return (size_t)M * (size_t)K * 2; }
 
+// Waves per CU of the register GEMV: as many as the registers let stay resident (from the
+// runtime's occupancy calculation, once per instantiation), so that enough rows are in flight to
+// stream W while every wave also has its next pair of rows loading.
+template <int MM, int AM, int UB>
+static int64_t gemv_waves_per_cu() {
+    static std::atomic<int> cached{0};
+    int n = cached.load(std::memory_order_relaxed);
+    if (n == 0) {
+        int b = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_gemv_reg<MM, AM, UB>, 256, 0) != hipSuccess || b < 1)
+            b = 1;
+        n = b * 4;
+        cached.store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 // M <= 4: A in registers (K <= 4096) or LDS; M = 5: A in LDS.  Beyond that the dot products (8 per
 // 16-element block and row of A) outweigh the stream of W: at M = 8 the LDS form measured 19.3 us
 // against 22.5 us tiled at N = K = 3072, but 48.6 against 37.8 us at N = 18432, so the tiled kernels
@@ -1092,8 +1128,11 @@ template <int MM, int AM, int UB>
 static void launch_gemv_reg(const GemmA &a, const nvfp4_tensor *w, float *c, int64_t ldc, int num_cus,
                             hipStream_t stream) {
     const int64_t N = w->rows, K = w->cols;
-    int64_t grid = (N + 7) / 8;  // one pass of two rows per wave, at most 16 workgroups per CU
-    if (grid > (int64_t)num_cus * 16) grid = (int64_t)num_cus * 16;
+    // two rows per wave and pass, at most the resident waves; the passes spread evenly
+    const int64_t pairs = (N + 1) / 2;
+    const int64_t max_waves = (int64_t)num_cus * gemv_waves_per_cu<MM, AM, UB>();
+    const int64_t passes = (pairs + max_waves - 1) / max_waves;
+    int64_t grid = ((pairs + passes - 1) / passes + 3) / 4;
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL((k_gemv_reg<MM, AM, UB>), dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16 *)a.bf16,
                        a.lda, a.codes, a.scales, a.g, w->codes, w->scales, w->global_scale, c, ldc, N, K);

@@ -176,8 +176,9 @@ __device__ __forceinline__ uint32_t tile_block_max(const TileRegs<SRC> &t, int l
 #pragma unroll
     for (int j = 0; j < VPB; j++) {
         pm[j] = vec_absmax_bits<SRC>(t.raw[j]);
-#pragma unroll
-        for (int o = 1; o < VPB; o <<= 1) pm[j] = max(pm[j], (uint32_t)__shfl_xor((int)pm[j], o, 64));
+        // the VPB lanes of a block are neighbours (lanes i ^ 1, and i ^ 2 for four)
+        if constexpr (VPB >= 2) pm[j] = max(pm[j], dpp_u32<kDppXor1>(pm[j]));
+        if constexpr (VPB >= 4) pm[j] = max(pm[j], dpp_u32<kDppXor2>(pm[j]));
     }
     if constexpr (VPB == 1) {
         return pm[0];
