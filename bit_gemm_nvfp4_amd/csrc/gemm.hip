@@ -492,9 +492,13 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
     rc[1] = make_rsrc(w_codes + n0 * (K / 2), nrows * (K / 2));
     rs[1] = make_rsrc(w_scales + n0 * (K / 16), nrows * (K / 16));
 
+    // LDS rows are 128 bytes (64 16-bit values) and hold their eight 16-byte chunks at chunk index
+    // chunk ^ ((row / 2) % 8).  The LDS serves a 16-byte-per-lane access sixteen lanes at a time
+    // across its 64 banks (256 bytes); a fragment read has those lanes on 16 consecutive rows at one
+    // logical chunk, and this swizzle puts them on 16 distinct 16-byte bank groups (rows of either
+    // parity fill one half of the banks; row / 2 spreads the eight of each parity over that half).
     // Expansion unit u of this thread: 8-element chunk d = tid + NT * j of the step's tile (row d / 8,
-    // chunk d % 8: one NVFP4 code dword, or 8 E4M3 bytes), j = u for A (u < AD), u - AD for W.  LDS
-    // rows hold 16-byte chunks at chunk index (chunk ^ row % 8).
+    // chunk d % 8: one NVFP4 code dword, or 8 E4M3 bytes), j = u for A (u < AD), u - AD for W.
     uint32_t q_coff[QD], q_soff[QD], q_lds[QD];
 #pragma unroll
     for (int u = 0; u < QD; u++) {
@@ -504,22 +508,25 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
                     : (A_QS && u < AD) ? (row * (uint32_t)lda + c * 8) * 2
                                        : row * (uint32_t)(K / 2) + c * 4;
         q_soff[u] = row * (uint32_t)(K / 16) + (c >> 1);
-        q_lds[u] = (u < AD ? 0u : (uint32_t)W_OFF) + row * ROWB + ((c ^ (row & 7)) << 4);
+        q_lds[u] = (u < AD ? 0u : (uint32_t)W_OFF) + row * ROWB + ((c ^ ((row >> 1) & 7)) << 4);
     }
     // Direct-to-LDS load b of this wave fills the 1 KiB LDS block of tile rows (wid * A_DMA + b) * 8
     // .. + 7: lane l writes 16 bytes at l * 16, i.e. row l / 8, swizzled chunk l % 8, so it loads
-    // logical chunk (l % 8) ^ (row % 8).
-    uint32_t a_dma_off;
+    // logical chunk (l % 8) ^ ((row / 2) % 8) = (l % 8) ^ (l / 16) ^ (4 if the block is odd).
+    static_assert(A_DMA % 2 == 0, "block parity of direct-to-LDS load b is that of b");
+    uint32_t a_dma_off[2];
     {
         const uint32_t row = (uint32_t)(wid * A_DMA) * 8 + (uint32_t)(lane >> 3);
-        const uint32_t c = (uint32_t)((lane & 7) ^ ((lane >> 3) & 7));
-        a_dma_off = row * (uint32_t)lda * 2 + c * 16;
+        const uint32_t c = (uint32_t)((lane & 7) ^ (lane >> 4));
+        a_dma_off[0] = row * (uint32_t)lda * 2 + c * 16;
+        a_dma_off[1] = row * (uint32_t)lda * 2 + (c ^ 4u) * 16;
     }
-    // Fragment reads: 32x32x16 operands take row (lane % 32), k = 16 kk + 8 (lane / 32) .. + 7.
+    // Fragment reads: 32x32x16 operands take row (lane % 32), k = 16 kk + 8 (lane / 32) .. + 7; the
+    // fragment rows start at multiples of 32, so the swizzle of row lane % 32 is (lane / 2) % 8.
     uint32_t offA[4], offB[4];
 #pragma unroll
     for (int kk = 0; kk < 4; kk++) {
-        const uint32_t ch = ((uint32_t)(2 * kk + (lane >> 5)) ^ (uint32_t)(lane & 7)) << 4;
+        const uint32_t ch = ((uint32_t)(2 * kk + (lane >> 5)) ^ (uint32_t)((lane >> 1) & 7)) << 4;
         offA[kk] = (uint32_t)(wm * WTM + (lane & 31)) * ROWB + ch;
         offB[kk] = (uint32_t)W_OFF + (uint32_t)(wn * WTN + (lane & 31)) * ROWB + ch;
     }
@@ -543,7 +550,7 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
 #pragma unroll
             for (int b = 0; b < A_DMA; b++)
                 load_to_lds16(ra, smem + a_stage * A_STAGE + (wid * A_DMA + b) * 1024,
-                              a_dma_off + (uint32_t)(b * 8) * (uint32_t)lda * 2, k0 * 2);
+                              a_dma_off[b & 1] + (uint32_t)(b * 8) * (uint32_t)lda * 2, k0 * 2);
         }
 #pragma unroll
         for (int u = 0; u < QD; u++) {
@@ -1184,6 +1191,7 @@ static const TileCfg kTiles[] = {
     {256, 192, 1, 0.97},  // 8 waves, 64 x 96 per wave
     {128, 256, 1, 0.79},  // 8 waves, 64 x 64 per wave
     {128, 128, 2, 0.72},  // 4 waves, 64 x 64 per wave, two workgroups per CU
+    {128, 192, 1, 0.75},  // 8 waves, 32 x 96 per wave
 };
 constexpr double kUsPerTileStep = 2.0;      // one 256 x 256 x 64 step on one CU, microseconds
 constexpr double kReduceBytesPerUs = 4.0e6;  // HBM rate of the partial-sum pass
@@ -1284,6 +1292,7 @@ static bool launch_tiled(const GemmA &a, int64_t M, const nvfp4_tensor *w, float
         if (plan.cfg == 0) return launch_tile<256, 256, 4, 2, AM>(a, M, w, c, ldc, plan, partials, lr, stream);
         if (plan.cfg == 1) return launch_tile<256, 192, 4, 2, AM>(a, M, w, c, ldc, plan, partials, lr, stream);
     }
+    if (plan.cfg == 4) return launch_tile<128, 192, 4, 2, AM>(a, M, w, c, ldc, plan, partials, lr, stream);
     if (plan.cfg == 2) return launch_tile<128, 256, 2, 4, AM>(a, M, w, c, ldc, plan, partials, lr, stream);
     return launch_tile<128, 128, 2, 2, AM>(a, M, w, c, ldc, plan, partials, lr, stream);
 }

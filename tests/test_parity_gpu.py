@@ -596,9 +596,9 @@ def test_percentile_counter_capacity(nv):
 
 
 # shapes that select each of the GEMM kernel's tile configurations (256x256, 256x192, 128x256,
-# 128x128), with aligned and ragged K and ragged M / N edges
-@pytest.mark.parametrize("mnk", [(576, 16384, 64), (448, 16512, 64), (130, 1000, 128), (704, 10880, 128),
-                                 (3000, 5000, 80), (250, 12400, 48)])
+# 128x128, 128x192), with aligned and ragged K and ragged M / N edges
+@pytest.mark.parametrize("mnk", [(576, 16384, 64), (448, 16512, 64), (390, 16300, 128), (704, 10880, 128),
+                                 (130, 1000, 128), (3000, 5000, 80), (250, 12400, 48), (700, 10800, 80)])
 def test_gemm_tile_configs(nv, mnk):
     m, n, k = mnk
     _note(f"gemm tile configs {mnk}")
