@@ -146,7 +146,7 @@ def main():
     clr = torch.empty((M_TOK, N_OUT), dtype=torch.float32, device=dev)
     # static activation amax, calibrated once: max over channels of the per-channel p99.9 of |A|
     qa_amax = nv.amax_percentile(sets[0][1], 99.9, per_channel=True)[0].max().reshape(1).contiguous()
-    qa_ws = torch.empty(max(nv.workspace_size(nv.OP_GEMM_QA, M_TOK, N_OUT, K_IN), 1), dtype=torch.uint8, device=dev)
+    qa_ws = nv.gemm_qa_workspace(M_TOK, N_OUT, K_IN, dev)
     cqa = torch.empty((M_TOK, N_OUT), dtype=torch.float32, device=dev)
 
     ops = ["quantize", "requantize", "dequantize", "act_quantize", "gemm_w4a16", "gemm_w4a4", "gemv_w4a16",
@@ -592,7 +592,7 @@ def bench_configs(nv, dev, reps, warmup):
     t3 = torch.randn((4096, 12288), generator=g, device=dev).to(torch.bfloat16)
     amax_t3 = nv.amax_percentile(t3, 99.9, per_channel=True)[0].max().reshape(1).contiguous()
     c_out = {s_: torch.empty((4096, s_[0]), dtype=torch.float32, device=dev) for s_ in set(shapes)}
-    qa_ws = torch.empty(max(nv.workspace_size(nv.OP_GEMM_QA, 4096, r, c) for r, c in shapes), dtype=torch.uint8,
+    qa_ws = torch.zeros(max(nv.workspace_size(nv.OP_GEMM_QA, 4096, r, c) for r, c in shapes), dtype=torch.uint8,
                         device=dev)
 
     def gemms(form):

@@ -357,6 +357,14 @@ def gemm(a: torch.Tensor | NVFP4Tensor | FP8Tensor, w: NVFP4Tensor, out: torch.T
     return out
 
 
+def gemm_qa_workspace(m: int, n: int, k: int, device) -> torch.Tensor:
+    """A workspace for gemm_qa on [m, k] activations and an [n, k] weight: zeroed, as the library
+    requires of its first bytes (the staged form's group counters) before their first use; every
+    call leaves them zero, so it can be reused for any shape it is large enough for.  Calls that
+    share one must be ordered (same stream, or events)."""
+    return torch.zeros(max(workspace_size(OP_GEMM_QA, m, n, k), 1), dtype=torch.uint8, device=device)
+
+
 def gemm_qa(a: torch.Tensor, w: NVFP4Tensor, amax: torch.Tensor, out: torch.Tensor | None = None,
             workspace: torch.Tensor | None = None) -> torch.Tensor:
     """C [M, N] fp32 = A_hat . W_hat^T with A (bf16 [M, K]) quantized to NVFP4 inside the GEMM under
@@ -369,7 +377,7 @@ def gemm_qa(a: torch.Tensor, w: NVFP4Tensor, amax: torch.Tensor, out: torch.Tens
     m = a.shape[0]
     out, ldc = _gemm_out(out, m, n, device)
     ws_bytes = workspace_size(OP_GEMM_QA, m, n, k)
-    ws = workspace if workspace is not None else _workspace(ws_bytes, device)
+    ws = workspace if workspace is not None else gemm_qa_workspace(m, n, k, device)
     wct = w.c()
     st = load_library().nvfp4_gemm_qa(_ptr(a), _ptr(amax), m, lda, ctypes.byref(wct), _ptr(out), ldc, _ptr(ws),
                                       ws.numel() if workspace is not None else ws_bytes, _stream(device))

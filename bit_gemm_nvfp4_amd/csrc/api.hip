@@ -2,6 +2,7 @@
 //
 // Every entry point validates all of its arguments before enqueuing anything, so an error status
 // means no work was queued.  No entry point synchronizes, allocates or keeps a pointer.
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -147,12 +148,14 @@ size_t nvfp4_workspace_size(int op, int64_t rows, int64_t cols, int64_t k) {
     case NVFP4_OP_PERCENTILE: return cols >= 0 ? percentile_ws_bytes(cols, k ? 1 : 0) : 0;
     case NVFP4_OP_STATS: return stats_ws_bytes();
     case NVFP4_OP_GEMM_QA: {
+        // the group counters of the staged form, then the largest of the three forms' needs
         if (rows < 0 || cols < 0 || k < 0) return 0;
         const int cus = current_device_cus();
         const int c2 = cus > 0 ? cus : 256;
         const size_t fused = gemm_ws_bytes(rows, cols, k, c2, kFirstQuantTileCfg);
         const size_t two_step = qa_ws_bytes(rows, k) + gemm_ws_bytes(rows, cols, k, c2);
-        return fused > two_step ? fused : two_step;
+        const size_t staged = gemm_qa_staged_ws_bytes(rows, cols, k, c2) - kQaSyncBytes;
+        return kQaSyncBytes + std::max(fused, std::max(two_step, staged));
     }
     case NVFP4_OP_LOWRANK: {
         if (rows < 0 || cols < 0 || k < 0) return 0;
@@ -342,27 +345,37 @@ nvfp4_status nvfp4_gemm_qa(const void *a_bf16, const float *a_amax, int64_t M, i
     st = check_matrix(c, M, N, ldc, 4, 4);
     if (st != NVFP4_OK) return st;
     if (workspace && !aligned16(workspace)) return NVFP4_ERR_ALIGN;
-    // Fused only where it is not slower: each N tile quantizes its A rows again, so beyond two
-    // 256-wide N tiles the separate quantize pass plus the W4A4 kernel wins (measured on MI355X:
-    // equal at N = 256 .. 512, 1.1x slower fused at N = 1024, 1.85x at N = 3072).
-    const bool fused = gemm_qa_fusable(M, K, lda) && N <= kQaFusedMaxN;
-    if (!fused && M > 0 && K > 0 && (!workspace || workspace_bytes < qa_ws_bytes(M, K))) return NVFP4_ERR_WORKSPACE;
     const int cus = current_device_cus();
+    // Three forms.  Staged (one launch): where all of the W4A4 product's workgroups run in one
+    // round, each quantizes a share of its A row block into the workspace, waits for the other
+    // workgroups of that row block, then runs the main loop on the quantized rows.  Otherwise the
+    // fused kernel, which quantizes A in its staging path once per N tile, where that is not slower
+    // (measured on MI355X: equal at N = 256 .. 512, 1.1x slower at N = 1024, 1.85x at N = 3072),
+    // else a quantize pass into the workspace and the W4A4 kernel.  The first kQaSyncBytes of the
+    // workspace hold the staged form's group counters; the other forms use what follows.
+    const bool has_sync = workspace && workspace_bytes >= kQaSyncBytes;
+    const bool staged = has_sync && workspace_bytes >= gemm_qa_staged_ws_bytes(M, N, K, cus) &&
+                        gemm_qa_staged_applies(M, N, K, lda, cus);
+    const bool fused = !staged && gemm_qa_fusable(M, K, lda) && N <= kQaFusedMaxN;
+    uint8_t *rest = has_sync ? reinterpret_cast<uint8_t *>(workspace) + kQaSyncBytes : nullptr;
+    const size_t rest_bytes = has_sync ? workspace_bytes - kQaSyncBytes : 0;
+    if (!staged && !fused && M > 0 && K > 0 && rest_bytes < qa_ws_bytes(M, K)) return NVFP4_ERR_WORKSPACE;
     if (cus == 0) return NVFP4_ERR_DEVICE;
     hipError_t e;
     if (K == 0 || M == 0) {
         e = launch_fill_zero_f32(c, M, N, ldc, stream);
+    } else if (staged) {
+        e = launch_gemm_qa_staged(a_bf16, a_amax, M, lda, w, c, ldc, workspace, workspace_bytes, cus, stream);
     } else if (fused) {
-        e = launch_gemm_qa_fused(a_bf16, a_amax, M, lda, w, c, ldc, workspace, workspace_bytes, cus, stream);
+        e = launch_gemm_qa_fused(a_bf16, a_amax, M, lda, w, c, ldc, rest, rest_bytes, cus, stream);
     } else {
         // quantize A with the static amax into the workspace, then the W4A4 product
-        uint8_t *ws = reinterpret_cast<uint8_t *>(workspace);
         const size_t qb = qa_ws_bytes(M, K);
         const size_t cb = align256((size_t)M * (size_t)(K / 2)), sb = align256((size_t)M * (size_t)(K / 16));
-        const nvfp4_tensor aq{ws, ws + cb, reinterpret_cast<float *>(ws + cb + sb), M, K};
+        const nvfp4_tensor aq{rest, rest + cb, reinterpret_cast<float *>(rest + cb + sb), M, K};
         e = launch_quantize(a_bf16, NVFP4_BF16, lda, nullptr, a_amax, &aq, nullptr, nullptr, cus, stream);
         if (e == hipSuccess)
-            e = launch_gemm(nullptr, &aq, M, K, w, c, ldc, ws + qb, workspace_bytes - qb, cus, stream);
+            e = launch_gemm(nullptr, &aq, M, K, w, c, ldc, rest + qb, rest_bytes - qb, cus, stream);
     }
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
 }

@@ -41,6 +41,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstdlib>
 
 #include <type_traits>
 
@@ -83,13 +84,14 @@ constexpr int kAmNvfp4 = 1;  // NVFP4 tensor (W4A4)
 constexpr int kAmFp8 = 2;    // E4M3 bytes with one tensor scale (FP8 activations)
 constexpr int kAmQuant = 3;  // bf16 rows quantized to NVFP4 in the kernel with a static amax (W4A4)
 
-// Quantize one unit of 8 bf16 activations to NVFP4 with the static global scale g (six_g = fl(6 g))
-// and return their exact values e2m1 x s as 8 f16.  The unit's 16-element block is completed by
-// the neighbouring lane (lane ^ 1), which holds the other 8 elements: the block amax is exchanged
-// with one DPP move.  The steps and roundings are those of the quantize kernel (block scale byte
-// = nearest E4M3 of fl(bamax / six_g), r = fl(1 / fl(s g)), code = nearest E2M1 of fl(v r), zero
-// kept at zero), so the values equal the expansion of what nvfp4_quantize with this amax stores.
-__device__ __forceinline__ u32x4 quant8_f16(u32x4 raw, float g, float six_g) {
+// Quantize one unit of 8 bf16 activations to NVFP4 with the static global scale g (six_g =
+// fl(6 g)): returns the unit's 8 codes (element i in nibble i) and its block's scale byte.  The
+// unit's 16-element block is completed by the neighbouring lane (lane ^ 1), which holds the other
+// 8 elements: the block amax is exchanged with one DPP move.  The steps and roundings are those of
+// the quantize kernel (block scale byte = nearest E4M3 of fl(bamax / six_g), r = fl(1 / fl(s g)),
+// code = nearest E2M1 of fl(v r), zero kept at zero), so the codes are what nvfp4_quantize with
+// this amax stores.
+__device__ __forceinline__ uint32_t quant8_codes(u32x4 raw, float g, float six_g, uint32_t &sbyte) {
     float v[8];
     uint32_t bm = 0;
 #pragma unroll
@@ -103,15 +105,160 @@ __device__ __forceinline__ u32x4 quant8_f16(u32x4 raw, float g, float six_g) {
     const uint32_t bo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)bm, 0xB1, 0xF, 0xF, false);  // lane ^ 1
     bm = bm > bo ? bm : bo;
     const float q = u2f(bm) / six_g;
-    const uint32_t sbyte = g != 0.0f ? e4m3_from_f32(q) : 0u;
+    sbyte = g != 0.0f ? e4m3_from_f32(q) : 0u;
     const float s = e4m3_to_f32(sbyte);
     const float rd = 1.0f / (s * g);
     const float r = s == 0.0f ? 0.0f : rd;
     float y[8];
 #pragma unroll
     for (int e = 0; e < 8; e++) y[e] = v[e] == 0.0f ? v[e] : v[e] * r;
-    const _Float16 sh = (_Float16)s;
-    return expand8_f16(fp4_pack8(y), f16x2{sh, sh});
+    return fp4_pack8(y);
+}
+
+// The same unit quantized and returned as its 8 exact values e2m1 x s in f16.
+__device__ __forceinline__ u32x4 quant8_f16(u32x4 raw, float g, float six_g) {
+    uint32_t sbyte;
+    const uint32_t codes = quant8_codes(raw, g, six_g, sbyte);
+    const _Float16 sh = (_Float16)e4m3_to_f32(sbyte);
+    return expand8_f16(codes, f16x2{sh, sh});
+}
+
+// Quantize one 16-element block of bf16 activations (lo: elements 0..7, hi: 8..15) in one lane,
+// with the steps and roundings of quant8_codes: returns the 16 codes (element i in nibble i) and
+// the block scale byte.
+__device__ __forceinline__ uint64_t quant16_codes(u32x4 lo, u32x4 hi, float g, float six_g, uint32_t &sbyte) {
+    float v[16];
+    uint32_t bm = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const uint32_t w = i < 4 ? lo[i] : hi[i - 4];
+        v[2 * i] = u2f(w << 16);
+        v[2 * i + 1] = u2f(w & 0xFFFF0000u);
+        const uint32_t m0 = (w << 16) & 0x7FFFFFFFu, m1 = w & 0x7FFF0000u;
+        bm = bm > m0 ? bm : m0;
+        bm = bm > m1 ? bm : m1;
+    }
+    const float q = u2f(bm) / six_g;
+    sbyte = g != 0.0f ? e4m3_from_f32(q) : 0u;
+    const float s = e4m3_to_f32(sbyte);
+    const float rd = 1.0f / (s * g);
+    const float r = s == 0.0f ? 0.0f : rd;
+    float y[16];
+#pragma unroll
+    for (int e = 0; e < 16; e++) y[e] = v[e] == 0.0f ? v[e] : v[e] * r;
+    return (uint64_t)fp4_pack8(y) | ((uint64_t)fp4_pack8(y + 8) << 32);
+}
+
+// s_waitcnt immediate: wait until at most `vm` vector-memory and `lgkm` LDS operations are pending.
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | ((vm >> 4) << 14); }
+
+// Activations quantized once inside the W4A4 product (the staged form of nvfp4_gemm_qa): the bf16
+// rows, the static amax, the workspace arrays the NVFP4 activations go to (those the product then
+// reads as its A operand) and the group counters.
+struct QaPre {
+    const __bf16 *x;
+    int64_t ldx;
+    const float *amax;
+    uint32_t *sync;  // arrival counters [kQaMaxGroups], then departure counters [kQaMaxGroups]
+    uint8_t *codes;  // [M][K / 2]
+    uint8_t *scales; // [M][K / 16]
+    uint32_t spin_limit;  // polls of the group counter before a member quantizes its whole region itself
+};
+
+// Staged quantization of one workgroup's A region.  The members of a group (the workgroups of one
+// A row block and K slice, one per N tile) each quantize a share of the group's 16-element blocks
+// into the workspace, publish it and wait until every member has: then all of the region is
+// there.  Publication: the codes and scale bytes are written with agent-coherent (sc1) stores,
+// which do not stay dirty in one XCD's L2, so no writeback of the L2 is needed; every wave waits
+// for its stores to complete, then one thread adds 1 to the group's arrival counter; a waiting
+// member polls the counter and then acquires at agent scope.  The last member to leave resets the counters to zero,
+// so a zeroed counter area stays zeroed from one call to the next.  A member whose wait runs out
+// (the group not co-resident for a very long time) quantizes the whole region itself: the values
+// are the same, so correctness never depends on the wait.
+template <int NT>
+__device__ __forceinline__ void qa_stage(const QaPre &pre, int64_t K, int64_t m0, int64_t mrows, int kblk0, int nblk_row, int group,
+                         int members, int member, bool publish) {
+    __shared__ int timed_out;
+    const float g = *pre.amax / 2688.0f;
+    const float six_g = 6.0f * g;
+    // work unit: four consecutive blocks of a row (64 elements; nblk_row is a multiple of 4)
+    const int nq_row = nblk_row / 4;
+    const int64_t nq = mrows * nq_row;
+    constexpr int kBatch = 4;  // units per thread whose loads are issued before the first is used
+    // agent-coherent (sc1) 16-byte stores through buffer resources over the region's rows
+    const __amdgpu_buffer_rsrc_t rcode = lr_rsrc(pre.codes + m0 * (K / 2), mrows * (K / 2));
+    const __amdgpu_buffer_rsrc_t rscale = lr_rsrc(pre.scales + m0 * (K / 16), mrows * (K / 16));
+    constexpr int kSc1 = 16;  // cache policy bit of an agent-coherent store
+    auto quantize_units = [&](int64_t q0, int64_t q1) {
+        for (int64_t base = q0 + threadIdx.x; base < q1; base += (int64_t)kBatch * NT) {
+            u32x4 raw[kBatch][8];
+#pragma unroll
+            for (int j = 0; j < kBatch; j++) {
+                const int64_t q = base + (int64_t)j * NT;
+                if (q < q1) {
+                    const int64_t r = m0 + q / nq_row, kb = kblk0 + (q % nq_row) * 4;
+                    const u32x4 *src = reinterpret_cast<const u32x4 *>(pre.x + r * pre.ldx + kb * 16);
+#pragma unroll
+                    for (int h = 0; h < 8; h++) raw[j][h] = src[h];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; j++) {
+                const int64_t q = base + (int64_t)j * NT;
+                if (q < q1) {
+                    const int64_t rr = q / nq_row, kb = kblk0 + (q % nq_row) * 4;  // row within the region
+                    uint64_t cw[4];
+                    uint32_t sw = 0;
+#pragma unroll
+                    for (int t = 0; t < 4; t++) {
+                        uint32_t sb;
+                        cw[t] = quant16_codes(raw[j][2 * t], raw[j][2 * t + 1], g, six_g, sb);
+                        sw |= sb << (8 * t);
+                    }
+                    const uint32_t co = (uint32_t)(rr * (K / 2) + kb * 8);
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        u32x4{(uint32_t)cw[0], (uint32_t)(cw[0] >> 32), (uint32_t)cw[1], (uint32_t)(cw[1] >> 32)}, rcode,
+                        co, 0, kSc1);
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        u32x4{(uint32_t)cw[2], (uint32_t)(cw[2] >> 32), (uint32_t)cw[3], (uint32_t)(cw[3] >> 32)}, rcode,
+                        co + 16, 0, kSc1);
+                    __builtin_amdgcn_raw_buffer_store_b32(sw, rscale, (uint32_t)(rr * (K / 16) + kb), 0, kSc1);
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));  // this wave's stores are complete
+    };
+    uint32_t *arrive = pre.sync + group, *depart = pre.sync + kQaMaxGroups + group;
+    if (publish) {  // first phase: this member's share, then its arrival
+        quantize_units(nq * member / members, nq * (member + 1) / members);
+        __syncthreads();
+        if (threadIdx.x == 0) __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    // second phase: wait for the group, then leave
+    if (threadIdx.x == 0) {
+        uint32_t polls = 0;
+        while (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)members &&
+               polls < pre.spin_limit) {
+            polls++;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        timed_out = __hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)members;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+    if (timed_out) {
+        quantize_units(0, nq);
+        __syncthreads();
+        if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        if (__hip_atomic_fetch_add(depart, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)members - 1) {
+            __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(depart, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
 // Expand 8 E4M3 bytes (two dwords, element i in byte i) into 8 exact f16 values: e4m3 values have
@@ -185,6 +332,26 @@ __device__ __forceinline__ void tile_coords(int id, int tiles_m, int tiles_n, in
     const int r = id - group * GM * tiles_n;
     tm = first_m + r % gm;
     tn = r / gm;
+}
+
+// The tiles of tile_coords, each XCD's set of tiles started row block by row block: where the
+// tiles an XCD takes form a rectangle of GM row blocks x C N tiles, its i-th workgroup takes row
+// block i / C, N tile i % C of it, so that the workgroups of one row block start one after another
+// (the staged quantization waits for all of them); otherwise the order of tile_coords.
+__device__ __forceinline__ void tile_coords_grouped(int lin, int tiles_m, int tiles_n, int &tm, int &tn) {
+    const int ntiles = tiles_m * tiles_n;
+    const int per_xcd = ntiles / 8;
+    constexpr int GM = 4;
+    if (per_xcd > 0 && lin < per_xcd * 8 && tiles_m % GM == 0 && per_xcd % GM == 0 && (GM * tiles_n) % per_xcd == 0) {
+        const int x = lin % 8, pos = lin / 8;
+        const int id0 = x * per_xcd;  // first id of this XCD's range
+        const int group = id0 / (GM * tiles_n), r0 = id0 % (GM * tiles_n);
+        const int cols = per_xcd / GM;
+        tm = group * GM + pos / cols;
+        tn = r0 / GM + pos % cols;
+        return;
+    }
+    tile_coords(lin, tiles_m, tiles_n, tm, tn);
 }
 
 template <int BM, int BN, int WM, int WN, int AM>
@@ -418,15 +585,13 @@ struct StepIdx {
     static constexpr int value = V;
 };
 
-// s_waitcnt immediate: wait until at most `vm` vector-memory and `lgkm` LDS operations are pending.
-constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | ((vm >> 4) << 14); }
 
 // 16 bytes per lane from buffer `r` at (voff + soff) straight into LDS: lane l writes lds + 16 l.
 __device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff, uint32_t soff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
 }
 
-template <int BM, int BN, int WM, int WN, int AM, bool LR = false>
+template <int BM, int BN, int WM, int WN, int AM, bool LR = false, bool PRE = false>
 __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restrict__ A, int64_t lda,
                                                           const uint8_t *__restrict__ a_codes,
                                                           const uint8_t *__restrict__ a_scales,
@@ -435,9 +600,11 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
                                                           const uint8_t *__restrict__ w_scales,
                                                           const float *__restrict__ w_g, float *__restrict__ C,
                                                           int64_t ldc, int64_t M, int64_t N, int64_t K,
-                                                          int slice_steps, LrArgs lr) {
+                                                          int slice_steps, LrArgs lr, QaPre pre) {
     // A_X: activations expanded from registers into LDS as f16 (NVFP4 codes, or E4M3 bytes), with W
-    // expanded to f16 too; otherwise bf16 activations are copied straight into LDS.
+    // expanded to f16 too; otherwise bf16 activations are copied straight into LDS.  PRE (NVFP4
+    // activations only): the workgroup first takes part in quantizing its A region into the arrays
+    // the NVFP4 operand points to (qa_stage), and *a_g is then the static amax.
     constexpr bool A_Q = AM == kAmNvfp4, A_F8 = AM == kAmFp8, A_QS = AM == kAmQuant, A_X = AM != kAmBf16;
     constexpr int NT = 64 * WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;    // wave tile
@@ -463,7 +630,11 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
     const int tiles_m = (int)((M + BM - 1) / BM);
     const int tiles_n = (int)((N + BN - 1) / BN);
     int tm_idx, tn_idx;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, tm_idx, tn_idx);
+    const int slice = (int)blockIdx.y;
+    if constexpr (PRE)
+        tile_coords_grouped(blockIdx.x, tiles_m, tiles_n, tm_idx, tn_idx);
+    else
+        tile_coords(blockIdx.x, tiles_m, tiles_n, tm_idx, tn_idx);
     const int64_t m0 = (int64_t)tm_idx * BM;
     const int64_t n0 = (int64_t)tn_idx * BN;
 
@@ -535,16 +706,22 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
     u32x2 qa8[2][A_F8 ? AD : 1];     // E4M3 activations: two register sets of 8-byte chunks
     u32x4 qa16[2][A_QS ? AD : 1];    // bf16 activations to quantize: two register sets of 16 bytes
     // static amax -> global scale of the quantized activations (as the quantize kernel forms it)
-    const float qs_g = A_QS ? *a_g / 2688.0f : 0.0f;
+    static_assert(!PRE || (A_Q && !LR), "staged quantization feeds the NVFP4-activation product");
+    const float qs_g = (A_QS || PRE) ? *a_g / 2688.0f : 0.0f;
     const float qs_six_g = 6.0f * qs_g;
 
-    // K slice of this workgroup (split-K: blockIdx.y; otherwise the whole of K)
+    // K slice of this workgroup (split-K: `slice`; otherwise the whole of K)
     const int total_steps = (int)(K / kBK);
-    const int kbase = (int)blockIdx.y * slice_steps;
+    const int kbase = slice * slice_steps;
     const int nsteps = (total_steps - kbase) < slice_steps ? (total_steps - kbase) : slice_steps;
     const int last = nsteps - 1;
+    auto stage_a = [&](bool publish) {
+        if constexpr (PRE)
+            qa_stage<NT>(pre, K, m0, mrows, kbase * (kBK / 16), nsteps * (kBK / 16), slice * tiles_m + tm_idx,
+                         tiles_n, tn_idx, publish);
+    };
     // Loads past the last step repeat it: harmless, and the loop body stays free of branches.
-    auto issue = [&](int s, int a_stage, int r) {
+    auto issue = [&](int s, int a_stage, int r, int u0 = 0, int u1 = 1 << 30) {
         const uint32_t k0 = (uint32_t)((kbase + (s < last ? s : last)) * kBK);
         if constexpr (!A_X) {
 #pragma unroll
@@ -554,6 +731,7 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
         }
 #pragma unroll
         for (int u = 0; u < QD; u++) {
+            if (u < u0 || u >= u1) continue;
             if (A_F8 && u < AD) {
                 qa8[r][A_F8 ? u : 0] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rc[0], q_coff[u], k0, 0));
                 continue;
@@ -630,10 +808,25 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
 
     // prologue: steps 0 and 1 in flight, step 0 expanded (and, register-resident, slices 0 and 1
     // of step 0 read)
-    issue(0, 0, 0);
-    issue(1, 1, 1);
+    if constexpr (PRE) {
+        // the W tiles of steps 0 and 1 load while this workgroup quantizes its share of A, and
+        // step 0's is expanded before the wait for the rest of the group
+        issue(0, 0, 0, AD, QD);
+        issue(1, 1, 1, AD, QD);
+        stage_a(true);
 #pragma unroll
-    for (int u = 0; u < QD; u++) expand_unit(u, 0, 0, 0);
+        for (int u = AD; u < QD; u++) expand_unit(u, 0, 0, 0);
+        stage_a(false);
+        issue(0, 0, 0, 0, AD);
+        issue(1, 1, 1, 0, AD);
+#pragma unroll
+        for (int u = 0; u < AD; u++) expand_unit(u, 0, 0, 0);
+    } else {
+        issue(0, 0, 0);
+        issue(1, 1, 1);
+#pragma unroll
+        for (int u = 0; u < QD; u++) expand_unit(u, 0, 0, 0);
+    }
     end_step();
     if constexpr (RESIDENT) {
         read_frags(0, 0, 0, 0);
@@ -735,8 +928,8 @@ __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restr
     // (w_g == nullptr) stores its raw partial sums into its own [M x ldc] plane of C instead ----
     const bool partial = w_g == nullptr;
     const float gw = partial ? 1.0f : *w_g;
-    const float ga = (A_X && !partial) ? (A_QS ? qs_g : *a_g) : 1.0f;
-    float *Cs = C + (int64_t)blockIdx.y * M * ldc;
+    const float ga = (A_X && !partial) ? ((A_QS || PRE) ? qs_g : *a_g) : 1.0f;
+    float *Cs = C + (int64_t)slice * M * ldc;
     if constexpr (LR) {
         // low-rank branch (unsplit products only): scale the sums first, with the same roundings as
         // the store below, then add T . U^T on the matrix cores and store
@@ -1229,22 +1422,48 @@ size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus, int first_cfg
 }
 
 // Returns true when the low-rank branch `lr` (if any) was added in the epilogue.
+// k_gemm_mfma addresses one tile's rows with 32-bit buffer offsets
+template <int AM>
+static bool mfma_fits(int64_t BM, int64_t BN, int64_t K, int64_t lda) {
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t a_row_bytes = (AM == kAmBf16 || AM == kAmQuant) ? lda * 2 : AM == kAmNvfp4 ? K / 2 : lda;
+    return (BM + 1) * a_row_bytes + K * 2 < lim && BN * (K / 2) < lim;
+}
+
 template <int BM, int BN, int WM, int WN, int AM>
 static bool launch_tile(const GemmA &a, int64_t M, const nvfp4_tensor *w, float *c, int64_t ldc,
-                        const GemmPlan &plan, float *partials, const LrArgs *lr, hipStream_t stream) {
+                        const GemmPlan &plan, float *partials, const LrArgs *lr, hipStream_t stream,
+                        const QaPre *pre = nullptr) {
     const int64_t N = w->rows, K = w->cols;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int64_t lda = a.lda;
-    // k_gemm_mfma addresses one tile's rows with 32-bit buffer offsets
-    const int64_t lim = (int64_t)1 << 31;
-    const int64_t a_row_bytes = (AM == kAmBf16 || AM == kAmQuant) ? lda * 2 : AM == kAmNvfp4 ? K / 2 : lda;
-    const bool fits = (int64_t)(BM + 1) * a_row_bytes + K * 2 < lim && (int64_t)BN * (K / 2) < lim;
+    const bool fits = mfma_fits<AM>(BM, BN, K, lda);
+    if constexpr (AM == kAmNvfp4) {
+        if (pre) {  // staged quantization (checked to apply: K % 64 == 0, fits)
+            if (partials) {
+                hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, AM, false, true>),
+                                   dim3((unsigned)tiles, (unsigned)plan.splits), dim3(64 * WM * WN), 0, stream,
+                                   (const __bf16 *)nullptr, lda, a.codes, a.scales, a.g, w->codes, w->scales, nullptr,
+                                   partials, N, M, N, K, plan.slice_steps, LrArgs{}, *pre);
+                const int64_t total = M * N;
+                const int64_t blocks = (total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536;
+                hipLaunchKernelGGL((k_splitk_reduce<2>), dim3((unsigned)blocks), dim3(256), 0, stream, partials,
+                                   plan.splits, M, N, N, a.g, w->global_scale, c, ldc);
+            } else {
+                hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, AM, false, true>), dim3((unsigned)tiles),
+                                   dim3(64 * WM * WN), 0, stream, (const __bf16 *)nullptr, lda, a.codes, a.scales,
+                                   a.g, w->codes, w->scales, w->global_scale, c, ldc, M, N, K, (int)(K / kBK),
+                                   LrArgs{}, *pre);
+            }
+            return false;
+        }
+    }
     if (K % kBK == 0 && fits) {
         if (partials) {
             // K slices into their own planes of the workspace, then the ordered sum and scaling
             hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, AM>), dim3((unsigned)tiles, (unsigned)plan.splits),
                                dim3(64 * WM * WN), 0, stream, (const __bf16 *)a.bf16, lda, a.codes, a.scales, a.g,
-                               w->codes, w->scales, nullptr, partials, N, M, N, K, plan.slice_steps, LrArgs{});
+                               w->codes, w->scales, nullptr, partials, N, M, N, K, plan.slice_steps, LrArgs{}, QaPre{});
             const int64_t total = M * N;
             const int64_t blocks = (total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536;
             hipLaunchKernelGGL((k_splitk_reduce<AM == kAmBf16 ? 0 : AM == kAmQuant ? 2 : 1>), dim3((unsigned)blocks),
@@ -1256,13 +1475,13 @@ static bool launch_tile(const GemmA &a, int64_t M, const nvfp4_tensor *w, float 
             if constexpr (AM == kAmBf16 || AM == kAmNvfp4) {
                 hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, AM, true>), dim3((unsigned)tiles), dim3(64 * WM * WN),
                                    0, stream, (const __bf16 *)a.bf16, lda, a.codes, a.scales, a.g, w->codes,
-                                   w->scales, w->global_scale, c, ldc, M, N, K, (int)(K / kBK), *lr);
+                                   w->scales, w->global_scale, c, ldc, M, N, K, (int)(K / kBK), *lr, QaPre{});
                 return true;
             }
         }
         hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, AM>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0, stream,
                            (const __bf16 *)a.bf16, lda, a.codes, a.scales, a.g, w->codes, w->scales,
-                           w->global_scale, c, ldc, M, N, K, (int)(K / kBK), LrArgs{});
+                           w->global_scale, c, ldc, M, N, K, (int)(K / kBK), LrArgs{}, QaPre{});
     } else if constexpr (AM != kAmQuant) {  // the fused quantization runs only where K % 64 == 0
         hipLaunchKernelGGL((k_gemm_tile<BM, BN, WM, WN, AM>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0, stream,
                            (const __bf16 *)a.bf16, lda, a.codes, a.scales, a.g, w->codes, w->scales,
@@ -1278,7 +1497,8 @@ constexpr int first_tile_cfg() { return AM == kAmQuant ? kFirstQuantTileCfg : 0;
 
 template <int AM>
 static bool launch_tiled(const GemmA &a, int64_t M, const nvfp4_tensor *w, float *c, int64_t ldc, void *workspace,
-                         size_t workspace_bytes, int num_cus, hipStream_t stream, const LrArgs *lr = nullptr) {
+                         size_t workspace_bytes, int num_cus, hipStream_t stream, const LrArgs *lr = nullptr,
+                         const QaPre *pre = nullptr) {
     GemmPlan plan = plan_gemm(M, w->rows, w->cols, num_cus, first_tile_cfg<AM>());
     float *partials = nullptr;
     if (plan.splits > 1) {
@@ -1289,12 +1509,12 @@ static bool launch_tiled(const GemmA &a, int64_t M, const nvfp4_tensor *w, float
             plan = GemmPlan{plan.cfg, 1, (int)(w->cols / kBK)};
     }
     if constexpr (first_tile_cfg<AM>() == 0) {
-        if (plan.cfg == 0) return launch_tile<256, 256, 4, 2, AM>(a, M, w, c, ldc, plan, partials, lr, stream);
-        if (plan.cfg == 1) return launch_tile<256, 192, 4, 2, AM>(a, M, w, c, ldc, plan, partials, lr, stream);
+        if (plan.cfg == 0) return launch_tile<256, 256, 4, 2, AM>(a, M, w, c, ldc, plan, partials, lr, stream, pre);
+        if (plan.cfg == 1) return launch_tile<256, 192, 4, 2, AM>(a, M, w, c, ldc, plan, partials, lr, stream, pre);
     }
-    if (plan.cfg == 4) return launch_tile<128, 192, 4, 2, AM>(a, M, w, c, ldc, plan, partials, lr, stream);
-    if (plan.cfg == 2) return launch_tile<128, 256, 2, 4, AM>(a, M, w, c, ldc, plan, partials, lr, stream);
-    return launch_tile<128, 128, 2, 2, AM>(a, M, w, c, ldc, plan, partials, lr, stream);
+    if (plan.cfg == 4) return launch_tile<128, 192, 4, 2, AM>(a, M, w, c, ldc, plan, partials, lr, stream, pre);
+    if (plan.cfg == 2) return launch_tile<128, 256, 2, 4, AM>(a, M, w, c, ldc, plan, partials, lr, stream, pre);
+    return launch_tile<128, 128, 2, 2, AM>(a, M, w, c, ldc, plan, partials, lr, stream, pre);
 }
 
 hipError_t launch_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, int64_t lda, const nvfp4_tensor *w,
@@ -1327,7 +1547,8 @@ hipError_t launch_gemm_lowrank(const void *a_bf16, const nvfp4_tensor *a_q, int6
     const LrArgs lr{reinterpret_cast<const __bf16 *>(ws), reinterpret_cast<const __bf16 *>(u), r};
     bool fused = false;
     if (K == 0) {
-        launch_fill_zero_f32(c, M, N, ldc, stream);
+        e = launch_fill_zero_f32(c, M, N, ldc, stream);
+        if (e != hipSuccess) return e;
     } else if (gemv_applies(M, K)) {
         if (a_q) launch_gemv<kAmNvfp4>(M, GemmA{nullptr, a_q->codes, a_q->scales, a_q->global_scale, K}, w, c, ldc,
                                        num_cus, stream);
@@ -1356,6 +1577,68 @@ hipError_t launch_gemm_qa_fused(const void *a_bf16, const float *amax, int64_t M
                                 hipStream_t stream) {
     const GemmA a{a_bf16, nullptr, nullptr, amax, lda};
     launch_tiled<kAmQuant>(a, M, w, c, ldc, workspace, workspace_bytes, num_cus, stream);
+    return hipGetLastError();
+}
+
+static size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+// Workgroups of the staged kernel of tile configuration `cfg` that one CU holds at once (queried
+// from the runtime for the instantiation itself: registers and LDS decide it).
+template <int BM, int BN, int WM, int WN>
+static int staged_per_cu() {
+    static std::atomic<int> cached{-1};
+    int n = cached.load();
+    if (n < 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gemm_mfma<BM, BN, WM, WN, kAmNvfp4, false, true>,
+                                                         64 * WM * WN, 0) != hipSuccess)
+            n = 0;
+        cached.store(n);
+    }
+    return n;
+}
+
+static int staged_per_cu(int cfg) {
+    switch (cfg) {
+    case 0: return staged_per_cu<256, 256, 4, 2>();
+    case 1: return staged_per_cu<256, 192, 4, 2>();
+    case 2: return staged_per_cu<128, 256, 2, 4>();
+    case 3: return staged_per_cu<128, 128, 2, 2>();
+    default: return staged_per_cu<128, 192, 4, 2>();
+    }
+}
+
+bool gemm_qa_staged_applies(int64_t M, int64_t N, int64_t K, int64_t lda, int num_cus) {
+    if (M <= 0 || N <= 0 || K <= 0 || K % kBK != 0 || gemv_applies(M, K) || num_cus <= 0) return false;
+    const GemmPlan p = plan_gemm(M, N, K, num_cus, 0);
+    const TileCfg &t = kTiles[p.cfg];
+    const int64_t tiles_m = (M + t.bm - 1) / t.bm, tiles = tiles_m * ((N + t.bn - 1) / t.bn);
+    // one round of workgroups on the device (every group co-resident when nothing else runs), and
+    // the group counters fit
+    return tiles * p.splits <= (int64_t)num_cus * staged_per_cu(p.cfg) && tiles_m * p.splits <= kQaMaxGroups &&
+           mfma_fits<kAmNvfp4>(t.bm, t.bn, K, K) && lda >= K;
+}
+
+size_t gemm_qa_staged_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus) {
+    if (M <= 0 || K <= 0) return kQaSyncBytes;
+    return kQaSyncBytes + round256((size_t)M * (size_t)(K / 2)) + round256((size_t)M * (size_t)(K / 16)) +
+           gemm_ws_bytes(M, N, K, num_cus);
+}
+
+hipError_t launch_gemm_qa_staged(const void *a_bf16, const float *amax, int64_t M, int64_t lda, const nvfp4_tensor *w,
+                                 float *c, int64_t ldc, void *workspace, size_t workspace_bytes, int num_cus,
+                                 hipStream_t stream) {
+    const int64_t K = w->cols;
+    uint8_t *ws = reinterpret_cast<uint8_t *>(workspace);
+    const size_t cb = round256((size_t)M * (size_t)(K / 2)), sb = round256((size_t)M * (size_t)(K / 16));
+    // the wait's bound: about a second of polling; NVFP4_QA_SPIN_LIMIT overrides it (tests set it
+    // tiny to run the fallback on every workgroup that finds its group incomplete)
+    const char *env = getenv("NVFP4_QA_SPIN_LIMIT");
+    const uint32_t spin_limit = env ? (uint32_t)strtoul(env, nullptr, 10) : (1u << 22);
+    const QaPre pre{reinterpret_cast<const __bf16 *>(a_bf16), lda, amax, reinterpret_cast<uint32_t *>(ws),
+                    ws + kQaSyncBytes, ws + kQaSyncBytes + cb, spin_limit};
+    const GemmA a{nullptr, pre.codes, pre.scales, amax, K};
+    const size_t head = kQaSyncBytes + cb + sb;
+    launch_tiled<kAmNvfp4>(a, M, w, c, ldc, ws + head, workspace_bytes - head, num_cus, stream, nullptr, &pre);
     return hipGetLastError();
 }
 

@@ -74,6 +74,21 @@ hipError_t launch_gemm_qa_fused(const void *a_bf16, const float *amax, int64_t M
                                 float *c, int64_t ldc, void *workspace, size_t workspace_bytes, int num_cus,
                                 hipStream_t stream);
 
+// The staged one-launch form: every workgroup quantizes a share of its A row block (and K slice)
+// into the workspace and waits for the other workgroups of that row block, then runs the W4A4 main
+// loop on the quantized activations.  The workspace starts with kQaSyncBytes of group counters that
+// must be zero before the first call and that every call leaves zero; the NVFP4 activations
+// ([M][K/2] codes, [M][K/16] scales, each 256-byte aligned) and the split-K planes follow.  Applies
+// when the product's plan runs all its workgroups in one round on the device (every group
+// co-resident) with at most kQaMaxGroups groups; returns false (nothing launched) otherwise.
+constexpr int kQaMaxGroups = 512;
+constexpr size_t kQaSyncBytes = 2 * kQaMaxGroups * 4;
+bool gemm_qa_staged_applies(int64_t M, int64_t N, int64_t K, int64_t lda, int num_cus);
+size_t gemm_qa_staged_ws_bytes(int64_t M, int64_t N, int64_t K, int num_cus);
+hipError_t launch_gemm_qa_staged(const void *a_bf16, const float *amax, int64_t M, int64_t lda, const nvfp4_tensor *w,
+                                 float *c, int64_t ldc, void *workspace, size_t workspace_bytes, int num_cus,
+                                 hipStream_t stream);
+
 size_t percentile_ws_bytes(int64_t cols, int per_channel);
 
 hipError_t launch_percentile(const void *x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld_x, uint32_t k,

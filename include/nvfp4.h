@@ -213,14 +213,26 @@ nvfp4_status nvfp4_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, 
  * heretic-NVFP4", "Quantization Details": NVFP4 activations with a per-tensor amax;
  * "Qwen-Rapid-AIO-NVFP4", "Recommended Model": static per-layer amax from p99.9 calibration; with
  * a static amax the quantization of a tile needs nothing outside the tile).  Values above the amax
- * saturate.  Each workgroup quantizes the A rows of its tile in its staging path (the block scale,
- * the codes and their exact f16 values; see nvfp4_quantize for the steps).
- * The fused kernel runs when K % 64 == 0, M > 4 and N <= 512 (every N tile quantizes its rows of A
- * again, so for wider products a separate quantize pass into the workspace followed by the W4A4
- * kernel is faster and is what runs); otherwise NVFP4_ERR_WORKSPACE if the workspace is NULL or
- * smaller than the quantized activations.
+ * saturate.  One launch in the usual case; three forms, chosen per problem:
+ *   - staged: when all of the W4A4 product's workgroups run in one round on the device (as at
+ *     4096 x 3072 x 3072, 512 x 12288 x 4096 and 512 x 4096 x 12288), the workgroups that share an
+ *     A row block (and K slice) each quantize a share of its 16-element blocks into the workspace,
+ *     wait for one another on a counter in the workspace, then run the W4A4 main loop on them --
+ *     each block is quantized once, and the result is bit-identical to nvfp4_quantize(amax_in =
+ *     a_amax) followed by nvfp4_gemm (W4A4).  Needs the full workspace; its first 4096 bytes are
+ *     the group counters, which must be zero before the first call that uses this workspace and
+ *     which every call leaves zero (allocate it zeroed once and reuse it; calls that share it must
+ *     not overlap).  The wait assumes the product's workgroups can all be resident together (no
+ *     kernel on another stream holding the CUs for long); a workgroup whose wait runs out quantizes
+ *     its whole row block itself, so results never depend on it.
+ *   - fused (K % 64 == 0, M > 4, N <= 512, when staged does not apply): each workgroup quantizes
+ *     the A rows of its tile in its staging path (the block scale, the codes and their exact f16
+ *     values; see nvfp4_quantize for the steps);
+ *   - otherwise a quantize pass into the workspace followed by the W4A4 kernel (NVFP4_ERR_WORKSPACE
+ *     if the workspace is NULL or smaller than the quantized activations).
  * a_amax: device pointer to one float (>= 0; 0 gives C = 0).  Inputs must be finite (no flag).
- * workspace: nvfp4_workspace_size(NVFP4_OP_GEMM_QA, M, N, K) bytes covers either form.
+ * workspace (16-byte aligned): nvfp4_workspace_size(NVFP4_OP_GEMM_QA, M, N, K) bytes covers every
+ * form.
  */
 nvfp4_status nvfp4_gemm_qa(const void *a_bf16, const float *a_amax, int64_t M, int64_t lda, const nvfp4_tensor *w,
                            float *c, int64_t ldc, void *workspace, size_t workspace_bytes, hipStream_t stream);

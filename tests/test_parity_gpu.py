@@ -982,30 +982,89 @@ def test_gemm_lowrank_attention_projection_full(nv):
 # ------------------------------------------------------------------------------------------------
 # W4A4 with the activation quantization inside the GEMM (static amax)
 # ------------------------------------------------------------------------------------------------
-# fused where K % 64 == 0, M > 4 and N <= 512 (128-row tiles, split-K for few tiles); elsewhere
-# (M <= 4, K % 64 != 0, wider N) A is quantized into the workspace first.  The reference quantizes
-# A with the same static amax in the oracle and contracts the exact operands in float64.
+# With its full workspace the call runs the staged form wherever the W4A4 product's workgroups fit
+# in one round (every shape below but M <= 4 and K % 64 != 0, where A is quantized into the
+# workspace first): both are bit-identical to the separate static-amax quantize + W4A4 product.
+# The reference quantizes A with the same static amax in the oracle and contracts the exact
+# operands in float64.
 QA_SHAPES = [(16, 64, 256), (2, 300, 1024), (64, 96, 112), (200, 300, 512), (100, 500, 4096), (2048, 384, 3072),
-             (130, 1000, 128), (100, 1000, 4096), (512, 12288, 4096), (300, 520, 640), (8, 300, 3072)]
+             (130, 1000, 128), (100, 1000, 4096), (512, 12288, 4096), (300, 520, 640), (8, 300, 3072),
+             (512, 4096, 12288), (4096, 3072, 3072)]
+
+
+def _qa_case(nv, m, n, k):
+    q, ref = _rand_q(nv, n, k, seed=m * 11 + n, sigma=0.015)
+    a_bits = synth.bf16_bits(np.random.default_rng(m * 5 + k).standard_normal((m, k)).astype(np.float32))
+    amax = np.float32(0.8 * np.abs(oracle.bf16_bits_to_f64(a_bits)).max())  # static amax below max: clipping
+    return q, ref, a_bits, amax
 
 
 @pytest.mark.parametrize("mnk", QA_SHAPES)
 def test_gemm_qa(nv, mnk):
     m, n, k = mnk
     _note(f"gemm qa (static amax) {mnk}")
-    q, ref = _rand_q(nv, n, k, seed=m * 11 + n, sigma=0.015)
-    a_bits = synth.bf16_bits(np.random.default_rng(m * 5 + k).standard_normal((m, k)).astype(np.float32))
-    amax = np.float32(0.8 * np.abs(oracle.bf16_bits_to_f64(a_bits)).max())  # static amax below max: clipping
-    aref, _ = oracle.quantize(a_bits, oracle.BF16, amax=float(amax))
-    cref = oracle.gemm_w4a4(aref, ref)
+    q, ref, a_bits, amax = _qa_case(nv, m, n, k)
     amax_d = torch.tensor([amax], dtype=torch.float32, device=DEV)
-    c = nv.gemm_qa(to_dev_bf16(a_bits), q, amax_d).cpu().numpy()
-    err = oracle.gemm_error(c, cref)
+    a = to_dev_bf16(a_bits)
+    c = nv.gemm_qa(a, q, amax_d).cpu().numpy()
+    # the separate static-amax quantize and the W4A4 product: the same bits
+    c_two = nv.gemm(_quant(nv, a, amax=amax_d), q).cpu().numpy()
+    assert np.array_equal(c.view(np.uint32), c_two.view(np.uint32))
+    rows = np.arange(m) if m * n * k <= 2 ** 31 else np.random.default_rng(m).choice(m, 128, replace=False)
+    aref, _ = oracle.quantize(a_bits[rows] if len(rows) < m else a_bits, oracle.BF16, amax=float(amax))
+    err = oracle.gemm_error(c[rows], oracle.gemm_w4a4(aref, ref))
     assert err <= GEMM_TOL, err
-    if m > 1:  # strided A and C
+    if m > 1 and len(rows) == m:  # strided A and C
         out = padded(torch.empty((m, n), dtype=torch.float32, device=DEV), 4)
-        nv.gemm_qa(padded(to_dev_bf16(a_bits), 8), q, amax_d, out=out)
-        assert oracle.gemm_error(out.cpu().numpy(), cref) <= GEMM_TOL
+        nv.gemm_qa(padded(a, 8), q, amax_d, out=out)
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), c.view(np.uint32))
+
+
+def _gemm_qa_raw(nv, a, w, amax, out, ws):
+    # the C entry point with an explicit workspace (None: NULL, which leaves the staged form out)
+    import ctypes
+    wct = w.c()
+    st = nv.lib.nvfp4_gemm_qa(a.data_ptr(), amax.data_ptr(), a.shape[0], a.stride(0), ctypes.byref(wct),
+                              out.data_ptr(), out.stride(0), ws.data_ptr() if ws is not None else None,
+                              ws.numel() if ws is not None else 0, nv._stream(a.device))
+    assert st == 0, st
+    return out
+
+
+@pytest.mark.parametrize("mnk", [(200, 300, 512), (2048, 384, 3072), (300, 512, 640), (100, 500, 4096)])
+def test_gemm_qa_fused_form(nv, mnk):
+    # without a workspace (N <= 512, K % 64 == 0) the fused kernel quantizes A in its staging path:
+    # the same operand values, another tile shape and summation order
+    m, n, k = mnk
+    _note(f"gemm qa fused form {mnk}")
+    q, ref, a_bits, amax = _qa_case(nv, m, n, k)
+    amax_d = torch.tensor([amax], dtype=torch.float32, device=DEV)
+    a = to_dev_bf16(a_bits)
+    c = _gemm_qa_raw(nv, a, q, amax_d, torch.empty((m, n), dtype=torch.float32, device=DEV), None)
+    torch.cuda.synchronize()
+    aref, _ = oracle.quantize(a_bits, oracle.BF16, amax=float(amax))
+    assert oracle.gemm_error(c.cpu().numpy(), oracle.gemm_w4a4(aref, ref)) <= GEMM_TOL
+    assert oracle.gemm_error(c.cpu().numpy(), nv.gemm_qa(a, q, amax_d).cpu().numpy()) <= 1e-5
+
+
+def test_gemm_qa_staged_workspace_reuse_and_fallback(nv, monkeypatch):
+    # one zeroed workspace for products of different group structures (row blocks, K slices, N
+    # tiles): each call leaves the group counters zero.  Then with the wait bound at zero polls every
+    # workgroup that finds its group incomplete quantizes its whole region itself: same bits.
+    shapes = [(512, 12288, 4096), (100, 1000, 4096), (2048, 384, 3072), (512, 4096, 12288), (130, 1000, 128)]
+    ws = torch.zeros(max(nv.workspace_size(nv.OP_GEMM_QA, *s) for s in shapes), dtype=torch.uint8, device=DEV)
+    for spin in (None, "0"):
+        if spin is not None:
+            monkeypatch.setenv("NVFP4_QA_SPIN_LIMIT", spin)
+        for m, n, k in shapes:
+            _note(f"gemm qa staged {m}x{n}x{k}, wait bound {spin}")
+            q, _, a_bits, amax = _qa_case(nv, m, n, k)
+            amax_d = torch.tensor([amax], dtype=torch.float32, device=DEV)
+            a = to_dev_bf16(a_bits)
+            c = nv.gemm_qa(a, q, amax_d, workspace=ws)
+            c_two = nv.gemm(_quant(nv, a, amax=amax_d), q)
+            assert torch.equal(c.view(torch.int32), c_two.view(torch.int32)), (m, n, k, spin)
+            assert not ws[:4096].any().item(), "group counters left non-zero"
 
 
 def test_gemm_qa_exact_cases(nv):
