@@ -437,7 +437,7 @@ nvfp4_status amax_percentile(const void *x, nvfp4_dtype x_dtype, int64_t rows, i
     const int64_t n = per_channel ? rows : rows * cols;
     if (n > (int64_t)0xFFFFFFFFll) return NVFP4_ERR_SHAPE;
     if (!aligned4(out_pct) || (out_max && !aligned4(out_max)) || (flags && !aligned4(flags))) return NVFP4_ERR_ALIGN;
-    if (!workspace || workspace_bytes < percentile_ws_bytes(cols, per_channel)) return NVFP4_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < percentile_ws_min_bytes(cols, per_channel)) return NVFP4_ERR_WORKSPACE;
     if (!aligned16(workspace)) return NVFP4_ERR_ALIGN;
     const int cus = current_device_cus();
     if (cus == 0) return NVFP4_ERR_DEVICE;
@@ -446,7 +446,7 @@ nvfp4_status amax_percentile(const void *x, nvfp4_dtype x_dtype, int64_t rows, i
     if (kk < 1.0) kk = 1.0;
     if (kk > (double)n) kk = (double)n;
     hipError_t e = launch_percentile(x, x_dtype, rows, cols, ld_x, (uint32_t)kk, per_channel, out_pct, out_max, flags,
-                                     workspace, cus, stream);
+                                     workspace, workspace_bytes, cus, stream);
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
 }
 

@@ -127,6 +127,14 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return max(max(readlane_u32(v, 0), readlane_u32(v, 16)), max(readlane_u32(v, 32), readlane_u32(v, 48)));
 }
 
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+    v += dpp_u32<kDppXor1>(v);
+    v += dpp_u32<kDppXor2>(v);
+    v += dpp_u32<kDppHalfMirror>(v);
+    v += dpp_u32<kDppMirror>(v);
+    return (readlane_u32(v, 0) + readlane_u32(v, 16)) + (readlane_u32(v, 32) + readlane_u32(v, 48));
+}
+
 __device__ __forceinline__ float wave_sum_f32(float v) {
     v += u2f(dpp_u32<kDppXor1>(f2u(v)));
     v += u2f(dpp_u32<kDppXor2>(f2u(v)));

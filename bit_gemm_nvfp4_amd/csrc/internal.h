@@ -89,11 +89,14 @@ hipError_t launch_gemm_qa_staged(const void *a_bf16, const float *amax, int64_t 
                                  float *c, int64_t ldc, void *workspace, size_t workspace_bytes, int num_cus,
                                  hipStream_t stream);
 
+// Workspace of amax_percentile: the full size (with the candidate lists of the per-channel
+// candidate path), and the least that runs (the radix passes only).
 size_t percentile_ws_bytes(int64_t cols, int per_channel);
+size_t percentile_ws_min_bytes(int64_t cols, int per_channel);
 
 hipError_t launch_percentile(const void *x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld_x, uint32_t k,
                              int per_channel, float *out_pct, float *out_max, int32_t *flags, void *workspace,
-                             int num_cus, hipStream_t stream);
+                             size_t workspace_bytes, int num_cus, hipStream_t stream);
 
 // Matrix statistics: partial sums of at most kStatsMaxGroups workgroups in the workspace.
 constexpr int kStatsMaxGroups = 2048;

@@ -281,8 +281,12 @@ nvfp4_status nvfp4_gemm_fp8a(const uint8_t *a_fp8, const float *a_scale, int64_t
  * instead of max aggregation; "Qwen-Image NVFP4 on a 16 GB Ada GPU", section "Quality: the error
  * of each matrix": percentiles by nearest rank).  The selection is exact on the bit patterns.
  * x_dtype: NVFP4_F32, NVFP4_BF16 or NVFP4_F16.  out_max and flags may be NULL.  workspace of
- * nvfp4_workspace_size(NVFP4_OP_PERCENTILE, rows, cols, per_channel) bytes.  -0 counts as +0.
- * rows must be >= 1.
+ * nvfp4_workspace_size(NVFP4_OP_PERCENTILE, rows, cols, per_channel) bytes; per channel that size
+ * holds candidate lists (8 KB per channel) for ranks 17 .. about 250 from an end over at least
+ * 32768 rows (one pass over x after a threshold from every 16th row; the exact passes only for
+ * channels the candidates cannot settle), and with less, down to 1036 bytes per channel, two or
+ * four radix passes over x run instead: the results are the same.  -0 counts as +0.  rows must be
+ * >= 1.
  */
 nvfp4_status amax_percentile(const void *x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
                              double p, int per_channel, float *out_pct, float *out_max, int32_t *flags,

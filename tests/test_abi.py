@@ -46,7 +46,8 @@ def test_status_strings_and_workspace(nv):
         assert nv.lib.nvfp4_status_string(s)
     assert nv.lib.nvfp4_status_string(99) == b"unknown status"
     assert nv.workspace_size(nv.OP_QUANTIZE, 10, 32) >= 4
-    assert nv.workspace_size(nv.OP_PERCENTILE, 100, 3072, 1) == 3072 * 259 * 4
+    # per channel: the radix state (259 words), the candidate path's 4 words and 2048-key list
+    assert nv.workspace_size(nv.OP_PERCENTILE, 100, 3072, 1) == 3072 * (259 + 4 + 2048) * 4
     assert nv.workspace_size(nv.OP_PERCENTILE, 100, 3072, 0) == 259 * 4
     assert nv.workspace_size(nv.OP_GEMM, 4096, 3072, 3072) == 0
 

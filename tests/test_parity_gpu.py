@@ -544,6 +544,59 @@ def test_percentile_rank_near_ends(nv, dtype, m):
         assert np.array_equal(mx.cpu().numpy(), rm), (m, k)
 
 
+def _pct_input(dtype, x):
+    if dtype == "bf16":
+        src = synth.bf16_bits(x)
+        return src, to_dev_bf16(src), oracle.BF16
+    if dtype == "f16":
+        src = x.astype(np.float16).view(np.uint16)
+        return src, to_dev_f16(src), oracle.F16
+    return x, to_dev_f32(x), oracle.F32
+
+
+# ranks 17 .. about 250 from an end on at least 32768 rows take the candidate path: a threshold
+# from every 16th row, one pass keeping the keys beyond it, the rank selected among them
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("cols", [64, 272])
+def test_percentile_candidate_path(nv, dtype, cols):
+    rows = 40000
+    _note(f"percentile candidate path {dtype} {rows}x{cols}")
+    rng = np.random.default_rng(4000 + cols)
+    x = rng.standard_t(3, size=(rows, cols)).astype(np.float32)
+    x[rng.random(x.shape) < 0.01] = -0.0
+    src, xd, odt = _pct_input(dtype, x)
+    for m in (17, 201, 250):
+        for k in (rows - m + 1, m):  # the m-th largest, then the m-th smallest
+            p = 100.0 * (k - 0.5) / rows
+            pct, mx = nv.amax_percentile(xd, p)
+            rp, rm = oracle.amax_percentile(src, p, dtype=odt)
+            assert np.array_equal(pct.cpu().numpy(), rp), (m, k)
+            assert np.array_equal(mx.cpu().numpy(), rm), (m, k)
+
+
+def test_percentile_candidate_fallbacks(nv, monkeypatch):
+    # channels the candidates cannot settle go through the exact passes: (a) a sample that
+    # overstates the tail (every 16th row, the sampled ones, is 8x larger in channels 0-31), (b)
+    # equal values (every candidate list overflows), (c) a list capacity of one (every channel)
+    rows, cols = 40000, 64
+    _note("percentile candidate fallbacks")
+    rng = np.random.default_rng(77)
+    x = rng.standard_t(3, size=(rows, cols)).astype(np.float32)
+    x[0::16, :32] *= 8.0
+    x[:, 40:48] = 1.5
+    src, xd, odt = _pct_input("bf16", x)
+    for p in (99.5, 0.5):
+        rp, rm = oracle.amax_percentile(src, p, dtype=odt)
+        pct, mx = nv.amax_percentile(xd, p)
+        assert np.array_equal(pct.cpu().numpy(), rp), p
+        assert np.array_equal(mx.cpu().numpy(), rm), p
+        monkeypatch.setenv("NVFP4_PCT_CAND_CAP", "1")
+        pct, mx = nv.amax_percentile(xd, p)
+        monkeypatch.delenv("NVFP4_PCT_CAND_CAP")
+        assert np.array_equal(pct.cpu().numpy(), rp), p
+        assert np.array_equal(mx.cpu().numpy(), rm), p
+
+
 def test_percentile_attention_activations_full(nv):
     # the activations of the attention projection, per-channel p99.9 (the 5th largest of 4096)
     _note("percentile 4096 x 3072 bf16")
