@@ -454,6 +454,33 @@ def _timed(fn, reps, warmup=2):
     return _median_ms(evs)
 
 
+def _graph_ms(fn, reps=5):
+    """Median time (ms) of one replay of fn captured in a HIP graph (fn issues only kernels of this
+    library on the current stream): the same kernels without the eager stream's per-launch gaps.  None
+    if the capture fails (informational)."""
+    import torch
+    try:
+        fn(0)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn(0)
+        g.replay()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        del g
+        return _median_ms(evs)
+    except Exception:  # capture is informational: report nothing rather than fail the run
+        return None
+
+
 def _rate(amount, ms, unit):
     r = amount / (ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
     peak = HBM_PEAK_GBS if unit == "GB/s" else BF16_MFMA_PEAK_TFLOPS
@@ -490,6 +517,7 @@ def bench_configs(nv, dev, reps, warmup):
         for (b, sc), q in zip(fp8, qs):
             nv.quantize(b, src_scale=sc, out=q, workspace=ws, flags=flags)
     rq_ms = _timed(requant_all, max(3, reps // 3), 1)
+    rq_graph_ms = _graph_ms(requant_all)
     a2 = torch.randn((2, C), generator=g, device=dev).to(torch.bfloat16)
     cv = torch.empty((2, R), dtype=torch.float32, device=dev)
 
@@ -497,13 +525,20 @@ def bench_configs(nv, dev, reps, warmup):
         for q in qs:
             nv.gemm(a2, q, out=cv)
     gv_ms = _timed(gemv_all, max(3, reps // 3), 1)
+    gv_graph_ms = _graph_ms(gemv_all)
     n = R * C
+    rq_bytes, gv_bytes = 60 * (n * 1.5625 + 4), 60 * (n * 0.5625 + 2 * C * 2 + 2 * R * 4)
     out["modulation_18432x3072"] = {
         "quantize_fp32": _rate(n * 4.5625 + 4, q_ms, "GB/s"),
-        "requantize_fp8_x60": dict(_rate(60 * (n * 1.5625 + 4), rq_ms, "GB/s"), per_weight_ms=round(rq_ms / 60, 5)),
-        "gemv_m2_x60": dict(_rate(60 * (n * 0.5625 + 2 * C * 2 + 2 * R * 4), gv_ms, "GB/s"),
-                            per_call_ms=round(gv_ms / 60, 5)),
+        "requantize_fp8_x60": dict(_rate(rq_bytes, rq_ms, "GB/s"), per_weight_ms=round(rq_ms / 60, 5)),
+        "gemv_m2_x60": dict(_rate(gv_bytes, gv_ms, "GB/s"), per_call_ms=round(gv_ms / 60, 5)),
     }
+    if rq_graph_ms:
+        out["modulation_18432x3072"]["requantize_fp8_x60_graph"] = dict(
+            _rate(rq_bytes, rq_graph_ms, "GB/s"), note="the 60 calls replayed from a HIP graph")
+    if gv_graph_ms:
+        out["modulation_18432x3072"]["gemv_m2_x60_graph"] = dict(
+            _rate(gv_bytes, gv_graph_ms, "GB/s"), note="the 60 calls replayed from a HIP graph")
     del wmod, fp8, qs, qmod
     torch.cuda.empty_cache()
 
@@ -557,6 +592,11 @@ def bench_configs(nv, dev, reps, warmup):
         "gemm_down": _rate(fl, ms["gemm_down"], "TFLOP/s"),
         "chain": dict(_rate(3 * fl, total, "TFLOP/s"), note="quantize A, gate, up, quantize up output, down"),
     }
+    chain_graph_ms = _graph_ms(lambda _: [chain(j) for j in range(4)])
+    if chain_graph_ms:
+        out["qwen3vl_mlp_m512"]["chain_graph"] = dict(
+            _rate(4 * 3 * fl, chain_graph_ms, "TFLOP/s"), per_chain_ms=round(chain_graph_ms / 4, 5),
+            note="the chain over the four layer copies replayed from a HIP graph")
     del layers, a, qa, cg, cu, qu, cd
     torch.cuda.empty_cache()
 
@@ -586,6 +626,7 @@ def bench_configs(nv, dev, reps, warmup):
                 b, sc = stack[blk][j]
                 nv.quantize(b, src_scale=sc, out=qstack[blk][j], workspace=ws, flags=flags)
     rs_ms = _timed(requant_stack, 3, 1)
+    rs_graph_ms = _graph_ms(requant_stack, 3)
     n_el = 60 * sum(r * c for r, c in shapes)
     del stack
     torch.cuda.empty_cache()
@@ -616,6 +657,9 @@ def bench_configs(nv, dev, reps, warmup):
                                           note="activations quantized under the calibrated amax by the same call"),
         "gemm_w4a16_360": _rate(fl5, g16_ms, "TFLOP/s"),
     }
+    if rs_graph_ms:
+        out["calibration_stack"]["requantize_360_graph"] = dict(
+            _rate(n_el * 1.5625 + 360 * 4, rs_graph_ms, "GB/s"), note="the 360 calls replayed from a HIP graph")
     return out
 
 
