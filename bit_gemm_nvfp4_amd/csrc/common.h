@@ -114,6 +114,8 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within each 8
 constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within each 16
+constexpr int kDppRowRor4 = 0x124;    // lane i takes lane (i - 4) mod 16 of its row of 16
+constexpr int kDppRowRor8 = 0x128;    // lane i takes lane (i - 8) mod 16 of its row of 16
 
 __device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int l) {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, l);

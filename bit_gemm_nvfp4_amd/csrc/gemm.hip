@@ -1168,53 +1168,100 @@ __global__ __launch_bounds__(256) void k_gemv(const __bf16 *__restrict__ A, int6
     }
 }
 
+// Sums over the wave of V per-lane values at once (V a multiple of 4), in about 4.5 instructions per
+// value instead of the 11 of a reduction each: lanes exchange halves of their values with the lane
+// across bit 0, then bit 1 (each step halves the values a lane holds), so lane class c = lane & 3
+// ends up with the quad sums of values c, c + 4, ...; two row rotations finish the rows of 16 lanes
+// and four lane reads the wave.  out[] is the same in every lane.
+template <int V>
+__device__ __forceinline__ void wave_sum_multi(const float (&v)[V], float (&out)[V]) {
+    static_assert(V % 4 == 0, "values in groups of four");
+    const int lane = threadIdx.x & 63;
+    const bool b0 = lane & 1, b1 = lane & 2;
+    float h[V / 2];
+#pragma unroll
+    for (int i = 0; i < V / 2; i++) {
+        const float send = b0 ? v[2 * i] : v[2 * i + 1];
+        const float keep = b0 ? v[2 * i + 1] : v[2 * i];
+        h[i] = keep + u2f(dpp_u32<kDppXor1>(f2u(send)));
+    }
+    float q[V / 4];
+#pragma unroll
+    for (int i = 0; i < V / 4; i++) {
+        const float send = b1 ? h[2 * i] : h[2 * i + 1];
+        const float keep = b1 ? h[2 * i + 1] : h[2 * i];
+        q[i] = keep + u2f(dpp_u32<kDppXor2>(f2u(send)));
+        q[i] += u2f(dpp_u32<kDppRowRor4>(f2u(q[i])));
+        q[i] += u2f(dpp_u32<kDppRowRor8>(f2u(q[i])));
+    }
+    // lane class c holds value 4 i + c in q[i]
+#pragma unroll
+    for (int i = 0; i < V / 4; i++)
+#pragma unroll
+        for (int c = 0; c < 4; c++)
+            out[4 * i + c] = (u2f(readlane_u32(f2u(q[i]), c)) + u2f(readlane_u32(f2u(q[i]), 16 + c))) +
+                             (u2f(readlane_u32(f2u(q[i]), 32 + c)) + u2f(readlane_u32(f2u(q[i]), 48 + c)));
+}
+
 // k_gemv_reg: the same product for K <= 4096 without LDS.  Lane l works on blocks l + 64 u (u < UB) of
 // every row it visits, so it loads those blocks of A (expanded to bf16 for NVFP4 and E4M3
-// activations) into registers once; a wave then streams pairs of W rows, the loads of its next pair
-// issued before the arithmetic of the current one (two register buffers, used alternately).
-template <int MM, int AM, int UB>
+// activations) into registers once; lanes past the last block hold zeros there and add nothing.
+// A wave takes RW rows (n, n + nwaves, ...) and issues the loads of all of them (A's first, then
+// every row's scale bytes, then the rows' codes in order) before any arithmetic, so that with the
+// grid sized to the resident waves the whole of W is requested at once; each row's arithmetic then
+// waits for that row's codes only (the code is straight-line, so the compiler's wait counts follow
+// the order of the loads).  The wave's RW x MM sums are reduced together at the end.  One launch
+// covers at most RW x (launched waves) rows; the host offsets further launches for taller W.
+template <int MM, int AM, int UB, int RW>
 __global__ __launch_bounds__(256) void k_gemv_reg(const __bf16 *__restrict__ A, int64_t lda,
                                                   const uint8_t *__restrict__ a_codes,
                                                   const uint8_t *__restrict__ a_scales, const float *__restrict__ a_g,
                                                   const uint8_t *__restrict__ w_codes,
                                                   const uint8_t *__restrict__ w_scales, const float *__restrict__ w_g,
                                                   float *__restrict__ C, int64_t ldc, int64_t N, int64_t K) {
+    constexpr int V = (RW * MM + 3) / 4 * 4;
     const int lane = threadIdx.x & 63;
     const int64_t nblk = K / 16;
     // wave-uniform indices, so that row addresses are scalar and each lane adds a 32-bit offset
     const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
-    // lanes past the last block use the last block and add nothing
+    // lanes past the last block load the last block (in bounds) and multiply it by zeros of A
     uint32_t blk[UB];
 #pragma unroll
     for (int u = 0; u < UB; u++) {
         const int64_t b = lane + 64 * u;
         blk[u] = (uint32_t)(b < nblk ? b : nblk - 1);
     }
-    struct RowPair {
-        int64_t rows[2];
-        u32x2 cw[2][UB];
-        uint32_t sb[2][UB];
+    u32x2 cw[RW][UB];
+    uint32_t sb[RW][UB];
+    // rows past the end read row N - 1 and store nothing; the loads are unconditional so that the
+    // compiler's wait counts follow this one order of loads
+    const auto row_of = [&](int j) {
+        const int64_t n = wave + j * nwaves;
+        return n < N ? n : N - 1;
     };
-    // the pair of rows a wave takes at position n (the second one is n + nwaves, or n again)
-    auto load_pair = [&](RowPair &p, int64_t n) {
-        p.rows[0] = n;
-        p.rows[1] = (n + nwaves) < N ? (n + nwaves) : n;
+    // the scale bytes of all the wave's rows (small) go before any codes: the compiler widens a
+    // loaded byte wherever it likes, and waiting for these then never waits for codes
+    const __amdgpu_buffer_rsrc_t rs = lr_rsrc(w_scales, N * nblk);
+    const auto load_scales = [&]() {
 #pragma unroll
-        for (int h = 0; h < 2; h++) {
-            const uint8_t *cr = w_codes + p.rows[h] * (K / 2);
-            const uint8_t *sr = w_scales + p.rows[h] * nblk;
+        for (int j = 0; j < RW; j++) {
+            const uint32_t so = (uint32_t)(row_of(j) * nblk);
 #pragma unroll
-            for (int u = 0; u < UB; u++) {
-                p.cw[h][u] = *reinterpret_cast<const u32x2 *>(cr + blk[u] * 8u);
-                p.sb[h][u] = sr[blk[u]];
-            }
+            for (int u = 0; u < UB; u++) sb[j][u] = __builtin_amdgcn_raw_buffer_load_b8(rs, blk[u], so, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
     };
-    RowPair buf[2];
-    if (wave < N) load_pair(buf[0], wave);
-    // A's blocks of this lane, 16 bf16 each
+    const auto load_row = [&](int j) {
+        const uint8_t *cr = w_codes + row_of(j) * (K / 2);
+#pragma unroll
+        for (int u = 0; u < UB; u++) cw[j][u] = *reinterpret_cast<const u32x2 *>(cr + blk[u] * 8u);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // A's blocks of this lane, 16 bf16 each.  A's loads go first (a wave's loads complete in issue
+    // order); NVFP4 and E4M3 activations are expanded once W's first loads are on their way.
     u32x4 av[MM][UB][2];
+    uint32_t as[MM][UB];
 #pragma unroll
     for (int m = 0; m < MM; m++)
 #pragma unroll
@@ -1225,65 +1272,80 @@ __global__ __launch_bounds__(256) void k_gemv_reg(const __bf16 *__restrict__ A, 
                 av[m][u][1] = ap[1];
             } else if constexpr (AM == kAmNvfp4) {
                 const u32x2 c = *reinterpret_cast<const u32x2 *>(a_codes + m * (K / 2) + blk[u] * 8u);
-                const float s = __builtin_amdgcn_cvt_f32_fp8((int)a_scales[m * nblk + blk[u]], 0);
-                av[m][u][0] = expand8(c[0], s);
-                av[m][u][1] = expand8(c[1], s);
+                av[m][u][0][0] = c[0];
+                av[m][u][1][0] = c[1];
+                as[m][u] = a_scales[m * nblk + blk[u]];
             } else {
                 const u32x4 b = *reinterpret_cast<const u32x4 *>(a_codes + m * lda + blk[u] * 16u);
+                av[m][u][0] = b;
+            }
+        }
+    __builtin_amdgcn_sched_barrier(0);
+    load_scales();
+#pragma unroll
+    for (int j = 0; j < RW; j++) load_row(j);
+#pragma unroll
+    for (int m = 0; m < MM; m++)
+#pragma unroll
+        for (int u = 0; u < UB; u++) {
+            if constexpr (AM == kAmNvfp4) {
+                const float s = __builtin_amdgcn_cvt_f32_fp8((int)as[m][u], 0);
+                const uint32_t c0 = av[m][u][0][0], c1 = av[m][u][1][0];
+                av[m][u][0] = expand8(c0, s);
+                av[m][u][1] = expand8(c1, s);
+            } else if constexpr (AM == kAmFp8) {
+                const u32x4 b = av[m][u][0];
                 av[m][u][0] = expand8_fp8_bf16(u32x2{b[0], b[1]});
                 av[m][u][1] = expand8_fp8_bf16(u32x2{b[2], b[3]});
             }
         }
-    const float gw = *w_g;
-    const float ga = AM != kAmBf16 ? *a_g : 1.0f;
-    auto compute = [&](const RowPair &p) {
-        float acc[2][MM];
+    if (nblk < 64 * UB) {  // some lanes hold blocks past the end: their A is zero
 #pragma unroll
-        for (int h = 0; h < 2; h++)
+        for (int u = 0; u < UB; u++)
+            if (lane + 64 * u >= nblk)
 #pragma unroll
-            for (int m = 0; m < MM; m++) acc[h][m] = 0.0f;
+                for (int m = 0; m < MM; m++) av[m][u][0] = av[m][u][1] = u32x4{0u, 0u, 0u, 0u};
+    }
+    float acc[V];
+#pragma unroll
+    for (int t = 0; t < V; t++) acc[t] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < RW; j++) {
 #pragma unroll
         for (int u = 0; u < UB; u++) {
-            const bool live = lane + 64 * u < nblk;
-#pragma unroll
-            for (int h = 0; h < 2; h++) {
-                const float sc = __builtin_amdgcn_cvt_f32_fp8((int)p.sb[h][u], 0);
-                bf16x2 wv[8];
-                fp4_unpack8_bf16x2(p.cw[h][u][0], wv);
-                fp4_unpack8_bf16x2(p.cw[h][u][1], wv + 4);
-#pragma unroll
-                for (int m = 0; m < MM; m++) {
-                    const u32x4 a0 = av[m][u][0], a1 = av[m][u][1];
-                    float part = 0.0f;
-#pragma unroll
-                    for (int q = 0; q < 4; q++) {
-                        part = __builtin_amdgcn_fdot2_f32_bf16(wv[q], as_bf16x2(a0[q]), part, false);
-                        part = __builtin_amdgcn_fdot2_f32_bf16(wv[4 + q], as_bf16x2(a1[q]), part, false);
-                    }
-                    acc[h][m] += live ? part * sc : 0.0f;
-                }
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < 2; h++) {
-            if (h == 1 && p.rows[1] == p.rows[0]) break;
+            const float sc = __builtin_amdgcn_cvt_f32_fp8((int)sb[j][u], 0);
+            bf16x2 wv[8];
+            fp4_unpack8_bf16x2(cw[j][u][0], wv);
+            fp4_unpack8_bf16x2(cw[j][u][1], wv + 4);
 #pragma unroll
             for (int m = 0; m < MM; m++) {
-                float v = wave_sum_f32(acc[h][m]);
-                if (AM != kAmBf16) v = v * ga;
-                if (lane == 0) C[m * ldc + p.rows[h]] = v * gw;
+                const u32x4 a0 = av[m][u][0], a1 = av[m][u][1];
+                float part = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    part = __builtin_amdgcn_fdot2_f32_bf16(wv[q], as_bf16x2(a0[q]), part, false);
+                    part = __builtin_amdgcn_fdot2_f32_bf16(wv[4 + q], as_bf16x2(a1[q]), part, false);
+                }
+                acc[j * MM + m] = __builtin_fmaf(part, sc, acc[j * MM + m]);
             }
         }
-    };
-    // pairs n = wave, wave + 2 nwaves, ...: load the next pair into the other buffer, then compute
-    for (int64_t n = wave; n < N; n += 4 * nwaves) {
-        const int64_t n1 = n + 2 * nwaves;
-        if (n1 < N) load_pair(buf[1], n1);
-        compute(buf[0]);
-        if (n1 >= N) break;
-        const int64_t n2 = n1 + 2 * nwaves;
-        if (n2 < N) load_pair(buf[0], n2);
-        compute(buf[1]);
+    }
+    float tot[V];
+    wave_sum_multi<V>(acc, tot);
+    const float gw = *w_g;
+    const float ga = AM != kAmBf16 ? *a_g : 1.0f;
+    if (lane == 0) {
+#pragma unroll
+        for (int j = 0; j < RW; j++) {
+            const int64_t n = wave + j * nwaves;
+            if (n < N)
+#pragma unroll
+                for (int m = 0; m < MM; m++) {
+                    float v = tot[j * MM + m];
+                    if (AM != kAmBf16) v = v * ga;
+                    C[m * ldc + n] = v * gw;
+                }
+        }
     }
 }
 
@@ -1301,16 +1363,19 @@ struct GemmA {
 
 size_t gemv_lds_bytes(int64_t M, int64_t K) { return (size_t)M * (size_t)K * 2; }
 
+// Rows per wave of the register GEMV for tall W: at 18 432 x 3072 (M = 2) the resident waves then
+// take all of W in one round (6 rows each measured faster than 4 or 8).
+constexpr int kGemvRows = 6;
+
 // Waves per CU of the register GEMV: as many as the registers let stay resident (from the
-// runtime's occupancy calculation, once per instantiation), so that enough rows are in flight to
-// stream W while every wave also has its next pair of rows loading.
-template <int MM, int AM, int UB>
+// runtime's occupancy calculation, once per instantiation).
+template <int MM, int AM, int UB, int RW>
 static int64_t gemv_waves_per_cu() {
     static std::atomic<int> cached{0};
     int n = cached.load(std::memory_order_relaxed);
     if (n == 0) {
         int b = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_gemv_reg<MM, AM, UB>, 256, 0) != hipSuccess || b < 1)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_gemv_reg<MM, AM, UB, RW>, 256, 0) != hipSuccess || b < 1)
             b = 1;
         n = b * 4;
         cached.store(n, std::memory_order_relaxed);
@@ -1324,18 +1389,33 @@ static int64_t gemv_waves_per_cu() {
 // run from M = 6.
 bool gemv_applies(int64_t M, int64_t K) { return M >= 1 && M <= 5 && gemv_lds_bytes(M, K) <= 64 * 1024; }
 
-template <int MM, int AM, int UB>
+// The grid: enough waves that each takes at most RW rows, capped at the resident waves, with the
+// rows spread evenly over the waves.  W taller than RW x (resident waves) rows takes several
+// launches, each on its own band of rows (codes, scales and output columns offset by the band).
+template <int MM, int AM, int UB, int RW>
 static void launch_gemv_reg(const GemmA &a, const nvfp4_tensor *w, float *c, int64_t ldc, int num_cus,
                             hipStream_t stream) {
     const int64_t N = w->rows, K = w->cols;
-    // two rows per wave and pass, at most the resident waves; the passes spread evenly
-    const int64_t pairs = (N + 1) / 2;
-    const int64_t max_waves = (int64_t)num_cus * gemv_waves_per_cu<MM, AM, UB>();
-    const int64_t passes = (pairs + max_waves - 1) / max_waves;
-    int64_t grid = ((pairs + passes - 1) / passes + 3) / 4;
-    if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((k_gemv_reg<MM, AM, UB>), dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16 *)a.bf16,
-                       a.lda, a.codes, a.scales, a.g, w->codes, w->scales, w->global_scale, c, ldc, N, K);
+    const int64_t max_waves = (int64_t)num_cus * gemv_waves_per_cu<MM, AM, UB, RW>();
+    const int64_t band = max_waves * RW;
+    for (int64_t r0 = 0; r0 < N; r0 += band) {
+        const int64_t rows = N - r0 < band ? N - r0 : band;
+        const int64_t waves = (rows + RW - 1) / RW;
+        const int64_t grid = (waves + 3) / 4;
+        hipLaunchKernelGGL((k_gemv_reg<MM, AM, UB, RW>), dim3((unsigned)grid), dim3(256), 0, stream,
+                           (const __bf16 *)a.bf16, a.lda, a.codes, a.scales, a.g, w->codes + r0 * (K / 2),
+                           w->scales + r0 * (K / 16), w->global_scale, c + r0, ldc, rows, K);
+    }
+}
+
+// Rows per wave: 2 while the resident waves cover W two rows each, else kGemvRows.
+template <int MM, int AM, int UB>
+static void launch_gemv_rows(const GemmA &a, const nvfp4_tensor *w, float *c, int64_t ldc, int num_cus,
+                             hipStream_t stream) {
+    const int64_t N = w->rows;
+    if (N <= 2 * (int64_t)num_cus * gemv_waves_per_cu<MM, AM, UB, 2>())
+        return launch_gemv_reg<MM, AM, UB, 2>(a, w, c, ldc, num_cus, stream);
+    launch_gemv_reg<MM, AM, UB, kGemvRows>(a, w, c, ldc, num_cus, stream);
 }
 
 template <int MM, int AM>
@@ -1344,10 +1424,10 @@ static void launch_gemv_t(const GemmA &a, const nvfp4_tensor *w, float *c, int64
     const int64_t N = w->rows, K = w->cols;
     const int64_t ub = (K / 16 + 63) / 64;  // blocks per lane
     if constexpr (MM <= 4) {  // beyond 4 rows the register form would hold too many blocks of A per lane
-        if (ub <= 1) return launch_gemv_reg<MM, AM, 1>(a, w, c, ldc, num_cus, stream);
-        if (ub <= 2) return launch_gemv_reg<MM, AM, 2>(a, w, c, ldc, num_cus, stream);
-        if (ub <= 3) return launch_gemv_reg<MM, AM, 3>(a, w, c, ldc, num_cus, stream);
-        if (ub <= 4) return launch_gemv_reg<MM, AM, 4>(a, w, c, ldc, num_cus, stream);
+        if (ub <= 1) return launch_gemv_rows<MM, AM, 1>(a, w, c, ldc, num_cus, stream);
+        if (ub <= 2) return launch_gemv_rows<MM, AM, 2>(a, w, c, ldc, num_cus, stream);
+        if (ub <= 3) return launch_gemv_rows<MM, AM, 3>(a, w, c, ldc, num_cus, stream);
+        if (ub <= 4) return launch_gemv_rows<MM, AM, 4>(a, w, c, ldc, num_cus, stream);
     }
     // a wave takes two rows per pass, one pass per wave up to 16 workgroups per CU
     int64_t grid = (N + 7) / 8;
