@@ -146,6 +146,24 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
            (u2f(readlane_u32(f2u(v), 32)) + u2f(readlane_u32(f2u(v), 48)));
 }
 
+// s_waitcnt immediate: wait until at most `vm` vector-memory and `lgkm` LDS operations are pending.
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | ((vm >> 4) << 14); }
+
+// Buffer resource over `bytes` bytes at `base` (raw addressing: offsets in bytes, at most 2^31 - 1 of
+// them in range; a load at an offset past the range returns zeros).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint64_t bytes) {
+    const int n = bytes < 0x7FFFFFFFull ? (int)bytes : 0x7FFFFFFF;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+// An offset past every buffer_rsrc range.
+constexpr uint32_t kOffsetPastRange = 0x80000000u;
+
+// 16 bytes per lane from buffer `r` at (voff + soff) straight into LDS: lane l writes lds + 16 l.
+// The compiler does not see these LDS writes: wait for the load (vmcnt) before reading them.
+__device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
+}
+
 // Pack two fp32 values that are exactly representable in bf16 (the decoded e2m1 x s products)
 // into one dword of two bf16 (first value in the low half): the high halves are the bf16 values.
 __device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {

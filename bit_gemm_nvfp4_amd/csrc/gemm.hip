@@ -149,8 +149,6 @@ __device__ __forceinline__ uint64_t quant16_codes(u32x4 lo, u32x4 hi, float g, f
     return (uint64_t)fp4_pack8(y) | ((uint64_t)fp4_pack8(y + 8) << 32);
 }
 
-// s_waitcnt immediate: wait until at most `vm` vector-memory and `lgkm` LDS operations are pending.
-constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | ((vm >> 4) << 14); }
 
 // Activations quantized once inside the W4A4 product (the staged form of nvfp4_gemm_qa): the bf16
 // rows, the static amax, the workspace arrays the NVFP4 activations go to (those the product then
@@ -586,10 +584,6 @@ struct StepIdx {
 };
 
 
-// 16 bytes per lane from buffer `r` at (voff + soff) straight into LDS: lane l writes lds + 16 l.
-__device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff, uint32_t soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
-}
 
 template <int BM, int BN, int WM, int WN, int AM, bool LR = false, bool PRE = false>
 __global__ __launch_bounds__(64 * WM *WN) void k_gemm_mfma(const __bf16 *__restrict__ A, int64_t lda,

@@ -495,42 +495,85 @@ __global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const flo
 
     // ---- phase 1: load the resident tiles, block maxima (NVFP4), tensor maximum ----
     // Tile s of the wave is tile wave + s * nwaves of the tensor: s < TPW stay in registers,
-    // TPW <= s < TPW + LPW are kept in LDS, the rest is streamed.  The LDS tiles pass through the
-    // register tiles first, in rounds of TPW.
+    // TPW <= s < TPW + LPW are kept in LDS, the rest is streamed.
     TileRegs<SRC> t[TPW];
     uint32_t bm[TPW];
     uint32_t bm_lds[LPW > 0 ? LPW : 1];
     uint32_t m = 0;
     u32x4 *my_lds = lds_tiles + (size_t)wid * (LPW > 0 ? LPW : 0) * VPB * 64;
-#pragma unroll
-    for (int r0 = 0; r0 < LPW; r0 += TPW) {
-#pragma unroll
-        for (int i = 0; i < TPW; i++)
-            if (r0 + i < LPW) tile_load<SRC>(t[i], gm, wave + (TPW + r0 + i) * nwaves, lane);
-#pragma unroll
-        for (int i = 0; i < TPW; i++) {
-            if (r0 + i < LPW) {
-                if constexpr (OUTF == kOutFp8) {
-                    m = max(m, tile_lane_max<SRC>(t[i]));
-                } else {
-                    bm_lds[r0 + i] = tile_block_max<SRC>(t[i], lane);
-                    m = max(m, bm_lds[r0 + i]);
-                }
-#pragma unroll
-                for (int j = 0; j < VPB; j++) my_lds[((r0 + i) * VPB + j) * 64 + lane] = t[i].raw[j];
-            }
-        }
-    }
-#pragma unroll
-    for (int s = 0; s < TPW; s++) tile_load<SRC>(t[s], gm, wave + s * nwaves, lane);
-#pragma unroll
-    for (int s = 0; s < TPW; s++) {
+    const auto resident_max = [&](int s) {
         if constexpr (OUTF == kOutFp8) {
             m = max(m, tile_lane_max<SRC>(t[s]));
         } else {
             bm[s] = tile_block_max<SRC>(t[s], lane);
             m = max(m, bm[s]);
         }
+    };
+    const auto lds_tile_max = [&](int l, const TileRegs<SRC> &x) {
+        if constexpr (OUTF == kOutFp8) {
+            m = max(m, tile_lane_max<SRC>(x));
+        } else {
+            bm_lds[l] = tile_block_max<SRC>(x, lane);
+            m = max(m, bm_lds[l]);
+        }
+    };
+    // (Where the LDS tiles fit in one round through the registers, that round measured faster.)
+    if (gm.contiguous && (LPW == 0 || LPW > TPW)) {
+        // Every load of the phase in flight at once: the LDS tiles go straight into LDS
+        // (direct-to-LDS loads, no pass through registers), then the register tiles.  Vectors past
+        // the end of the tensor read as zeros through the resource's range, so there is no branch.
+        // (The offsets stay below 2^31: the resident tiles are the first (TPW + LPW) x waves tiles.)
+        const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(gm.x, gm.nblocks * VPB * 16);
+        const auto vec_off = [&](uint64_t tile, int j) {
+            const uint32_t vt = j * 64 + lane;
+            const uint64_t blk = tile * 64 + vt / VPB;
+            return blk < gm.nblocks ? (uint32_t)((blk * VPB + vt % VPB) * 16) : kOffsetPastRange;
+        };
+#pragma unroll
+        for (int l = 0; l < LPW; l++)
+#pragma unroll
+            for (int j = 0; j < VPB; j++)
+                load_to_lds16(rx, my_lds + (l * VPB + j) * 64, vec_off(wave + (TPW + l) * nwaves, j), 0);
+#pragma unroll
+        for (int s = 0; s < TPW; s++)
+#pragma unroll
+            for (int j = 0; j < VPB; j++)
+                t[s].raw[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, vec_off(wave + s * nwaves, j), 0, 0));
+        __builtin_amdgcn_sched_barrier(0);  // every load issued before the first maximum waits
+#pragma unroll
+        for (int s = 0; s < TPW; s++) resident_max(s);
+        if constexpr (LPW > 0) {
+            // the wave's own LDS tiles: landed once all its loads have (the compiler does not
+            // see the direct-to-LDS writes, so wait explicitly)
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+#pragma unroll
+            for (int l = 0; l < LPW; l++) {
+                TileRegs<SRC> x;
+#pragma unroll
+                for (int j = 0; j < VPB; j++) x.raw[j] = my_lds[(l * VPB + j) * 64 + lane];
+                lds_tile_max(l, x);
+            }
+        }
+    } else {
+        // the LDS tiles pass through the register tiles first, in rounds of TPW
+#pragma unroll
+        for (int r0 = 0; r0 < LPW; r0 += TPW) {
+#pragma unroll
+            for (int i = 0; i < TPW; i++)
+                if (r0 + i < LPW) tile_load<SRC>(t[i], gm, wave + (TPW + r0 + i) * nwaves, lane);
+#pragma unroll
+            for (int i = 0; i < TPW; i++) {
+                if (r0 + i < LPW) {
+                    lds_tile_max(r0 + i, t[i]);
+#pragma unroll
+                    for (int j = 0; j < VPB; j++) my_lds[((r0 + i) * VPB + j) * 64 + lane] = t[i].raw[j];
+                }
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < TPW; s++) tile_load<SRC>(t[s], gm, wave + s * nwaves, lane);
+#pragma unroll
+        for (int s = 0; s < TPW; s++) resident_max(s);
     }
     // tiles beyond the resident ones are streamed, PB loads in flight per wave
     for (uint64_t tile = wave + (TPW + LPW) * nwaves; tile < ntiles; tile += PB * nwaves) {
