@@ -1343,6 +1343,182 @@ __global__ __launch_bounds__(256) void k_gemv_reg(const __bf16 *__restrict__ A, 
     }
 }
 
+// k_gemv_mfma: the same product for up to 16 rows of A on the matrix cores.  The W rows are the
+// 16-row operand of v_mfma_f32_16x16x32_bf16 and the rows of A (expanded exactly to bf16) the
+// 16-column operand, so one instruction covers 16 W rows x 32 K whatever M is.  Four waves take 16
+// W rows (a row group) at a time; they take the 128-element K chunks c = wave, wave + 4, ...:
+// lane l loads 32 codes (16 bytes) of row l % 16 at K offset 32 (l / 16) of each chunk and the two
+// scale bytes of those two blocks, and expands them with their block scales into the operands of
+// four instructions.  A sits in LDS once per workgroup, with one more row of zeros that the lanes
+// past row M read.  The four waves' 16 x 16 tiles are added in a fixed order through LDS.
+// Workgroups loop over the row groups with the same trip count (the surplus iterations at the end
+// repeat the last row group, from cache, and store nothing), and the loads of the next row group are
+// issued before the arithmetic of the current one, so the code has no branch around a load and the
+// compiler's waits count exactly.  Loads past K or past W read zeros through the buffer ranges.
+constexpr int kGemvFillBatch = 4;  // A units (8 elements) per thread loaded before any is written
+
+template <int AM, int CPW>
+__global__ __launch_bounds__(256) void k_gemv_mfma(const __bf16 *__restrict__ A, int64_t lda,
+                                                   const uint8_t *__restrict__ a_codes,
+                                                   const uint8_t *__restrict__ a_scales, const float *__restrict__ a_g,
+                                                   const uint8_t *__restrict__ w_codes,
+                                                   const uint8_t *__restrict__ w_scales, const float *__restrict__ w_g,
+                                                   float *__restrict__ C, int64_t ldc, int M, int64_t N, int64_t K) {
+    extern __shared__ __align__(16) uint8_t gemv_smem[];
+    __bf16 *act = reinterpret_cast<__bf16 *>(gemv_smem);
+    const int k32 = (int)K;  // K <= 4096: every offset below fits 32 bits
+    const uint32_t kh = (uint32_t)k32 / 2, kb = (uint32_t)k32 / 16;  // code and scale bytes per row
+    const int nch = (k32 + 127) / 128;
+    const int ks = nch * 128 + 8;  // LDS row stride (bf16): 16 bytes past a multiple of 256, so the 16 rows
+                                   // of one read fall in different banks
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // K quarter
+    f32x4 *red = reinterpret_cast<f32x4 *>(gemv_smem + (size_t)(M + 1) * ks * 2);
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int64_t nrg = (N + 15) / 16;
+    const int64_t iters = (nrg + gridDim.x - 1) / gridDim.x;
+
+    // ---- A (rows 0..M-1) as exact bf16 and a row of zeros (row M), 8 elements per unit ----
+    const int upr = nch * 16;  // units per row
+    const int units = (M + 1) * upr;
+    // A through buffer ranges: units past row M - 1, past K or past the last unit read zeros, and
+    // their stores land in the zero row (so neither loads nor stores sit under a branch)
+    const __amdgpu_buffer_rsrc_t ra =
+        AM == kAmBf16  ? buffer_rsrc(A, (uint64_t)((M - 1) * lda + k32) * 2)
+        : AM == kAmFp8 ? buffer_rsrc(a_codes, (uint64_t)((M - 1) * lda + k32))
+                       : buffer_rsrc(a_codes, (uint64_t)M * kh);
+    const __amdgpu_buffer_rsrc_t ras = buffer_rsrc(a_scales, AM == kAmNvfp4 ? (uint64_t)M * kb : 0);
+    const auto fill_load = [&](int u) {
+        const int m = u / upr;
+        const int k8 = (u - m * upr) * 8;
+        const uint32_t past = ((u < units) & (m < M) & (k8 < k32)) ? 0u : kOffsetPastRange;
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if constexpr (AM == kAmBf16) {
+            v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              ra, ((uint32_t)(m * lda + k8) * 2) | past, 0, 0));
+        } else if constexpr (AM == kAmNvfp4) {
+            v[0] = __builtin_amdgcn_raw_buffer_load_b32(ra, (m * kh + k8 / 2) | past, 0, 0);
+            v[1] = __builtin_amdgcn_raw_buffer_load_b8(ras, (m * kb + k8 / 16) | past, 0, 0);
+        } else {
+            const u32x2 b = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_raw_buffer_load_b64(ra, (uint32_t)(m * lda + k8) | past, 0, 0));
+            v[0] = b[0];
+            v[1] = b[1];
+        }
+        return v;
+    };
+    const auto fill_store = [&](int u, u32x4 v) {
+        const int m = u / upr;
+        const int k8 = (u - m * upr) * 8;
+        if constexpr (AM == kAmNvfp4) v = expand8(v[0], __builtin_amdgcn_cvt_f32_fp8((int)v[1], 0));
+        else if constexpr (AM == kAmFp8) v = expand8_fp8_bf16(u32x2{v[0], v[1]});
+        // zeros past K and in row M; units past the last go to row M too (zeros)
+        __bf16 *dst = u < units ? act + m * ks + k8 : act + M * ks + (u % upr) * 8;
+        *reinterpret_cast<u32x4 *>(dst) = v;
+    };
+    u32x4 fv[kGemvFillBatch];
+#pragma unroll
+    for (int b = 0; b < kGemvFillBatch; b++) fv[b] = fill_load(tid + 256 * b);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- the W loads of one row group ----
+    const auto rg_of = [&](int64_t it) {
+        const int64_t rg = (int64_t)blockIdx.x + it * gridDim.x;
+        return rg < nrg ? rg : nrg - 1;
+    };
+    uint32_t sc[CPW];
+    u32x4 q[CPW];
+    const auto load_w = [&](int64_t rg) {
+        const int64_t r0 = rg * 16, nr = N - r0 < 16 ? N - r0 : 16;
+        const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(w_codes + r0 * kh, (uint64_t)nr * kh);
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(w_scales + r0 * kb, (uint64_t)nr * kb);
+        // rows past the end repeat the last and store nothing
+        const uint32_t row = (uint32_t)(r16 < nr ? r16 : (int)nr - 1);
+        // offsets of chunks past K get the bit that puts them past the range (an OR, so that the
+        // compiler does not branch around the offset arithmetic and the load)
+        uint32_t past[CPW];
+#pragma unroll
+        for (int i = 0; i < CPW; i++) {
+            const int c = wv + 4 * i;
+            past[i] = ((c < nch) & (c * 128 + 32 * g4 < k32)) ? 0u : kOffsetPastRange;
+        }
+#pragma unroll
+        for (int i = 0; i < CPW; i++)
+            sc[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, (row * kb + (wv + 4 * i) * 8 + 2 * g4) | past[i], 0, 0);
+#pragma unroll
+        for (int i = 0; i < CPW; i++)
+            q[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rc, (row * kh + (wv + 4 * i) * 64 + 16 * g4) | past[i], 0, 0));
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    load_w(rg_of(0));
+
+    // ---- A into LDS (the first batch was loaded before W; larger A in further batches) ----
+#pragma unroll
+    for (int b = 0; b < kGemvFillBatch; b++) fill_store(tid + 256 * b, fv[b]);
+    for (int base = 256 * kGemvFillBatch; base < units; base += 256 * kGemvFillBatch) {
+#pragma unroll
+        for (int b = 0; b < kGemvFillBatch; b++) fv[b] = fill_load(base + tid + 256 * b);
+#pragma unroll
+        for (int b = 0; b < kGemvFillBatch; b++) fill_store(base + tid + 256 * b, fv[b]);
+    }
+    __syncthreads();
+
+    const float gw = *w_g;
+    const float ga = AM != kAmBf16 ? *a_g : 1.0f;
+    // the A rows this lane reads: its own, or the zero row past M
+    const __bf16 *arow = act + (r16 < M ? r16 : M) * ks + 32 * g4;
+    const auto chunk_of = [&](int i) {
+        const int c = wv + 4 * i;
+        return c < nch ? c : nch - 1;  // chunks past K have zero W
+    };
+    // one row group: per chunk, the four A reads, then the W expansion (which covers their latency),
+    // then the four matrix instructions
+    const auto compute = [&]() {
+        f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < CPW; i++) {
+            bf16x8 av[4];
+#pragma unroll
+            for (int st = 0; st < 4; st++) av[st] = *reinterpret_cast<const bf16x8 *>(arow + chunk_of(i) * 128 + 8 * st);
+            __builtin_amdgcn_sched_barrier(0);
+            const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)sc[i], 0);
+            const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)sc[i], 1);
+            u32x4 w[4];
+#pragma unroll
+            for (int st = 0; st < 4; st++) w[st] = expand8(q[i][st], st < 2 ? s0 : s1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int st = 0; st < 4; st++)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w[st]), av[st], acc, 0, 0, 0);
+        }
+        return acc;
+    };
+    // the waves' tiles, added in a fixed order; lane l holds C[l % 16][r0 + 4 (l / 16) + e]
+    const auto finish = [&](int64_t it, f32x4 acc) {
+        if (wv > 0) red[(wv - 1) * 64 + lane] = acc;
+        __syncthreads();
+        const int64_t rg = (int64_t)blockIdx.x + it * gridDim.x;
+        if (wv == 0 && r16 < M && rg < nrg) {
+            const f32x4 t1 = red[lane], t2 = red[64 + lane], t3 = red[128 + lane];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int64_t n = rg * 16 + 4 * g4 + e;
+                float v = ((acc[e] + t1[e]) + t2[e]) + t3[e];
+                if (AM != kAmBf16) v = v * ga;
+                if (n < N) C[r16 * ldc + n] = v * gw;
+            }
+        }
+        __syncthreads();
+    };
+    // one row group per trip: its loads, then its arithmetic (nothing is pending across the loop)
+    for (int64_t it = 0;; it++) {
+        finish(it, compute());
+        if (it + 1 >= iters) break;
+        load_w(rg_of(it + 1));
+    }
+}
+
 // ------------------------------------------------------------------------------------------------
 // host launchers
 // ------------------------------------------------------------------------------------------------
@@ -1381,7 +1557,21 @@ static int64_t gemv_waves_per_cu() {
 // 16-element block and row of A) outweigh the stream of W: at M = 8 the LDS form measured 19.3 us
 // against 22.5 us tiled at N = K = 3072, but 48.6 against 37.8 us at N = 18432, so the tiled kernels
 // run from M = 6.
-bool gemv_applies(int64_t M, int64_t K) { return M >= 1 && M <= 5 && gemv_lds_bytes(M, K) <= 64 * 1024; }
+// The matrix-core GEMV: up to 16 rows of A, K a multiple of 32 up to 4096 (at most 8 chunks per wave).
+static size_t gemv_mfma_lds_bytes(int64_t M, int64_t K) {
+    return (size_t)(M + 1) * (size_t)(((K + 127) / 128) * 128 + 8) * 2 + 3 * 64 * 16;
+}
+static bool gemv_mfma_fits(int64_t M, int64_t K) {
+    return M >= 1 && M <= 16 && K > 0 && K % 32 == 0 && K <= 4096 && gemv_mfma_lds_bytes(M, K) <= 160 * 1024;
+}
+// From this many rows of A the matrix-core GEMV takes over from the register GEMV (at 18432 x 3072,
+// M = 3 and 4 took 11.1 and 12.9 us in the register form against 14.5 and 14.8 us; M = 5 24.6 in the
+// LDS form against 15.2 us).
+constexpr int kGemvMfmaMinM = 5;
+
+bool gemv_applies(int64_t M, int64_t K) {
+    return (M >= 1 && M <= 5 && gemv_lds_bytes(M, K) <= 64 * 1024) || (M >= kGemvMfmaMinM && gemv_mfma_fits(M, K));
+}
 
 // The grid: enough waves that each takes at most RW rows, capped at the resident waves, with the
 // rows spread evenly over the waves.  W taller than RW x (resident waves) rows takes several
@@ -1432,9 +1622,52 @@ static void launch_gemv_t(const GemmA &a, const nvfp4_tensor *w, float *c, int64
                        ldc, N, K);
 }
 
+// Workgroups of k_gemv_mfma<AM, CPW> per CU with `lds` bytes of LDS (runtime occupancy calculation).
+template <int AM, int CPW>
+static int gemv_mfma_per_cu(size_t lds) {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_gemv_mfma<AM, CPW>, 256, lds) != hipSuccess || b < 1) b = 1;
+    return b;
+}
+
+// The grid: as many workgroups as fit at once, no more than there are row groups, and then evened
+// out so that every workgroup takes the same number of iterations.  (Workgroups of 16 waves taking
+// four row groups at once against one copy of A measured slower: 18.0 against 14.5-15.7 us for
+// M = 3-8 at 18432 x 3072.)
+template <int AM, int CPW>
+static void launch_gemv_mfma_t(int64_t M, const GemmA &a, const nvfp4_tensor *w, float *c, int64_t ldc, int num_cus,
+                               hipStream_t stream) {
+    const int64_t N = w->rows, K = w->cols;
+    const size_t lds = gemv_mfma_lds_bytes(M, K);
+    const int64_t nrg = (N + 15) / 16;
+    int64_t grid = (int64_t)num_cus * gemv_mfma_per_cu<AM, CPW>(lds);
+    if (grid > nrg) grid = nrg;
+    const int64_t iters = (nrg + grid - 1) / grid;
+    grid = (nrg + iters - 1) / iters;
+    hipLaunchKernelGGL((k_gemv_mfma<AM, CPW>), dim3((unsigned)grid), dim3(256), lds, stream, (const __bf16 *)a.bf16,
+                       a.lda, a.codes, a.scales, a.g, w->codes, w->scales, w->global_scale, c, ldc, (int)M, N, K);
+}
+
+template <int AM>
+static void launch_gemv_mfma(int64_t M, const GemmA &a, const nvfp4_tensor *w, float *c, int64_t ldc, int num_cus,
+                             hipStream_t stream) {
+    const int64_t cpw = ((w->cols + 127) / 128 + 3) / 4;  // chunks per wave
+    switch (cpw) {
+    case 1: return launch_gemv_mfma_t<AM, 1>(M, a, w, c, ldc, num_cus, stream);
+    case 2: return launch_gemv_mfma_t<AM, 2>(M, a, w, c, ldc, num_cus, stream);
+    case 3: return launch_gemv_mfma_t<AM, 3>(M, a, w, c, ldc, num_cus, stream);
+    case 4: return launch_gemv_mfma_t<AM, 4>(M, a, w, c, ldc, num_cus, stream);
+    case 5: return launch_gemv_mfma_t<AM, 5>(M, a, w, c, ldc, num_cus, stream);
+    case 6: return launch_gemv_mfma_t<AM, 6>(M, a, w, c, ldc, num_cus, stream);
+    case 7: return launch_gemv_mfma_t<AM, 7>(M, a, w, c, ldc, num_cus, stream);
+    default: return launch_gemv_mfma_t<AM, 8>(M, a, w, c, ldc, num_cus, stream);
+    }
+}
+
 template <int AM>
 static void launch_gemv(int64_t M, const GemmA &a, const nvfp4_tensor *w, float *c, int64_t ldc, int num_cus,
                         hipStream_t stream) {
+    if (M >= kGemvMfmaMinM && gemv_mfma_fits(M, w->cols)) return launch_gemv_mfma<AM>(M, a, w, c, ldc, num_cus, stream);
     switch (M) {
     case 1: launch_gemv_t<1, AM>(a, w, c, ldc, num_cus, stream); break;
     case 2: launch_gemv_t<2, AM>(a, w, c, ldc, num_cus, stream); break;

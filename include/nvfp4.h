@@ -200,6 +200,8 @@ nvfp4_status nvfp4_dequantize(const nvfp4_tensor *in, void *out, nvfp4_dtype out
  * W4A4.  workspace (16-byte aligned, or NULL): with nvfp4_workspace_size(NVFP4_OP_GEMM, M, N, K)
  * bytes, problems with few output tiles and a long K are split along K (fp32 partial sums per
  * slice in the workspace, then summed in slice order); with less, or NULL, the unsplit kernel runs.
+ * Up to 16 rows of A (M <= 5, or M <= 16 with K a multiple of 32 up to 4096) take the GEMV forms,
+ * which stream W once and need no workspace.
  */
 nvfp4_status nvfp4_gemm(const void *a_bf16, const nvfp4_tensor *a_q, int64_t M, int64_t lda,
                         const nvfp4_tensor *w, float *c, int64_t ldc, void *workspace, size_t workspace_bytes,
@@ -264,10 +266,11 @@ nvfp4_status nvfp4_gemm_lowrank(const void *a_bf16, const nvfp4_tensor *a_q, int
  * [M x K] E4M3 bytes (row stride lda bytes, from nvfp4_quantize_fp8) with tensor scale *a_scale,
  * and W an NVFP4 tensor [N x K] ("Qwen3-VL-8B-Instruct-heretic-NVFP4", "Runtime / hardware": FP4
  * weight x dynamically quantized FP8 activation).  Both operands are expanded exactly to f16
- * inside the kernel (e4m3 values and e2m1 x s both fit f16 exactly; bf16 in the M <= 5 GEMV form);
- * products are summed in fp32 and the sum is multiplied by *a_scale and the weight's global scale
- * at the end.  workspace as for nvfp4_gemm (split-K partial sums; NULL runs the unsplit kernel;
- * none needed for M <= 5 with M x K x 2 <= 64 KiB).
+ * inside the kernel (e4m3 values and e2m1 x s both fit f16 exactly; bf16 in the GEMV forms for
+ * M <= 16); products are summed in fp32 and the sum is multiplied by *a_scale and the weight's
+ * global scale at the end.  workspace as for nvfp4_gemm (split-K partial sums; NULL runs the
+ * unsplit kernel; none needed where the GEMV forms run: M <= 5 with M x K x 2 <= 64 KiB, and
+ * M <= 16 with K a multiple of 32 up to 4096).
  */
 nvfp4_status nvfp4_gemm_fp8a(const uint8_t *a_fp8, const float *a_scale, int64_t M, int64_t lda,
                              const nvfp4_tensor *w, float *c, int64_t ldc, void *workspace, size_t workspace_bytes,

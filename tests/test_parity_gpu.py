@@ -327,8 +327,9 @@ def _rand_q(nv, rows, cols, seed, sigma=0.02):
     return q, ref
 
 
-# M <= 4 takes the GEMV kernels: A in registers up to K = 4096 (here 16 .. 4096), A in LDS beyond
-# (6144, 8192); M = 5 the LDS form; M >= 6 the tiled kernels
+# M <= 4 take the register GEMV up to K = 4096 and the LDS form beyond (6144, 8192); 5 <= M <= 16 with
+# K a multiple of 32 up to 4096 the matrix-core GEMV; other M = 5 the LDS GEMV; the rest the tiled
+# kernels
 @pytest.mark.parametrize("mnk", [(16, 64, 256), (1, 64, 128), (2, 100, 48), (3, 33, 4096), (4, 17, 16),
                                  (5, 70, 80), (37, 129, 272), (130, 257, 1024), (256, 128, 64), (300, 200, 3072),
                                  (2, 300, 8192), (4, 129, 6144), (6, 1000, 3072), (7, 65, 4096), (8, 300, 4096),
@@ -810,6 +811,48 @@ def test_gemm_fp8a(nv, mnk):
         out = padded(torch.empty((m, n), dtype=torch.float32, device=DEV), 4)
         nv.gemm(a, q, out=out)
         assert np.array_equal(out.cpu().numpy(), c)
+
+
+# The matrix-core GEMV (5 <= M <= 16, K % 32 == 0, K <= 4096): K ending inside a 128-element chunk
+# (32, 96, 160, 4064), N not a multiple of 16, and the three activation forms
+@pytest.mark.parametrize("form", ["w4a16", "w4a4", "fp8a"])
+@pytest.mark.parametrize("mnk", [(5, 17, 32), (5, 100, 96), (11, 33, 160), (16, 1000, 4064), (16, 37, 3072),
+                                 (7, 250, 4096), (12, 129, 1024)])
+def test_gemv_mfma(nv, form, mnk):
+    m, n, k = mnk
+    _note(f"gemv mfma {form} {mnk}")
+    q, ref = _rand_q(nv, n, k, seed=m * 19 + n + k)
+    x = np.random.default_rng(m * 5 + k).standard_normal((m, k)).astype(np.float32)
+    if form == "w4a16":
+        a_bits = synth.bf16_bits(x)
+        c = nv.gemm(to_dev_bf16(a_bits), q).cpu().numpy()
+        want = oracle.gemm_w4a16(a_bits, ref)
+    elif form == "w4a4":
+        a_bits = synth.bf16_bits(x)
+        aq = _quant(nv, to_dev_bf16(a_bits))
+        aref, _ = oracle.quantize(a_bits, oracle.BF16)
+        _assert_q_equal(aq, aref, "activations")
+        c = nv.gemm(aq, q).cpu().numpy()
+        want = oracle.gemm_w4a4(aref, ref)
+    else:
+        a8 = _quant_fp8(nv, to_dev_f32(x))
+        rb, rs, _ = oracle.quantize_fp8(x)
+        _assert_fp8_equal(a8, rb, rs, "activations")
+        c = nv.gemm(a8, q).cpu().numpy()
+        want = oracle.gemm_w4a8(rb, rs, ref)
+    err = oracle.gemm_error(c, want)
+    assert err <= GEMM_TOL, err
+
+
+# the matrix-core GEMV at the modulation shape (18432 x 3072) with 16 rows of A: every output
+def test_gemv_mfma_modulation_full(nv):
+    n, k, m = 18432, 3072, 16
+    _note("gemv mfma 16 x 18432 x 3072")
+    q, ref = _rand_q(nv, n, k, seed=4242)
+    a_bits = synth.bf16_bits(np.random.default_rng(4243).standard_normal((m, k)).astype(np.float32))
+    c = nv.gemm(to_dev_bf16(a_bits), q).cpu().numpy()
+    err = oracle.gemm_error(c, oracle.gemm_w4a16(a_bits, ref))
+    assert err <= GEMM_TOL, err
 
 
 def test_gemm_fp8a_one_hot_all_bytes(nv):
