@@ -109,6 +109,7 @@ def main():
             out["achievable_peaks"] = achievable_peaks(dev)
         if cpu is not None:
             out["cpu_baseline"] = cpu
+        calibration_copies(args.calibrate_copy_mib, dev)
         print(json.dumps(out), flush=True)
         return
 
@@ -336,14 +337,20 @@ def main():
                 r["frac_of_measured"] = round(r["rate"] / meas, 4)
     if cpu is not None:
         out["cpu_baseline"] = cpu
-    if args.calibrate_copy_mib > 0:
-        n = args.calibrate_copy_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev)
+    calibration_copies(args.calibrate_copy_mib, dev)
+    print(json.dumps(out), flush=True)
+
+
+def calibration_copies(mib, dev):
+    """Three device-to-device copies of `mib` MiB (a plain copy of known size, whose HBM byte counters
+    scale those of the other kernels in a counter run); nothing when mib is 0."""
+    import torch
+    if mib > 0:
+        src = torch.empty(mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-    print(json.dumps(out), flush=True)
 
 
 def measured_traffic(op):
