@@ -165,6 +165,28 @@ def test_requantize_modulation_fp8(nv):
     _assert_q_equal(q, ref, "modulation fp8")
 
 
+@pytest.mark.parametrize("shape", [(64, 256), (1000, 3072), (18432, 3072)])
+def test_requantize_partial_range_fp8(nv, shape):
+    # E4M3 sources whose largest magnitude byte is below 0x7E (448), and an all-zero one: the
+    # kernel's full-range guess of the global scale fails and the agreed scale re-encodes every
+    # resident tile; codes and scales must still equal the oracle's bit for bit
+    _note(f"requantize, partial-range FP8 {shape}")
+    rows, cols = shape
+    x = synth.normal_f32((rows, cols), 0.01, 77)
+    b, sc = synth.fp8_tensorwise(x)
+    mag = b & 0x7F
+    b = np.where(mag > 0x77, (b & 0x80) | 0x77, b).astype(np.uint8)  # largest magnitude byte 0x77 (240)
+    ref, _ = oracle.quantize(b, oracle.E4M3, float(sc))
+    assert (ref.codes != 0).any()
+    q = _quant(nv, to_dev_u8(b), src_scale=torch.tensor([sc], dtype=torch.float32, device=DEV))
+    _assert_q_equal(q, ref, f"partial-range fp8 {shape}")
+    if rows <= 1000:
+        z = np.zeros_like(b)
+        ref0, _ = oracle.quantize(z, oracle.E4M3, float(sc))
+        _assert_q_equal(_quant(nv, to_dev_u8(z), src_scale=torch.tensor([sc], dtype=torch.float32, device=DEV)),
+                        ref0, f"zero fp8 {shape}")
+
+
 def test_quantize_replayed_from_hip_graph(nv):
     # run-time amax quantizes (NVFP4 and FP8) captured once in a HIP graph and replayed on new
     # inputs whose amax differs each time: the replays reuse the kernel arguments, so each call's
