@@ -98,7 +98,7 @@ nvfp4_status check_matrix(const void *p, int64_t rows, int64_t cols, int64_t ld,
     return NVFP4_OK;
 }
 
-// Scratch of nvfp4_quantize_noalloc: the run-time amax agreement's tag word and slots, one array
+// Scratch of nvfp4_quantize_noalloc: the run-time amax agreement's tag records and slots, one array
 // per GPU for the life of the process.  Zero-initialized when the code object loads, which is the
 // state the agreement needs before its first use; each call leaves it consistent for the next.
 // The host sees only a stand-in for this name: kernels get the device address from
