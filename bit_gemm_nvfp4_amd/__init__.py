@@ -25,7 +25,7 @@ NVFP4_F32, NVFP4_BF16, NVFP4_F16, NVFP4_E4M3 = 0, 1, 2, 3
 OP_QUANTIZE, OP_DEQUANTIZE, OP_GEMM, OP_PERCENTILE, OP_STATS, OP_LOWRANK, OP_GEMM_QA, OP_AMAX = 0, 1, 2, 3, 4, 5, 6, 7
 STATUS_NAMES = ["NVFP4_OK", "NVFP4_ERR_NULL", "NVFP4_ERR_SHAPE", "NVFP4_ERR_ALIGN", "NVFP4_ERR_DTYPE",
                 "NVFP4_ERR_WORKSPACE", "NVFP4_ERR_ARG", "NVFP4_ERR_DEVICE", "NVFP4_ERR_LAUNCH"]
-EXPORTED = ["nvfp4_quantize", "nvfp4_quantize_noalloc", "nvfp4_quantize_fp8", "nvfp4_tensor_amax", "nvfp4_dequantize", "nvfp4_gemm",
+EXPORTED = ["nvfp4_quantize", "nvfp4_quantize_batch", "nvfp4_quantize_noalloc", "nvfp4_quantize_fp8", "nvfp4_tensor_amax", "nvfp4_dequantize", "nvfp4_gemm",
             "nvfp4_gemm_fp8a", "nvfp4_matrix_stats", "nvfp4_gemm_lowrank", "nvfp4_gemm_qa", "amax_percentile",
             "nvfp4_workspace_size", "nvfp4_status_string"]
 # bits of the quantize `flags` word
@@ -43,6 +43,7 @@ _PT = ctypes.POINTER(CTensor)
 _SIGNATURES = {
     "nvfp4_quantize": [_P, _I32, _I64, _P, _P, _PT, _P, _P, _SZ, _P],
     "nvfp4_quantize_noalloc": [_P, _I32, _I64, _P, _P, _PT, _P, _P],
+    "nvfp4_quantize_batch": [_I32, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P],
     "nvfp4_quantize_fp8": [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "nvfp4_tensor_amax": [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P],
     "nvfp4_gemm_fp8a": [_P, _P, _I64, _I64, _PT, _P, _I64, _P, _SZ, _P],
@@ -259,6 +260,50 @@ def quantize(x: torch.Tensor, amax: torch.Tensor | None = None, src_scale: torch
     if check:
         check_flags(flags, "nvfp4_quantize")
     return out
+
+
+QUANTIZE_MAX_BATCH = 8
+
+
+def quantize_batch(xs, src_scales=None, outs=None, flags: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None, check: bool = False) -> list:
+    """Quantize up to 8 device tensors of one dtype to NVFP4, each with its own run-time amax, in one
+    launch where they fit on chip together (else one launch each): the results of quantize() on
+    each.  src_scales: None, or one device fp32 [1] tensor (or None) per tensor (E4M3 sources).
+    flags: one int32 word for the whole batch (allocated and zeroed when not given; returned as the
+    `flags` of every output).  workspace: as for quantize()."""
+    xs = list(xs)
+    n = len(xs)
+    assert n <= QUANTIZE_MAX_BATCH, f"at most {QUANTIZE_MAX_BATCH} tensors per batch"
+    if n == 0:
+        return []
+    dev = xs[0].device
+    assert all(x.dtype == xs[0].dtype and x.device == dev for x in xs), "one dtype and device per batch"
+    lds = [_rows(x, f"xs[{i}]") for i, x in enumerate(xs)]
+    if outs is None:
+        outs = [NVFP4Tensor.empty(x.shape[0], x.shape[1], dev) for x in xs]
+    if flags is None:
+        flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = quantize_workspace(dev)
+    cts = (CTensor * n)()
+    for i, (x, o) in enumerate(zip(xs, outs)):
+        cts[i] = o.c()
+        cts[i].rows, cts[i].cols = x.shape
+    xp = (ctypes.c_void_p * n)(*[x.data_ptr() for x in xs])
+    ldp = (ctypes.c_int64 * n)(*lds)
+    scp = None
+    if src_scales is not None:
+        assert len(src_scales) == n
+        scp = (ctypes.c_void_p * n)(*[None if s is None else s.data_ptr() for s in src_scales])
+    st = load_library().nvfp4_quantize_batch(n, xp, _DT[xs[0].dtype], ldp, scp, cts, _ptr(flags), _ptr(workspace),
+                                             workspace.numel(), _stream(dev))
+    _check(st, "nvfp4_quantize_batch")
+    for o in outs:
+        o.flags = flags
+    if check:
+        check_flags(flags, "nvfp4_quantize_batch")
+    return outs
 
 
 def quantize_noalloc(x: torch.Tensor, out: NVFP4Tensor, amax: torch.Tensor | None = None,

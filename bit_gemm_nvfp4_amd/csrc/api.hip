@@ -191,6 +191,39 @@ nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype x_dtype, int64_t ld_x, co
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
 }
 
+nvfp4_status nvfp4_quantize_batch(int count, const void *const *x, nvfp4_dtype x_dtype, const int64_t *ld_x,
+                                  const float *const *src_scale, const nvfp4_tensor *out, int32_t *flags,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (count < 0 || count > kQuantizeMaxBatch) return NVFP4_ERR_ARG;
+    if (count == 0) return NVFP4_OK;
+    if (!x || !ld_x || !out) return NVFP4_ERR_NULL;
+    const int eb = elem_bytes(x_dtype);
+    if (eb == 0) return NVFP4_ERR_DTYPE;
+    for (int i = 0; i < count; i++) {
+        nvfp4_status st = check_qtensor(&out[i]);
+        if (st != NVFP4_OK) return st;
+        st = check_matrix(x[i], out[i].rows, out[i].cols, ld_x[i], eb);
+        if (st != NVFP4_OK) return st;
+        const float *sc = src_scale ? src_scale[i] : nullptr;
+        if (sc && x_dtype != NVFP4_E4M3) return NVFP4_ERR_ARG;
+        if (sc && !aligned4(sc)) return NVFP4_ERR_ALIGN;
+    }
+    if (flags && !aligned4(flags)) return NVFP4_ERR_ALIGN;
+    if (!workspace || workspace_bytes < kQuantizeWsBytes) return NVFP4_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return NVFP4_ERR_ALIGN;
+    const int cus = current_device_cus();
+    if (cus == 0) return NVFP4_ERR_DEVICE;
+    bool batched = false;
+    hipError_t e = launch_quantize_batch(count, x, x_dtype, ld_x, src_scale, out, flags, workspace, cus, stream,
+                                         &batched);
+    // not batched (a tensor too large to stay resident beside the others): one call per tensor,
+    // in order on the stream, sharing the workspace
+    for (int i = 0; e == hipSuccess && !batched && i < count; i++)
+        e = launch_quantize(x[i], x_dtype, ld_x[i], src_scale ? src_scale[i] : nullptr, nullptr, &out[i], flags,
+                            workspace, cus, stream);
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+}
+
 nvfp4_status nvfp4_quantize_noalloc(const void *x, nvfp4_dtype x_dtype, int64_t ld_x, const float *src_scale,
                                     const float *amax_in, const nvfp4_tensor *out, int32_t *flags,
                                     hipStream_t stream) {

@@ -17,6 +17,14 @@ constexpr size_t kQuantizeWsBytes = 16384;
 hipError_t launch_quantize(const void *x, nvfp4_dtype dt, int64_t ld_x, const float *src_scale, const float *amax_in,
                            const nvfp4_tensor *out, int32_t *flags, void *workspace, int num_cus, hipStream_t stream);
 
+// Run-time amax quantizes of up to kQuantizeMaxBatch tensors of one source dtype in one launch of the
+// single-pass kernel, each tensor with its own amax, when every tensor stays resident on chip;
+// otherwise nothing is launched and *batched is false.
+constexpr int kQuantizeMaxBatch = 8;
+hipError_t launch_quantize_batch(int count, const void *const *x, nvfp4_dtype dt, const int64_t *ld_x,
+                                 const float *const *src_scale, const nvfp4_tensor *out, int32_t *flags,
+                                 void *workspace, int num_cus, hipStream_t stream, bool *batched);
+
 // Run-time amax as a pass of its own: *amax_out = max |v| (fp32; E4M3 source: the largest byte's
 // value times *src_scale), from per-workgroup partial maxima in the workspace (kAmaxWsBytes).
 constexpr int kAmaxMaxParts = 2048;

@@ -463,12 +463,15 @@ constexpr int max_grid_for(int num_cus) { return num_cus < kMaxSlots ? num_cus :
 
 constexpr uint32_t kPollLimit = 1u << 22;
 
+// The body of the single-pass kernel for one tensor, worked on by the launch's workgroups lo .. hi - 1
+// (all of them for one tensor; a share of them in a batch).  Every workgroup of the launch takes
+// part in one agreement: it publishes its tensor's partial maximum in its own slot and waits for
+// every slot, and the amax of its tensor is the maximum over the slots lo .. hi - 1.
 template <int SRC, int TPW, int PB, int OUTF, int NWV, int LPW>
-__global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const float *__restrict__ src_scale,
-                                                          uint32_t *__restrict__ ws, int nrec,
-                                                          uint8_t *__restrict__ codes,
-                                                          uint8_t *__restrict__ scales, float *__restrict__ g_out,
-                                                          int32_t *__restrict__ flags) {
+__device__ __forceinline__ void quant_fused_part(const TileGeom &gm, const float *__restrict__ src_scale,
+                                                 uint32_t *__restrict__ ws, int nrec, uint8_t *__restrict__ codes,
+                                                 uint8_t *__restrict__ scales, float *__restrict__ g_out,
+                                                 int32_t *__restrict__ flags, uint32_t lo, uint32_t hi) {
     constexpr int VPB = kVpb<SRC>;
     __shared__ uint32_t red[NWV];
     __shared__ uint32_t amax_bits;
@@ -476,7 +479,7 @@ __global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const flo
     __shared__ u32x4 lds_tiles[LPW > 0 ? NWV * LPW * VPB * 64 : 1];
     const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint64_t ntiles = (gm.nblocks + 63) / 64;
-    const uint64_t wave = (uint64_t)blockIdx.x * NWV + wid, nwaves = (uint64_t)gridDim.x * NWV;
+    const uint64_t wave = (uint64_t)(blockIdx.x - lo) * NWV + wid, nwaves = (uint64_t)(hi - lo) * NWV;
     const float sc = (SRC == NVFP4_E4M3 && src_scale) ? *src_scale : 1.0f;
     uint32_t *records = ws + kHeadWords;
     uint64_t *slots = reinterpret_cast<uint64_t *>(reinterpret_cast<uint8_t *>(ws) + kSlotByteOffset);
@@ -626,8 +629,9 @@ __global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const flo
                 }
 #pragma unroll
                 for (int k = 0; k < 8; k++) {
+                    const uint32_t i = base + (uint32_t)lane + 64u * k;
                     if ((uint32_t)(v[k] >> 32) != epoch) ready = false;
-                    a = max(a, (uint32_t)v[k]);
+                    if (i >= lo && i < hi) a = max(a, (uint32_t)v[k]);
                 }
             }
             if (__all(ready)) {
@@ -651,7 +655,7 @@ __global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const flo
     bool nonfinite = false;
     const float amax = amax_from_bits<SRC>(m, sc, &nonfinite);
     const float g = OUTF == kOutFp8 ? fp8_scale(amax) : amax / 2688.0f;
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (blockIdx.x == lo && threadIdx.x == 0) {
         *g_out = g;
         if (nonfinite && flags) atomicOr(flags, 1);
     }
@@ -717,6 +721,41 @@ __global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const flo
                                         scales, flags, lane);
         }
     }
+}
+
+template <int SRC, int TPW, int PB, int OUTF, int NWV, int LPW>
+__global__ __launch_bounds__(NWV * 64) void k_quant_fused(TileGeom gm, const float *__restrict__ src_scale,
+                                                          uint32_t *__restrict__ ws, int nrec,
+                                                          uint8_t *__restrict__ codes,
+                                                          uint8_t *__restrict__ scales, float *__restrict__ g_out,
+                                                          int32_t *__restrict__ flags) {
+    quant_fused_part<SRC, TPW, PB, OUTF, NWV, LPW>(gm, src_scale, ws, nrec, codes, scales, g_out, flags, 0u,
+                                                   gridDim.x);
+}
+
+// A batch of tensors in one launch: tensor i is worked on by the workgroups part[i].wg_lo ..
+// part[i].wg_hi - 1 (consecutive ranges covering the grid), each with its own amax.
+struct QPart {
+    TileGeom gm;
+    const float *src_scale;
+    uint8_t *codes;
+    uint8_t *scales;
+    float *g_out;
+    uint32_t wg_lo, wg_hi;
+};
+struct QBatch {
+    QPart part[kQuantizeMaxBatch];
+    int n;
+};
+
+template <int SRC, int TPW, int NWV>
+__global__ __launch_bounds__(NWV * 64) void k_quant_fused_batch(QBatch b, uint32_t *__restrict__ ws, int nrec,
+                                                                int32_t *__restrict__ flags) {
+    int i = 0;
+    while (i + 1 < b.n && blockIdx.x >= b.part[i].wg_hi) i++;
+    const QPart &p = b.part[i];
+    quant_fused_part<SRC, TPW, 1, kOutNvfp4, NWV, 0>(p.gm, p.src_scale, ws, nrec, p.codes, p.scales, p.g_out, flags,
+                                                     p.wg_lo, p.wg_hi);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -881,6 +920,124 @@ static hipError_t launch_quantize_t(const void *x, int64_t ld_x, int64_t rows, i
     hipLaunchKernelGGL((k_encode<SRC, OUTF>), dim3(grid_for(ntiles, 4, num_cus * 8)), dim3(256), 0, stream, gm,
                        src_scale, amax_in, out.codes, out.scales, out.scale, flags);
     return hipGetLastError();
+}
+
+// Workgroups of k_quant_fused_batch<SRC, TPW, NWV> one CU holds at once (at least one is assumed).
+template <int SRC, int TPW, int NWV>
+static int batch_per_cu() {
+    static std::atomic<int> cached{0};
+    int n = cached.load(std::memory_order_relaxed);
+    if (n == 0) {
+        int b = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_quant_fused_batch<SRC, TPW, NWV>, NWV * 64, 0) !=
+                hipSuccess ||
+            b < 1)
+            b = 1;
+        n = b;
+        cached.store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// The batch's workgroups are shared out in proportion to the tensors' tiles (at least one each,
+// about 16 tiles per workgroup at least, at most one workgroup per CU), and the tiles per wave
+// that the largest share needs pick the residency; beyond the register residency nothing is
+// launched (the caller then quantizes the tensors one by one).
+template <int SRC>
+static hipError_t launch_quantize_batch_t(int count, const void *const *x, const int64_t *ld_x,
+                                          const float *const *src_scale, const nvfp4_tensor *out,
+                                          int32_t *flags, uint32_t *ws, int num_cus, hipStream_t stream,
+                                          bool *batched) {
+    constexpr int NWV = 16;
+    constexpr int EB = SrcTraits<SRC>::kElemBytes;
+    QBatch b{};
+    b.n = count;
+    uint64_t tiles[kQuantizeMaxBatch], total = 0;
+    for (int i = 0; i < count; i++) {
+        TileGeom &gm = b.part[i].gm;
+        gm.x = (const uint8_t *)x[i];
+        gm.nblocks = (uint64_t)out[i].rows * (uint64_t)(out[i].cols / 16);
+        gm.vpr = (uint32_t)(out[i].cols / 16) * (uint32_t)kVpb<SRC>;
+        gm.ld_bytes = ld_x[i] * EB;
+        gm.contiguous = (ld_x[i] == out[i].cols) ? 1 : 0;
+        b.part[i].src_scale = src_scale ? src_scale[i] : nullptr;
+        b.part[i].codes = out[i].codes;
+        b.part[i].scales = out[i].scales;
+        b.part[i].g_out = out[i].global_scale;
+        tiles[i] = (gm.nblocks + 63) / 64;
+        total += tiles[i];
+    }
+    const uint64_t max_grid = (uint64_t)max_grid_for(num_cus);
+    uint64_t grid = (total + 15) / 16;
+    if (grid > max_grid) grid = max_grid;
+    if (grid < (uint64_t)count) grid = (uint64_t)count;
+    if (grid > max_grid) return hipSuccess;  // more tensors than workgroups: not batched
+    uint64_t share[kQuantizeMaxBatch], used = 0;
+    for (int i = 0; i < count; i++) {
+        share[i] = total ? tiles[i] * grid / total : 1;
+        if (share[i] < 1) share[i] = 1;
+        used += share[i];
+    }
+    while (used > grid) {  // rounding up to one workgroup each can overshoot: trim the largest shares
+        int k = 0;
+        for (int i = 1; i < count; i++)
+            if (share[i] > share[k]) k = i;
+        share[k]--;
+        used--;
+    }
+    while (used < grid) {  // hand the rest to the shares with the most tiles per workgroup
+        int k = 0;
+        for (int i = 1; i < count; i++)
+            if (tiles[i] * share[k] > tiles[k] * share[i]) k = i;
+        share[k]++;
+        used++;
+    }
+    uint64_t tpw = 1;
+    uint32_t lo = 0;
+    for (int i = 0; i < count; i++) {
+        const uint64_t t = (tiles[i] + NWV * share[i] - 1) / (NWV * share[i]);
+        tpw = t > tpw ? t : tpw;
+        b.part[i].wg_lo = lo;
+        lo += (uint32_t)share[i];
+        b.part[i].wg_hi = lo;
+    }
+    constexpr int T = kMaxTpw4<SRC>;
+    if (tpw > (uint64_t)T) return hipSuccess;  // beyond the register residency: not batched
+#define NVFP4_LAUNCH_BATCH(T_)                                                                                   \
+    do {                                                                                                         \
+        if ((uint64_t)batch_per_cu<SRC, (T_), NWV>() * (uint64_t)num_cus < grid) return hipSuccess;             \
+        hipLaunchKernelGGL((k_quant_fused_batch<SRC, (T_), NWV>), dim3((unsigned)grid), dim3(NWV * 64), 0,      \
+                           stream, b, ws, max_grid_for(num_cus), flags);                                       \
+    } while (0)
+    if (tpw <= 1) NVFP4_LAUNCH_BATCH(1);
+    else if (tpw <= 2) NVFP4_LAUNCH_BATCH(2);
+    else if (tpw <= 3) NVFP4_LAUNCH_BATCH(3);
+    else if (tpw <= 4 || T < 5) NVFP4_LAUNCH_BATCH(T < 4 ? T : 4);
+    else if (tpw <= 5 || T < 6) NVFP4_LAUNCH_BATCH(T < 5 ? T : 5);
+    else if (tpw <= 6 || T < 8) NVFP4_LAUNCH_BATCH(T < 6 ? T : 6);
+    else if (tpw <= 8 || T < 12) NVFP4_LAUNCH_BATCH(T < 8 ? T : 8);
+    else NVFP4_LAUNCH_BATCH(T < 12 ? T : 12);
+#undef NVFP4_LAUNCH_BATCH
+    *batched = true;
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_batch(int count, const void *const *x, nvfp4_dtype dt, const int64_t *ld_x,
+                                 const float *const *src_scale, const nvfp4_tensor *out, int32_t *flags,
+                                 void *workspace, int num_cus, hipStream_t stream, bool *batched) {
+    *batched = false;
+    if (count < 1 || count > kQuantizeMaxBatch) return hipSuccess;
+    uint32_t *ws = reinterpret_cast<uint32_t *>(workspace);
+    switch (dt) {
+    case NVFP4_F32:
+        return launch_quantize_batch_t<NVFP4_F32>(count, x, ld_x, src_scale, out, flags, ws, num_cus, stream, batched);
+    case NVFP4_BF16:
+        return launch_quantize_batch_t<NVFP4_BF16>(count, x, ld_x, src_scale, out, flags, ws, num_cus, stream, batched);
+    case NVFP4_F16:
+        return launch_quantize_batch_t<NVFP4_F16>(count, x, ld_x, src_scale, out, flags, ws, num_cus, stream, batched);
+    default:
+        return launch_quantize_batch_t<NVFP4_E4M3>(count, x, ld_x, src_scale, out, flags, ws, num_cus, stream, batched);
+    }
 }
 
 template <int SRC>

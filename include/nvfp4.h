@@ -122,6 +122,23 @@ nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype x_dtype, int64_t ld_x, co
                             size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * nvfp4_quantize_batch -- count (0 .. 8) tensors of one source dtype quantized to NVFP4, each with
+ * its own run-time amax: exactly what count calls of nvfp4_quantize (amax_in NULL) on the same
+ * stream produce, in one launch when the tensors together stay resident on chip (a layer's four
+ * 3072 x 3072 FP8 projection weights do; "Qwen-Rapid-AIO-NVFP4", section "Why This Exists": every
+ * FP8 weight of the model is requantized to NVFP4), else one launch per tensor.  Steps 1-6 of
+ * nvfp4_quantize per tensor.  x[i], ld_x[i], src_scale[i] and out[i] are the arguments of tensor
+ * i's call; the arrays x, ld_x, src_scale and out are host memory (src_scale may be NULL: no source
+ * scale for any tensor; an element may be NULL), the pointers in them device memory.  One flags
+ * word (nullable) collects the bits of every tensor.  The workspace and its preconditions are
+ * those of nvfp4_quantize (the same workspace may serve both); in one launch every workgroup waits
+ * for all the others, as in nvfp4_quantize.  NVFP4_ERR_ARG for count outside 0 .. 8.
+ */
+nvfp4_status nvfp4_quantize_batch(int count, const void *const *x, nvfp4_dtype x_dtype, const int64_t *ld_x,
+                                  const float *const *src_scale, const nvfp4_tensor *out, int32_t *flags,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * nvfp4_quantize_noalloc -- nvfp4_quantize without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc).  Same arguments, steps, results and flags as nvfp4_quantize; the run-time amax

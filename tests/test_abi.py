@@ -24,7 +24,8 @@ def nv():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == sorted(["nvfp4_quantize", "nvfp4_quantize_noalloc", "nvfp4_quantize_fp8",
+    assert _declared_functions() == sorted(["nvfp4_quantize", "nvfp4_quantize_batch", "nvfp4_quantize_noalloc",
+                                            "nvfp4_quantize_fp8",
                                             "nvfp4_tensor_amax",
                                             "nvfp4_dequantize", "nvfp4_gemm",
                                             "nvfp4_gemm_fp8a", "nvfp4_matrix_stats", "nvfp4_gemm_lowrank", "nvfp4_gemm_qa",
@@ -93,6 +94,41 @@ def test_quantize_noalloc_validation(nv):
     assert q(P(FAKE + 4), 0, 32, None, None, ctypes.byref(t), None, None) == 3  # align
     assert q(P(FAKE), 0, 32, P(FAKE), None, ctypes.byref(t), None, None) == 6  # scale without e4m3
     assert q(P(FAKE), 0, 32, None, None, ctypes.byref(t), P(FAKE + 2), None) == 3  # flags align
+
+
+def test_quantize_batch_validation(nv):
+    q = nv.lib.nvfp4_quantize_batch
+    P = ctypes.c_void_p
+    ws = nv.workspace_size(nv.OP_QUANTIZE, 4, 32)
+
+    def arrays(n, xs=None, lds=None, outs=None, scs=None):
+        xa = (ctypes.c_void_p * n)(*(xs or [FAKE] * n))
+        la = (ctypes.c_int64 * n)(*(lds or [32] * n))
+        oa = (nv.CTensor * n)(*(outs or [_qt(nv, 4, 32) for _ in range(n)]))
+        sa = None if scs is None else (ctypes.c_void_p * n)(*scs)
+        return xa, la, oa, sa
+
+    x, ld, o, _ = arrays(2)
+    assert q(0, None, 0, None, None, None, None, P(FAKE), ws, None) == 0  # nothing to do
+    assert q(9, x, 0, ld, None, o, None, P(FAKE), ws, None) == 6  # more than 8 tensors
+    assert q(-1, x, 0, ld, None, o, None, P(FAKE), ws, None) == 6
+    assert q(2, None, 0, ld, None, o, None, P(FAKE), ws, None) == 1  # NULL arrays
+    assert q(2, x, 0, None, None, o, None, P(FAKE), ws, None) == 1
+    assert q(2, x, 0, ld, None, None, None, P(FAKE), ws, None) == 1
+    assert q(2, x, 9, ld, None, o, None, P(FAKE), ws, None) == 4  # dtype
+    x2, ld2, o2, _ = arrays(2, xs=[FAKE, 0])
+    assert q(2, x2, 0, ld2, None, o2, None, P(FAKE), ws, None) == 1  # NULL second tensor
+    x3, ld3, o3, _ = arrays(2, lds=[32, 16])
+    assert q(2, x3, 0, ld3, None, o3, None, P(FAKE), ws, None) == 2  # second ld < cols
+    x4, ld4, o4, _ = arrays(2, outs=[_qt(nv, 4, 32), _qt(nv, 4, 24)])
+    assert q(2, x4, 0, ld4, None, o4, None, P(FAKE), ws, None) == 2  # second cols % 16
+    x5, ld5, o5, sc5 = arrays(2, scs=[None, FAKE])
+    assert q(2, x5, 0, ld5, sc5, o5, None, P(FAKE), ws, None) == 6  # source scale without e4m3
+    x6, ld6, o6, sc6 = arrays(2, scs=[None, FAKE + 2])
+    assert q(2, x6, 3, ld6, sc6, o6, None, P(FAKE), ws, None) == 3  # source scale alignment
+    assert q(2, x, 0, ld, None, o, None, None, 0, None) == 5  # workspace
+    assert q(2, x, 0, ld, None, o, None, P(FAKE), ws - 1, None) == 5
+    assert q(2, x, 0, ld, None, o, P(FAKE + 2), P(FAKE), ws, None) == 3  # flags alignment
 
 
 def test_tensor_amax_validation(nv):
